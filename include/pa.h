@@ -1,0 +1,173 @@
+/*
+ * pa.h - paged KV-cache kernels for one AMD Instinct MI355X (gfx950).
+ *
+ * The method (as the pages describe it):
+ *  - "How PagedAttention Powers vLLM's KV Cache", section "PagedAttention:
+ *    paging, borrowed from the operating system": keys and values live in
+ *    fixed-size blocks of a shared physical pool; each sequence's block table
+ *    maps its logical block j to the physical block holding it.
+ *  - same page, section "The attention kernel has to read scattered blocks":
+ *    decode attention walks the table and gathers K/V block by block.
+ *  - attention-lab "PagedAttention" page, reference entry "How it works" and
+ *    widget "Measure memory use across requests": the attention equation is
+ *    unchanged, softmax(scale * q K^T) V over the logical sequence.
+ *  - same page, reference entry "Shared blocks and copy-on-write": a request
+ *    about to modify a shared block first gets a private copy.
+ *
+ * Conventions for every entry point below:
+ *  - Pointers named *_pool, q, out, block_tables, context_lens, slot_mapping,
+ *    pairs, k_new, v_new, workspace and the table-update arrays are DEVICE
+ *    pointers; `pool` points to a HOST struct.  The caller owns all memory;
+ *    the library allocates no device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL: the default stream).
+ *    Work is enqueued asynchronously on it; no call synchronizes, except that
+ *    with the environment variable PA_DEBUG=1 the device-resident indices are
+ *    copied to the host on `stream` and validated first (synchronizing).
+ *  - Host-visible arguments are validated before anything is launched; a bad
+ *    one returns PA_EINVAL (or PA_EUNSUPPORTED for a valid but unimplemented
+ *    shape) and has no effect.  Device-resident indices (tables, lengths,
+ *    slots, pairs) are trusted unless PA_DEBUG=1.  A failed launch returns
+ *    PA_EHIP.
+ *  - Calls that touch the same buffers must be ordered by the caller (same
+ *    stream or events).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,        /* bad argument; nothing was done                  */
+  PA_ENOMEM = 2,        /* block pool exhausted (block manager only)       */
+  PA_EHIP = 3,          /* a HIP runtime call or kernel launch failed      */
+  PA_EUNSUPPORTED = 4   /* valid arguments, shape not implemented          */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * Pool geometry.  Two separate device buffers hold the pool:
+ *   k_pool: [num_blocks][num_kv_heads][block_size][head_dim]   token-major
+ *   v_pool: [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ * so one (block, kv head) is one contiguous run of block_size*head_dim
+ * elements in each buffer.  V is dim-major so that decode can reduce over
+ * tokens inside each lane (the reduction dimension of P.V).  The pages leave
+ * the physical layout open.
+ */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;    /* tokens per block; decode supports 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* decode supports 64 and 128 */
+  pa_dtype dtype;        /* element type of both pools */
+} pa_pool;
+
+/*
+ * Slot write: store each new token's keys and values in the slot the block
+ * manager gave it ("Dynamic Growth" on the glossary page; "Add pages as the
+ * request grows" on the attention-lab page).
+ *   k_new, v_new: [T][num_kv_heads][head_dim], pool dtype, dense.
+ *   slot_mapping: int64 [T]; slot = block * block_size + offset; a negative
+ *                 slot skips that token.  Slots must be distinct (a repeated
+ *                 slot is a write race) and below num_blocks * block_size.
+ * Every other byte of the pools is left unchanged.  T = 0 is a no-op.
+ */
+pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool,
+                      const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, int32_t T, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (0 when no
+ * sequence can span more than one partition).  partition_tokens as for
+ * pa_decode.  Returns 0 also for invalid arguments; pa_decode reports those.
+ */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 int32_t partition_tokens);
+
+/*
+ * The partition size (tokens) pa_decode uses for these arguments; equal to
+ * partition_tokens when that is non-zero.  0 on invalid arguments.
+ */
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                   int32_t partition_tokens);
+
+/*
+ * Paged decode attention: for every sequence s and query head h, with
+ * g = h / (num_q_heads / num_kv_heads) and L = context_lens[s],
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t,   t in [0, L),
+ * where token t is read from physical block block_tables[s][t / block_size],
+ * slot t % block_size, KV head g.  Accumulation is in fp32.
+ *   q, out:        [num_seqs][num_q_heads][head_dim], pool dtype; out is
+ *                  rounded to nearest even when the dtype is bf16.
+ *   block_tables:  int32 [num_seqs][max_blocks_per_seq], entries in
+ *                  [0, num_blocks); entries at j >= ceil(L / block_size) are
+ *                  never read.
+ *   context_lens:  int32 [num_seqs], 1 <= L <= max_blocks_per_seq*block_size.
+ *   partition_tokens: 0 lets the library choose; otherwise a positive
+ *                  multiple of block_size.  A sequence longer than one
+ *                  partition is processed in pieces whose (max, sum-exp,
+ *                  unnormalised output) partials go to `workspace` and are
+ *                  combined by a second kernel.
+ *   workspace:     device buffer of at least pa_decode_workspace_bytes(...)
+ *                  bytes (may be NULL when that is 0); contents on entry are
+ *                  irrelevant.
+ * Requires num_q_heads % num_kv_heads == 0, block_size 16, head_dim 64 or
+ * 128.  The result does not depend on where blocks sit in the pool, and two
+ * calls with the same inputs give identical bits.
+ */
+pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                    const void* q, int32_t num_seqs, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Copy-on-write block copy ("The bonus contiguous storage can't give you:
+ * sharing" on the vLLM KV-cache page; "Shared blocks and copy-on-write" on
+ * the attention-lab page): for each (src, dst) pair, every KV head and slot
+ * of block src is copied bit for bit to block dst, in both pools.
+ *   pairs: int32 [num_pairs][2] = (src, dst), both in [0, num_blocks).
+ *          Destinations must be distinct and no destination may also be a
+ *          source in the same call (the copies run concurrently).
+ * num_pairs = 0 is a no-op.
+ */
+pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool,
+                        const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/*
+ * Device-side mirror of table growth ("PagedAttention: paging, borrowed from
+ * the operating system": a growing sequence appends an entry to its block
+ * table).  For every i with slot_mapping[i] >= 0:
+ *   block_tables[seq_ids[i] * max_blocks_per_seq + positions[i] / block_size]
+ *       = slot_mapping[i] / block_size,
+ * i.e. the entry covering the token's logical position now names the block
+ * the token was written to (a new block, or a private copy after
+ * copy-on-write).  seq_ids, positions: int32 [T]; slot_mapping: int64 [T].
+ * positions[i] / block_size must be below max_blocks_per_seq.  Tokens of one
+ * sequence that land in one block write the same value.  T = 0 is a no-op.
+ */
+pa_status pa_table_update(int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t block_size, const int32_t* seq_ids,
+                          const int32_t* positions, const int64_t* slot_mapping,
+                          int32_t T, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_str(pa_status status);
+
+/* Library version, e.g. "pagedkv 0.1 gfx950". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,131 @@
+/*
+ * pa_bm.h - host block manager for a paged KV cache (plain C, no GPU).
+ *
+ * What it follows:
+ *  - "How PagedAttention Powers vLLM's KV Cache", section "PagedAttention:
+ *    paging, borrowed from the operating system": a sequence that needs room
+ *    takes a free physical block from a shared pool and appends an entry to
+ *    its block table; a finished sequence's blocks return to the pool; only
+ *    each sequence's last block can be partly empty.
+ *  - same page, section "The bonus contiguous storage can't give you:
+ *    sharing": block tables of several sequences may name one physical block,
+ *    which carries a reference count; before writing into a shared block a
+ *    sequence copies it (copy-on-write); parallel samples reuse the prompt's
+ *    blocks.
+ *  - attention-lab "PagedAttention" page, reference entry "Shared blocks and
+ *    copy-on-write": growing past a full shared block needs only a new block.
+ *  - same page, section "Where it bites" of the vLLM page: a full pool forces
+ *    the engine to preempt; this library reports the condition (PA_ENOMEM)
+ *    and leaves the policy to the caller.
+ *
+ * Deterministic choices (the pages leave them open):
+ *  - The free pool is a stack initialised to [N-1, ..., 1, 0] (so the first
+ *    pop yields block 0) and, when shuffle_seed != 0, shuffled by
+ *    Fisher-Yates driven by SplitMix64(shuffle_seed): for i = N-1 down to 1,
+ *    j = next() % (i + 1), swap a[i], a[j].  Blocks are popped from the top.
+ *  - Freeing a sequence pushes its blocks on the top, last table entry first.
+ *  - Sequence ids are 0, 1, 2, ... in creation order, never reused.
+ *  - A sequence appending into a partly filled tail block whose refcount is
+ *    above 1 takes a new block, reports the pair (old, new) for the caller to
+ *    copy (pa_block_copy) before writing, and drops one reference to the old
+ *    block; the last holder writes in place.
+ *  - Appends are all or nothing: on PA_ENOMEM no state changes.
+ *
+ * All pointers are HOST pointers owned by the caller.  A pa_bm is not
+ * thread-safe; use one per thread or lock around it.
+ */
+#ifndef PA_BM_H_
+#define PA_BM_H_
+
+#include <stdint.h>
+
+#include "pa.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_bm pa_bm;
+
+typedef struct {
+  int64_t num_blocks;
+  int64_t block_size;
+  int64_t free_blocks;      /* blocks on the free stack                      */
+  int64_t used_blocks;      /* blocks with refcount >= 1                     */
+  int64_t shared_blocks;    /* blocks with refcount >= 2                     */
+  int64_t live_seqs;
+  int64_t logical_tokens;   /* sum of live sequences' token counts           */
+  int64_t logical_blocks;   /* sum of live sequences' table lengths          */
+  int64_t stored_tokens;    /* distinct filled slots over used blocks        */
+  int64_t allocated_slots;  /* used_blocks * block_size                      */
+  int64_t cow_copies;       /* copy-on-write pairs emitted so far            */
+  int64_t enomem_events;    /* appends refused for lack of blocks            */
+} pa_bm_stats_t;
+
+/* New manager over blocks [0, num_blocks); NULL on bad sizes or host OOM. */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed);
+void pa_bm_destroy(pa_bm* bm);
+
+/* New empty sequence; its id is written to *seq_id. */
+pa_status pa_bm_add_seq(pa_bm* bm, int32_t* seq_id);
+
+/* New sequence sharing every block (and the token count) of `parent`. */
+pa_status pa_bm_fork(pa_bm* bm, int32_t parent, int32_t* child);
+
+/*
+ * Append n_tokens >= 0 tokens to `seq`.  slots_out[n_tokens] receives each
+ * new token's slot (block * block_size + offset) in order.  If the tail block
+ * was shared and partly filled, cow_pairs_out[0..1] receives (src, dst) and
+ * *n_cow = 1, else *n_cow = 0.  PA_ENOMEM: not enough free blocks; nothing
+ * changed.  PA_EINVAL: unknown or freed sequence, n_tokens < 0, NULL output.
+ */
+pa_status pa_bm_append(pa_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                       int32_t* cow_pairs_out, int32_t* n_cow);
+
+/*
+ * Append to several distinct sequences at once: n_tokens[i] tokens to
+ * seqs[i].  Outputs, concatenated in call order:
+ *   slots_out[sum n]      slot of each new token,
+ *   seq_out[sum n]        its sequence id,
+ *   pos_out[sum n]        its logical position,
+ *   cow_pairs_out[2*k]    (src, dst) of every copy-on-write, *n_cow = k
+ *                         (at most n_seqs pairs).
+ * All or nothing over the whole batch (PA_ENOMEM / PA_EINVAL change nothing;
+ * a repeated sequence id is PA_EINVAL).  seq_out and pos_out may be NULL.
+ */
+pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_tokens,
+                             int32_t n_seqs, int64_t* slots_out, int32_t* seq_out,
+                             int32_t* pos_out, int32_t* cow_pairs_out, int32_t* n_cow);
+
+/* Return every block of `seq` (refcount - 1; pushed when it reaches 0). */
+pa_status pa_bm_free_seq(pa_bm* bm, int32_t seq);
+
+/*
+ * Copy seq's table into out[cap] (as many entries as fit); *n_blocks and
+ * *n_tokens receive the table length and token count (either may be NULL).
+ */
+pa_status pa_bm_block_table(const pa_bm* bm, int32_t seq, int32_t* out, int32_t cap,
+                            int32_t* n_blocks, int32_t* n_tokens);
+
+/*
+ * Dense export for a decode batch: row i of tables_out[n_seqs][width] gets
+ * seqs[i]'s table, entries past its length set to pad_block; lens_out[i] its
+ * token count.  PA_EINVAL if a table is longer than width.
+ */
+pa_status pa_bm_export(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
+                       int32_t* tables_out, int32_t width, int32_t pad_block,
+                       int32_t* lens_out);
+
+/* Refcount of one block (-1 if out of range). */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
+
+/* Copy the free stack, bottom first, into out[cap]; returns its length. */
+int32_t pa_bm_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
+
+pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_BM_H_ */

@@ -1,0 +1,68 @@
+"""Build libpagedkv.so in-tree: HIP kernels and the C-ABI for gfx950 with
+hipcc, the host block manager with gcc.  ``python -m
+paged_kv_cache_335_amd.build`` or :func:`build`."""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libpagedkv.so")
+
+ARCH = "gfx950"
+HIP_SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_cache_ops.hip"]
+C_SOURCES = ["bm.c"]
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+    # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
+
+
+def _hipcc():
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    noisy = [ln for ln in (r.stderr or "").splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln]
+    if verbose and noisy:
+        print("\n".join(noisy), flush=True)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    jobs = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in C_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        jobs.append(["gcc", *GCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,250 @@
+// C-ABI entry points of libpagedkv: argument validation, workspace sizing,
+// partition choice and dispatch to the kernels.  Contract: include/pa.h.
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pa_internal.h"
+
+using pakv::DecodeArgs;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool debug_checks() {
+  const char* v = getenv("PA_DEBUG");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+int elem_bytes(pa_dtype dt) { return dt == PA_BF16 ? 2 : 4; }
+
+bool pool_ok(const pa_pool* p) {
+  return p && p->num_blocks > 0 && p->block_size > 0 && p->num_kv_heads > 0 &&
+         p->head_dim > 0 && (p->dtype == PA_F32 || p->dtype == PA_BF16);
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Copy n device elements to a host vector on `stream` (debug validation only).
+template <typename T>
+bool fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+// Partition size: enough (partition, kv head, sequence) workgroups to cover
+// the chip several times over at the maximum length, between 256 and 4096
+// tokens, a power of two, never longer than the table can address.
+int32_t choose_partition(const pa_pool* pool, int32_t S, int32_t maxB) {
+  const int64_t max_len = (int64_t)maxB * pool->block_size;
+  const int64_t columns = (int64_t)S * pool->num_kv_heads;
+  const int64_t target_wgs = 8192;
+  int64_t want = (max_len * columns + target_wgs - 1) / target_wgs;
+  int64_t P = 256;
+  while (P < want && P < 4096) P *= 2;
+  const int64_t cap = (max_len + pool->block_size - 1) / pool->block_size * pool->block_size;
+  if (P > cap) P = cap;
+  if (P < pool->block_size) P = pool->block_size;
+  return static_cast<int32_t>(P);
+}
+
+pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
+                       int32_t req_partition, int32_t* P_out, int32_t* parts_out,
+                       size_t* ws_out) {
+  if (!pool_ok(pool) || S < 0 || Hq <= 0 || maxB <= 0) return PA_EINVAL;
+  if (Hq % pool->num_kv_heads != 0) return PA_EINVAL;
+  if (req_partition < 0 || (req_partition > 0 && req_partition % pool->block_size != 0))
+    return PA_EINVAL;
+  if ((int64_t)maxB * pool->block_size > INT32_MAX) return PA_EINVAL;
+  const int32_t P = req_partition > 0 ? req_partition : choose_partition(pool, S, maxB);
+  const int64_t max_len = (int64_t)maxB * pool->block_size;
+  const int32_t parts = static_cast<int32_t>((max_len + P - 1) / P);
+  size_t ws = 0;
+  if (parts > 1) {
+    const size_t n = (size_t)S * Hq * parts;
+    ws = 2 * align_up(n * sizeof(float)) + align_up(n * pool->head_dim * sizeof(float));
+  }
+  *P_out = P;
+  *parts_out = parts;
+  *ws_out = ws;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_ENOMEM: return "block pool exhausted";
+    case PA_EHIP: return "HIP runtime error";
+    case PA_EUNSUPPORTED: return "unsupported shape";
+  }
+  return "unknown status";
+}
+
+const char* pa_version(void) { return "pagedkv 0.1 gfx950"; }
+
+pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int64_t* slot_mapping, int32_t T,
+                      void* stream) {
+  if (!pool_ok(pool) || T < 0) return PA_EINVAL;
+  if (T == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_EINVAL;
+  hipStream_t st = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int64_t> s;
+    if (!fetch(s, slot_mapping, (size_t)T, st)) return PA_EHIP;
+    const int64_t nslots = (int64_t)pool->num_blocks * pool->block_size;
+    std::vector<uint8_t> seen((size_t)nslots, 0);
+    for (int64_t x : s) {
+      if (x < 0) continue;
+      if (x >= nslots || seen[(size_t)x]) return PA_EINVAL;
+      seen[(size_t)x] = 1;
+    }
+  }
+  hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
+                                       pool->num_kv_heads, pool->block_size, pool->head_dim,
+                                       elem_bytes(pool->dtype), st);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_blocks_per_seq, int32_t partition_tokens) {
+  int32_t P, parts;
+  size_t ws;
+  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
+                   &parts, &ws) != PA_OK)
+    return 0;
+  return ws;
+}
+
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_blocks_per_seq, int32_t partition_tokens) {
+  int32_t P, parts;
+  size_t ws;
+  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
+                   &parts, &ws) != PA_OK)
+    return 0;
+  return P;
+}
+
+pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                    const void* q, int32_t num_seqs, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int32_t P, parts;
+  size_t ws;
+  pa_status st = decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                              partition_tokens, &P, &parts, &ws);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !block_tables || !context_lens || !out) return PA_EINVAL;
+  if (ws > 0 && (!workspace || workspace_bytes < ws)) return PA_EINVAL;
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return PA_EINVAL;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (pool->block_size != pakv::kBlock) return PA_EUNSUPPORTED;
+  if (pakv::decode_path(pool->dtype, pool->head_dim, group) == pakv::DecodePath::kUnsupported)
+    return PA_EUNSUPPORTED;
+  hipStream_t hs = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> lens, tab;
+    if (!fetch(lens, context_lens, (size_t)num_seqs, hs)) return PA_EHIP;
+    if (!fetch(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, hs)) return PA_EHIP;
+    const int64_t max_len = (int64_t)max_blocks_per_seq * pool->block_size;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 1 || lens[s] > max_len) return PA_EINVAL;
+      const int32_t nb = (lens[s] + pool->block_size - 1) / pool->block_size;
+      for (int32_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= pool->num_blocks) return PA_EINVAL;
+      }
+    }
+  }
+  DecodeArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  if (ws > 0) {
+    const size_t n = (size_t)num_seqs * num_q_heads * parts;
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.part_m = reinterpret_cast<float*>(w);
+    a.part_l = reinterpret_cast<float*>(w + align_up(n * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(w + 2 * align_up(n * sizeof(float)));
+  }
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_tokens = P;
+  a.max_parts = parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, hs);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool, const int32_t* pairs,
+                        int32_t num_pairs, void* stream) {
+  if (!pool_ok(pool) || num_pairs < 0) return PA_EINVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !pairs) return PA_EINVAL;
+  hipStream_t st = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> pr;
+    if (!fetch(pr, pairs, (size_t)num_pairs * 2, st)) return PA_EHIP;
+    std::vector<uint8_t> is_src((size_t)pool->num_blocks, 0), is_dst((size_t)pool->num_blocks, 0);
+    for (int32_t p = 0; p < num_pairs; ++p) {
+      const int32_t s = pr[2 * p], d = pr[2 * p + 1];
+      if (s < 0 || s >= pool->num_blocks || d < 0 || d >= pool->num_blocks || s == d)
+        return PA_EINVAL;
+      if (is_dst[(size_t)d]) return PA_EINVAL;
+      is_dst[(size_t)d] = 1;
+      is_src[(size_t)s] = 1;
+    }
+    for (int32_t b = 0; b < pool->num_blocks; ++b)
+      if (is_src[(size_t)b] && is_dst[(size_t)b]) return PA_EINVAL;
+  }
+  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
+                             elem_bytes(pool->dtype);
+  hipError_t e = pakv::launch_block_copy(k_pool, v_pool, pairs, num_pairs, block_bytes, st);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+pa_status pa_table_update(int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t block_size, const int32_t* seq_ids, const int32_t* positions,
+                          const int64_t* slot_mapping, int32_t T, void* stream) {
+  if (max_blocks_per_seq <= 0 || block_size <= 0 || T < 0) return PA_EINVAL;
+  if (T == 0) return PA_OK;
+  if (!block_tables || !seq_ids || !positions || !slot_mapping) return PA_EINVAL;
+  hipStream_t st = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> sq, ps;
+    std::vector<int64_t> sl;
+    if (!fetch(sq, seq_ids, (size_t)T, st) || !fetch(ps, positions, (size_t)T, st) ||
+        !fetch(sl, slot_mapping, (size_t)T, st))
+      return PA_EHIP;
+    for (int32_t i = 0; i < T; ++i) {
+      if (sl[i] < 0) continue;
+      if (sq[i] < 0 || ps[i] < 0 || ps[i] / block_size >= max_blocks_per_seq) return PA_EINVAL;
+    }
+  }
+  hipError_t e = pakv::launch_table_update(block_tables, max_blocks_per_seq, block_size,
+                                           seq_ids, positions, slot_mapping, T, st);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Cache-maintenance kernels: slot write, copy-on-write block copy and the
+// device-side table update.  All are bitwise data movement.
+//
+//  * Slot write ("Dynamic Growth" on the glossary page; "Add pages as the
+//    request grows" on the attention-lab page): token i's K row for kv head g
+//    goes to k_pool[b][g][r][:], its V row to v_pool[b][g][:][r], with
+//    b = slot / block_size, r = slot % block_size.
+//  * Block copy ("The bonus contiguous storage can't give you: sharing" on
+//    the vLLM KV-cache page; "Shared blocks and copy-on-write" on the
+//    attention-lab page): the whole of block src, every kv head and slot, is
+//    copied to block dst in both pools.
+//  * Table update: the block-table entry covering a written token's logical
+//    position takes the block the token went to.
+#include "pa_internal.h"
+
+namespace pakv {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kThreads = 256;
+
+// One workgroup per new token.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void kv_write_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t block_size,
+    int32_t head_dim) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  const int r = static_cast<int>(slot % block_size);
+  constexpr int ES = sizeof(E);
+  const size_t row_bytes = (size_t)head_dim * ES;
+  const size_t tok_bytes = (size_t)num_kv_heads * row_bytes;
+  const size_t blk_bytes = tok_bytes * block_size;
+  const uint8_t* ksrc = k_new + (size_t)i * tok_bytes;
+  const uint8_t* vsrc = v_new + (size_t)i * tok_bytes;
+  // K: each kv head's row is contiguous at [blk][g][r][:]
+  if (row_bytes % 16 == 0) {
+    const int n16 = static_cast<int>(tok_bytes / 16);
+    const int per_row = static_cast<int>(row_bytes / 16);
+    for (int c = threadIdx.x; c < n16; c += kThreads) {
+      const int g = c / per_row, off = (c % per_row) * 16;
+      uint8_t* dst = k_pool + blk * blk_bytes + ((size_t)g * block_size + r) * row_bytes + off;
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(ksrc + (size_t)c * 16);
+    }
+  } else {
+    const int n = num_kv_heads * head_dim;
+    for (int c = threadIdx.x; c < n; c += kThreads) {
+      const int g = c / head_dim, d = c % head_dim;
+      E* dst = reinterpret_cast<E*>(k_pool + blk * blk_bytes +
+                                    ((size_t)g * block_size + r) * row_bytes) + d;
+      *dst = reinterpret_cast<const E*>(ksrc)[c];
+    }
+  }
+  // V: dim-major, element (g, d) at [blk][g][d][r]
+  const int n = num_kv_heads * head_dim;
+  for (int c = threadIdx.x; c < n; c += kThreads) {
+    const int g = c / head_dim, d = c % head_dim;
+    E* dst = reinterpret_cast<E*>(v_pool + blk * blk_bytes) +
+             ((size_t)g * head_dim + d) * block_size + r;
+    *dst = reinterpret_cast<const E*>(vsrc)[c];
+  }
+}
+
+// grid (num_pairs, 2): y = 0 copies the K block, y = 1 the V block.
+__global__ __launch_bounds__(kThreads) void block_copy16_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const int32_t* __restrict__ pairs, size_t block_bytes) {
+  const int p = blockIdx.x;
+  uint8_t* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const size_t src = (size_t)pairs[2 * p] * block_bytes;
+  const size_t dst = (size_t)pairs[2 * p + 1] * block_bytes;
+  const size_t n16 = block_bytes / 16;
+  for (size_t c = threadIdx.x; c < n16; c += kThreads)
+    *reinterpret_cast<u32x4*>(pool + dst + c * 16) =
+        *reinterpret_cast<const u32x4*>(pool + src + c * 16);
+}
+
+__global__ __launch_bounds__(kThreads) void block_copy_bytes_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const int32_t* __restrict__ pairs, size_t block_bytes) {
+  const int p = blockIdx.x;
+  uint8_t* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const size_t src = (size_t)pairs[2 * p] * block_bytes;
+  const size_t dst = (size_t)pairs[2 * p + 1] * block_bytes;
+  for (size_t c = threadIdx.x; c < block_bytes; c += kThreads) pool[dst + c] = pool[src + c];
+}
+
+__global__ __launch_bounds__(kThreads) void table_update_kernel(
+    int32_t* __restrict__ tables, int32_t max_blocks, int32_t block_size,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
+    const int64_t* __restrict__ slots, int32_t T) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= T) return;
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  tables[(size_t)seq_ids[i] * max_blocks + positions[i] / block_size] =
+      static_cast<int32_t>(slot / block_size);
+}
+
+}  // namespace
+
+hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int64_t* slots, int32_t T, int32_t num_kv_heads,
+                           int32_t block_size, int32_t head_dim, int32_t elem_bytes,
+                           hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  auto kp = static_cast<uint8_t*>(k_pool);
+  auto vp = static_cast<uint8_t*>(v_pool);
+  auto kn = static_cast<const uint8_t*>(k_new);
+  auto vn = static_cast<const uint8_t*>(v_new);
+  if (elem_bytes == 2)
+    kv_write_kernel<uint16_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
+                                                      block_size, head_dim);
+  else
+    kv_write_kernel<uint32_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
+                                                      block_size, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
+                             int32_t num_pairs, size_t block_bytes, hipStream_t st) {
+  if (num_pairs <= 0) return hipSuccess;
+  const dim3 grid(num_pairs, 2);
+  auto kp = static_cast<uint8_t*>(k_pool);
+  auto vp = static_cast<uint8_t*>(v_pool);
+  if (block_bytes % 16 == 0)
+    block_copy16_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, block_bytes);
+  else
+    block_copy_bytes_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_update(int32_t* block_tables, int32_t max_blocks, int32_t block_size,
+                               const int32_t* seq_ids, const int32_t* positions,
+                               const int64_t* slots, int32_t T, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  table_update_kernel<<<(T + kThreads - 1) / kThreads, kThreads, 0, st>>>(
+      block_tables, max_blocks, block_size, seq_ids, positions, slots, T);
+  return hipGetLastError();
+}
+
+}  // namespace pakv

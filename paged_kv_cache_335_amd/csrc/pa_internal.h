@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI layer (pa_api.hip) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pakv {
+
+// Compile-time tuning knobs of the decode kernels; the defaults are the
+// values measured fastest on MI355X.
+#ifndef PA_WAVES
+#define PA_WAVES 4   // waves per decode workgroup
+#endif
+#ifndef PA_NBUF
+#define PA_NBUF 2    // register buffers per wave: blocks in flight = PA_NBUF - 1
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 0  // 1: K/V loads carry the non-temporal hint
+#endif
+
+constexpr int kBlock = 16;       // tokens per block supported by decode
+constexpr int kWaves = PA_WAVES;
+constexpr int kNBuf = PA_NBUF;
+constexpr int kMaxMfmaGroup = 16;
+
+struct DecodeArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;
+  void* out;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_m;   // [S][Hq][max_parts]   running max, log2 units
+  float* part_l;   // [S][Hq][max_parts]   sum of exp2(score - m)
+  float* part_o;   // [S][Hq][max_parts][D] unnormalised output
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t partition_tokens;
+  int32_t max_parts;
+  float scale_log2;  // scale * log2(e): scores are kept in log2 units
+};
+
+// Which decode kernel family handles a shape.
+enum class DecodePath { kUnsupported, kValu, kMfma };
+DecodePath decode_path(pa_dtype dtype, int head_dim, int group);
+
+hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
+                         hipStream_t stream);
+
+hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new,
+                           const void* v_new, const int64_t* slots, int32_t T,
+                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                           int32_t elem_bytes, hipStream_t stream);
+
+hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
+                             int32_t num_pairs, size_t block_bytes, hipStream_t stream);
+
+hipError_t launch_table_update(int32_t* block_tables, int32_t max_blocks,
+                               int32_t block_size, const int32_t* seq_ids,
+                               const int32_t* positions, const int64_t* slots, int32_t T,
+                               hipStream_t stream);
+
+}  // namespace pakv

@@ -1,0 +1,149 @@
+"""One paged KV cache on one GPU, driven step by step.
+
+Glue only: the host block manager (C) decides blocks, slots and copies; one
+packed host-to-device copy per step carries the step's metadata; the HIP
+library applies copies, writes, table growth and decode.  Torch provides the
+device buffers, pinned staging memory and the stream.
+
+A decode step for a batch of live sequences:
+  1. pa_bm_append_batch: one new slot per sequence (new block when the tail
+     is full, copy-on-write pair when the tail is shared and partly filled);
+  2. one async copy of [slots | row ids | positions | lengths] to the device;
+  3. pa_block_copy for copy-on-write pairs (if any);
+  4. pa_table_update: device table rows follow the growth;
+  5. pa_kv_write: the new tokens' K/V go into their slots;
+  6. pa_decode: attention over the grown contexts.
+"""
+import numpy as np
+import torch
+
+from . import (PA_OK, PagedKVError, pa_block_copy, pa_decode, pa_decode_partition_tokens,
+               pa_decode_workspace_bytes, pa_kv_write, pa_table_update)
+from .block_manager import BlockManager
+
+_RING = 8
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks, num_kv_heads, head_dim, max_seqs, table_width,
+                 block_size=16, dtype=torch.bfloat16, shuffle_seed=0, device="cuda"):
+        self.B = block_size
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.max_seqs = max_seqs
+        self.width = table_width
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.bm = BlockManager(num_blocks, block_size, shuffle_seed)
+        self.k_pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
+                                  device=self.device)
+        self.v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype,
+                                  device=self.device)
+        self.tables = torch.zeros((max_seqs, table_width), dtype=torch.int32, device=self.device)
+        # device lengths of the latest step (a view into its staging buffer)
+        self.lens = torch.zeros(max_seqs, dtype=torch.int32, device=self.device)
+        self.host_lens = np.zeros(max_seqs, dtype=np.int32)
+        self.rows = {}          # sequence id -> row of the device table
+        self._ring = None
+        self._ring_events = [None] * _RING
+        self._ring_pos = 0
+        self._ws = None
+
+    # --- sequences ------------------------------------------------------
+    def add_sequence(self) -> int:
+        if len(self.rows) >= self.max_seqs:
+            raise ValueError("table rows exhausted")
+        s = self.bm.add_seq()
+        self.rows[s] = len(self.rows)
+        return s
+
+    def fork(self, parent: int) -> int:
+        st, child = self.bm.fork(parent)
+        if st != PA_OK:
+            raise PagedKVError(st, "pa_bm_fork")
+        if len(self.rows) >= self.max_seqs:
+            raise ValueError("table rows exhausted")
+        r = len(self.rows)
+        self.rows[child] = r
+        self.tables[r].copy_(self.tables[self.rows[parent]])
+        self.host_lens[r] = self.host_lens[self.rows[parent]]
+        self.lens = torch.from_numpy(self.host_lens.copy()).to(self.device)
+        return child
+
+    # --- staging ----------------------------------------------------------
+    def _staging(self, T, S):
+        need = T * 8 + T * 4 * 2 + S * 4 + 64
+        if self._ring is None or self._ring[0][0].numel() < need:
+            self._ring = [(torch.empty(need, dtype=torch.uint8, pin_memory=True),
+                           torch.empty(need, dtype=torch.uint8, device=self.device))
+                          for _ in range(_RING)]
+            self._ring_events = [None] * _RING
+        i = self._ring_pos
+        self._ring_pos = (i + 1) % _RING
+        ev = self._ring_events[i]
+        if ev is not None:
+            ev.synchronize()  # the copy that last used this host buffer has run
+        return i
+
+    def append(self, seqs, n_tokens, k_new, v_new, stream=None):
+        """Append n_tokens[i] tokens to seqs[i]; k_new/v_new [sum n][Hkv][d].
+        Returns the number of copy-on-write pairs applied."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n_tokens = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        st, slots, sq, pos, pairs = self.bm.append_batch(seqs, n_tokens)
+        if st != PA_OK:
+            raise PagedKVError(st, "pa_bm_append_batch")
+        T = len(slots)
+        rows = np.fromiter((self.rows[int(s)] for s in seqs), dtype=np.int32, count=len(seqs))
+        row_of_tok = np.repeat(rows, n_tokens)
+        self.host_lens[rows] += n_tokens
+        S = len(self.rows)
+        i = self._staging(T, S)
+        host, dev = self._ring[i]
+        o_sq = T * 8
+        o_pos = o_sq + T * 4
+        o_len = o_pos + T * 4
+        hv = host.numpy()
+        hv[:o_sq].view(np.int64)[:] = slots
+        hv[o_sq:o_pos].view(np.int32)[:] = row_of_tok
+        hv[o_pos:o_len].view(np.int32)[:] = pos
+        hv[o_len:o_len + S * 4].view(np.int32)[:] = self.host_lens[:S]
+        stream = stream or torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(stream):
+            dev[:o_len + S * 4].copy_(host[:o_len + S * 4], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            self._ring_events[i] = ev
+            d_slots = dev[:o_sq].view(torch.int64)
+            d_rows = dev[o_sq:o_pos].view(torch.int32)
+            d_pos = dev[o_pos:o_len].view(torch.int32)
+            self.lens = dev[o_len:o_len + S * 4].view(torch.int32)
+            if len(pairs):
+                d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device,
+                                                                           non_blocking=False)
+                pa_block_copy(self.k_pool, self.v_pool, d_pairs, stream=stream)
+            pa_table_update(self.tables, self.B, d_rows, d_pos, d_slots, stream=stream)
+            pa_kv_write(self.k_pool, self.v_pool, k_new, v_new, d_slots, stream=stream)
+        return len(pairs)
+
+    # --- decode -------------------------------------------------------------
+    def workspace(self, num_q_heads, partition_tokens=0):
+        S = len(self.rows)
+        need = pa_decode_workspace_bytes(self.k_pool, self.v_pool, S, num_q_heads, self.width,
+                                         partition_tokens)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws if need else None
+
+    def partition_tokens(self, num_q_heads, partition_tokens=0):
+        return pa_decode_partition_tokens(self.k_pool, self.v_pool, len(self.rows), num_q_heads,
+                                          self.width, partition_tokens)
+
+    def decode(self, q, out=None, scale=None, partition_tokens=0, stream=None):
+        """Attention of q [S][Hq][d] (rows in table order) over every live
+        sequence's context."""
+        S = len(self.rows)
+        scale = self.head_dim ** -0.5 if scale is None else scale
+        ws = self.workspace(q.shape[1], partition_tokens)
+        return pa_decode(q, self.k_pool, self.v_pool, self.tables[:S], self.lens[:S], scale,
+                         out=out, partition_tokens=partition_tokens, workspace=ws, stream=stream)
