@@ -48,6 +48,9 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device-to-device copy of this many MiB "
+                         "(a kernel of known traffic, to scale the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -176,6 +179,16 @@ def main():
     # the last step's output again, for the sampled parity check below
     cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
     torch.cuda.synchronize()
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del src, dst
 
     lens_now = cache.host_lens[:S].copy()
     stats = cache.bm.stats()

@@ -1,6 +1,8 @@
 """Build libpagedkv.so in-tree: HIP kernels and the C-ABI for gfx950 with
-hipcc, the host block manager with gcc.  ``python -m
-paged_kv_cache_335_amd.build`` or :func:`build`."""
+hipcc, the host block manager with gcc.  Run as a script
+(``python paged_kv_cache_335_amd/build.py``) or call :func:`build`; it must not
+be imported through the package, whose ``__init__`` loads the built library.
+"""
 import os
 import shutil
 import subprocess
