@@ -111,8 +111,11 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *                  [0, num_blocks); entries at j >= ceil(L / block_size) are
  *                  never read.
  *   context_lens:  int32 [num_seqs], 1 <= L <= max_blocks_per_seq*block_size.
- *   partition_tokens: 0 lets the library choose; otherwise a positive
- *                  multiple of block_size.  A sequence longer than one
+ *   partition_tokens: 0 lets the library choose (256 tokens, doubled while
+ *                  a full-length sequence would span more than 256
+ *                  partitions, at most 4096); otherwise a positive multiple
+ *                  of block_size giving at most 65535 partitions per
+ *                  sequence (else PA_EINVAL).  A sequence longer than one
  *                  partition is processed in pieces whose (max, sum-exp,
  *                  unnormalised output) partials go to `workspace` and are
  *                  combined by a second kernel.

@@ -38,16 +38,16 @@ bool fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
-// Partition size: enough (partition, kv head, sequence) workgroups to cover
-// the chip several times over at the maximum length, between 256 and 4096
-// tokens, a power of two, never longer than the table can address.
-int32_t choose_partition(const pa_pool* pool, int32_t S, int32_t maxB) {
+// Partition size: one wave streams one partition of one (sequence, kv head),
+// so short partitions keep every wave's share of a ragged batch small and the
+// end of the launch short.  256 tokens (16 blocks) unless a sequence at the
+// table's full length would need more than 256 partitions; then doubled (the
+// partials stay a small fraction of the K/V bytes), never beyond 4096 nor
+// beyond what the table can address.
+int32_t choose_partition(const pa_pool* pool, int32_t maxB) {
   const int64_t max_len = (int64_t)maxB * pool->block_size;
-  const int64_t columns = (int64_t)S * pool->num_kv_heads;
-  const int64_t target_wgs = 8192;
-  int64_t want = (max_len * columns + target_wgs - 1) / target_wgs;
   int64_t P = 256;
-  while (P < want && P < 4096) P *= 2;
+  while (P < 4096 && (max_len + P - 1) / P > 256) P *= 2;
   const int64_t cap = (max_len + pool->block_size - 1) / pool->block_size * pool->block_size;
   if (P > cap) P = cap;
   if (P < pool->block_size) P = pool->block_size;
@@ -62,8 +62,9 @@ pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
   if (req_partition < 0 || (req_partition > 0 && req_partition % pool->block_size != 0))
     return PA_EINVAL;
   if ((int64_t)maxB * pool->block_size > INT32_MAX) return PA_EINVAL;
-  const int32_t P = req_partition > 0 ? req_partition : choose_partition(pool, S, maxB);
+  const int32_t P = req_partition > 0 ? req_partition : choose_partition(pool, maxB);
   const int64_t max_len = (int64_t)maxB * pool->block_size;
+  if ((max_len + P - 1) / P > pakv::kMaxParts) return PA_EINVAL;
   const int32_t parts = static_cast<int32_t>((max_len + P - 1) / P);
   size_t ws = 0;
   if (parts > 1) {

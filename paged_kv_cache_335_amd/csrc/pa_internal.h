@@ -13,19 +13,24 @@ namespace pakv {
 // Compile-time tuning knobs of the decode kernels; the defaults are the
 // values measured fastest on MI355X.
 #ifndef PA_WAVES
-#define PA_WAVES 4   // waves per decode workgroup
+#define PA_WAVES 4   // waves per decode workgroup (one kv head each)
 #endif
 #ifndef PA_NBUF
 #define PA_NBUF 2    // register buffers per wave: blocks in flight = PA_NBUF - 1
 #endif
+#ifndef PA_MFMA_MIN_WG
+#define PA_MFMA_MIN_WG 2  // MFMA decode: workgroups per CU the register budget must allow
+#endif
 #ifndef PA_NT_LOADS
-#define PA_NT_LOADS 0  // 1: K/V loads carry the non-temporal hint
+#define PA_NT_LOADS 1  // 1: K/V loads carry the non-temporal hint
 #endif
 
 constexpr int kBlock = 16;       // tokens per block supported by decode
 constexpr int kWaves = PA_WAVES;
 constexpr int kNBuf = PA_NBUF;
 constexpr int kMaxMfmaGroup = 16;
+constexpr int kMaxParts = 65535;  // partitions per sequence
+constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan)
 
 struct DecodeArgs {
   const void* k_pool;

@@ -153,29 +153,55 @@ def test_deterministic_and_placement_invariant(pk):
     assert torch.equal(a, out2)
 
 
-# --- full-size configs, sampled outputs --------------------------------------
+def test_decode_plan_equal_tail_buckets(pk):
+    """Many sequences whose last partitions have the same length (the same
+    bucket of the work plan), over several placement chunks and far more
+    units than workgroups: every output against the oracle, and three calls
+    bit-identical.  A plan that differed between workgroups would skip some
+    units and repeat others."""
+    rng = np.random.default_rng(77)
+    S, P = 600, 64
+    lens = 64 * rng.integers(0, 4, S) + rng.choice([5, 5, 5, 37, 64], S)
+    c = _custom_case(lens, Hq=16, Hkv=4, d=64, nb=40, width=16, seed=78)
+    ref = oracle.decode(*c.oracle_inputs(), c.scale)
+    a = _gpu_decode(pk, c, P).clone()
+    _check(_to64(a), ref, "bf16", "equal tails")
+    for _ in range(2):
+        assert torch.equal(a, _gpu_decode(pk, c, P))
+
+
+def test_decode_batch_beyond_one_launch(pk):
+    """More sequences than one launch plans for (the batch is split into
+    slices): every output against the oracle, split and unsplit sequences."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(1, 101, 4100)
+    c = _custom_case(lens, Hq=4, Hkv=1, d=64, nb=64, width=7, seed=92)
+    ref = oracle.decode(*c.oracle_inputs(), c.scale)
+    for P in (32, 0):
+        _check(_to64(_gpu_decode(pk, c, P)), ref, "bf16", f"S=4100 P={P}")
+
+
+# --- full-size configs: every output ------------------------------------------
 FULL = ["cfg2", "cfg3", "cfg4", "cfg5"]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("key", FULL)
-def test_decode_full_size_sampled(pk, key):
+def test_decode_full_size_all_outputs(pk, key):
+    """The configuration at its full size, in the launch configuration the
+    benchmark uses: every (sequence, head) output against the oracle, and a
+    second call bit-identical to the first."""
     cfg = CONFIGS[key]
     _log(f"{key}: generating on the GPU")
     c = decode_case(cfg, payload="torch", device="cuda")
-    got = _gpu_decode(pk, c, cfg.partition_tokens)
-    rng = np.random.default_rng(1000 + cfg.seed)
+    got = _gpu_decode(pk, c, cfg.partition_tokens).clone()
+    assert torch.equal(got, _gpu_decode(pk, c, cfg.partition_tokens)), f"{key}: not deterministic"
     S, Hq = cfg.num_seqs, cfg.num_q_heads
-    longest = int(np.argmax(c.lens))
-    shortest = int(np.argmin(c.lens))
-    seqs = np.concatenate([[longest, shortest], rng.integers(0, S, 10)])
-    heads = rng.integers(0, Hq, len(seqs))
-    heads[:2] = [0, Hq - 1]
-    pairs = np.stack([seqs, heads], 1).astype(np.int32)
-    _log(f"{key}: copying pools to the host for {len(pairs)} sampled outputs")
+    pairs = np.array([[s, h] for s in range(S) for h in range(Hq)], np.int32)
+    _log(f"{key}: copying pools to the host for all {len(pairs)} outputs")
     ref = oracle.decode_pairs(*c.oracle_inputs(), c.scale, pairs)
     g64 = _to64(got)
-    _check(g64[pairs[:, 0], pairs[:, 1]], ref, cfg.dtype, f"{key} full sampled")
+    _check(g64[pairs[:, 0], pairs[:, 1]], ref, cfg.dtype, f"{key} full size, all outputs")
     del c
     torch.cuda.empty_cache()
 
