@@ -83,17 +83,19 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool,
                       const int64_t* slot_mapping, int32_t T, void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for these sizes (0 when no
- * sequence can span more than one partition).  partition_tokens as for
- * pa_decode.  Returns 0 also for invalid arguments; pa_decode reports those.
+ * Bytes of device workspace pa_decode needs for these sizes (non-zero for
+ * num_seqs > 0: per-piece partials and per-sequence piece counts).
+ * partition_tokens as for pa_decode.  Returns 0 also for invalid arguments;
+ * pa_decode reports those.
  */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
                                  int32_t partition_tokens);
 
 /*
- * The partition size (tokens) pa_decode uses for these arguments; equal to
- * partition_tokens when that is non-zero.  0 on invalid arguments.
+ * The smallest piece (tokens) pa_decode cuts a sequence into for these
+ * arguments; equal to partition_tokens when that is non-zero.  0 on invalid
+ * arguments.
  */
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
                                    int32_t num_q_heads, int32_t max_blocks_per_seq,
@@ -111,17 +113,18 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *                  [0, num_blocks); entries at j >= ceil(L / block_size) are
  *                  never read.
  *   context_lens:  int32 [num_seqs], 1 <= L <= max_blocks_per_seq*block_size.
- *   partition_tokens: 0 lets the library choose (256 tokens, doubled while
- *                  a full-length sequence would span more than 256
- *                  partitions, at most 4096); otherwise a positive multiple
- *                  of block_size giving at most 65535 partitions per
- *                  sequence (else PA_EINVAL).  A sequence longer than one
- *                  partition is processed in pieces whose (max, sum-exp,
- *                  unnormalised output) partials go to `workspace` and are
- *                  combined by a second kernel.
+ *   partition_tokens: smallest piece of a sequence one workgroup streams
+ *                  (0: the library's choice, 256 tokens); otherwise a
+ *                  positive multiple of block_size.  The work is split by
+ *                  blocks, not by sequence: per group of 4 kv heads the
+ *                  batch's blocks, sequence after sequence, are cut into
+ *                  equal contiguous ranges, one per workgroup of a grid that
+ *                  fills the chip, each range at least partition_tokens
+ *                  long.  A sequence cut by range boundaries is processed in
+ *                  pieces whose (max, sum-exp, unnormalised output) partials
+ *                  go to `workspace` and are combined by a second kernel.
  *   workspace:     device buffer of at least pa_decode_workspace_bytes(...)
- *                  bytes (may be NULL when that is 0); contents on entry are
- *                  irrelevant.
+ *                  bytes; contents on entry are irrelevant.
  * Requires num_q_heads % num_kv_heads == 0, block_size 16, head_dim 64 or
  * 128.  The result does not depend on where blocks sit in the pool, and two
  * calls with the same inputs give identical bits.

@@ -38,42 +38,30 @@ bool fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
-// Partition size: one wave streams one partition of one (sequence, kv head),
-// so short partitions keep every wave's share of a ragged batch small and the
-// end of the launch short.  256 tokens (16 blocks) unless a sequence at the
-// table's full length would need more than 256 partitions; then doubled (the
-// partials stay a small fraction of the K/V bytes), never beyond 4096 nor
-// beyond what the table can address.
-int32_t choose_partition(const pa_pool* pool, int32_t maxB) {
-  const int64_t max_len = (int64_t)maxB * pool->block_size;
-  int64_t P = 256;
-  while (P < 4096 && (max_len + P - 1) / P > 256) P *= 2;
-  const int64_t cap = (max_len + pool->block_size - 1) / pool->block_size * pool->block_size;
-  if (P > cap) P = cap;
-  if (P < pool->block_size) P = pool->block_size;
-  return static_cast<int32_t>(P);
-}
+// Smallest piece a workgroup streams when the library chooses: 256 tokens
+// (16 blocks).  Ranges are normally much longer (the batch's blocks divided
+// evenly over the grid); the floor only matters for small batches, where it
+// bounds the number of partials.
+constexpr int32_t kDefaultMinPiece = 256;
 
 pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
-                       int32_t req_partition, int32_t* P_out, int32_t* parts_out,
+                       int32_t req_piece, int32_t* P_out, int32_t* slots_out,
                        size_t* ws_out) {
   if (!pool_ok(pool) || S < 0 || Hq <= 0 || maxB <= 0) return PA_EINVAL;
   if (Hq % pool->num_kv_heads != 0) return PA_EINVAL;
-  if (req_partition < 0 || (req_partition > 0 && req_partition % pool->block_size != 0))
-    return PA_EINVAL;
+  if (req_piece < 0 || (req_piece > 0 && req_piece % pool->block_size != 0)) return PA_EINVAL;
   if ((int64_t)maxB * pool->block_size > INT32_MAX) return PA_EINVAL;
-  const int32_t P = req_partition > 0 ? req_partition : choose_partition(pool, maxB);
+  const int32_t P = req_piece > 0 ? req_piece : kDefaultMinPiece;
   const int64_t max_len = (int64_t)maxB * pool->block_size;
-  if ((max_len + P - 1) / P > pakv::kMaxParts) return PA_EINVAL;
-  const int32_t parts = static_cast<int32_t>((max_len + P - 1) / P);
-  size_t ws = 0;
-  if (parts > 1) {
-    const size_t n = (size_t)S * Hq * parts;
-    ws = 2 * align_up(n * sizeof(float)) + align_up(n * pool->head_dim * sizeof(float));
-  }
+  // a sequence of n blocks meets at most ceil(n / min piece) + 1 ranges
+  const int64_t slots = (max_len + P - 1) / P + 1;
+  if (slots > pakv::kMaxSlots) return PA_EINVAL;
+  const size_t n = (size_t)S * Hq * slots;
   *P_out = P;
-  *parts_out = parts;
-  *ws_out = ws;
+  *slots_out = static_cast<int32_t>(slots);
+  *ws_out = S == 0 ? 0
+                   : 2 * align_up(n * sizeof(float)) + align_up(n * pool->head_dim * sizeof(float)) +
+                         align_up((size_t)S * sizeof(int32_t));
   return PA_OK;
 }
 
@@ -120,20 +108,20 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool, const voi
 
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_blocks_per_seq, int32_t partition_tokens) {
-  int32_t P, parts;
+  int32_t P, slots;
   size_t ws;
   if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
-                   &parts, &ws) != PA_OK)
+                   &slots, &ws) != PA_OK)
     return 0;
   return ws;
 }
 
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_blocks_per_seq, int32_t partition_tokens) {
-  int32_t P, parts;
+  int32_t P, slots;
   size_t ws;
   if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
-                   &parts, &ws) != PA_OK)
+                   &slots, &ws) != PA_OK)
     return 0;
   return P;
 }
@@ -144,20 +132,20 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const int32_t* context_lens, float scale, void* out,
                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  int32_t P, parts;
+  int32_t P, slots;
   size_t ws;
   pa_status st = decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
-                              partition_tokens, &P, &parts, &ws);
+                              partition_tokens, &P, &slots, &ws);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !block_tables || !context_lens || !out) return PA_EINVAL;
-  if (ws > 0 && (!workspace || workspace_bytes < ws)) return PA_EINVAL;
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
     return PA_EINVAL;
   const int group = num_q_heads / pool->num_kv_heads;
   if (pool->block_size != pakv::kBlock) return PA_EUNSUPPORTED;
   if (pakv::decode_path(pool->dtype, pool->head_dim, group) == pakv::DecodePath::kUnsupported)
     return PA_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < ws) return PA_EINVAL;
   hipStream_t hs = as_stream(stream);
   if (debug_checks()) {
     std::vector<int32_t> lens, tab;
@@ -180,19 +168,19 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
   a.out = out;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  if (ws > 0) {
-    const size_t n = (size_t)num_seqs * num_q_heads * parts;
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    a.part_m = reinterpret_cast<float*>(w);
-    a.part_l = reinterpret_cast<float*>(w + align_up(n * sizeof(float)));
-    a.part_o = reinterpret_cast<float*>(w + 2 * align_up(n * sizeof(float)));
-  }
+  const size_t n = (size_t)num_seqs * num_q_heads * slots;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.part_m = reinterpret_cast<float*>(w);
+  a.part_l = reinterpret_cast<float*>(w + align_up(n * sizeof(float)));
+  a.part_o = reinterpret_cast<float*>(w + 2 * align_up(n * sizeof(float)));
+  a.seg_count = reinterpret_cast<int32_t*>(w + 2 * align_up(n * sizeof(float)) +
+                                           align_up(n * pool->head_dim * sizeof(float)));
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
-  a.partition_tokens = P;
-  a.max_parts = parts;
+  a.min_seg_blocks = P / pool->block_size;
+  a.max_slots = slots;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, hs);
   return e == hipSuccess ? PA_OK : PA_EHIP;

@@ -7,20 +7,21 @@
 // reading K/V block by block through the sequence's block table.  The
 // equation is the textbook one; only the gather is new.
 //
-// Work decomposition: the unit of work is one (sequence, kv head,
-// partition), where a partition is `partition_tokens` consecutive logical
-// tokens (a multiple of the 16-token block), and ONE WAVE processes one unit
-// from start to finish: it walks the unit's blocks in order, keeping a ring
-// of register buffers so that several blocks' K/V loads are in flight while
-// the oldest is consumed, and carries an online-softmax state (reference max
-// m, running sum l, unnormalised output o) for every query head of the
-// group.  A workgroup is 4 waves on 4 consecutive kv heads of the same
-// (sequence, partition), so its waves have equal work.  The grid is
-// persistent: each workgroup builds the list of units in LDS from the
-// context lengths (full partitions first, then each sequence's partial last
-// partition, longest first) and walks its share of it.  A sequence that
-// fits one partition is finished in place; otherwise each unit writes
-// (m, l, o) to the workspace and decode_reduce_kernel combines them:
+// Work decomposition.  For each group of 4 kv heads, the batch is one flat
+// list of blocks: sequence 0's blocks in logical order, then sequence 1's,
+// and so on.  The grid is persistent (as many workgroups as fit on the chip
+// at once) and every workgroup takes one equal, contiguous range of that
+// list for one head group; its 4 waves each stream the range for one kv head
+// of the group.  Every workgroup thus reads the same number of blocks
+// whatever the length mix, and a range spans only a few sequences.  Inside
+// the range a wave walks piece by piece (a piece is the part of one
+// sequence inside the range), keeping a ring of register buffers so that
+// the next block's K/V loads are in flight while the current one is
+// consumed, and carries an online-softmax state (reference max m, running
+// sum l, unnormalised output o) for every query head of the group.  A
+// sequence that lies inside one range is finished in place; a sequence cut
+// by range boundaries leaves one (m, l, o) partial per piece in the
+// workspace, and decode_reduce_kernel combines them:
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
 // Scores are kept in log2 units (scale * log2 e folded in), so v_exp_f32
 // (2^x) serves as the exponential.
@@ -135,34 +136,24 @@ __device__ __forceinline__ void store_out<__bf16>(void* out, size_t idx, float v
   static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);  // v_cvt_pk_bf16_f32, RNE
 }
 
-// Work list.  A unit is (sequence s, partition p) for one group of kWaves
-// kv heads; wave w of a workgroup takes kv head group * kWaves + w, so the
-// four waves of a unit stream the same token range.  The grid is persistent
-// (a few workgroups per CU) and every workgroup first builds the unit list
-// in LDS from context_lens:
-//   - full units: partition p < L_s / P of every sequence, sequence-major;
-//   - then one partial unit per sequence with L_s % P > 0, sorted by length
-//     in blocks, longest first (a counting sort over P/16 buckets),
-// and then walks items blockIdx.x, blockIdx.x + gridDim.x, ...  Every item
-// is real work (no empty workgroups for partitions past a short sequence's
-// end), consecutive items sit on different XCDs (workgroups go to the 8
-// XCDs round-robin), and each workgroup's last items are its smallest, so
-// the launch ends on short units.  Which workgroup runs a unit does not
-// change the unit's result.
+// A piece of work for one wave: tokens [t0, t1) of sequence s, kv head g;
+// `part` is the piece's slot among the sequence's `nparts` pieces.
 struct Unit {
   int s, g, part, L, t0, t1, nparts;
 };
 
+// The plan every workgroup builds in LDS from the context lengths: block
+// prefix sums over the batch and the range length.  Built from scans only,
+// so every workgroup gets the same plan.
 struct Plan {
-  const int* pre;    // [S + 1] full units before sequence s; pre[S] = NF
-  const int* lens;   // [S] context lengths
-  const int* plist;  // [S] sequences with a partial unit, longest first
-  int S, NF, U, HG;
+  const int* pre;   // [S + 1] blocks before sequence s; pre[S] = T
+  const int* lens;  // [S] context lengths (clamped to the table capacity)
+  int S, T, q, R, HG;
 };
 
-// Dynamic LDS bytes for a plan over S sequences with partition P.
-__host__ __device__ constexpr size_t plan_lds_bytes(int S, int P) {
-  return ((size_t)3 * S + 1 + 6 * (P / 16 + 2) + 8) * sizeof(int);
+// Dynamic LDS bytes for a plan over S sequences.
+__host__ __device__ constexpr size_t plan_lds_bytes(int S) {
+  return ((size_t)2 * S + 1 + 8) * sizeof(int);
 }
 
 // Inclusive scan of one value per lane over a wave.
@@ -183,133 +174,93 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
   __syncthreads();
   int off = 0;
   for (int w = 0; w < wave; ++w) off += wsum[w];
-  if (total) *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   __syncthreads();
   return off + inc - v;
 }
 
-// Collective over the workgroup (256 threads); ends with a barrier.  Every
-// workgroup builds the same plan from the same lengths, so nothing in it may
-// depend on timing: counts use atomics (order-free), positions come from
-// scans and ballots only.
+// Collective over the workgroup (256 threads); ends with a barrier.
 __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
-  const int S = a.num_seqs, P = a.partition_tokens, NBK = P / 16, NB2 = NBK + 2;
-  int* pre = lds;             // S + 1: full units before sequence s
-  int* lens = pre + S + 1;    // S: clamped context lengths
-  int* plist = lens + S;      // S: sequences with a partial unit, longest first
-  int* base = plist + S;      // NB2: bucket count, then position of its first unit
-  int* run = base + NB2;      // NB2: units of the bucket placed by earlier chunks
-  int* cw = run + NB2;        // 4 * NB2: per-wave bucket counts of the current chunk
-  int* wsum = cw + 4 * NB2;   // 8: scan scratch
-  const int T = blockDim.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int b = t; b < NB2; b += T) {
-    base[b] = 0;
-    run[b] = 0;
-  }
-  const int C = (S + T - 1) / T;  // contiguous chunk of sequences per thread
+  const int S = a.num_seqs;
+  int* pre = lds;            // S + 1
+  int* lens = pre + S + 1;   // S
+  int* wsum = lens + S;      // 8
+  const int T_ = blockDim.x, t = threadIdx.x;
+  const int C = (S + T_ - 1) / T_;  // contiguous chunk of sequences per thread
   const int s0 = min(S, t * C), s1 = min(S, s0 + C);
   // lengths outside [0, table capacity] violate the contract; clamping them
   // keeps every LDS and table index in range whatever the device data says
   const int cap = a.max_blocks * kBlock;
-  __syncthreads();
-  int nfull = 0;
+  int nb = 0;
   for (int s = s0; s < s1; ++s) {
     const int L = min(max(a.context_lens[s], 0), cap);
     lens[s] = L;
-    nfull += L / P;
-    if (L % P) atomicAdd(&base[(L % P + 15) / 16], 1);
+    nb += (L + kBlock - 1) / kBlock;
   }
-  int NF;
-  int run_full = block_excl_scan(nfull, wsum, &NF);
+  int T;
+  int run = block_excl_scan(nb, wsum, &T);
   for (int s = s0; s < s1; ++s) {
-    pre[s] = run_full;
-    run_full += lens[s] / P;
+    pre[s] = run;
+    run += (lens[s] + kBlock - 1) / kBlock;
   }
-  if (t == 0) pre[S] = NF;
-  // bucket b holds partial units of b blocks; longest first: bucket NBK at 0
-  int NPt = 0;
-  for (int b0 = 0; b0 < NBK; b0 += T) {
-    const int b = NBK - (b0 + t);
-    const int c = (b >= 1) ? base[b] : 0;
-    int tot;
-    const int off = block_excl_scan(c, wsum, &tot);
-    if (b >= 1) base[b] = NPt + off;
-    NPt += tot;
-    __syncthreads();
-  }
-  // stable placement, sequence order inside a bucket: chunks of T
-  // consecutive sequences; a lane's rank among lower lanes of its wave with
-  // the same bucket comes from ballots, earlier waves and chunks from counts
-  for (int c0 = 0; c0 < S; c0 += T) {
-    const int s = c0 + t;
-    int b = 0;
-    if (s < S) {
-      const int r = lens[s] % P;
-      if (r) b = (r + 15) / 16;
-    }
-    for (int i = lane; i < NB2; i += 64) cw[wave * NB2 + i] = 0;
-    uint64_t todo = __ballot(b != 0);
-    int rank = 0;
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const int bl = __builtin_amdgcn_readlane(b, leader);
-      const uint64_t m = __ballot(b == bl);
-      if (b == bl) rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-      if (lane == 0) cw[wave * NB2 + bl] = __builtin_popcountll(m);
-      todo &= ~m;
-    }
-    __syncthreads();
-    if (b) {
-      int pos = base[b] + run[b] + rank;
-      for (int w = 0; w < wave; ++w) pos += cw[w * NB2 + b];
-      plist[pos] = s;
-    }
-    __syncthreads();
-    for (int i = t; i < NB2; i += T)
-      run[i] += (cw[i] + cw[NB2 + i]) + (cw[2 * NB2 + i] + cw[3 * NB2 + i]);
-    __syncthreads();
-  }
+  if (t == 0) pre[S] = T;
+  __syncthreads();
   Plan pl;
   pl.pre = pre;
   pl.lens = lens;
-  pl.plist = plist;
   pl.S = S;
-  pl.NF = NF;
-  pl.U = NF + NPt;
+  pl.T = T;
   pl.HG = (a.num_kv_heads + kWaves - 1) / kWaves;
+  pl.R = max(1, (int)gridDim.x / pl.HG);
+  pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
   return pl;
 }
 
-// The unit of `item` for this wave; false if the wave has no kv head there.
-__device__ __forceinline__ bool plan_unit(const DecodeArgs& a, const Plan& pl, int item,
-                                          int wave, Unit& u) {
-  const int k = item / pl.HG;
-  u.g = (item - k * pl.HG) * kWaves + wave;
-  if (u.g >= a.num_kv_heads) return false;
-  const int P = a.partition_tokens;
-  if (k < pl.NF) {
-    // largest s with pre[s] <= k (then pre[s + 1] > k: s has a full unit k)
-    int lo = 0, hi = pl.S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pl.pre[mid] <= k) lo = mid; else hi = mid - 1;
-    }
-    u.s = lo;
-    u.part = k - pl.pre[lo];
-  } else {
-    u.s = pl.plist[k - pl.NF];
-    u.part = pl.pre[u.s + 1] - pl.pre[u.s];
-  }
-  u.L = pl.lens[u.s];
-  u.t0 = u.part * P;
-  u.t1 = min(u.L, u.t0 + P);
-  u.nparts = (u.L + P - 1) / P;
-  return true;
+// Pieces sequence s is cut into (0 for an empty sequence).
+__device__ __forceinline__ int seg_count_of(const Plan& pl, int s) {
+  const int b = pl.pre[s], e = pl.pre[s + 1];
+  return e > b ? (e - 1) / pl.q - b / pl.q + 1 : 0;
 }
 
-// Index of (sequence, query head, partition) in the partial buffers.
+// Collective over the workgroup: the reduce kernel's per-sequence piece counts.
+__device__ void write_seg_counts(const DecodeArgs& a, const Plan& pl) {
+  for (int s = threadIdx.x; s < pl.S; s += blockDim.x) a.seg_count[s] = seg_count_of(pl, s);
+}
+
+// Walk this workgroup's range for kv head g, calling f(unit) per piece.
+template <typename F>
+__device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, int r, int g, F&& f) {
+  int b0 = r * pl.q;
+  const int b1 = min(pl.T, b0 + pl.q);
+  if (b0 >= b1) return;
+  // sequence holding block b0: the largest s with pre[s] <= b0 (then
+  // pre[s + 1] > b0 because b0 < T)
+  int lo = 0, hi = pl.S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pl.pre[mid] <= b0) lo = mid; else hi = mid - 1;
+  }
+  int s = lo;
+  while (b0 < b1) {
+    while (pl.pre[s + 1] <= b0) ++s;  // skip empty sequences
+    const int sb = pl.pre[s], se = pl.pre[s + 1];
+    const int e = min(b1, se);
+    Unit u;
+    u.s = s;
+    u.g = g;
+    u.L = pl.lens[s];
+    u.t0 = (b0 - sb) * kBlock;
+    u.t1 = min(u.L, (e - sb) * kBlock);
+    u.part = r - sb / pl.q;
+    u.nparts = (se - 1) / pl.q - sb / pl.q + 1;
+    f(u);
+    b0 = e;
+  }
+}
+
+// Index of (sequence, query head, piece) in the partial buffers.
 __device__ __forceinline__ size_t part_index(const DecodeArgs& a, int s, int hq, int part) {
-  return ((size_t)s * a.num_q_heads + hq) * a.max_parts + part;
+  return ((size_t)s * a.num_q_heads + hq) * a.max_slots + part;
 }
 
 // Online softmax with a lazy reference: probabilities are 2^(x - m_ref) for a
@@ -536,13 +487,15 @@ template <int D, int GM, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan(a, plan_lds);
+  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
+  if (r >= pl.R) return;
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  for (int item = blockIdx.x; item < pl.U * pl.HG; item += gridDim.x) {
-    Unit u;
-    if (plan_unit(a, pl, item, wave, u)) mfma_unit<D, GM, NBUF>(a, G, u, lane);
-  }
+  const int g = hg * kWaves + wave;
+  if (g >= a.num_kv_heads) return;
+  walk_range(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, GM, NBUF>(a, G, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -739,12 +692,14 @@ template <typename T, int D, int G, int NBUF>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan(a, plan_lds);
+  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
+  if (r >= pl.R) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  for (int item = blockIdx.x; item < pl.U * pl.HG; item += gridDim.x) {
-    Unit u;
-    if (plan_unit(a, pl, item, wave, u)) valu_unit<T, D, G, NBUF>(a, u, lane);
-  }
+  const int g = hg * kWaves + wave;
+  if (g >= a.num_kv_heads) return;
+  walk_range(a, pl, r, g, [&](const Unit& u) { valu_unit<T, D, G, NBUF>(a, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -757,10 +712,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
   constexpr int NW = 4, EPL = D / 64, UNR = 4;
   const int hq = blockIdx.x, s = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int L = min(a.context_lens[s], a.max_blocks * kBlock);  // as clamped by the plan
-  const int P = a.partition_tokens;
-  const int np = (L + P - 1) / P;
-  if (np <= 1) return;  // finished by the partition kernel (or no context)
+  const int np = a.seg_count[s];
+  if (np <= 1) return;  // finished in place by the decode kernel (or no context)
   const size_t base = part_index(a, s, hq, 0);
   const float* pm = a.part_m + base;
   const float* pl = a.part_l + base;
@@ -816,18 +769,13 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 
 template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {
-  if (a.max_parts <= 1) return hipSuccess;
   decode_reduce_kernel<T, D><<<dim3(a.num_q_heads, a.num_seqs), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
-// Persistent grid: kDecodeWgPerCu workgroups per CU (the MFMA kernel's
-// register budget is sized for 2), never more than there are items.
-#ifndef PA_WG_PER_CU
-#define PA_WG_PER_CU 2
-#endif
-constexpr int kDecodeWgPerCu = PA_WG_PER_CU;
-
+// Persistent grid: as many workgroups as the chip holds at once (the
+// occupancy of the kernel at hand), rounded down to a multiple of the head
+// groups so that every head group gets the same number of ranges.
 int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -846,36 +794,56 @@ struct Launch {
   size_t lds;
 };
 
-Launch decode_launch(const DecodeArgs& a) {
-  const int64_t hg = (a.num_kv_heads + kWaves - 1) / kWaves;
-  const int64_t items = (int64_t)a.num_seqs * a.max_parts * hg;
-  const int64_t wgs = std::min<int64_t>(items, (int64_t)cu_count() * kDecodeWgPerCu);
-  return {dim3((unsigned)std::max<int64_t>(wgs, 1)), dim3(kWaves * 64),
-          plan_lds_bytes(a.num_seqs, a.partition_tokens)};
+template <typename K>
+Launch decode_launch(const DecodeArgs& a, K kernel) {
+  static int per_cu = 0;  // per kernel instantiation
+  const size_t lds = plan_lds_bytes(a.num_seqs);
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kWaves * 64,
+                                                     plan_lds_bytes(kMaxPlanSeqs)) != hipSuccess ||
+        n < 1)
+      n = 1;
+    per_cu = n;
+  }
+  const int hg = (a.num_kv_heads + kWaves - 1) / kWaves;
+  const int ranges = std::max(1, cu_count() * per_cu / hg);
+  return {dim3((unsigned)(ranges * hg)), dim3(kWaves * 64), lds};
+}
+
+template <int D, int GM>
+hipError_t launch_mfma_g(const DecodeArgs& a, int G, hipStream_t st) {
+  const Launch l = decode_launch(a, decode_mfma_kernel<D, GM, kNBuf>);
+  decode_mfma_kernel<D, GM, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a);
-  if (G <= 4) decode_mfma_kernel<D, 4, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
-  else if (G <= 8) decode_mfma_kernel<D, 8, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
-  else decode_mfma_kernel<D, 16, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
-  hipError_t e = hipGetLastError();
+  hipError_t e = G <= 4 ? launch_mfma_g<D, 4>(a, G, st)
+               : G <= 8 ? launch_mfma_g<D, 8>(a, G, st)
+                        : launch_mfma_g<D, 16>(a, G, st);
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
 }
 
+template <typename T, int D, int G>
+hipError_t launch_valu_g(const DecodeArgs& a, hipStream_t st) {
+  const Launch l = decode_launch(a, decode_valu_kernel<T, D, G, kNBuf>);
+  decode_valu_kernel<T, D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_valu(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a);
+  hipError_t e;
   switch (G) {
-    case 1: decode_valu_kernel<T, D, 1, kNBuf><<<l.grid, l.block, l.lds, st>>>(a); break;
-    case 2: decode_valu_kernel<T, D, 2, kNBuf><<<l.grid, l.block, l.lds, st>>>(a); break;
-    case 3: decode_valu_kernel<T, D, 3, kNBuf><<<l.grid, l.block, l.lds, st>>>(a); break;
-    case 4: decode_valu_kernel<T, D, 4, kNBuf><<<l.grid, l.block, l.lds, st>>>(a); break;
+    case 1: e = launch_valu_g<T, D, 1>(a, st); break;
+    case 2: e = launch_valu_g<T, D, 2>(a, st); break;
+    case 3: e = launch_valu_g<T, D, 3>(a, st); break;
+    case 4: e = launch_valu_g<T, D, 4>(a, st); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<T, D>(a, st);
 }
@@ -926,12 +894,11 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int 
     b.out = static_cast<uint8_t*>(a.out) + (size_t)s0 * qrow;
     b.block_tables = a.block_tables + (size_t)s0 * a.max_blocks;
     b.context_lens = a.context_lens + s0;
-    if (a.part_m) {
-      const size_t pr = (size_t)s0 * a.num_q_heads * a.max_parts;
-      b.part_m = a.part_m + pr;
-      b.part_l = a.part_l + pr;
-      b.part_o = a.part_o + pr * head_dim;
-    }
+    const size_t pr = (size_t)s0 * a.num_q_heads * a.max_slots;
+    b.part_m = a.part_m + pr;
+    b.part_l = a.part_l + pr;
+    b.part_o = a.part_o + pr * head_dim;
+    b.seg_count = a.seg_count + s0;
     const hipError_t e = launch_decode_slice(b, dtype, head_dim, group, st);
     if (e != hipSuccess) return e;
   }

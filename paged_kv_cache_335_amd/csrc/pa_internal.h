@@ -29,7 +29,7 @@ constexpr int kBlock = 16;       // tokens per block supported by decode
 constexpr int kWaves = PA_WAVES;
 constexpr int kNBuf = PA_NBUF;
 constexpr int kMaxMfmaGroup = 16;
-constexpr int kMaxParts = 65535;  // partitions per sequence
+constexpr int kMaxSlots = 1 << 20;  // partial slots per (sequence, head)
 constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan)
 
 struct DecodeArgs {
@@ -39,15 +39,16 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_m;   // [S][Hq][max_parts]   running max, log2 units
-  float* part_l;   // [S][Hq][max_parts]   sum of exp2(score - m)
-  float* part_o;   // [S][Hq][max_parts][D] unnormalised output
+  float* part_m;       // [S][Hq][max_slots]    reference max, log2 units
+  float* part_l;       // [S][Hq][max_slots]    sum of exp2(score - m)
+  float* part_o;       // [S][Hq][max_slots][D] unnormalised output
+  int32_t* seg_count;  // [S] pieces each sequence was cut into
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
-  int32_t partition_tokens;
-  int32_t max_parts;
+  int32_t min_seg_blocks;  // smallest range a workgroup streams (blocks)
+  int32_t max_slots;       // partial slots per (sequence, query head)
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
 };
 

@@ -54,21 +54,25 @@ def _desc(nb=64, B=16, nkv=8, d=128, dt=1):
 
 
 def test_workspace_and_partition_sizing():
+    """The workspace holds one (m, l, o) slot per possible piece of every
+    (sequence, query head): a sequence of n blocks meets at most
+    ceil(n / min piece) + 1 ranges; plus one piece count per sequence."""
     import paged_kv_cache_335_amd as pk
     L = pk.lib()
     d = _desc(nb=32768)
-    # long context: 4 sequences x 8192 blocks, 512-token partitions
+    # long context: 4 sequences x 8192 blocks, 512-token minimum pieces
     P = L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 512)
     assert P == 512
     ws = L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 512)
-    n = 4 * 32 * 256
-    assert ws >= n * 4 * 2 + n * 128 * 4
-    # library choice: a power of two between 256 and 4096 tokens
-    P0 = L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 0)
-    assert P0 in (256, 512, 1024, 2048, 4096)
-    # one partition covers every sequence: no workspace
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8, 256) == 0
-    # invalid: partition not a multiple of the block, heads not divisible
+    slots = 8192 * 16 // 512 + 1
+    n = 4 * 32 * slots
+    assert ws >= n * 4 * 2 + n * 128 * 4 + 4 * 4
+    # library choice: 256-token minimum pieces
+    assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 0) == 256
+    # even short sequences can be cut by a range boundary: never 0 for S > 0
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8, 256) > 0
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 0, 32, 8, 256) == 0
+    # invalid: piece not a multiple of the block, heads not divisible
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 100) == 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 30, 8192, 512) == 0
 
@@ -101,7 +105,7 @@ def test_host_checks_reject_before_any_launch():
     st = L.pa_decode(ctypes.byref(d8), dummy, dummy, dummy, 1, 32, dummy, 4, dummy, 0.1,
                      dummy, 0, null, 0, null)
     assert st == pk.PA_EUNSUPPORTED
-    # split needed but no workspace given
+    # no workspace given (every decode needs one)
     st = L.pa_decode(ctypes.byref(d), dummy, dummy, dummy, 4, 32, dummy, 8192, dummy, 0.1,
                      dummy, 512, null, 0, null)
     assert st == pk.PA_EINVAL
