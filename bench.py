@@ -146,8 +146,10 @@ def main():
     for i in range(W, steps):
         step(i)
         step_bytes.append(int(cache.host_lens[:S].sum()) * kv_per_token)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    host_ms = (t_enq - t0) * 1e3 / K
     ms_step = (t1 - t0) * 1e3 / K
     timed_bytes = step_bytes[W:]
     dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(W, steps)]
@@ -156,7 +158,7 @@ def main():
     value = kv_avg / (ms_step * 1e-3) / 1e9
     dec_gbps = kv_avg / (dec_ms_avg * 1e-3) / 1e9
     log(f"step {ms_step:.3f} ms ({value:.0f} GB/s); decode {dec_ms_avg * 1e3:.1f} us "
-        f"({dec_gbps:.0f} GB/s, min {min(dec_ms) * 1e3:.1f} us)")
+        f"({dec_gbps:.0f} GB/s, min {min(dec_ms) * 1e3:.1f} us); host enqueue {host_ms:.3f} ms/step")
 
     # cold decode: caches flushed before each call (outside the event window)
     cold = None
@@ -209,6 +211,7 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "host_enqueue_ms_per_step": round(host_ms, 4),
         "decode": {"us_mean": round(dec_ms_avg * 1e3, 2), "us_min": round(min(dec_ms) * 1e3, 2),
                    "GBps": round(dec_gbps, 1),
                    "tokens_per_s": round(S / (dec_ms_avg * 1e-3), 1)},

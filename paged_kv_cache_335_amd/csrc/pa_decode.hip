@@ -789,6 +789,16 @@ int cu_count() {
   return cached[dev];
 }
 
+// One workgroup per CU: with two, the CU's memory arbitration favoured the
+// older workgroup so much that the two finished up to 1.7x apart and the
+// younger one streamed its last ranges alone (measured with per-wave
+// timestamps); alone on its CU, each workgroup's four waves keep 32 KB in
+// flight, which a read-bandwidth probe found is what this HBM rewards.
+#ifndef PA_MAX_WG_PER_CU
+#define PA_MAX_WG_PER_CU 1
+#endif
+constexpr int kMaxWgPerCu = PA_MAX_WG_PER_CU;
+
 struct Launch {
   dim3 grid, block;
   size_t lds;
@@ -804,7 +814,7 @@ Launch decode_launch(const DecodeArgs& a, K kernel) {
                                                      plan_lds_bytes(kMaxPlanSeqs)) != hipSuccess ||
         n < 1)
       n = 1;
-    per_cu = n;
+    per_cu = std::min(n, kMaxWgPerCu);
   }
   const int hg = (a.num_kv_heads + kWaves - 1) / kWaves;
   const int ranges = std::max(1, cu_count() * per_cu / hg);
