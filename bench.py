@@ -37,6 +37,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_cfg3_hbm_traffic.md")
+DECODE_SOURCES = ("paged_kv_cache_335_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_335_amd/csrc/pa_internal.h")
+
+
+def measured_traffic(kv_bytes):
+    """HBM bytes per decode launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy's counters), or
+    None when the decode sources changed since the counters were taken or this
+    run's workload is not the one they were taken on."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(ln.split(": ", 1) for ln in text.splitlines()
+                  if ln.startswith(("traffic_bytes_per_launch:", "algorithmic_bytes_per_launch:",
+                                    "decode_source_sha256:")))
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("decode_source_sha256") != h.hexdigest():
+        return None
+    if int(fields.get("algorithmic_bytes_per_launch", -1)) != int(kv_bytes):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,7 +247,7 @@ def main():
         "decode_cold": cold,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(kv_avg) if args.partition == 0 else None},
         "block_manager": {"tail_waste_pct": round(tail_waste, 3),
                           "contiguous_reservation_utilisation_pct": round(contiguous_util, 2),
                           "cow_copies": stats["cow_copies"]},
