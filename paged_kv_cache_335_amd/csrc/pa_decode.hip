@@ -27,20 +27,24 @@
 // (2^x) serves as the exponential.
 //
 // Two kernel families:
-//  * decode_mfma_kernel (bf16, 3..16 query heads per kv head): q.K and P.V
-//    run on v_mfma_f32_16x16x32_bf16.  For q.K, A = the 16 tokens of a block
-//    x 32 dims, B = 32 dims x 16 head slots (the group's heads, zero padded).
-//    Its output layout (lane holds tokens 4*(lane/16)+i of head lane%16) is
-//    exactly the A layout P.V needs, so probabilities never leave the lane.
-//    P is split into a bf16 high part (truncation) and a bf16 low part
-//    (p - high, rounded), laid side by side along the MFMA's K dimension with
-//    V repeated, so the product carries about 16 bits of P at no extra
-//    instruction count.  V is stored dim-major in the pool so each lane's 4
-//    tokens of one dim are one 8-byte load.
-//  * decode_valu_kernel (fp32, or bf16 with 1..2 heads per kv head, where no
-//    dense tile exists): 4 lanes per token share a K row for q.K
-//    (v_dot2c_f32_bf16 for bf16), then each lane owns head_dim/64 output dims
-//    and accumulates P.V with FMAs, P broadcast through v_readlane.
+//  * decode_mfma_kernel (bf16, 1..16 query heads per kv head): q.K runs on
+//    v_mfma_f32_16x16x32_bf16 with A = the 16 tokens of a block x 32 dims and
+//    B = 32 dims x 16 head slots (the group's heads, zero padded).  Its
+//    output layout (lane holds tokens 4*(lane/16)+i of head lane%16) is
+//    exactly the A layout of P.V on v_mfma_f32_16x16x16_bf16, so
+//    probabilities never leave the lane.  P goes in twice, as its bf16 high
+//    part (truncation) and then its low part (p - high, rounded to nearest
+//    even), which carries P to about 16 significant bits.  V is stored
+//    dim-major in the pool so each lane's 4 tokens of one dim are one 8-byte
+//    load.
+//    With a single query head per kv head (MHA) the 16 head slots hold one
+//    real head; the instruction count per block does not depend on the group
+//    size, and measured against a VALU kernel on the 32/32-head workload the
+//    MFMA form was 37% faster (its V loads are contiguous 512-byte runs).
+//  * decode_valu_kernel (fp32 pools): 4 lanes per token share a K row for
+//    q.K with FMAs and a DPP quad reduce, then each lane owns head_dim/64
+//    output dims and accumulates P.V with FMAs, P broadcast through
+//    v_readlane.
 // Both stream each K/V byte of a (block, kv head) from HBM once.
 #include <algorithm>
 #include <type_traits>
@@ -61,7 +65,6 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Global-memory (address space 1) byte pointer.
@@ -499,15 +502,13 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kerne
 }
 
 // ---------------------------------------------------------------------------
-// VALU kernel: fp32 or bf16 pools, G (template) query heads per kv head.
+// VALU kernel: fp32 pools, G (template) query heads per kv head.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, int NBUF>
+template <int D, int G, int NBUF>
 __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, int lane) {
   constexpr int B = kBlock;
-  constexpr int ES = sizeof(T);
-  constexpr bool BF = ES == 2;
-  constexpr int CH = 16 / ES;         // elements per 16-byte chunk
-  constexpr int NC = D / CH / 4;      // q.K chunks per lane
+  constexpr int ES = 4;
+  constexpr int NC = D / 16;          // 16-byte q.K chunks per lane (4 lanes per token)
   constexpr int QW = NC * 4;          // 32-bit words of q per head per lane
   constexpr int EPL = D / 64;         // output dims per lane
   constexpr int NV = EPL * B * ES / 16;  // 16-byte V loads per lane
@@ -579,16 +580,9 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
           const uint32_t kw[4] = {kb[jj].x, kb[jj].y, kb[jj].z, kb[jj].w};
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            if constexpr (BF) {
-              const float t = __builtin_amdgcn_fdot2_f32_bf16(
-                  __builtin_bit_cast(bf16x2, kw[w]), __builtin_bit_cast(bf16x2, qw[h][jj * 4 + w]),
-                  (w & 1) ? d1 : d0, false);
-              if (w & 1) d1 = t; else d0 = t;
-            } else {
-              const float t = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[h][jj * 4 + w]),
-                                   (w & 1) ? d1 : d0);
-              if (w & 1) d1 = t; else d0 = t;
-            }
+            const float t = fmaf(__uint_as_float(kw[w]), __uint_as_float(qw[h][jj * 4 + w]),
+                                 (w & 1) ? d1 : d0);
+            if (w & 1) d1 = t; else d0 = t;
           }
         }
         float d = d0 + d1;
@@ -606,15 +600,8 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
           uint32_t* w = reinterpret_cast<uint32_t*>(&vb[v]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            // word q of load v: token index within its V^T row
-            const int word = (v * 4 + q) % (B * ES / 4);
-            if constexpr (BF) {
-              const int tk = word * 2;
-              const uint32_t m = (tk < valid ? 0x0000ffffu : 0u) | (tk + 1 < valid ? 0xffff0000u : 0u);
-              w[q] &= m;
-            } else {
-              if (word >= valid) w[q] = 0u;
-            }
+            // word q of load v holds token (v*4 + q) % 16 of its V^T row
+            if ((v * 4 + q) % B >= valid) w[q] = 0u;
           }
         }
       }
@@ -654,11 +641,8 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
           pt[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[h]), 4 * t));
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          const int word = (e * B * ES + t * ES) / 4;  // word within this lane's V bytes
-          const uint32_t w = reinterpret_cast<const uint32_t*>(vb)[word];
-          float vv;
-          if constexpr (BF) vv = (t & 1) ? bf16_hi(w) : bf16_lo(w);
-          else vv = __uint_as_float(w);
+          // word within this lane's V bytes: row e, token t
+          const float vv = __uint_as_float(reinterpret_cast<const uint32_t*>(vb)[e * B + t]);
 #pragma unroll
           for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pt[h], vv, acc[h][e]);
         }
@@ -675,7 +659,7 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
     if (u.nparts == 1) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
-        store_out<T>(a.out, ((size_t)s * a.num_q_heads + hq) * D + lane * EPL + e, acc[h][e] / lt);
+        store_out<float>(a.out, ((size_t)s * a.num_q_heads + hq) * D + lane * EPL + e, acc[h][e] / lt);
     } else {
       const size_t pi = part_index(a, s, hq, u.part);
 #pragma unroll
@@ -688,7 +672,7 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
   }
 }
 
-template <typename T, int D, int G, int NBUF>
+template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan(a, plan_lds);
@@ -699,7 +683,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) 
   const int lane = threadIdx.x & 63;
   const int g = hg * kWaves + wave;
   if (g >= a.num_kv_heads) return;
-  walk_range(a, pl, r, g, [&](const Unit& u) { valu_unit<T, D, G, NBUF>(a, u, lane); });
+  walk_range(a, pl, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -837,25 +821,25 @@ hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
   return launch_reduce<__bf16, D>(a, st);
 }
 
-template <typename T, int D, int G>
+template <int D, int G>
 hipError_t launch_valu_g(const DecodeArgs& a, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_valu_kernel<T, D, G, kNBuf>);
-  decode_valu_kernel<T, D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(a);
+  const Launch l = decode_launch(a, decode_valu_kernel<D, G, kNBuf>);
+  decode_valu_kernel<D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <int D>
 hipError_t launch_valu(const DecodeArgs& a, int G, hipStream_t st) {
   hipError_t e;
   switch (G) {
-    case 1: e = launch_valu_g<T, D, 1>(a, st); break;
-    case 2: e = launch_valu_g<T, D, 2>(a, st); break;
-    case 3: e = launch_valu_g<T, D, 3>(a, st); break;
-    case 4: e = launch_valu_g<T, D, 4>(a, st); break;
+    case 1: e = launch_valu_g<D, 1>(a, st); break;
+    case 2: e = launch_valu_g<D, 2>(a, st); break;
+    case 3: e = launch_valu_g<D, 3>(a, st); break;
+    case 4: e = launch_valu_g<D, 4>(a, st); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  return launch_reduce<T, D>(a, st);
+  return launch_reduce<float, D>(a, st);
 }
 
 }  // namespace
@@ -864,7 +848,6 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group) {
   if (head_dim != 64 && head_dim != 128) return DecodePath::kUnsupported;
   if (group < 1) return DecodePath::kUnsupported;
   if (dtype == PA_BF16) {
-    if (group <= 2) return DecodePath::kValu;
     if (group <= kMaxMfmaGroup) return DecodePath::kMfma;
     return DecodePath::kUnsupported;
   }
@@ -879,11 +862,7 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
     case DecodePath::kMfma:
       return head_dim == 128 ? launch_mfma<128>(a, group, st) : launch_mfma<64>(a, group, st);
     case DecodePath::kValu:
-      if (dtype == PA_BF16)
-        return head_dim == 128 ? launch_valu<__bf16, 128>(a, group, st)
-                               : launch_valu<__bf16, 64>(a, group, st);
-      return head_dim == 128 ? launch_valu<float, 128>(a, group, st)
-                             : launch_valu<float, 64>(a, group, st);
+      return head_dim == 128 ? launch_valu<128>(a, group, st) : launch_valu<64>(a, group, st);
     default:
       return hipErrorInvalidValue;
   }
