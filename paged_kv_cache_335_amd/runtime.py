@@ -14,6 +14,8 @@ A decode step for a batch of live sequences:
   5. pa_kv_write: the new tokens' K/V go into their slots;
   6. pa_decode: attention over the grown contexts.
 """
+import ctypes
+
 import numpy as np
 import torch
 
@@ -21,7 +23,73 @@ from . import (PA_OK, PagedKVError, pa_block_copy, pa_decode, pa_decode_partitio
                pa_decode_workspace_bytes, pa_kv_write, pa_table_update)
 from .block_manager import BlockManager
 
-_RING = 8
+# Staging for the per-step metadata: a ring of pinned host buffers, each
+# copied to its own device buffer.  An event is recorded only after the last
+# copy of each group of _GROUP buffers (any event between two kernels delays
+# the second by a few microseconds), and the host waits on a group's event
+# only when it comes back to that group a lap later.
+_RING = 32
+_GROUP = 8
+
+# --- fence-free stream events ---------------------------------------------------
+# A default HIP event performs a system-scope release when it is recorded:
+# caches are written back and invalidated, and on this GPU the kernel after
+# each record started about 5 us late.  Events that only order work on the
+# device, time it, or tell the host that a host-to-device copy has finished
+# reading its source need no such fence.
+_HIP_EVENT_DISABLE_TIMING = 0x2
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime torch already loaded (opened by soname, so no second
+    copy is mapped into the process)."""
+    global _hip
+    if _hip is None:
+        lib = ctypes.CDLL("libamdhip64.so.7")
+        vp = ctypes.c_void_p
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventSynchronize.argtypes = [vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        _hip = lib
+    return _hip
+
+
+class DeviceEvent:
+    """A HIP event recorded without a system-scope fence."""
+
+    def __init__(self, timing=False):
+        hip = _hip_runtime()
+        flags = _HIP_EVENT_DISABLE_SYSTEM_FENCE | (0 if timing else _HIP_EVENT_DISABLE_TIMING)
+        self._ev = ctypes.c_void_p()
+        st = hip.hipEventCreateWithFlags(ctypes.byref(self._ev), flags)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream):
+        st = _hip_runtime().hipEventRecord(self._ev, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def synchronize(self):
+        st = _hip_runtime().hipEventSynchronize(self._ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventSynchronize failed ({st})")
+
+    def elapsed_ms(self, end):
+        ms = ctypes.c_float()
+        st = _hip_runtime().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "_ev", None) and _hip is not None:
+            _hip.hipEventDestroy(self._ev)
+            self._ev = None
 
 
 class PagedKVCache:
@@ -45,7 +113,7 @@ class PagedKVCache:
         self.host_lens = np.zeros(max_seqs, dtype=np.int32)
         self.rows = {}          # sequence id -> row of the device table
         self._ring = None
-        self._ring_events = [None] * _RING
+        self._ring_events = [None] * (_RING // _GROUP)
         self._ring_pos = 0
         self._ws = None
 
@@ -74,15 +142,19 @@ class PagedKVCache:
     def _staging(self, T, S):
         need = T * 8 + T * 4 * 2 + S * 4 + 64
         if self._ring is None or self._ring[0][0].numel() < need:
+            if self._ring is not None:
+                torch.cuda.current_stream(self.device).synchronize()  # old buffers idle
             self._ring = [(torch.empty(need, dtype=torch.uint8, pin_memory=True),
                            torch.empty(need, dtype=torch.uint8, device=self.device))
                           for _ in range(_RING)]
-            self._ring_events = [None] * _RING
+            self._ring_events = [None] * (_RING // _GROUP)
+            self._ring_pos = 0
         i = self._ring_pos
         self._ring_pos = (i + 1) % _RING
-        ev = self._ring_events[i]
-        if ev is not None:
-            ev.synchronize()  # the copy that last used this host buffer has run
+        if i % _GROUP == 0:
+            ev = self._ring_events[i // _GROUP]
+            if ev is not None:
+                ev.synchronize()  # every copy of this group's previous lap has run
         return i
 
     def append(self, seqs, n_tokens, k_new, v_new, stream=None):
@@ -111,9 +183,12 @@ class PagedKVCache:
         stream = stream or torch.cuda.current_stream(self.device)
         with torch.cuda.stream(stream):
             dev[:o_len + S * 4].copy_(host[:o_len + S * 4], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(stream)
-            self._ring_events[i] = ev
+            if i % _GROUP == _GROUP - 1:
+                # after the group's last copy: the host may refill the group once it fires
+                g = i // _GROUP
+                ev = self._ring_events[g] or DeviceEvent()
+                ev.record(stream)
+                self._ring_events[g] = ev
             d_slots = dev[:o_sq].view(torch.int64)
             d_rows = dev[o_sq:o_pos].view(torch.int32)
             d_pos = dev[o_pos:o_len].view(torch.int32)

@@ -126,3 +126,14 @@ def test_binding_rejects_cpu_tensors():
         pk.pa_block_copy(k, v, torch.zeros(1, 2, dtype=torch.int32))
     with pytest.raises(ValueError):
         pk.pool_desc(k, torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16))
+
+
+def test_event_helper_uses_the_hip_runtime_torch_loaded():
+    """The fence-free event helper opens the HIP runtime by soname: the copy
+    torch loaded is reused, never a second one (two runtimes in one process
+    would not share streams)."""
+    from paged_kv_cache_335_amd.runtime import _hip_runtime
+    _hip_runtime()
+    maps = open("/proc/self/maps").read().splitlines()
+    copies = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(copies) == 1, copies
