@@ -166,6 +166,22 @@ pa_status pa_table_update(int32_t* block_tables, int32_t max_blocks_per_seq,
                           const int32_t* positions, const int64_t* slot_mapping,
                           int32_t T, void* stream);
 
+/*
+ * Append: pa_table_update and pa_kv_write in one launch (a growing sequence
+ * writes its new tokens and appends table entries; vLLM post, "PagedAttention:
+ * paging, borrowed from the operating system").  For every i with
+ * slot_mapping[i] >= 0, token i's K/V go to its slot as in pa_kv_write and
+ *   block_tables[seq_ids[i] * max_blocks_per_seq + positions[i] / block_size]
+ *       = slot_mapping[i] / block_size.
+ * Arguments and requirements as for those two calls (block_tables is
+ * int32 [rows][max_blocks_per_seq] on the device).  T = 0 is a no-op.
+ */
+pa_status pa_kv_append(const pa_pool* pool, void* k_pool, void* v_pool,
+                       const void* k_new, const void* v_new,
+                       const int64_t* slot_mapping, int32_t T,
+                       int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_ids, const int32_t* positions, void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_str(pa_status status);
 

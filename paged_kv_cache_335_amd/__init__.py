@@ -59,6 +59,7 @@ def _load():
         "pa_decode": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp, sz, vp]),
         "pa_block_copy": (i32, [P, vp, vp, vp, i32, vp]),
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
+        "pa_kv_append": (i32, [P, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_version": (ctypes.c_char_p, []),
         "pa_bm_create": (vp, [i32, i32, ctypes.c_uint64]),
@@ -84,7 +85,7 @@ def _load():
 _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
-    "pa_block_copy", "pa_table_update", "pa_status_str", "pa_version", "pa_bm_create",
+    "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_status_str", "pa_version", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch",
     "pa_bm_free_seq", "pa_bm_block_table", "pa_bm_export", "pa_bm_refcount",
     "pa_bm_free_list", "pa_bm_stats")
@@ -234,6 +235,32 @@ def pa_table_update(block_tables, block_size, seq_ids, positions, slot_mapping, 
                               _dev(positions, "positions"), _dev(slot_mapping, "slot_mapping"),
                               T, _stream(stream))
     _check(st, "pa_table_update")
+
+
+def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, seq_ids, positions,
+                 stream=None):
+    """pa_table_update and pa_kv_write in one launch."""
+    desc = pool_desc(k_pool, v_pool)
+    T = slot_mapping.numel()
+    if slot_mapping.dtype != torch.int64 or seq_ids.dtype != torch.int32 or \
+            positions.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise TypeError("block_tables/seq_ids/positions int32, slot_mapping int64")
+    shape = (T, desc.num_kv_heads, desc.head_dim)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new and v_new must be {shape}")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("k_new/v_new must have the pool dtype")
+    if seq_ids.numel() != T or positions.numel() != T:
+        raise ValueError("seq_ids, positions and slot_mapping must have one entry per token")
+    if T == 0:
+        return
+    st = _lib.pa_kv_append(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                           _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                           _dev(slot_mapping, "slot_mapping"), T,
+                           _dev(block_tables, "block_tables"), block_tables.shape[1],
+                           _dev(seq_ids, "seq_ids"), _dev(positions, "positions"),
+                           _stream(stream))
+    _check(st, "pa_kv_append")
 
 
 from .block_manager import BlockManager  # noqa: E402,F401

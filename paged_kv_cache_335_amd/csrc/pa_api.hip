@@ -102,7 +102,42 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool, const voi
   }
   hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
                                        pool->num_kv_heads, pool->block_size, pool->head_dim,
-                                       elem_bytes(pool->dtype), st);
+                                       elem_bytes(pool->dtype), nullptr, 0, nullptr, nullptr,
+                                       st);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+pa_status pa_kv_append(const pa_pool* pool, void* k_pool, void* v_pool, const void* k_new,
+                       const void* v_new, const int64_t* slot_mapping, int32_t T,
+                       int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* seq_ids, const int32_t* positions, void* stream) {
+  if (!pool_ok(pool) || T < 0 || max_blocks_per_seq <= 0) return PA_EINVAL;
+  if (T == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping || !block_tables || !seq_ids ||
+      !positions)
+    return PA_EINVAL;
+  hipStream_t st = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int64_t> sl;
+    std::vector<int32_t> sq, ps;
+    if (!fetch(sl, slot_mapping, (size_t)T, st) || !fetch(sq, seq_ids, (size_t)T, st) ||
+        !fetch(ps, positions, (size_t)T, st))
+      return PA_EHIP;
+    const int64_t nslots = (int64_t)pool->num_blocks * pool->block_size;
+    std::vector<uint8_t> seen((size_t)nslots, 0);
+    for (int32_t i = 0; i < T; ++i) {
+      const int64_t x = sl[i];
+      if (x < 0) continue;
+      if (x >= nslots || seen[(size_t)x]) return PA_EINVAL;
+      seen[(size_t)x] = 1;
+      if (sq[i] < 0 || ps[i] < 0 || ps[i] / pool->block_size >= max_blocks_per_seq)
+        return PA_EINVAL;
+    }
+  }
+  hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
+                                       pool->num_kv_heads, pool->block_size, pool->head_dim,
+                                       elem_bytes(pool->dtype), block_tables,
+                                       max_blocks_per_seq, seq_ids, positions, st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 

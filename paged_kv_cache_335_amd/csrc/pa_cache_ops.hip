@@ -10,7 +10,8 @@
 //    attention-lab page): the whole of block src, every kv head and slot, is
 //    copied to block dst in both pools.
 //  * Table update: the block-table entry covering a written token's logical
-//    position takes the block the token went to.
+//    position takes the block the token went to.  The append entry point
+//    runs it inside the slot-write launch.
 #include "pa_internal.h"
 
 namespace pakv {
@@ -29,17 +30,29 @@ __device__ __forceinline__ void st_pool(T* dst, T v) {
 
 constexpr int kThreads = 256;
 
+// Optional table growth done by the slot-write launch (append = table
+// update + slot write in one kernel).  tables == nullptr: no table update.
+struct TableArgs {
+  int32_t* tables;
+  int32_t max_blocks;
+  const int32_t* seq_ids;
+  const int32_t* positions;
+};
+
 // One workgroup per new token.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     const uint8_t* __restrict__ k_new, const uint8_t* __restrict__ v_new,
     const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t block_size,
-    int32_t head_dim) {
+    int32_t head_dim, TableArgs ta) {
   const int i = blockIdx.x;
   const int64_t slot = slots[i];
   if (slot < 0) return;
   const int64_t blk = slot / block_size;
+  if (ta.tables != nullptr && threadIdx.x == 0)
+    ta.tables[(size_t)ta.seq_ids[i] * ta.max_blocks + ta.positions[i] / block_size] =
+        static_cast<int32_t>(blk);
   const int r = static_cast<int>(slot % block_size);
   constexpr int ES = sizeof(E);
   const size_t row_bytes = (size_t)head_dim * ES;
@@ -116,18 +129,20 @@ __global__ __launch_bounds__(kThreads) void table_update_kernel(
 hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slots, int32_t T, int32_t num_kv_heads,
                            int32_t block_size, int32_t head_dim, int32_t elem_bytes,
-                           hipStream_t st) {
+                           int32_t* block_tables, int32_t max_blocks, const int32_t* seq_ids,
+                           const int32_t* positions, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   auto kp = static_cast<uint8_t*>(k_pool);
   auto vp = static_cast<uint8_t*>(v_pool);
   auto kn = static_cast<const uint8_t*>(k_new);
   auto vn = static_cast<const uint8_t*>(v_new);
+  const TableArgs ta{block_tables, max_blocks, seq_ids, positions};
   if (elem_bytes == 2)
     kv_write_kernel<uint16_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
-                                                      block_size, head_dim);
+                                                      block_size, head_dim, ta);
   else
     kv_write_kernel<uint32_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
-                                                      block_size, head_dim);
+                                                      block_size, head_dim, ta);
   return hipGetLastError();
 }
 

@@ -59,10 +59,13 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group);
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
                          hipStream_t stream);
 
+// block_tables == nullptr: no table update (plain slot write).
 hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new,
                            const void* v_new, const int64_t* slots, int32_t T,
                            int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
-                           int32_t elem_bytes, hipStream_t stream);
+                           int32_t elem_bytes, int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* seq_ids, const int32_t* positions,
+                           hipStream_t stream);
 
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
                              int32_t num_pairs, size_t block_bytes, hipStream_t stream);

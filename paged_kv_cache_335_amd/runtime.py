@@ -10,9 +10,9 @@ A decode step for a batch of live sequences:
      is full, copy-on-write pair when the tail is shared and partly filled);
   2. one async copy of [slots | row ids | positions | lengths] to the device;
   3. pa_block_copy for copy-on-write pairs (if any);
-  4. pa_table_update: device table rows follow the growth;
-  5. pa_kv_write: the new tokens' K/V go into their slots;
-  6. pa_decode: attention over the grown contexts.
+  4. pa_kv_append: device table rows follow the growth and the new tokens'
+     K/V go into their slots, in one launch;
+  5. pa_decode: attention over the grown contexts.
 """
 import ctypes
 
@@ -20,7 +20,7 @@ import numpy as np
 import torch
 
 from . import (PA_OK, PagedKVError, pa_block_copy, pa_decode, pa_decode_partition_tokens,
-               pa_decode_workspace_bytes, pa_kv_write, pa_table_update)
+               pa_decode_workspace_bytes, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -197,8 +197,8 @@ class PagedKVCache:
                 d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device,
                                                                            non_blocking=False)
                 pa_block_copy(self.k_pool, self.v_pool, d_pairs, stream=stream)
-            pa_table_update(self.tables, self.B, d_rows, d_pos, d_slots, stream=stream)
-            pa_kv_write(self.k_pool, self.v_pool, k_new, v_new, d_slots, stream=stream)
+            pa_kv_append(self.k_pool, self.v_pool, k_new, v_new, d_slots, self.tables, d_rows,
+                         d_pos, stream=stream)
         return len(pairs)
 
     # --- decode -------------------------------------------------------------

@@ -271,6 +271,40 @@ def test_table_update_bit_exact(pk):
     assert np.array_equal(t.cpu().numpy(), expect)
 
 
+def test_kv_append_bit_exact(pk):
+    """Append = table update + slot write in one launch: the pools match the
+    oracle's slot write and the table the update rule, bit for bit."""
+    rng = np.random.default_rng(12)
+    nb, Hkv, d, B, S, W = 300, 8, 128, 16, 24, 20
+    w = kv_write_case(nb, Hkv, d, B, 0, dtype="bf16", seed=13)
+    # one token per sequence at a random position, into distinct random slots
+    T = S
+    seq = np.arange(S, dtype=np.int32)
+    pos = rng.integers(0, W * B, T).astype(np.int32)
+    slots = rng.permutation(nb * B)[:T].astype(np.int64)
+    slots[::5] = -1
+    k_new = rng.standard_normal((T, Hkv, d), dtype=np.float32)
+    v_new = rng.standard_normal((T, Hkv, d), dtype=np.float32)
+    kn = torch.from_numpy(k_new).to(torch.bfloat16)
+    vn = torch.from_numpy(v_new).to(torch.bfloat16)
+    kref, vref = oracle.kv_write(w.k_pool, w.v_pool, to_numpy_storage(kn), to_numpy_storage(vn),
+                                 slots)
+    tables = rng.integers(0, nb, (S, W)).astype(np.int32)
+    expect = tables.copy()
+    for s_, p_, sl in zip(seq, pos, slots):
+        if sl >= 0:
+            expect[s_, p_ // B] = sl // B
+    k = from_numpy_storage(w.k_pool, "bf16", "cuda")
+    v = from_numpy_storage(w.v_pool, "bf16", "cuda")
+    t = torch.from_numpy(tables).cuda()
+    pk.pa_kv_append(k, v, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda(), t,
+                    torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_numpy_storage(k), kref)
+    assert np.array_equal(to_numpy_storage(v), vref)
+    assert np.array_equal(t.cpu().numpy(), expect)
+
+
 # --- the whole path: block manager -> copy -> write -> decode -----------------
 def _run_path_both(pk, prompts, samples, shared, private_lo, private_hi, Hq, Hkv, d, seed,
                    decode_steps=3):
