@@ -687,73 +687,62 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Split-context reduce: one workgroup of 4 waves per (query head, sequence).
-// Wave w combines partitions w, w+4, ...; lanes own output dims; the four
-// waves meet in LDS.
+// Split-context reduce: one wave per (query head, sequence), four query
+// heads per workgroup.  A wave reads its pieces' m values across lanes for
+// the maximum, then walks the pieces 16 at a time (their (m, l) as uniform
+// loads, o as two 256-byte rows per piece) so that a long sequence's pieces
+// are fetched in a few rounds; lanes own output dims.  Sequences finished in
+// place by the decode kernel return at once.
 // ---------------------------------------------------------------------------
+constexpr int kReduceHeads = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int NW = 4, EPL = D / 64, UNR = 4;
-  const int hq = blockIdx.x, s = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int EPL = D / 64, UNR = 16;
+  const int s = blockIdx.y;
   const int np = a.seg_count[s];
   if (np <= 1) return;  // finished in place by the decode kernel (or no context)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hq = blockIdx.x * kReduceHeads + wave;
+  if (hq >= a.num_q_heads) return;
   const size_t base = part_index(a, s, hq, 0);
   const float* pm = a.part_m + base;
   const float* pl = a.part_l + base;
 
-  __shared__ float sm_x[NW];
-  __shared__ float sm_num[NW][D];
   float M = kNegInf;
-  for (int p = threadIdx.x; p < np; p += NW * 64) M = fmaxf(M, pm[p]);
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, pm[p]);
   M = wave_max(M);
-  if (lane == 0) sm_x[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(sm_x[0], sm_x[1]), fmaxf(sm_x[2], sm_x[3]));
-  __syncthreads();
 
   float den = 0.f, num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-  for (int p0 = wave; p0 < np; p0 += NW * UNR) {
+  for (int p0 = 0; p0 < np; p0 += UNR) {
     float f[UNR], o[UNR][EPL];
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int p = p0 + k * NW;
-      f[k] = 0.f;
+      const int p = min(p0 + k, np - 1);  // clamped: past-the-end terms get f = 0
+      f[k] = p0 + k < np ? fexp2(pm[p] - M) : 0.f;
+      den = fmaf(f[k], pl[p], den);
+      const float* po = a.part_o + (base + p) * D;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[k][e] = 0.f;
-      if (p < np) {
-        f[k] = fexp2(pm[p] - M);
-        den = fmaf(f[k], pl[p], den);
-        const float* po = a.part_o + (base + p) * D;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[k][e] = po[e * 64 + lane];
-      }
+      for (int e = 0; e < EPL; ++e) o[k][e] = po[e * 64 + lane];
     }
 #pragma unroll
     for (int k = 0; k < UNR; ++k)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) num[e] = fmaf(f[k], o[k][e], num[e]);
   }
-  if (lane == 0) sm_x[wave] = den;
+  const float inv = 1.f / den;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) sm_num[wave][e * 64 + lane] = num[e];
-  __syncthreads();
-  if (wave == 0) {
-    const float dt = (sm_x[0] + sm_x[1]) + (sm_x[2] + sm_x[3]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int i = e * 64 + lane;
-      const float n = (sm_num[0][i] + sm_num[1][i]) + (sm_num[2][i] + sm_num[3][i]);
-      store_out<T>(a.out, ((size_t)s * a.num_q_heads + hq) * D + i, n / dt);
-    }
-  }
+  for (int e = 0; e < EPL; ++e)
+    store_out<T>(a.out, ((size_t)s * a.num_q_heads + hq) * D + e * 64 + lane, num[e] * inv);
 }
 
 template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {
-  decode_reduce_kernel<T, D><<<dim3(a.num_q_heads, a.num_seqs), 256, 0, st>>>(a);
+  const dim3 grid((a.num_q_heads + kReduceHeads - 1) / kReduceHeads, a.num_seqs);
+  decode_reduce_kernel<T, D><<<grid, kReduceHeads * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
