@@ -19,6 +19,7 @@ from .build import LIB, build
 
 F32 = 0
 BF16 = 1
+FP8 = 2
 
 _lib = None
 
@@ -44,6 +45,10 @@ def lib():
         L.oracle_kv_write.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
         L.oracle_block_copy.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32]
         L.oracle_max_threads.argtypes = []
+        L.oracle_e4m3_encode.argtypes = [vp, vp, i32]
+        L.oracle_e4m3_decode.argtypes = [vp, vp, i32]
+        L.oracle_e4m3_encode.restype = None
+        L.oracle_e4m3_decode.restype = None
         for fn in ("oracle_decode_pairs", "oracle_decode", "oracle_decode_dense",
                    "oracle_decode_split", "oracle_gather", "oracle_kv_write",
                    "oracle_block_copy", "oracle_max_threads"):
@@ -57,7 +62,10 @@ def _dtype_code(arr):
         return F32
     if arr.dtype == np.uint16:  # bf16 bit patterns
         return BF16
-    raise TypeError(f"pool dtype must be float32 or uint16 (bf16 bits), got {arr.dtype}")
+    if arr.dtype == np.uint8:  # 8-bit regions: E4M3 codes then per-token fp32 scales
+        return FP8
+    raise TypeError(f"pool dtype must be float32, uint16 (bf16 bits) or uint8 (8-bit "
+                    f"regions), got {arr.dtype}")
 
 
 def _c(arr, dtype=None):
@@ -74,8 +82,22 @@ def _check(rc, what):
         raise OracleError(f"{what} failed with code {rc}")
 
 
-def _geom(k_pool):
-    # k_pool: [num_blocks][H_kv][B][d]
+def fp8_region_bytes(block_size, head_dim):
+    """Bytes of one (block, kv head) region of an 8-bit pool: block_size *
+    head_dim E4M3 codes (K token-major [B][d], V dim-major [d][B]) followed by
+    block_size fp32 scales, one per token."""
+    return block_size * head_dim + 4 * block_size
+
+
+def _geom(k_pool, head_dim=None):
+    """(num_blocks, B, H_kv, d) of a pool.  fp32 / bf16 pools are
+    [num_blocks][H_kv][B][d]; 8-bit pools are uint8 [num_blocks][H_kv][R] with
+    R = B * (d + 4), so d must be given (the queries or new tokens carry it)."""
+    if k_pool.dtype == np.uint8:
+        nb, nkv, R = k_pool.shape
+        if head_dim is None or R % (head_dim + 4):
+            raise ValueError(f"8-bit region of {R} bytes does not fit head_dim {head_dim}")
+        return nb, R // (head_dim + 4), nkv, head_dim
     nb, nkv, B, d = k_pool.shape
     return nb, B, nkv, d
 
@@ -87,8 +109,8 @@ def decode(k_pool, v_pool, q, block_tables, context_lens, scale, threads=0):
     uint16 holding bf16 bits.  block_tables int32 [S][maxB], context_lens int32
     [S].  Returns float64 [S][Hq][d].
     """
-    nb, B, nkv, d = _geom(k_pool)
-    S, Hq, _ = q.shape
+    S, Hq, dq = q.shape
+    nb, B, nkv, d = _geom(k_pool, dq)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -105,8 +127,8 @@ def decode(k_pool, v_pool, q, block_tables, context_lens, scale, threads=0):
 def decode_pairs(k_pool, v_pool, q, block_tables, context_lens, scale, pairs, threads=0):
     """Paged decode attention for selected (sequence, query head) pairs.
     Returns float64 [n_pairs][d]."""
-    nb, B, nkv, d = _geom(k_pool)
-    S, Hq, _ = q.shape
+    S, Hq, dq = q.shape
+    nb, B, nkv, d = _geom(k_pool, dq)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -142,8 +164,8 @@ def decode_dense(k_dense, v_dense, q, context_lens, scale, threads=0):
 def decode_split(k_pool, v_pool, q, block_tables, context_lens, scale, partition_tokens,
                  threads=0):
     """Split-context attention (partials combined by max/sum-exp)."""
-    nb, B, nkv, d = _geom(k_pool)
-    S, Hq, _ = q.shape
+    S, Hq, dq = q.shape
+    nb, B, nkv, d = _geom(k_pool, dq)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -158,9 +180,10 @@ def decode_split(k_pool, v_pool, q, block_tables, context_lens, scale, partition
     return out
 
 
-def gather(k_pool, v_pool, table_row, kv_head, length):
-    """Walk one table row and return contiguous float64 (Kc [L][d], Vc [L][d])."""
-    nb, B, nkv, d = _geom(k_pool)
+def gather(k_pool, v_pool, table_row, kv_head, length, head_dim=None):
+    """Walk one table row and return contiguous float64 (Kc [L][d], Vc [L][d]),
+    dequantised for 8-bit pools (which need head_dim)."""
+    nb, B, nkv, d = _geom(k_pool, head_dim)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     tr, trp = _c(table_row, np.int32)
@@ -175,12 +198,15 @@ def gather(k_pool, v_pool, table_row, kv_head, length):
 
 
 def kv_write(k_pool, v_pool, k_new, v_new, slot_mapping):
-    """Return copies of the pools with each token's K/V written into its slot."""
-    nb, B, nkv, d = _geom(k_pool)
+    """Return copies of the pools with each token's K/V written into its slot.
+    k_new, v_new [T][H_kv][d] have the pool's element type, or bf16 bits
+    (uint16) for an 8-bit pool, which stores them quantised."""
+    nb, B, nkv, d = _geom(k_pool, k_new.shape[-1])
     kp = np.array(k_pool, copy=True, order="C")
     vp_ = np.array(v_pool, copy=True, order="C")
-    kn, knp = _c(k_new, kp.dtype)
-    vn, vnp = _c(v_new, kp.dtype)
+    src_dtype = np.uint16 if kp.dtype == np.uint8 else kp.dtype
+    kn, knp = _c(k_new, src_dtype)
+    vn, vnp = _c(v_new, src_dtype)
     sm, smp = _c(slot_mapping, np.int64)
     rc = lib().oracle_kv_write(_dtype_code(kp), nb, B, nkv, d,
                                kp.ctypes.data_as(ctypes.c_void_p),
@@ -190,9 +216,10 @@ def kv_write(k_pool, v_pool, k_new, v_new, slot_mapping):
     return kp, vp_
 
 
-def block_copy(k_pool, v_pool, pairs):
-    """Return copies of the pools with each (src, dst) block copied."""
-    nb, B, nkv, d = _geom(k_pool)
+def block_copy(k_pool, v_pool, pairs, head_dim=None):
+    """Return copies of the pools with each (src, dst) block copied (8-bit
+    pools need head_dim)."""
+    nb, B, nkv, d = _geom(k_pool, head_dim)
     kp = np.array(k_pool, copy=True, order="C")
     vp_ = np.array(v_pool, copy=True, order="C")
     pr, prp = _c(np.asarray(pairs).reshape(-1, 2), np.int32)
@@ -201,6 +228,22 @@ def block_copy(k_pool, v_pool, pairs):
                                  vp_.ctypes.data_as(ctypes.c_void_p), prp, pr.shape[0])
     _check(rc, "oracle_block_copy")
     return kp, vp_
+
+
+def e4m3_encode(x):
+    """OCP E4M3 codes (uint8) of float32 values, nearest even, saturating."""
+    xx, xp = _c(np.asarray(x, np.float32).reshape(-1), np.float32)
+    out = np.empty(xx.shape[0], np.uint8)
+    lib().oracle_e4m3_encode(xp, out.ctypes.data_as(ctypes.c_void_p), xx.shape[0])
+    return out.reshape(np.shape(x))
+
+
+def e4m3_decode(codes):
+    """Values (float64) of OCP E4M3 codes; NaN for the two NaN codes."""
+    cc, cp = _c(np.asarray(codes, np.uint8).reshape(-1), np.uint8)
+    out = np.empty(cc.shape[0], np.float64)
+    lib().oracle_e4m3_decode(cp, out.ctypes.data_as(ctypes.c_void_p), cc.shape[0])
+    return out.reshape(np.shape(codes))
 
 
 def max_threads():

@@ -24,7 +24,13 @@
  * Pool layout (an interface fact the pages leave open; this build fixes it):
  *   K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
  *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major)
- * Element types: 0 = IEEE fp32, 1 = bf16 (upper 16 bits of an fp32).
+ * Element types: 0 = IEEE fp32, 1 = bf16 (upper 16 bits of an fp32),
+ * 2 = 8-bit float cache (OCP FP8 E4M3 codes with one fp32 scale per token and
+ * kv head).  For type 2 each (block, kv head) is one region of
+ * block_size*head_dim code bytes -- K token-major [B][d], V dim-major [d][B]
+ * -- followed by block_size fp32 scales, one per token; a stored element's
+ * value is decode(code) * scale[token].  Queries, outputs and the tokens
+ * handed to the slot write are bf16 for type 2.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 #include <math.h>
@@ -37,6 +43,56 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_FP8 2
+
+/*
+ * OCP 8-bit floating point, E4M3 ("OCP 8-bit Floating Point Specification",
+ * the E4M3 format): sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; there are
+ * no infinities, so the largest magnitude is S.1111.110 = 448.
+ */
+static double orc_e4m3_decode(uint8_t c) {
+  const int sign = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 0xF && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/*
+ * Round an fp32 value to the nearest E4M3 code, ties to even; magnitudes at
+ * or past 464 (the midpoint between 448 and the next power of two's first
+ * step, which E4M3 lacks) saturate to 448.  Written on the fp32 bit pattern.
+ */
+static uint8_t orc_e4m3_encode(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80);
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7F;  /* NaN */
+  if (a >= 0x43E80000u) return sign | 0x7E; /* |x| >= 464: saturate to 448 */
+  if (a < 0x3C800000u) {                    /* |x| < 2^-6: subnormal or zero */
+    float t;
+    memcpy(&t, &a, sizeof t);
+    return sign | (uint8_t)rintf(t * 512.0f); /* m = RNE(|x| / 2^-9); 8 is 2^-6 */
+  }
+  const uint32_t e = (a >> 23) - 120u;       /* biased E4M3 exponent, 1..15 */
+  const uint32_t m3 = (a >> 20) & 7u;        /* top three mantissa bits */
+  const uint32_t rest = a & 0xfffffu;        /* the 20 bits below them */
+  uint32_t code = (e << 3) | m3;
+  if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) code += 1; /* carries into e */
+  return sign | (uint8_t)code;
+}
+
+/* Bytes of one (block, kv head) region of an 8-bit pool. */
+static size_t orc_fp8_region(int B, int d) { return (size_t)B * d + 4u * (size_t)B; }
+
+static double orc_fp8_scale(const void* pool, size_t region_base, int B, int d, int r) {
+  float s;
+  memcpy(&s, (const char*)pool + region_base + (size_t)B * d + 4u * (size_t)r, sizeof s);
+  return (double)s;
+}
 
 /* Widen one stored element to double, exactly. */
 static double orc_load(int dtype, const void* base, size_t idx) {
@@ -59,6 +115,29 @@ static size_t v_index(int nkv, int B, int d, int32_t blk, int g, int r, int i) {
   return (((size_t)blk * nkv + g) * d + i) * (size_t)B + r;
 }
 
+/* Element i of token slot r of (block, kv head g), widened to double. */
+static double orc_k_elem(int dtype, int nkv, int B, int d, const void* k_pool, int32_t blk,
+                         int g, int r, int i) {
+  if (dtype == ORC_FP8) {
+    const size_t base = ((size_t)blk * nkv + g) * orc_fp8_region(B, d);
+    const uint8_t c = ((const uint8_t*)k_pool)[base + (size_t)r * d + i];
+    return orc_e4m3_decode(c) * orc_fp8_scale(k_pool, base, B, d, r);
+  }
+  return orc_load(dtype, k_pool, k_index(nkv, B, d, blk, g, r, i));
+}
+static double orc_v_elem(int dtype, int nkv, int B, int d, const void* v_pool, int32_t blk,
+                         int g, int r, int i) {
+  if (dtype == ORC_FP8) {
+    const size_t base = ((size_t)blk * nkv + g) * orc_fp8_region(B, d);
+    const uint8_t c = ((const uint8_t*)v_pool)[base + (size_t)i * B + r];
+    return orc_e4m3_decode(c) * orc_fp8_scale(v_pool, base, B, d, r);
+  }
+  return orc_load(dtype, v_pool, v_index(nkv, B, d, blk, g, r, i));
+}
+
+/* Element type of queries and outputs for a pool type. */
+static int orc_q_dtype(int dtype) { return dtype == ORC_FP8 ? ORC_BF16 : dtype; }
+
 /*
  * Gather logical tokens [0, L) of (sequence s, kv head g) into contiguous
  * double arrays Kc[L][d], Vc[L][d]: token t lives in physical block
@@ -71,8 +150,8 @@ static void orc_gather(int dtype, int nkv, int B, int d, const void* k_pool,
     int32_t blk = table_row[t / B];
     int r = t % B;
     for (int i = 0; i < d; ++i) {
-      Kc[(size_t)t * d + i] = orc_load(dtype, k_pool, k_index(nkv, B, d, blk, g, r, i));
-      Vc[(size_t)t * d + i] = orc_load(dtype, v_pool, v_index(nkv, B, d, blk, g, r, i));
+      Kc[(size_t)t * d + i] = orc_k_elem(dtype, nkv, B, d, k_pool, blk, g, r, i);
+      Vc[(size_t)t * d + i] = orc_v_elem(dtype, nkv, B, d, v_pool, blk, g, r, i);
     }
   }
 }
@@ -114,7 +193,7 @@ static void orc_attend(const double* qd, const double* Kc, const double* Vc, int
 }
 
 static int check_geometry(int dtype, int num_blocks, int B, int nkv, int d, int nq) {
-  if (dtype != ORC_F32 && dtype != ORC_BF16) return 1;
+  if (dtype != ORC_F32 && dtype != ORC_BF16 && dtype != ORC_FP8) return 1;
   if (num_blocks <= 0 || B <= 0 || nkv <= 0 || d <= 0 || nq <= 0) return 1;
   if (nq % nkv != 0) return 1;
   return 0;
@@ -170,7 +249,7 @@ int oracle_decode_pairs(int dtype, int num_blocks, int block_size, int num_kv_he
       failed = 1;
     } else {
       for (int i = 0; i < d; ++i)
-        qd[i] = orc_load(dtype, q, ((size_t)s * num_q_heads + h) * d + i);
+        qd[i] = orc_load(orc_q_dtype(dtype), q, ((size_t)s * num_q_heads + h) * d + i);
       orc_gather(dtype, nkv, B, d, k_pool, v_pool,
                  block_tables + (size_t)s * max_blocks_per_seq, g, L, Kc, Vc);
       orc_attend(qd, Kc, Vc, d, L, scale, sc, out + (size_t)p * d);
@@ -217,6 +296,7 @@ int oracle_decode_dense(int dtype, int num_kv_heads, int head_dim, const void* k
                         int num_q_heads, const int32_t* context_lens, double scale,
                         double* out, int num_threads) {
   if (check_geometry(dtype, 1, 1, num_kv_heads, head_dim, num_q_heads)) return 1;
+  if (dtype == ORC_FP8) return 1; /* dense copies are plain fp32 / bf16 arrays */
   const int d = head_dim, G = num_q_heads / num_kv_heads;
   for (int s = 0; s < num_seqs; ++s)
     if (context_lens[s] <= 0 || context_lens[s] > max_len) return 2;
@@ -235,7 +315,7 @@ int oracle_decode_dense(int dtype, int num_kv_heads, int head_dim, const void* k
       failed = 1;
     } else {
       for (int i = 0; i < d; ++i)
-        qd[i] = orc_load(dtype, q, ((size_t)s * num_q_heads + h) * d + i);
+        qd[i] = orc_load(orc_q_dtype(dtype), q, ((size_t)s * num_q_heads + h) * d + i);
       size_t base = ((size_t)s * num_kv_heads + g) * (size_t)max_len * d;
       for (int t = 0; t < L; ++t)
         for (int i = 0; i < d; ++i) {
@@ -296,7 +376,7 @@ int oracle_decode_split(int dtype, int num_blocks, int block_size, int num_kv_he
       failed = 1;
     } else {
       for (int i = 0; i < d; ++i)
-        qd[i] = orc_load(dtype, q, ((size_t)s * num_q_heads + h) * d + i);
+        qd[i] = orc_load(orc_q_dtype(dtype), q, ((size_t)s * num_q_heads + h) * d + i);
       orc_gather(dtype, nkv, B, d, k_pool, v_pool,
                  block_tables + (size_t)s * max_blocks_per_seq, g, L, Kc, Vc);
       double M = -INFINITY;
@@ -348,6 +428,46 @@ int oracle_gather(int dtype, int num_blocks, int block_size, int num_kv_heads,
 }
 
 /*
+ * Slot write into an 8-bit pool: each token's bf16 K row and V row of each
+ * kv head are quantised on their own.  In fp32: amax = max |x| over the row,
+ * scale = amax / 448 (0 for an all-zero row), code_e = E4M3(x_e / scale)
+ * rounded to nearest even; the codes go to the token's slot, the scale to
+ * the token's scale entry of the region.  Same slot rules as below.
+ */
+static int orc_kv_write_fp8(int B, int d, int nkv, uint8_t* k_pool, uint8_t* v_pool,
+                            const uint16_t* k_new, const uint16_t* v_new,
+                            const int64_t* slot_mapping, int T) {
+  const size_t region = orc_fp8_region(B, d);
+  for (int i = 0; i < T; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    int32_t blk = (int32_t)(slot / B);
+    int r = (int)(slot % B);
+    for (int g = 0; g < nkv; ++g) {
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t* src = (kv == 0 ? k_new : v_new) + ((size_t)i * nkv + g) * d;
+        uint8_t* pool = kv == 0 ? k_pool : v_pool;
+        const size_t base = ((size_t)blk * nkv + g) * region;
+        float amax = 0.0f;
+        for (int e = 0; e < d; ++e) {
+          float x = (float)orc_load(ORC_BF16, src, (size_t)e);
+          if (fabsf(x) > amax) amax = fabsf(x);
+        }
+        const float scale = amax / 448.0f;
+        for (int e = 0; e < d; ++e) {
+          float x = (float)orc_load(ORC_BF16, src, (size_t)e);
+          uint8_t c = scale > 0.0f ? orc_e4m3_encode(x / scale) : 0;
+          size_t at = kv == 0 ? (size_t)r * d + e : (size_t)e * B + r;
+          pool[base + at] = c;
+        }
+        memcpy(pool + base + (size_t)B * d + 4u * (size_t)r, &scale, sizeof scale);
+      }
+    }
+  }
+  return 0;
+}
+
+/*
  * Slot write ("Dynamic Growth" on the glossary page: a sequence grows token
  * by token into the block its table names).  For every i with
  * slot_mapping[i] >= 0: block = slot / B, offset = slot % B, and for every kv
@@ -364,6 +484,9 @@ int oracle_kv_write(int dtype, int num_blocks, int block_size, int num_kv_heads,
   const size_t es = orc_elem_size(dtype);
   for (int i = 0; i < T; ++i)
     if (slot_mapping[i] >= (int64_t)num_blocks * B) return 2;
+  if (dtype == ORC_FP8) return orc_kv_write_fp8(B, d, nkv, (uint8_t*)k_pool, (uint8_t*)v_pool,
+                                                (const uint16_t*)k_new, (const uint16_t*)v_new,
+                                                slot_mapping, T);
   for (int i = 0; i < T; ++i) {
     int64_t slot = slot_mapping[i];
     if (slot < 0) continue;
@@ -393,7 +516,8 @@ int oracle_block_copy(int dtype, int num_blocks, int block_size, int num_kv_head
   if (check_geometry(dtype, num_blocks, block_size, num_kv_heads, head_dim, num_kv_heads))
     return 1;
   const size_t block_bytes =
-      (size_t)num_kv_heads * block_size * head_dim * orc_elem_size(dtype);
+      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_region(block_size, head_dim)
+                       : (size_t)num_kv_heads * block_size * head_dim * orc_elem_size(dtype);
   for (int p = 0; p < num_pairs; ++p) {
     int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return 2;
@@ -406,6 +530,14 @@ int oracle_block_copy(int dtype, int num_blocks, int block_size, int num_kv_head
             (const char*)v_pool + (size_t)src * block_bytes, block_bytes);
   }
   return 0;
+}
+
+/* The E4M3 codec over arrays (for pinning it against the format). */
+void oracle_e4m3_encode(const float* x, uint8_t* codes, int n) {
+  for (int i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(x[i]);
+}
+void oracle_e4m3_decode(const uint8_t* codes, double* x, int n) {
+  for (int i = 0; i < n; ++i) x[i] = orc_e4m3_decode(codes[i]);
 }
 
 /* Threads OpenMP will use for the calls above (for reporting). */

@@ -18,7 +18,7 @@ class Config:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # pool storage: "f32", "bf16" or "fp8" (E4M3 + scales)
     block_size: int
     lengths: tuple             # see gen.draw_lengths
     pool: tuple                # ("fixed", n_blocks) or ("plus", fraction)

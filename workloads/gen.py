@@ -12,6 +12,14 @@ Pool layout (fixed by the library's interface):
 bf16 data is carried as uint16 bit patterns on the numpy side and as
 torch.bfloat16 on the torch side.
 
+8-bit pools ("fp8") are uint8 [num_blocks][H_kv][R] with R = B*d + 4*B: per
+(block, kv head) the E4M3 codes (K token-major [B][d], V dim-major [d][B])
+then B float32 scales, one per token.  Their payload is drawn directly as
+codes and scales, with no quantisation arithmetic: magnitude codes uniform
+over the 127 finite ones (0x00..0x7E), a random sign bit, and scales
+2^-7 * U[1, 2), so stored values reach 448 * 2^-6 = 7, the range of the
+bf16 cases' normal draws.  Queries and new tokens stay bf16.
+
 Every slot that no sequence's context covers is filled with poison
 (K = 64.0, V = 1024.0, both exact in bf16), so reading a slot that should be
 masked shows up far above any tolerance.
@@ -47,7 +55,7 @@ def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy()
-    if t.dtype in (torch.int32, torch.int64):
+    if t.dtype in (torch.int32, torch.int64, torch.uint8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
@@ -61,7 +69,78 @@ def from_numpy_storage(a: np.ndarray, dtype: str, device="cpu") -> torch.Tensor:
 
 
 def _torch_dtype(dtype: str):
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    """Element type of queries (and of pools other than 8-bit ones)."""
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+# --- 8-bit regions -----------------------------------------------------------
+FP8_POISON_CODE = 0x68          # E4M3 code of 64.0
+FP8_POISON_K_SCALE = 1.0        # poison K = 64.0
+FP8_POISON_V_SCALE = 16.0       # poison V = 1024.0
+
+
+def fp8_region_bytes(B: int, d: int) -> int:
+    return B * d + 4 * B
+
+
+def fp8_split(pool, B: int, d: int):
+    """Views (codes [nb][H][B*d] uint8, scales [nb][H][B] float32) of an
+    8-bit pool given as a numpy array or a torch tensor."""
+    if isinstance(pool, torch.Tensor):
+        return pool[..., :B * d], pool[..., B * d:].view(torch.float32)
+    return pool[..., :B * d], pool[..., B * d:].view(np.float32)
+
+
+def _fp8_codes_np(rng, n):
+    mag = rng.integers(0, 0x7F, size=n, dtype=np.uint8)
+    sign = (rng.integers(0, 2, size=n, dtype=np.uint8) << 7).astype(np.uint8)
+    return mag | sign
+
+
+def _fp8_pool_np(rng, nb, Hkv, B, d):
+    pool = np.empty((nb, Hkv, fp8_region_bytes(B, d)), np.uint8)
+    codes, scales = fp8_split(pool, B, d)
+    codes[...] = _fp8_codes_np(rng, nb * Hkv * B * d).reshape(nb, Hkv, B * d)
+    scales[...] = (rng.random((nb, Hkv, B), dtype=np.float32) + 1.0) * np.float32(2.0 ** -7)
+    return pool
+
+
+def _fp8_pool_torch(g, nb, Hkv, B, d, device):
+    pool = torch.empty((nb, Hkv, fp8_region_bytes(B, d)), dtype=torch.uint8, device=device)
+    codes, scales = fp8_split(pool, B, d)
+    chunk = max(1, (1 << 26) // (Hkv * B * d))
+    for b0 in range(0, nb, chunk):
+        b1 = min(nb, b0 + chunk)
+        mag = torch.randint(0, 0x7F, (b1 - b0, Hkv, B * d), generator=g, device=device,
+                            dtype=torch.uint8)
+        sign = torch.randint(0, 2, (b1 - b0, Hkv, B * d), generator=g, device=device,
+                             dtype=torch.uint8) << 7
+        codes[b0:b1] = mag | sign
+        scales[b0:b1] = (torch.rand((b1 - b0, Hkv, B), generator=g, device=device) + 1.0) \
+            * 2.0 ** -7
+    return pool
+
+
+def _fp8_poison(pool, dead, B, d, v_side: bool):
+    """Poison the dead token slots (dead: bool [nb][B]) of an 8-bit pool."""
+    codes, scales = fp8_split(pool, B, d)
+    sc = FP8_POISON_V_SCALE if v_side else FP8_POISON_K_SCALE
+    if isinstance(pool, torch.Tensor):
+        nb, H = pool.shape[0], pool.shape[1]
+        c = codes.view(nb, H, d, B) if v_side else codes.view(nb, H, B, d)
+        if v_side:
+            c.masked_fill_(dead[:, None, None, :], FP8_POISON_CODE)
+        else:
+            c.masked_fill_(dead[:, None, :, None], FP8_POISON_CODE)
+        scales.masked_fill_(dead[:, None, :], sc)
+        return
+    nb, H = pool.shape[0], pool.shape[1]
+    bi, ri = dead.nonzero()
+    if v_side:
+        codes.reshape(nb, H, d, B)[bi, :, :, ri] = FP8_POISON_CODE
+    else:
+        codes.reshape(nb, H, B, d)[bi, :, ri, :] = FP8_POISON_CODE
+    scales[bi, :, ri] = sc
 
 
 # --- lengths and pools -----------------------------------------------------
@@ -131,10 +210,12 @@ class DecodeCase:
         return self.k_pool.shape[0]
 
     def kv_bytes(self) -> int:
-        """Algorithmic KV bytes one decode reads: sum_s L_s * 2 * H_kv * d * e."""
-        e = 2 if self.dtype == "bf16" else 4
+        """Algorithmic KV bytes one decode reads: sum_s L_s * 2 * H_kv * (bytes
+        per token row: d * e, or d codes + one 4-byte scale for 8-bit pools)."""
         c = self.cfg
-        return int(self.lens.astype(np.int64).sum()) * 2 * c.num_kv_heads * c.head_dim * e
+        row = c.head_dim + 4 if self.dtype == "fp8" else \
+            c.head_dim * (2 if self.dtype == "bf16" else 4)
+        return int(self.lens.astype(np.int64).sum()) * 2 * c.num_kv_heads * row
 
     def oracle_inputs(self):
         """numpy views for the oracle (uint16 for bf16)."""
@@ -233,7 +314,26 @@ def decode_case(cfg: Config, payload: str = "numpy", device="cpu",
     q_shape = (cfg.num_seqs, cfg.num_q_heads, d)
     k_shape = (nb, Hkv, B, d)
     v_shape = (nb, Hkv, d, B)
-    if payload == "numpy":
+    if cfg.dtype == "fp8" and payload == "numpy":
+        q = torch.from_numpy(rng.standard_normal(q_shape, dtype=np.float32)).to(tdt)
+        k_np = _fp8_pool_np(rng, nb, Hkv, B, d)
+        v_np = _fp8_pool_np(rng, nb, Hkv, B, d)
+        _fp8_poison(k_np, ~live, B, d, v_side=False)
+        _fp8_poison(v_np, ~live, B, d, v_side=True)
+        q = q.to(device)
+        k = torch.from_numpy(k_np).to(device)
+        v = torch.from_numpy(v_np).to(device)
+    elif cfg.dtype == "fp8" and payload == "torch":
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        q = torch.randn(q_shape, generator=g, device=device, dtype=torch.float32).to(tdt)
+        k = _fp8_pool_torch(g, nb, Hkv, B, d, device)
+        v = _fp8_pool_torch(g, nb, Hkv, B, d, device)
+        dead = torch.from_numpy(~live).to(device)
+        if bool(dead.any()):
+            _fp8_poison(k, dead, B, d, v_side=False)
+            _fp8_poison(v, dead, B, d, v_side=True)
+    elif payload == "numpy":
         q32 = rng.standard_normal(q_shape, dtype=np.float32)
         k32 = rng.standard_normal(k_shape, dtype=np.float32)
         v32 = rng.standard_normal(v_shape, dtype=np.float32)
@@ -296,6 +396,12 @@ def kv_write_case(num_blocks, num_kv_heads, head_dim, block_size, T, dtype="bf16
     slots = rng.choice(nb * B, size=T, replace=False).astype(np.int64)
     if skip_fraction > 0:
         slots[rng.random(T) < skip_fraction] = -1
+    if dtype == "fp8":  # 8-bit pools take bf16 tokens
+        k_pool = _fp8_pool_np(rng, nb, Hkv, B, d)
+        v_pool = _fp8_pool_np(rng, nb, Hkv, B, d)
+        k_new = _payload_np(rng, (T, Hkv, d), "bf16")
+        v_new = _payload_np(rng, (T, Hkv, d), "bf16")
+        return KVWriteCase(dtype, k_pool, v_pool, k_new, v_new, slots)
     k_pool = _payload_np(rng, (nb, Hkv, B, d), dtype)
     v_pool = _payload_np(rng, (nb, Hkv, d, B), dtype)
     k_new = _payload_np(rng, (T, Hkv, d), dtype)
@@ -326,6 +432,9 @@ def block_copy_case(num_blocks, num_kv_heads, head_dim, block_size, P, dtype="bf
     src_pool = perm[P:]
     src = src_pool[rng.integers(0, len(src_pool), size=P)]
     pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    if dtype == "fp8":
+        return BlockCopyCase(dtype, _fp8_pool_np(rng, nb, Hkv, B, d),
+                             _fp8_pool_np(rng, nb, Hkv, B, d), pairs)
     k_pool = _payload_np(rng, (nb, Hkv, B, d), dtype)
     v_pool = _payload_np(rng, (nb, Hkv, d, B), dtype)
     return BlockCopyCase(dtype, k_pool, v_pool, pairs)
