@@ -83,21 +83,27 @@ def _check(rc, what):
 
 
 def fp8_region_bytes(block_size, head_dim):
-    """Bytes of one (block, kv head) region of an 8-bit pool: block_size *
-    head_dim E4M3 codes (K token-major [B][d], V dim-major [d][B]) followed by
-    block_size fp32 scales, one per token."""
-    return block_size * head_dim + 4 * block_size
+    """Bytes of one (block, kv head) region of an 8-bit pool: (K buffer, V
+    buffer).  K: block_size * head_dim E4M3 codes (token-major [B][d]), then
+    the bf16 scales of the region's slots, per group of 4 slots its 4 K
+    scales then its 4 V scales.  V: block_size * head_dim codes (dim-major
+    [d][B])."""
+    return block_size * head_dim + 4 * block_size, block_size * head_dim
 
 
-def _geom(k_pool, head_dim=None):
-    """(num_blocks, B, H_kv, d) of a pool.  fp32 / bf16 pools are
-    [num_blocks][H_kv][B][d]; 8-bit pools are uint8 [num_blocks][H_kv][R] with
-    R = B * (d + 4), so d must be given (the queries or new tokens carry it)."""
+def _geom(k_pool, v_pool):
+    """(num_blocks, B, H_kv, d) of a pool pair.  fp32 / bf16 pools are
+    [num_blocks][H_kv][B][d] and [num_blocks][H_kv][d][B]; 8-bit pools are
+    uint8 [num_blocks][H_kv][B*(d+4)] and [num_blocks][H_kv][B*d]."""
     if k_pool.dtype == np.uint8:
-        nb, nkv, R = k_pool.shape
-        if head_dim is None or R % (head_dim + 4):
-            raise ValueError(f"8-bit region of {R} bytes does not fit head_dim {head_dim}")
-        return nb, R // (head_dim + 4), nkv, head_dim
+        nb, nkv, rk = k_pool.shape
+        rv = v_pool.shape[2]
+        if v_pool.shape[:2] != (nb, nkv) or rk <= rv or (rk - rv) % 4:
+            raise ValueError(f"8-bit regions of {rk} and {rv} bytes do not pair up")
+        B = (rk - rv) // 4
+        if rv % B:
+            raise ValueError(f"8-bit V region of {rv} bytes is not B * d for B = {B}")
+        return nb, B, nkv, rv // B
     nb, nkv, B, d = k_pool.shape
     return nb, B, nkv, d
 
@@ -109,8 +115,8 @@ def decode(k_pool, v_pool, q, block_tables, context_lens, scale, threads=0):
     uint16 holding bf16 bits.  block_tables int32 [S][maxB], context_lens int32
     [S].  Returns float64 [S][Hq][d].
     """
-    S, Hq, dq = q.shape
-    nb, B, nkv, d = _geom(k_pool, dq)
+    S, Hq, _ = q.shape
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -127,8 +133,8 @@ def decode(k_pool, v_pool, q, block_tables, context_lens, scale, threads=0):
 def decode_pairs(k_pool, v_pool, q, block_tables, context_lens, scale, pairs, threads=0):
     """Paged decode attention for selected (sequence, query head) pairs.
     Returns float64 [n_pairs][d]."""
-    S, Hq, dq = q.shape
-    nb, B, nkv, d = _geom(k_pool, dq)
+    S, Hq, _ = q.shape
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -164,8 +170,8 @@ def decode_dense(k_dense, v_dense, q, context_lens, scale, threads=0):
 def decode_split(k_pool, v_pool, q, block_tables, context_lens, scale, partition_tokens,
                  threads=0):
     """Split-context attention (partials combined by max/sum-exp)."""
-    S, Hq, dq = q.shape
-    nb, B, nkv, d = _geom(k_pool, dq)
+    S, Hq, _ = q.shape
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     qq, qp = _c(q)
@@ -180,10 +186,10 @@ def decode_split(k_pool, v_pool, q, block_tables, context_lens, scale, partition
     return out
 
 
-def gather(k_pool, v_pool, table_row, kv_head, length, head_dim=None):
+def gather(k_pool, v_pool, table_row, kv_head, length):
     """Walk one table row and return contiguous float64 (Kc [L][d], Vc [L][d]),
-    dequantised for 8-bit pools (which need head_dim)."""
-    nb, B, nkv, d = _geom(k_pool, head_dim)
+    dequantised for 8-bit pools."""
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp, kpp = _c(k_pool)
     vp_, vpp = _c(v_pool)
     tr, trp = _c(table_row, np.int32)
@@ -201,7 +207,7 @@ def kv_write(k_pool, v_pool, k_new, v_new, slot_mapping):
     """Return copies of the pools with each token's K/V written into its slot.
     k_new, v_new [T][H_kv][d] have the pool's element type, or bf16 bits
     (uint16) for an 8-bit pool, which stores them quantised."""
-    nb, B, nkv, d = _geom(k_pool, k_new.shape[-1])
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp = np.array(k_pool, copy=True, order="C")
     vp_ = np.array(v_pool, copy=True, order="C")
     src_dtype = np.uint16 if kp.dtype == np.uint8 else kp.dtype
@@ -216,10 +222,9 @@ def kv_write(k_pool, v_pool, k_new, v_new, slot_mapping):
     return kp, vp_
 
 
-def block_copy(k_pool, v_pool, pairs, head_dim=None):
-    """Return copies of the pools with each (src, dst) block copied (8-bit
-    pools need head_dim)."""
-    nb, B, nkv, d = _geom(k_pool, head_dim)
+def block_copy(k_pool, v_pool, pairs):
+    """Return copies of the pools with each (src, dst) block copied."""
+    nb, B, nkv, d = _geom(k_pool, v_pool)
     kp = np.array(k_pool, copy=True, order="C")
     vp_ = np.array(v_pool, copy=True, order="C")
     pr, prp = _c(np.asarray(pairs).reshape(-1, 2), np.int32)

@@ -25,12 +25,14 @@
  *   K pool: [num_blocks][num_kv_heads][block_size][head_dim]   (token-major)
  *   V pool: [num_blocks][num_kv_heads][head_dim][block_size]   (dim-major)
  * Element types: 0 = IEEE fp32, 1 = bf16 (upper 16 bits of an fp32),
- * 2 = 8-bit float cache (OCP FP8 E4M3 codes with one fp32 scale per token and
- * kv head).  For type 2 each (block, kv head) is one region of
- * block_size*head_dim code bytes -- K token-major [B][d], V dim-major [d][B]
- * -- followed by block_size fp32 scales, one per token; a stored element's
- * value is decode(code) * scale[token].  Queries, outputs and the tokens
- * handed to the slot write are bf16 for type 2.
+ * 2 = 8-bit float cache (OCP FP8 E4M3 codes with one bf16 scale per token,
+ * kv head and side).  For type 2 the K buffer holds, per (block, kv head), a
+ * region of B*d code bytes (token-major [B][d]) followed by the scales of
+ * that (block, kv head): for each group of 4 token slots, their 4 K scales
+ * then their 4 V scales, as bf16 (B*4 bytes); the V buffer holds, per
+ * (block, kv head), only the B*d V codes (dim-major [d][B]).  A stored
+ * element's value is decode(code) * scale of its token and side.  Queries,
+ * outputs and the tokens handed to the slot write are bf16 for type 2.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 #include <math.h>
@@ -85,13 +87,24 @@ static uint8_t orc_e4m3_encode(float x) {
   return sign | (uint8_t)code;
 }
 
-/* Bytes of one (block, kv head) region of an 8-bit pool. */
-static size_t orc_fp8_region(int B, int d) { return (size_t)B * d + 4u * (size_t)B; }
+/* Bytes of one (block, kv head) region of an 8-bit K buffer / V buffer. */
+static size_t orc_fp8_k_region(int B, int d) { return (size_t)B * d + 4u * (size_t)B; }
+static size_t orc_fp8_v_region(int B, int d) { return (size_t)B * d; }
 
-static double orc_fp8_scale(const void* pool, size_t region_base, int B, int d, int r) {
-  float s;
-  memcpy(&s, (const char*)pool + region_base + (size_t)B * d + 4u * (size_t)r, sizeof s);
-  return (double)s;
+/* Byte offset, inside a K region, of the bf16 scale of token slot r, side
+ * v (0 = K, 1 = V): groups of 4 slots hold 4 K scales then 4 V scales. */
+static size_t orc_fp8_scale_at(int B, int d, int r, int v) {
+  return (size_t)B * d + 16u * (size_t)(r / 4) + 8u * (size_t)v + 2u * (size_t)(r % 4);
+}
+
+static double orc_fp8_scale(const void* k_pool, size_t k_region_base, int B, int d, int r,
+                            int v) {
+  uint16_t h;
+  memcpy(&h, (const char*)k_pool + k_region_base + orc_fp8_scale_at(B, d, r, v), sizeof h);
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
 }
 
 /* Widen one stored element to double, exactly. */
@@ -115,22 +128,24 @@ static size_t v_index(int nkv, int B, int d, int32_t blk, int g, int r, int i) {
   return (((size_t)blk * nkv + g) * d + i) * (size_t)B + r;
 }
 
-/* Element i of token slot r of (block, kv head g), widened to double. */
+/* Element i of token slot r of (block, kv head g), widened to double.  An
+ * 8-bit V element needs the K buffer too: its scale is stored there. */
 static double orc_k_elem(int dtype, int nkv, int B, int d, const void* k_pool, int32_t blk,
                          int g, int r, int i) {
   if (dtype == ORC_FP8) {
-    const size_t base = ((size_t)blk * nkv + g) * orc_fp8_region(B, d);
+    const size_t base = ((size_t)blk * nkv + g) * orc_fp8_k_region(B, d);
     const uint8_t c = ((const uint8_t*)k_pool)[base + (size_t)r * d + i];
-    return orc_e4m3_decode(c) * orc_fp8_scale(k_pool, base, B, d, r);
+    return orc_e4m3_decode(c) * orc_fp8_scale(k_pool, base, B, d, r, 0);
   }
   return orc_load(dtype, k_pool, k_index(nkv, B, d, blk, g, r, i));
 }
-static double orc_v_elem(int dtype, int nkv, int B, int d, const void* v_pool, int32_t blk,
-                         int g, int r, int i) {
+static double orc_v_elem(int dtype, int nkv, int B, int d, const void* k_pool,
+                         const void* v_pool, int32_t blk, int g, int r, int i) {
   if (dtype == ORC_FP8) {
-    const size_t base = ((size_t)blk * nkv + g) * orc_fp8_region(B, d);
-    const uint8_t c = ((const uint8_t*)v_pool)[base + (size_t)i * B + r];
-    return orc_e4m3_decode(c) * orc_fp8_scale(v_pool, base, B, d, r);
+    const size_t vbase = ((size_t)blk * nkv + g) * orc_fp8_v_region(B, d);
+    const size_t kbase = ((size_t)blk * nkv + g) * orc_fp8_k_region(B, d);
+    const uint8_t c = ((const uint8_t*)v_pool)[vbase + (size_t)i * B + r];
+    return orc_e4m3_decode(c) * orc_fp8_scale(k_pool, kbase, B, d, r, 1);
   }
   return orc_load(dtype, v_pool, v_index(nkv, B, d, blk, g, r, i));
 }
@@ -151,7 +166,7 @@ static void orc_gather(int dtype, int nkv, int B, int d, const void* k_pool,
     int r = t % B;
     for (int i = 0; i < d; ++i) {
       Kc[(size_t)t * d + i] = orc_k_elem(dtype, nkv, B, d, k_pool, blk, g, r, i);
-      Vc[(size_t)t * d + i] = orc_v_elem(dtype, nkv, B, d, v_pool, blk, g, r, i);
+      Vc[(size_t)t * d + i] = orc_v_elem(dtype, nkv, B, d, k_pool, v_pool, blk, g, r, i);
     }
   }
 }
@@ -427,40 +442,53 @@ int oracle_gather(int dtype, int num_blocks, int block_size, int num_kv_heads,
   return 0;
 }
 
+/* fp32 -> bf16 bits, round to nearest even (inputs here are finite). */
+static uint16_t orc_bf16_rne(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 /*
  * Slot write into an 8-bit pool: each token's bf16 K row and V row of each
- * kv head are quantised on their own.  In fp32: amax = max |x| over the row,
- * scale = amax / 448 (0 for an all-zero row), code_e = E4M3(x_e / scale)
- * rounded to nearest even; the codes go to the token's slot, the scale to
- * the token's scale entry of the region.  Same slot rules as below.
+ * kv head are quantised on their own.  amax = max |x| over the row; the
+ * scale is amax / 448 computed in fp32 and rounded to bf16 (nearest even);
+ * code_e = E4M3(x_e / scale) in fp32, rounded to nearest even (x_e / scale
+ * may exceed 448 by the scale's rounding, at most 448 * (1 + 2^-8), which
+ * still rounds to 448); a zero scale gives zero codes.  Codes go to the
+ * token's slot, the scale to the token's K or V entry of the scale group in
+ * the K buffer.  Same slot rules as below.
  */
 static int orc_kv_write_fp8(int B, int d, int nkv, uint8_t* k_pool, uint8_t* v_pool,
                             const uint16_t* k_new, const uint16_t* v_new,
                             const int64_t* slot_mapping, int T) {
-  const size_t region = orc_fp8_region(B, d);
   for (int i = 0; i < T; ++i) {
     int64_t slot = slot_mapping[i];
     if (slot < 0) continue;
     int32_t blk = (int32_t)(slot / B);
     int r = (int)(slot % B);
     for (int g = 0; g < nkv; ++g) {
+      const size_t kbase = ((size_t)blk * nkv + g) * orc_fp8_k_region(B, d);
+      const size_t vbase = ((size_t)blk * nkv + g) * orc_fp8_v_region(B, d);
       for (int kv = 0; kv < 2; ++kv) {
         const uint16_t* src = (kv == 0 ? k_new : v_new) + ((size_t)i * nkv + g) * d;
-        uint8_t* pool = kv == 0 ? k_pool : v_pool;
-        const size_t base = ((size_t)blk * nkv + g) * region;
         float amax = 0.0f;
         for (int e = 0; e < d; ++e) {
           float x = (float)orc_load(ORC_BF16, src, (size_t)e);
           if (fabsf(x) > amax) amax = fabsf(x);
         }
-        const float scale = amax / 448.0f;
+        const uint16_t sbits = orc_bf16_rne(amax / 448.0f);
+        const float scale = (float)orc_load(ORC_BF16, &sbits, 0);
         for (int e = 0; e < d; ++e) {
           float x = (float)orc_load(ORC_BF16, src, (size_t)e);
           uint8_t c = scale > 0.0f ? orc_e4m3_encode(x / scale) : 0;
-          size_t at = kv == 0 ? (size_t)r * d + e : (size_t)e * B + r;
-          pool[base + at] = c;
+          if (kv == 0)
+            k_pool[kbase + (size_t)r * d + e] = c;
+          else
+            v_pool[vbase + (size_t)e * B + r] = c;
         }
-        memcpy(pool + base + (size_t)B * d + 4u * (size_t)r, &scale, sizeof scale);
+        memcpy(k_pool + kbase + orc_fp8_scale_at(B, d, r, kv), &sbits, sizeof sbits);
       }
     }
   }
@@ -515,19 +543,21 @@ int oracle_block_copy(int dtype, int num_blocks, int block_size, int num_kv_head
                       int num_pairs) {
   if (check_geometry(dtype, num_blocks, block_size, num_kv_heads, head_dim, num_kv_heads))
     return 1;
-  const size_t block_bytes =
-      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_region(block_size, head_dim)
-                       : (size_t)num_kv_heads * block_size * head_dim * orc_elem_size(dtype);
+  const size_t plain = (size_t)num_kv_heads * block_size * head_dim * orc_elem_size(dtype);
+  const size_t k_bytes =
+      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_k_region(block_size, head_dim) : plain;
+  const size_t v_bytes =
+      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_v_region(block_size, head_dim) : plain;
   for (int p = 0; p < num_pairs; ++p) {
     int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return 2;
   }
   for (int p = 0; p < num_pairs; ++p) {
     int32_t src = pairs[2 * p], dst = pairs[2 * p + 1];
-    memmove((char*)k_pool + (size_t)dst * block_bytes,
-            (const char*)k_pool + (size_t)src * block_bytes, block_bytes);
-    memmove((char*)v_pool + (size_t)dst * block_bytes,
-            (const char*)v_pool + (size_t)src * block_bytes, block_bytes);
+    memmove((char*)k_pool + (size_t)dst * k_bytes, (const char*)k_pool + (size_t)src * k_bytes,
+            k_bytes);
+    memmove((char*)v_pool + (size_t)dst * v_bytes, (const char*)v_pool + (size_t)src * v_bytes,
+            v_bytes);
   }
   return 0;
 }

@@ -5,7 +5,7 @@ definition implies, and decode over an 8-bit pool against the already
 pinned fp32 path on the same values.  A quantized cache is one of the levers
 that shrink each token's footprint and stack with paging (the vLLM
 PagedAttention blog page, "Where it bites"); the format itself is OCP E4M3
-with one fp32 scale per (token, kv head).  CPU only."""
+with one bf16 scale per (token, kv head, side).  CPU only."""
 import json
 import os
 
@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from workloads import bf16_bits_to_f32, f32_to_bf16_bits
-from workloads.gen import fp8_region_bytes, fp8_split
+from workloads.gen import fp8_region_bytes
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 FINITE = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
@@ -103,28 +103,33 @@ def test_encode_special_values():
 
 # --- the quantising slot write -------------------------------------------------------
 def _fp8_case(rng, nb, nkv, B, d, T):
-    region = fp8_region_bytes(B, d)
-    k = rng.integers(0, 256, (nb, nkv, region), dtype=np.uint8)
-    v = rng.integers(0, 256, (nb, nkv, region), dtype=np.uint8)
+    rk, rv = fp8_region_bytes(B, d)
+    k = rng.integers(0, 256, (nb, nkv, rk), dtype=np.uint8)
+    v = rng.integers(0, 256, (nb, nkv, rv), dtype=np.uint8)
     kn = f32_to_bf16_bits(rng.standard_normal((T, nkv, d)).astype(np.float32) * 3)
     vn = f32_to_bf16_bits(rng.standard_normal((T, nkv, d)).astype(np.float32) * 3)
     slots = rng.choice(nb * B, size=T, replace=False).astype(np.int64)
     return k, v, kn, vn, slots
 
 
-def _read_back(pool, B, d, blk, g, r, v_side):
+def _read_back(k_pool, v_pool, B, d, blk, g, r, v_side):
     """Codes and scale of token slot r of (blk, g), read by the documented
-    region layout: codes K [B][d] / V [d][B], then B fp32 scales."""
-    codes, scales = fp8_split(pool, B, d)
-    c = codes[blk, g].reshape(d, B)[:, r] if v_side else codes[blk, g].reshape(B, d)[r]
-    return c, float(scales[blk, g, r])
+    layout: K codes [B][d] then the scale groups (4 K scales, 4 V scales per
+    4 slots, bf16) in the K buffer; V codes [d][B] in the V buffer."""
+    if v_side:
+        c = v_pool[blk, g].reshape(d, B)[:, r]
+    else:
+        c = k_pool[blk, g, :B * d].reshape(B, d)[r]
+    at = B * d + 16 * (r // 4) + 8 * int(v_side) + 2 * (r % 4)
+    bits = k_pool[blk, g, at:at + 2].view(np.uint16)
+    return c, float(bf16_bits_to_f32(bits)[0])
 
 
 def test_kv_write_fp8_error_bound_and_scale():
     """Each written row dequantises to within half an E4M3 step of its input:
     |x - x'| <= 2^-4 |x| for normal codes and <= 2^-10 s on the subnormal
     range, plus fp32 rounding of x / s; the largest |x| of a row maps to
-    448 (code 0x7E with x's sign), and 448 s equals max |x| to fp32 rounding."""
+    448 (code 0x7E with x's sign); 448 s equals max |x| to bf16 rounding."""
     rng = np.random.default_rng(82)
     nb, nkv, B, d, T = 12, 3, 16, 32, 40
     k, v, kn, vn, slots = _fp8_case(rng, nb, nkv, B, d, T)
@@ -133,14 +138,14 @@ def test_kv_write_fp8_error_bound_and_scale():
     for i, slot in enumerate(slots):
         blk, r = divmod(int(slot), B)
         for g in range(nkv):
-            for pool, src, v_side in ((k2, kn, False), (v2, vn, True)):
+            for src, v_side in ((kn, False), (vn, True)):
                 x = bf16_bits_to_f32(src[i, g]).astype(np.float64)
-                c, s = _read_back(pool, B, d, blk, g, r, v_side)
+                c, s = _read_back(k2, v2, B, d, blk, g, r, v_side)
                 amax = np.abs(x).max()
                 if amax == 0:
                     assert s == 0.0 and not c.any()
                     continue
-                assert abs(448.0 * s - amax) <= amax * 2.0 ** -23
+                assert abs(448.0 * s - amax) <= amax * 2.0 ** -8
                 top = int(np.argmax(np.abs(x)))
                 assert c[top] == (0xFE if x[top] < 0 else 0x7E)
                 deq = oracle.e4m3_decode(c) * s
@@ -163,27 +168,34 @@ def test_kv_write_fp8_touches_only_its_slots():
         blk, r = divmod(int(slot), B)
         touched_k[blk, :, r * d:(r + 1) * d] = True
         touched_v[blk, :, r:B * d:B] = True
-        for t in (touched_k, touched_v):
-            t[blk, :, B * d + 4 * r:B * d + 4 * r + 4] = True
+        for side in (0, 1):
+            at = B * d + 16 * (r // 4) + 8 * side + 2 * (r % 4)
+            touched_k[blk, :, at:at + 2] = True
     assert np.array_equal(k2[~touched_k], k[~touched_k])
     assert np.array_equal(v2[~touched_v], v[~touched_v])
     assert not np.array_equal(k2, k) and not np.array_equal(v2, v)
 
 
+def _bf16(x):
+    return np.array([x], np.float32).view(np.uint32).astype(np.uint32) >> 16
+
+
 def test_gather_reads_the_region_layout_by_hand():
-    """One token placed by hand: K codes at [r][i], V codes at [i][r], scale
-    after the codes; gather returns decode(code) * scale at (token, dim)."""
+    """One token placed by hand: K codes at [r][i], V codes at [i][r], bf16
+    scales in the K buffer's scale groups; gather returns decode(code) *
+    scale at (token, dim)."""
     nb, B, d = 3, 16, 8
-    region = fp8_region_bytes(B, d)
-    k = np.zeros((nb, 1, region), np.uint8)
-    v = np.zeros((nb, 1, region), np.uint8)
+    rk, rv = fp8_region_bytes(B, d)
+    k = np.zeros((nb, 1, rk), np.uint8)
+    v = np.zeros((nb, 1, rv), np.uint8)
     r, i = 5, 3
     k[2, 0, r * d + i] = 0x38                     # 1.0
     v[2, 0, i * B + r] = 0x42                     # 2.5
-    k[2, 0, B * d + 4 * r:B * d + 4 * r + 4] = np.array([2.0], np.float32).view(np.uint8)
-    v[2, 0, B * d + 4 * r:B * d + 4 * r + 4] = np.array([-4.0], np.float32).view(np.uint8)
+    grp = B * d + 16 * (r // 4) + 2 * (r % 4)
+    k[2, 0, grp:grp + 2] = np.array(_bf16(2.0), np.uint16).view(np.uint8)       # K scale
+    k[2, 0, grp + 8:grp + 10] = np.array(_bf16(-4.0), np.uint16).view(np.uint8)  # V scale
     table = np.array([0, 2], np.int32)
-    Kc, Vc = oracle.gather(k, v, table, 0, 2 * B, head_dim=d)
+    Kc, Vc = oracle.gather(k, v, table, 0, 2 * B)
     want_k = np.zeros((2 * B, d))
     want_v = np.zeros((2 * B, d))
     want_k[B + r, i] = 2.0
@@ -193,29 +205,36 @@ def test_gather_reads_the_region_layout_by_hand():
 
 # --- decode over an 8-bit pool ------------------------------------------------------------
 def _fp8_to_f32_pools(k8, v8, B, d):
-    """The fp32 pools holding the same values, built from the region layout."""
+    """The fp32 pools holding the same values, built from the documented layout."""
     nb, nkv = k8.shape[:2]
-    kc, ks = fp8_split(k8, B, d)
-    vc, vs = fp8_split(v8, B, d)
-    kval = oracle.e4m3_decode(kc).reshape(nb, nkv, B, d) * ks[:, :, :, None]
-    vval = oracle.e4m3_decode(vc).reshape(nb, nkv, d, B) * vs[:, :, None, :]
+    kc = k8[..., :B * d].reshape(nb, nkv, B, d)
+    vc = v8.reshape(nb, nkv, d, B)
+    sc = bf16_bits_to_f32(k8[..., B * d:].view(np.uint16)).reshape(nb, nkv, B // 4, 2, 4)
+    ks = sc[:, :, :, 0, :].reshape(nb, nkv, B)
+    vs = sc[:, :, :, 1, :].reshape(nb, nkv, B)
+    kval = oracle.e4m3_decode(kc) * ks[:, :, :, None]
+    vval = oracle.e4m3_decode(vc) * vs[:, :, None, :]
     return kval.astype(np.float32), vval.astype(np.float32)
 
 
+def _random_fp8_pools(rng, nb, nkv, B, d):
+    rk, rv = fp8_region_bytes(B, d)
+    k8 = np.empty((nb, nkv, rk), np.uint8)
+    k8[..., :B * d] = rng.choice(FINITE, size=(nb, nkv, B * d))
+    k8[..., B * d:] = f32_to_bf16_bits(
+        (rng.uniform(1, 2, (nb, nkv, 2 * B)) * 2.0 ** -7).astype(np.float32)).view(
+            np.uint8).reshape(nb, nkv, 4 * B)
+    v8 = rng.choice(FINITE, size=(nb, nkv, rv)).astype(np.uint8)
+    return k8, v8
+
+
 def test_fp8_decode_equals_fp32_decode_of_the_same_values():
-    """Scales with 16 significant bits make every code * scale exact in fp32,
-    so the fp32 oracle over those values must agree bit for bit with the
-    8-bit oracle (same doubles, same order); q is bf16 in both."""
+    """bf16 scales times 4-bit code significands are exact in fp32, so the
+    fp32 oracle over those values must agree bit for bit with the 8-bit
+    oracle (same doubles, same order); q is bf16 in both."""
     rng = np.random.default_rng(84)
     nb, nkv, B, d, S, Hq = 20, 2, 16, 32, 3, 4
-    region = fp8_region_bytes(B, d)
-    k8 = np.empty((nb, nkv, region), np.uint8)
-    v8 = np.empty((nb, nkv, region), np.uint8)
-    for p in (k8, v8):
-        c, s = fp8_split(p, B, d)
-        c[...] = rng.choice(FINITE, size=c.shape)
-        s[...] = (rng.uniform(1, 2, s.shape) * 2.0 ** -7).astype(np.float32)
-        s.view(np.uint32)[...] &= np.uint32(0xFFFF0000)
+    k8, v8 = _random_fp8_pools(rng, nb, nkv, B, d)
     q = f32_to_bf16_bits(rng.standard_normal((S, Hq, d)).astype(np.float32))
     tables = rng.permutation(nb)[:S * 4].reshape(S, 4).astype(np.int32)
     lens = np.array([1, 37, 64], np.int32)
@@ -231,17 +250,16 @@ def test_fp8_zero_keys_give_mean_of_dequantised_values():
     mean of the dequantised V rows of the context."""
     rng = np.random.default_rng(85)
     nb, B, d, L = 4, 16, 16, 23
-    region = fp8_region_bytes(B, d)
-    k8 = np.zeros((nb, 1, region), np.uint8)
-    fp8_split(k8, B, d)[1][...] = 1.0
-    v8 = np.zeros((nb, 1, region), np.uint8)
-    vc, vs = fp8_split(v8, B, d)
-    vc[...] = rng.choice(FINITE, size=vc.shape)
-    vs[...] = 0.25
+    rk, rv = fp8_region_bytes(B, d)
+    k8 = np.zeros((nb, 1, rk), np.uint8)
+    sc = k8[..., B * d:].view(np.uint16).reshape(nb, 1, B // 4, 2, 4)
+    sc[:, :, :, 0, :] = _bf16(1.0)
+    sc[:, :, :, 1, :] = _bf16(0.25)
+    v8 = rng.choice(FINITE, size=(nb, 1, rv)).astype(np.uint8)
     q = f32_to_bf16_bits(rng.standard_normal((1, 2, d)).astype(np.float32))
     table = np.array([[3, 1]], np.int32)
     out = oracle.decode(k8, v8, q, table, np.array([L], np.int32), 0.3)
-    rows = [oracle.e4m3_decode(vc[b, 0].reshape(d, B)[:, r]) * 0.25
+    rows = [oracle.e4m3_decode(v8[b, 0].reshape(d, B)[:, r]) * 0.25
             for b, n in ((3, B), (1, L - B)) for r in range(n)]
     want = np.mean(rows, axis=0)
     assert np.allclose(out[0, 0], want, rtol=0, atol=1e-12)
@@ -251,15 +269,25 @@ def test_fp8_zero_keys_give_mean_of_dequantised_values():
 def test_fp8_block_copy_copies_codes_and_scales():
     rng = np.random.default_rng(86)
     nb, nkv, B, d = 8, 2, 16, 32
-    region = fp8_region_bytes(B, d)
-    k = rng.integers(0, 256, (nb, nkv, region), dtype=np.uint8)
-    v = rng.integers(0, 256, (nb, nkv, region), dtype=np.uint8)
+    rk, rv = fp8_region_bytes(B, d)
+    k = rng.integers(0, 256, (nb, nkv, rk), dtype=np.uint8)
+    v = rng.integers(0, 256, (nb, nkv, rv), dtype=np.uint8)
     pairs = np.array([[1, 4], [1, 6], [7, 0]], np.int32)
-    k2, v2 = oracle.block_copy(k, v, pairs, head_dim=d)
+    k2, v2 = oracle.block_copy(k, v, pairs)
     for src, dst in pairs:
         assert np.array_equal(k2[dst], k[src]) and np.array_equal(v2[dst], v[src])
     others = [b for b in range(nb) if b not in pairs[:, 1]]
     assert np.array_equal(k2[others], k[others]) and np.array_equal(v2[others], v[others])
+
+
+def test_fp8_geometry_from_the_two_buffers():
+    """Block size and head dim follow from the region sizes: R_k - R_v = 4B,
+    R_v = B d; a pair that does not fit is refused."""
+    k = np.zeros((2, 1, 16 * 68), np.uint8)
+    v = np.zeros((2, 1, 16 * 64), np.uint8)
+    assert oracle._geom(k, v) == (2, 16, 1, 64)
+    with pytest.raises(ValueError):
+        oracle._geom(k, np.zeros((2, 1, 16 * 68), np.uint8))
 
 
 def test_fp8_dense_layout_is_rejected():

@@ -12,12 +12,13 @@ Pool layout (fixed by the library's interface):
 bf16 data is carried as uint16 bit patterns on the numpy side and as
 torch.bfloat16 on the torch side.
 
-8-bit pools ("fp8") are uint8 [num_blocks][H_kv][R] with R = B*d + 4*B: per
-(block, kv head) the E4M3 codes (K token-major [B][d], V dim-major [d][B])
-then B float32 scales, one per token.  Their payload is drawn directly as
-codes and scales, with no quantisation arithmetic: magnitude codes uniform
-over the 127 finite ones (0x00..0x7E), a random sign bit, and scales
-2^-7 * U[1, 2), so stored values reach 448 * 2^-6 = 7, the range of the
+8-bit pools ("fp8") are a uint8 pair: K [num_blocks][H_kv][B*d + 4*B] (per
+(block, kv head) the E4M3 K codes token-major [B][d], then bf16 scales: per
+group of 4 slots, 4 K scales then 4 V scales) and V [num_blocks][H_kv][B*d]
+(V codes dim-major [d][B]).  Their payload is drawn directly as codes and
+scales, with no quantisation arithmetic: magnitude codes uniform over the 127
+finite ones (0x00..0x7E), a random sign bit, and scales 2^-7 * U[1, 2)
+rounded to bf16, so stored values reach 448 * 2^-6 = 7, the range of the
 bf16 cases' normal draws.  Queries and new tokens stay bf16.
 
 Every slot that no sequence's context covers is filled with poison
@@ -79,68 +80,86 @@ FP8_POISON_K_SCALE = 1.0        # poison K = 64.0
 FP8_POISON_V_SCALE = 16.0       # poison V = 1024.0
 
 
-def fp8_region_bytes(B: int, d: int) -> int:
-    return B * d + 4 * B
+def fp8_region_bytes(B: int, d: int):
+    """(K region, V region) bytes per (block, kv head) of an 8-bit pool."""
+    return B * d + 4 * B, B * d
 
 
-def fp8_split(pool, B: int, d: int):
-    """Views (codes [nb][H][B*d] uint8, scales [nb][H][B] float32) of an
-    8-bit pool given as a numpy array or a torch tensor."""
-    if isinstance(pool, torch.Tensor):
-        return pool[..., :B * d], pool[..., B * d:].view(torch.float32)
-    return pool[..., :B * d], pool[..., B * d:].view(np.float32)
+def fp8_k_codes(k_pool, B: int, d: int):
+    """View of the K codes, [nb][H][B*d] (token-major inside)."""
+    return k_pool[..., :B * d]
 
 
-def _fp8_codes_np(rng, n):
+def fp8_scales(k_pool, B: int, d: int):
+    """View of the bf16 scale bits in the K buffer, [nb][H][B/4][2][4]:
+    per group of 4 slots, side 0 holds the K scales and side 1 the V scales."""
+    nb, H = k_pool.shape[0], k_pool.shape[1]
+    if isinstance(k_pool, torch.Tensor):
+        return k_pool[..., B * d:].view(torch.int16).view(nb, H, B // 4, 2, 4)
+    return k_pool[..., B * d:].view(np.uint16).reshape(nb, H, B // 4, 2, 4)
+
+
+def fp8_codes_np(rng, n):
     mag = rng.integers(0, 0x7F, size=n, dtype=np.uint8)
     sign = (rng.integers(0, 2, size=n, dtype=np.uint8) << 7).astype(np.uint8)
     return mag | sign
 
 
-def _fp8_pool_np(rng, nb, Hkv, B, d):
-    pool = np.empty((nb, Hkv, fp8_region_bytes(B, d)), np.uint8)
-    codes, scales = fp8_split(pool, B, d)
-    codes[...] = _fp8_codes_np(rng, nb * Hkv * B * d).reshape(nb, Hkv, B * d)
-    scales[...] = (rng.random((nb, Hkv, B), dtype=np.float32) + 1.0) * np.float32(2.0 ** -7)
-    return pool
+def fp8_pools_np(rng, nb, Hkv, B, d):
+    """Random 8-bit (K, V) pools: finite codes, bf16 scales 2^-7 * U[1, 2)."""
+    rk, rv = fp8_region_bytes(B, d)
+    k = np.empty((nb, Hkv, rk), np.uint8)
+    v = fp8_codes_np(rng, nb * Hkv * rv).reshape(nb, Hkv, rv)
+    fp8_k_codes(k, B, d)[...] = fp8_codes_np(rng, nb * Hkv * B * d).reshape(nb, Hkv, B * d)
+    sc = (rng.random((nb, Hkv, B // 4, 2, 4), dtype=np.float32) + 1.0) * np.float32(2.0 ** -7)
+    fp8_scales(k, B, d)[...] = f32_to_bf16_bits(sc)
+    return k, v
 
 
-def _fp8_pool_torch(g, nb, Hkv, B, d, device):
-    pool = torch.empty((nb, Hkv, fp8_region_bytes(B, d)), dtype=torch.uint8, device=device)
-    codes, scales = fp8_split(pool, B, d)
+def fp8_pools_torch(g, nb, Hkv, B, d, device):
+    rk, rv = fp8_region_bytes(B, d)
+    k = torch.empty((nb, Hkv, rk), dtype=torch.uint8, device=device)
+    v = torch.empty((nb, Hkv, rv), dtype=torch.uint8, device=device)
+    kc, ks = fp8_k_codes(k, B, d), fp8_scales(k, B, d)
     chunk = max(1, (1 << 26) // (Hkv * B * d))
+
+    def codes(n0):
+        mag = torch.randint(0, 0x7F, (n0, Hkv, B * d), generator=g, device=device,
+                            dtype=torch.uint8)
+        sign = torch.randint(0, 2, (n0, Hkv, B * d), generator=g, device=device,
+                             dtype=torch.uint8) << 7
+        return mag | sign
+
     for b0 in range(0, nb, chunk):
         b1 = min(nb, b0 + chunk)
-        mag = torch.randint(0, 0x7F, (b1 - b0, Hkv, B * d), generator=g, device=device,
-                            dtype=torch.uint8)
-        sign = torch.randint(0, 2, (b1 - b0, Hkv, B * d), generator=g, device=device,
-                             dtype=torch.uint8) << 7
-        codes[b0:b1] = mag | sign
-        scales[b0:b1] = (torch.rand((b1 - b0, Hkv, B), generator=g, device=device) + 1.0) \
+        kc[b0:b1] = codes(b1 - b0)
+        v[b0:b1] = codes(b1 - b0)
+        sc = (torch.rand((b1 - b0, Hkv, B // 4, 2, 4), generator=g, device=device) + 1.0) \
             * 2.0 ** -7
-    return pool
+        ks[b0:b1] = sc.to(torch.bfloat16).view(torch.int16)
+    return k, v
 
 
-def _fp8_poison(pool, dead, B, d, v_side: bool):
-    """Poison the dead token slots (dead: bool [nb][B]) of an 8-bit pool."""
-    codes, scales = fp8_split(pool, B, d)
-    sc = FP8_POISON_V_SCALE if v_side else FP8_POISON_K_SCALE
-    if isinstance(pool, torch.Tensor):
-        nb, H = pool.shape[0], pool.shape[1]
-        c = codes.view(nb, H, d, B) if v_side else codes.view(nb, H, B, d)
-        if v_side:
-            c.masked_fill_(dead[:, None, None, :], FP8_POISON_CODE)
-        else:
-            c.masked_fill_(dead[:, None, :, None], FP8_POISON_CODE)
-        scales.masked_fill_(dead[:, None, :], sc)
+def fp8_poison(k_pool, v_pool, dead, B, d):
+    """Poison the dead token slots (dead: bool [nb][B]) of an 8-bit pool pair:
+    K = 64 * 1.0, V = 64 * 16.0."""
+    nb, H = k_pool.shape[0], k_pool.shape[1]
+    kc = fp8_k_codes(k_pool, B, d)
+    sc = fp8_scales(k_pool, B, d)
+    if isinstance(k_pool, torch.Tensor):
+        kc.view(nb, H, B, d).masked_fill_(dead[:, None, :, None], FP8_POISON_CODE)
+        v_pool.view(nb, H, d, B).masked_fill_(dead[:, None, None, :], FP8_POISON_CODE)
+        dg = dead.view(nb, B // 4, 4)[:, None, :, :]
+        one = torch.tensor(FP8_POISON_K_SCALE, dtype=torch.bfloat16).view(torch.int16).item()
+        sixteen = torch.tensor(FP8_POISON_V_SCALE, dtype=torch.bfloat16).view(torch.int16).item()
+        sc[:, :, :, 0, :].masked_fill_(dg, one)
+        sc[:, :, :, 1, :].masked_fill_(dg, sixteen)
         return
-    nb, H = pool.shape[0], pool.shape[1]
     bi, ri = dead.nonzero()
-    if v_side:
-        codes.reshape(nb, H, d, B)[bi, :, :, ri] = FP8_POISON_CODE
-    else:
-        codes.reshape(nb, H, B, d)[bi, :, ri, :] = FP8_POISON_CODE
-    scales[bi, :, ri] = sc
+    kc.reshape(nb, H, B, d)[bi, :, ri, :] = FP8_POISON_CODE
+    v_pool.reshape(nb, H, d, B)[bi, :, :, ri] = FP8_POISON_CODE
+    sc[bi, :, ri // 4, 0, ri % 4] = f32_to_bf16_bits(np.float32(FP8_POISON_K_SCALE))
+    sc[bi, :, ri // 4, 1, ri % 4] = f32_to_bf16_bits(np.float32(FP8_POISON_V_SCALE))
 
 
 # --- lengths and pools -----------------------------------------------------
@@ -316,10 +335,8 @@ def decode_case(cfg: Config, payload: str = "numpy", device="cpu",
     v_shape = (nb, Hkv, d, B)
     if cfg.dtype == "fp8" and payload == "numpy":
         q = torch.from_numpy(rng.standard_normal(q_shape, dtype=np.float32)).to(tdt)
-        k_np = _fp8_pool_np(rng, nb, Hkv, B, d)
-        v_np = _fp8_pool_np(rng, nb, Hkv, B, d)
-        _fp8_poison(k_np, ~live, B, d, v_side=False)
-        _fp8_poison(v_np, ~live, B, d, v_side=True)
+        k_np, v_np = fp8_pools_np(rng, nb, Hkv, B, d)
+        fp8_poison(k_np, v_np, ~live, B, d)
         q = q.to(device)
         k = torch.from_numpy(k_np).to(device)
         v = torch.from_numpy(v_np).to(device)
@@ -327,12 +344,10 @@ def decode_case(cfg: Config, payload: str = "numpy", device="cpu",
         g = torch.Generator(device=device)
         g.manual_seed(seed)
         q = torch.randn(q_shape, generator=g, device=device, dtype=torch.float32).to(tdt)
-        k = _fp8_pool_torch(g, nb, Hkv, B, d, device)
-        v = _fp8_pool_torch(g, nb, Hkv, B, d, device)
+        k, v = fp8_pools_torch(g, nb, Hkv, B, d, device)
         dead = torch.from_numpy(~live).to(device)
         if bool(dead.any()):
-            _fp8_poison(k, dead, B, d, v_side=False)
-            _fp8_poison(v, dead, B, d, v_side=True)
+            fp8_poison(k, v, dead, B, d)
     elif payload == "numpy":
         q32 = rng.standard_normal(q_shape, dtype=np.float32)
         k32 = rng.standard_normal(k_shape, dtype=np.float32)
@@ -397,8 +412,7 @@ def kv_write_case(num_blocks, num_kv_heads, head_dim, block_size, T, dtype="bf16
     if skip_fraction > 0:
         slots[rng.random(T) < skip_fraction] = -1
     if dtype == "fp8":  # 8-bit pools take bf16 tokens
-        k_pool = _fp8_pool_np(rng, nb, Hkv, B, d)
-        v_pool = _fp8_pool_np(rng, nb, Hkv, B, d)
+        k_pool, v_pool = fp8_pools_np(rng, nb, Hkv, B, d)
         k_new = _payload_np(rng, (T, Hkv, d), "bf16")
         v_new = _payload_np(rng, (T, Hkv, d), "bf16")
         return KVWriteCase(dtype, k_pool, v_pool, k_new, v_new, slots)
@@ -433,8 +447,7 @@ def block_copy_case(num_blocks, num_kv_heads, head_dim, block_size, P, dtype="bf
     src = src_pool[rng.integers(0, len(src_pool), size=P)]
     pairs = np.stack([src, dst], axis=1).astype(np.int32)
     if dtype == "fp8":
-        return BlockCopyCase(dtype, _fp8_pool_np(rng, nb, Hkv, B, d),
-                             _fp8_pool_np(rng, nb, Hkv, B, d), pairs)
+        return BlockCopyCase(dtype, *fp8_pools_np(rng, nb, Hkv, B, d), pairs)
     k_pool = _payload_np(rng, (nb, Hkv, B, d), dtype)
     v_pool = _payload_np(rng, (nb, Hkv, d, B), dtype)
     return BlockCopyCase(dtype, k_pool, v_pool, pairs)
