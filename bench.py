@@ -6,6 +6,9 @@ Workload (default): Llama-3-8B-shape GQA layer decode -- 256 sequences,
 context lengths lognormal (median 1024, sigma 1) clipped to [16, 8192], a
 shuffled pool sized to the blocks needed plus 10%.
 
+With --kv fp8 the same workload runs on an 8-bit cache (E4M3 codes with one
+fp32 scale per token and kv head; queries and new tokens stay bf16).
+
 One step = the whole hot path for one batch: the host block manager appends
 one token to every sequence (slots, new blocks, copy-on-write decisions), one
 packed host-to-device metadata copy, the device table update, the slot write
@@ -73,6 +76,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="cfg3", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0: library)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="cache storage: bf16, or 8-bit E4M3 codes + per-token scales")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,8 +123,9 @@ def main():
     log(f"{cfg.key}: S={S} Hq={Hq} Hkv={Hkv} d={d} sum L={int(lens0.sum())} "
         f"pool={num_blocks} blocks width={width}")
 
+    fp8 = args.kv == "fp8"
     cache = PagedKVCache(num_blocks, Hkv, d, S, width, block_size=B, shuffle_seed=cfg.seed,
-                         device=dev)
+                         dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
     seqs = np.array([cache.add_sequence() for _ in range(S)], dtype=np.int32)
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed)
@@ -152,8 +158,8 @@ def main():
     ones = np.ones(S, np.int32)
     P = cache.partition_tokens(Hq, args.partition)
     cache.workspace(Hq, args.partition)
-    e = 2
-    kv_per_token = 2 * Hkv * d * e
+    # bytes of one token's K and V rows for every kv head (8-bit: codes + scale)
+    kv_per_token = 2 * Hkv * (d + 4 if fp8 else d * 2)
 
     # decode timing: events without a system-scope fence, so recording them
     # does not write back and invalidate the caches between the step's kernels
@@ -231,9 +237,12 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 kv, bf16 mfma" if fp8 else "bf16", "data": "synthetic",
         "config": {
-            "workload": f"{cfg.key}: {cfg.description}",
+            "workload": f"{cfg.key}: {cfg.description}" + (
+                "; 8-bit cache (E4M3 + per-token fp32 scales)" if fp8 else ""),
+            "kv_storage": args.kv,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
             "block_size": B, "pool_blocks": num_blocks, "partition_tokens": P,
             "mean_context_tokens": round(float(lens_now.mean()), 1),
@@ -248,7 +257,8 @@ def main():
         "decode_cold": cold,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(kv_avg) if args.partition == 0 else None},
+                     "traffic": measured_traffic(kv_avg)
+                     if args.partition == 0 and not fp8 else None},
         "block_manager": {"tail_waste_pct": round(tail_waste, 3),
                           "contiguous_reservation_utilisation_pct": round(contiguous_util, 2),
                           "cow_copies": stats["cow_copies"]},

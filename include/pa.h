@@ -13,6 +13,8 @@
  *    unchanged, softmax(scale * q K^T) V over the logical sequence.
  *  - same page, reference entry "Shared blocks and copy-on-write": a request
  *    about to modify a shared block first gets a private copy.
+ *  - vLLM post, section "Where it bites": a quantized cache shrinks each
+ *    token's footprint and stacks with paging (PA_FP8_E4M3 below).
  *
  * Conventions for every entry point below:
  *  - Pointers named *_pool, q, out, block_tables, context_lens, slot_mapping,
@@ -49,7 +51,11 @@ typedef enum {
   PA_EUNSUPPORTED = 4   /* valid arguments, shape not implemented          */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum {
+  PA_F32 = 0,       /* IEEE fp32 elements                                        */
+  PA_BF16 = 1,      /* bf16 elements                                             */
+  PA_FP8_E4M3 = 2   /* 8-bit cache: OCP E4M3 codes + one fp32 scale per token    */
+} pa_dtype;
 
 /*
  * Pool geometry.  Two separate device buffers hold the pool:
@@ -59,20 +65,40 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
  * elements in each buffer.  V is dim-major so that decode can reduce over
  * tokens inside each lane (the reduction dimension of P.V).  The pages leave
  * the physical layout open.
+ *
+ * PA_FP8_E4M3 pools hold E4M3 codes and one bf16 scale per (token slot,
+ * kv head, side).  Per (block, kv head):
+ *   k_pool region, R_k = block_size*head_dim + 4*block_size bytes: the K
+ *       codes token-major [block_size][head_dim], then the scales: for each
+ *       group of 4 token slots, their 4 K scales then their 4 V scales
+ *       (bf16, 16 bytes per group);
+ *   v_pool region, R_v = block_size*head_dim bytes: the V codes dim-major
+ *       [head_dim][block_size].
+ * Buffer layouts [num_blocks][num_kv_heads][R_k] and [..][R_v].  A stored
+ * element's value is e4m3(code) * scale of its slot and side; the V scales
+ * live with the K codes so that one 16-byte read fetches both scales of
+ * four tokens.  For this dtype q, out, k_new and v_new are bf16.  The slot
+ * write quantises each new (token, kv head) row x of K and of V on its own:
+ * scale = max_i |x_i| / 448 in fp32, rounded to bf16 (nearest even), and
+ * code_i = x_i / scale in fp32 rounded to the nearest E4M3 value, ties to
+ * even (all codes 0 when the scale is 0).  E4M3 (OCP 8-bit floating point):
+ * sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals, largest
+ * finite 448, S.1111.111 NaN, no infinities.
  */
 typedef struct {
   int32_t num_blocks;
   int32_t block_size;    /* tokens per block; decode supports 16 */
   int32_t num_kv_heads;
   int32_t head_dim;      /* decode supports 64 and 128 */
-  pa_dtype dtype;        /* element type of both pools */
+  pa_dtype dtype;        /* element type of both pools (PA_FP8_E4M3: regions) */
 } pa_pool;
 
 /*
  * Slot write: store each new token's keys and values in the slot the block
  * manager gave it ("Dynamic Growth" on the glossary page; "Add pages as the
  * request grows" on the attention-lab page).
- *   k_new, v_new: [T][num_kv_heads][head_dim], pool dtype, dense.
+ *   k_new, v_new: [T][num_kv_heads][head_dim], pool dtype (bf16 for an
+ *                 8-bit pool, stored quantised as described above), dense.
  *   slot_mapping: int64 [T]; slot = block * block_size + offset; a negative
  *                 slot skips that token.  Slots must be distinct (a repeated
  *                 slot is a write race) and below num_blocks * block_size.
@@ -107,8 +133,8 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t,   t in [0, L),
  * where token t is read from physical block block_tables[s][t / block_size],
  * slot t % block_size, KV head g.  Accumulation is in fp32.
- *   q, out:        [num_seqs][num_q_heads][head_dim], pool dtype; out is
- *                  rounded to nearest even when the dtype is bf16.
+ *   q, out:        [num_seqs][num_q_heads][head_dim], pool dtype (bf16 for
+ *                  an 8-bit pool); out is rounded to nearest even when bf16.
  *   block_tables:  int32 [num_seqs][max_blocks_per_seq], entries in
  *                  [0, num_blocks); entries at j >= ceil(L / block_size) are
  *                  never read.
@@ -140,7 +166,8 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
  * Copy-on-write block copy ("The bonus contiguous storage can't give you:
  * sharing" on the vLLM KV-cache page; "Shared blocks and copy-on-write" on
  * the attention-lab page): for each (src, dst) pair, every KV head and slot
- * of block src is copied bit for bit to block dst, in both pools.
+ * of block src is copied bit for bit to block dst, in both pools (for an
+ * 8-bit pool: the whole K region, codes and scales, and the V region).
  *   pairs: int32 [num_pairs][2] = (src, dst), both in [0, num_blocks).
  *          Destinations must be distinct and no destination may also be a
  *          source in the same call (the copies run concurrently).

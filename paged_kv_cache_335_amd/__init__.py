@@ -11,6 +11,11 @@ Layouts (see include/pa.h):
     k_pool  [num_blocks][num_kv_heads][block_size][head_dim]
     v_pool  [num_blocks][num_kv_heads][head_dim][block_size]
     q, out  [num_seqs][num_q_heads][head_dim]
+8-bit pools (PA_FP8_E4M3) are uint8: k_pool [num_blocks][num_kv_heads][R_k],
+R_k = block_size*(head_dim + 4), holding per (block, kv head) the E4M3 K
+codes token-major and then bf16 scales (per 4 slots: 4 K, then 4 V);
+v_pool [num_blocks][num_kv_heads][R_v], R_v = block_size*head_dim, holding
+the V codes dim-major.  Their q, out, k_new and v_new are bfloat16.
 """
 import ctypes
 import os
@@ -21,7 +26,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_EUNSUPPORTED = range(5)
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 
 
 class PagedKVError(RuntimeError):
@@ -113,7 +118,34 @@ def _dtype_code(t: torch.Tensor):
         return PA_BF16
     if t.dtype == torch.float32:
         return PA_F32
-    raise TypeError(f"pool dtype must be bfloat16 or float32, got {t.dtype}")
+    if t.dtype == torch.uint8:
+        return PA_FP8_E4M3
+    raise TypeError(f"pool dtype must be bfloat16, float32 or uint8 (8-bit regions), "
+                    f"got {t.dtype}")
+
+
+def io_dtype(k_pool: torch.Tensor):
+    """Element type of q, out, k_new and v_new for a pool."""
+    return torch.bfloat16 if k_pool.dtype == torch.uint8 else k_pool.dtype
+
+
+def fp8_region_bytes(block_size: int, head_dim: int):
+    """(K, V) bytes of one (block, kv head) region of an 8-bit pool."""
+    return block_size * head_dim + 4 * block_size, block_size * head_dim
+
+
+def alloc_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16,
+                device="cuda"):
+    """Uninitialised (k_pool, v_pool) in the library's layout; dtype
+    torch.uint8 gives 8-bit (E4M3 + scale) pools."""
+    if dtype == torch.uint8:
+        rk, rv = fp8_region_bytes(block_size, head_dim)
+        return (torch.empty((num_blocks, num_kv_heads, rk), dtype=dtype, device=device),
+                torch.empty((num_blocks, num_kv_heads, rv), dtype=dtype, device=device))
+    return (torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
+                        device=device),
+            torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype,
+                        device=device))
 
 
 def _dev(t: torch.Tensor, name: str):
@@ -131,6 +163,18 @@ def _stream(stream):
 
 
 def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PoolDesc:
+    if k_pool.dtype == torch.uint8:
+        if k_pool.dim() != 3 or v_pool.dim() != 3 or v_pool.dtype != torch.uint8:
+            raise ValueError("8-bit pools must be uint8 [num_blocks][num_kv_heads][R]")
+        nb, nkv, rk = k_pool.shape
+        rv = v_pool.shape[2]
+        if tuple(v_pool.shape[:2]) != (nb, nkv) or rk <= rv or (rk - rv) % 16:
+            raise ValueError(f"8-bit regions of {rk} (K) and {rv} (V) bytes do not pair up: "
+                             "R_k = B*(d+4), R_v = B*d with B a multiple of 4")
+        B = (rk - rv) // 4
+        if rv % B:
+            raise ValueError(f"8-bit V region of {rv} bytes is not block_size * head_dim")
+        return PoolDesc(nb, B, nkv, rv // B, PA_FP8_E4M3)
     if k_pool.dim() != 4:
         raise ValueError("k_pool must be [num_blocks][num_kv_heads][block_size][head_dim]")
     nb, nkv, B, d = k_pool.shape
@@ -149,8 +193,8 @@ def pa_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
     shape = (T, desc.num_kv_heads, desc.head_dim)
     if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
         raise ValueError(f"k_new and v_new must be {shape}")
-    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
-        raise TypeError("k_new/v_new must have the pool dtype")
+    if k_new.dtype != io_dtype(k_pool) or v_new.dtype != io_dtype(k_pool):
+        raise TypeError("k_new/v_new must have the pool's element type (bf16 for 8-bit)")
     if T == 0:
         return
     st = _lib.pa_kv_write(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
@@ -180,10 +224,10 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
     ``workspace`` is a uint8 GPU tensor of at least pa_decode_workspace_bytes
     bytes; when None one is allocated here with torch (the library itself
     never allocates)."""
-    desc = pool_desc(k_pool, v_pool)
     S, Hq, d = q.shape
-    if d != desc.head_dim or q.dtype != k_pool.dtype:
-        raise ValueError("q must be [S][Hq][head_dim] in the pool dtype")
+    desc = pool_desc(k_pool, v_pool)
+    if d != desc.head_dim or q.dtype != io_dtype(k_pool):
+        raise ValueError("q must be [S][Hq][head_dim] in the pool's element type")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
@@ -248,8 +292,8 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, seq_i
     shape = (T, desc.num_kv_heads, desc.head_dim)
     if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
         raise ValueError(f"k_new and v_new must be {shape}")
-    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
-        raise TypeError("k_new/v_new must have the pool dtype")
+    if k_new.dtype != io_dtype(k_pool) or v_new.dtype != io_dtype(k_pool):
+        raise TypeError("k_new/v_new must have the pool's element type (bf16 for 8-bit)")
     if seq_ids.numel() != T or positions.numel() != T:
         raise ValueError("seq_ids, positions and slot_mapping must have one entry per token")
     if T == 0:

@@ -19,11 +19,20 @@ bool debug_checks() {
   return v && v[0] && strcmp(v, "0") != 0;
 }
 
-int elem_bytes(pa_dtype dt) { return dt == PA_BF16 ? 2 : 4; }
-
 bool pool_ok(const pa_pool* p) {
-  return p && p->num_blocks > 0 && p->block_size > 0 && p->num_kv_heads > 0 &&
-         p->head_dim > 0 && (p->dtype == PA_F32 || p->dtype == PA_BF16);
+  if (!p || p->num_blocks <= 0 || p->block_size <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0)
+    return false;
+  if (p->dtype == PA_FP8_E4M3) return p->block_size % 4 == 0;  // whole scale groups
+  return p->dtype == PA_F32 || p->dtype == PA_BF16;
+}
+
+// Bytes of one block (every kv head) in the K buffer and in the V buffer; an
+// 8-bit K region also carries the block's scales.
+size_t block_bytes(const pa_pool* p, bool v_side) {
+  const size_t B = (size_t)p->block_size, d = (size_t)p->head_dim;
+  size_t per_head = B * d * (p->dtype == PA_F32 ? 4 : p->dtype == PA_BF16 ? 2 : 1);
+  if (p->dtype == PA_FP8_E4M3 && !v_side) per_head += 4 * B;
+  return (size_t)p->num_kv_heads * per_head;
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -102,8 +111,7 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool, const voi
   }
   hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
                                        pool->num_kv_heads, pool->block_size, pool->head_dim,
-                                       elem_bytes(pool->dtype), nullptr, 0, nullptr, nullptr,
-                                       st);
+                                       pool->dtype, nullptr, 0, nullptr, nullptr, st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -136,7 +144,7 @@ pa_status pa_kv_append(const pa_pool* pool, void* k_pool, void* v_pool, const vo
   }
   hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
                                        pool->num_kv_heads, pool->block_size, pool->head_dim,
-                                       elem_bytes(pool->dtype), block_tables,
+                                       pool->dtype, block_tables,
                                        max_blocks_per_seq, seq_ids, positions, st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
@@ -242,9 +250,8 @@ pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool, const i
     for (int32_t b = 0; b < pool->num_blocks; ++b)
       if (is_src[(size_t)b] && is_dst[(size_t)b]) return PA_EINVAL;
   }
-  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
-                             elem_bytes(pool->dtype);
-  hipError_t e = pakv::launch_block_copy(k_pool, v_pool, pairs, num_pairs, block_bytes, st);
+  hipError_t e = pakv::launch_block_copy(k_pool, v_pool, pairs, num_pairs,
+                                         block_bytes(pool, false), block_bytes(pool, true), st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 

@@ -12,6 +12,11 @@
 //  * Table update: the block-table entry covering a written token's logical
 //    position takes the block the token went to.  The append entry point
 //    runs it inside the slot-write launch.
+//  * 8-bit slot write (a quantized cache, vLLM post "Where it bites"): each
+//    (token, kv head) row of K and of V is quantised on its own to OCP E4M3
+//    codes with one scale, scale = bf16(max |x| / 448), code = x / scale
+//    rounded to nearest even.  Not bitwise: the one kernel here with
+//    arithmetic.
 #include "pa_internal.h"
 
 namespace pakv {
@@ -39,6 +44,14 @@ struct TableArgs {
   const int32_t* positions;
 };
 
+// Table entry of token i (thread 0 of token i's workgroup).
+__device__ __forceinline__ void update_table(const TableArgs& ta, int i, int64_t blk,
+                                             int block_size) {
+  if (ta.tables != nullptr && threadIdx.x == 0)
+    ta.tables[(size_t)ta.seq_ids[i] * ta.max_blocks + ta.positions[i] / block_size] =
+        static_cast<int32_t>(blk);
+}
+
 // One workgroup per new token.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(
@@ -50,9 +63,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
   const int64_t slot = slots[i];
   if (slot < 0) return;
   const int64_t blk = slot / block_size;
-  if (ta.tables != nullptr && threadIdx.x == 0)
-    ta.tables[(size_t)ta.seq_ids[i] * ta.max_blocks + ta.positions[i] / block_size] =
-        static_cast<int32_t>(blk);
+  update_table(ta, i, blk, block_size);
   const int r = static_cast<int>(slot % block_size);
   constexpr int ES = sizeof(E);
   const size_t row_bytes = (size_t)head_dim * ES;
@@ -88,12 +99,71 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(
   }
 }
 
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// E4M3 code of x (|x| within the finite range), nearest even: the gfx950
+// packed fp32 -> OCP fp8 conversion, low byte.
+__device__ __forceinline__ uint8_t to_e4m3(float x) {
+  return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xffu);
+}
+
+// 8-bit slot write: one workgroup per new token, one wave per (kv head,
+// K or V) row at a time.  K region of (block b, kv head g): [B*d codes,
+// token-major r*d + e][scale groups: per 4 slots, 4 K then 4 V bf16 scales];
+// V region: [B*d codes, dim-major e*B + r].
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t block_size,
+    int32_t head_dim, TableArgs ta) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  update_table(ta, i, blk, block_size);
+  const int r = static_cast<int>(slot % block_size);
+  const int B = block_size, d = head_dim;
+  const size_t k_region = (size_t)B * d + 4u * (size_t)B, v_region = (size_t)B * d;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int row = wave; row < 2 * num_kv_heads; row += kThreads / 64) {
+    const bool is_v = row >= num_kv_heads;
+    const int g = is_v ? row - num_kv_heads : row;
+    const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)i * num_kv_heads + g) * d;
+    uint8_t* kreg = k_pool + ((size_t)blk * num_kv_heads + g) * k_region;
+    uint8_t* vreg = v_pool + ((size_t)blk * num_kv_heads + g) * v_region;
+    float amax = 0.f;  // NaN inputs are skipped by fmaxf
+    for (int e = lane; e < d; e += 64)
+      amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)src[e] << 16)));
+    amax = wave_max64(amax);
+    // scale = amax / 448 (IEEE division), rounded to bf16 (v_cvt_pk_bf16_f32, RNE)
+    const __bf16 sb = static_cast<__bf16>(amax / 448.f);
+    const float scale = static_cast<float>(sb);
+    for (int e = lane; e < d; e += 64) {
+      const float x = __uint_as_float((uint32_t)src[e] << 16);
+      const uint8_t c = scale > 0.f ? to_e4m3(x / scale) : uint8_t{0};
+      if (is_v)
+        st_pool(vreg + (size_t)e * B + r, c);
+      else
+        st_pool(kreg + (size_t)r * d + e, c);
+    }
+    if (lane == 0)
+      st_pool(reinterpret_cast<uint16_t*>(kreg + (size_t)B * d + 16u * (r / 4) + 8u * is_v) +
+                  (r % 4),
+              __builtin_bit_cast(uint16_t, sb));
+  }
+}
+
 // grid (num_pairs, 2): y = 0 copies the K block, y = 1 the V block.
 __global__ __launch_bounds__(kThreads) void block_copy16_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-    const int32_t* __restrict__ pairs, size_t block_bytes) {
+    const int32_t* __restrict__ pairs, size_t k_bytes, size_t v_bytes) {
   const int p = blockIdx.x;
   uint8_t* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const size_t block_bytes = blockIdx.y == 0 ? k_bytes : v_bytes;
   const size_t src = (size_t)pairs[2 * p] * block_bytes;
   const size_t dst = (size_t)pairs[2 * p + 1] * block_bytes;
   const size_t n16 = block_bytes / 16;
@@ -104,9 +174,10 @@ __global__ __launch_bounds__(kThreads) void block_copy16_kernel(
 
 __global__ __launch_bounds__(kThreads) void block_copy_bytes_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-    const int32_t* __restrict__ pairs, size_t block_bytes) {
+    const int32_t* __restrict__ pairs, size_t k_bytes, size_t v_bytes) {
   const int p = blockIdx.x;
   uint8_t* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const size_t block_bytes = blockIdx.y == 0 ? k_bytes : v_bytes;
   const size_t src = (size_t)pairs[2 * p] * block_bytes;
   const size_t dst = (size_t)pairs[2 * p + 1] * block_bytes;
   for (size_t c = threadIdx.x; c < block_bytes; c += kThreads) st_pool(pool + dst + c, pool[src + c]);
@@ -128,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void table_update_kernel(
 
 hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slots, int32_t T, int32_t num_kv_heads,
-                           int32_t block_size, int32_t head_dim, int32_t elem_bytes,
+                           int32_t block_size, int32_t head_dim, pa_dtype dtype,
                            int32_t* block_tables, int32_t max_blocks, const int32_t* seq_ids,
                            const int32_t* positions, hipStream_t st) {
   if (T <= 0) return hipSuccess;
@@ -137,7 +208,11 @@ hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const 
   auto kn = static_cast<const uint8_t*>(k_new);
   auto vn = static_cast<const uint8_t*>(v_new);
   const TableArgs ta{block_tables, max_blocks, seq_ids, positions};
-  if (elem_bytes == 2)
+  if (dtype == PA_FP8_E4M3)
+    kv_write_fp8_kernel<<<T, kThreads, 0, st>>>(kp, vp, static_cast<const uint16_t*>(k_new),
+                                                static_cast<const uint16_t*>(v_new), slots,
+                                                num_kv_heads, block_size, head_dim, ta);
+  else if (dtype == PA_BF16)
     kv_write_kernel<uint16_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
                                                       block_size, head_dim, ta);
   else
@@ -147,15 +222,16 @@ hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const 
 }
 
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
-                             int32_t num_pairs, size_t block_bytes, hipStream_t st) {
+                             int32_t num_pairs, size_t k_bytes, size_t v_bytes,
+                             hipStream_t st) {
   if (num_pairs <= 0) return hipSuccess;
   const dim3 grid(num_pairs, 2);
   auto kp = static_cast<uint8_t*>(k_pool);
   auto vp = static_cast<uint8_t*>(v_pool);
-  if (block_bytes % 16 == 0)
-    block_copy16_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, block_bytes);
+  if (k_bytes % 16 == 0 && v_bytes % 16 == 0)
+    block_copy16_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, k_bytes, v_bytes);
   else
-    block_copy_bytes_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, block_bytes);
+    block_copy_bytes_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, k_bytes, v_bytes);
   return hipGetLastError();
 }
 

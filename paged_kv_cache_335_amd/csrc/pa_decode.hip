@@ -169,18 +169,24 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Exclusive scan of one value per thread over the 256-thread workgroup.
+// Exclusive scan of one value per thread over the workgroup (at most 8
+// waves: wsum holds one partial sum per wave).
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int inc = wave_incl_scan(v, lane);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wave; ++w) off += wsum[w];
-  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  int off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) off += wsum[w];
+    tot += wsum[w];
+  }
+  *total = tot;
   __syncthreads();
   return off + inc - v;
 }
+static_assert(kWaves >= 1 && kWaves <= 8, "the plan scan keeps one sum per wave, 8 at most");
 
 // Collective over the workgroup (256 threads); ends with a barrier.
 __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
@@ -310,10 +316,49 @@ __device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& com
   });
 }
 
+// Epilogue of an MFMA unit: acc[nt][r] holds head 4*grp + r, dim nt*16 + col
+// (unnormalised); a sequence finished in one piece is normalised and stored
+// as bf16, otherwise (m, l, o) go to the piece's partial slot.
+template <int D>
+__device__ __forceinline__ void finish_mfma_unit(const DecodeArgs& a, int G, const Unit& u,
+                                                 const f32x4* acc, float m_ref, float l_tot,
+                                                 int lane) {
+  constexpr int NT = D / 16;
+  const int s = u.s, g = u.g;
+  const int col = lane & 15, grp = lane >> 4;
+  if (u.nparts == 1) {
+    float den[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * grp + r;
+      if (h >= G) continue;
+      const size_t ob = ((size_t)s * a.num_q_heads + g * G + h) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) store_out<__bf16>(a.out, ob + nt * 16, acc[nt][r] / den[r]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * grp + r;
+      if (h >= G) continue;
+      float* po = a.part_o + part_index(a, s, g * G + h, u.part) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) po[nt * 16] = acc[nt][r];
+    }
+    if (grp == 0 && col < G) {
+      const size_t pi = part_index(a, s, g * G + col, u.part);
+      a.part_m[pi] = m_ref;
+      a.part_l[pi] = l_tot;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// MFMA kernel: bf16 pools, G in (GM/2, GM] query heads per kv head.
+// MFMA kernel: bf16 pools, 1..16 query heads per kv head.
 // ---------------------------------------------------------------------------
-template <int D, int GM, int NBUF>
+template <int D, int NBUF>
 __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
   constexpr int B = kBlock;
   constexpr int KJ = D / 32;  // q.K MFMAs per block (32 dims each)
@@ -455,38 +500,228 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
   // l over the four lane groups holding the same head; m_ref is uniform
   float l_tot = l_run + swap16(l_run);
   l_tot += swap32(l_tot);
-
-  // acc[nt][r] holds head 4*grp + r, dim nt*16 + col
-  if (u.nparts == 1) {
-    float den[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * grp + r;
-      if (h >= G) continue;
-      const size_t ob = ((size_t)s * a.num_q_heads + g * G + h) * D + col;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) store_out<__bf16>(a.out, ob + nt * 16, acc[nt][r] / den[r]);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * grp + r;
-      if (h >= G) continue;
-      float* po = a.part_o + part_index(a, s, g * G + h, u.part) * D + col;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) po[nt * 16] = acc[nt][r];
-    }
-    if (grp == 0 && col < G) {
-      const size_t pi = part_index(a, s, g * G + col, u.part);
-      a.part_m[pi] = m_ref;
-      a.part_l[pi] = l_tot;
-    }
-  }
+  finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
 }
 
-template <int D, int GM, int NBUF>
+// ---------------------------------------------------------------------------
+// MFMA kernel for 8-bit pools: per (block, kv head) a K region of E4M3 codes
+// ([16][D] token-major) followed by bf16 scales (per group of 4 tokens, 4 K
+// scales then 4 V scales) and a V region of codes ([D][16] dim-major).
+// Codes widen to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1), so
+// the bf16 MFMAs of the kernel above do the products; the per-token scales
+// are applied where each token has one value per lane: the K scale on its
+// score, the V scale on its probability.  Per block and lane (D = 128): two
+// 16-byte K code loads, one 16-byte load holding the K and V scales of the
+// lane's 4 tokens, and two 16-byte V code loads.
+// Load shape matters more than bytes at this granularity: a wave-wide load
+// that covers 1 KB contiguously streams 2 KB regions about 15% faster than
+// eight 4-byte-per-lane loads of 256 B each (measured on random 2 KB
+// chunks).  So V is read contiguously -- lane l gets the 16 tokens of one
+// dim -- and a 4x4 transpose between the four 16-lane rows and four
+// registers (v_permlane32_swap, then v_permlane16_swap) turns that into the
+// MFMA operand layout, 4 tokens of a dim per lane.
+// ---------------------------------------------------------------------------
+// 4x4 transpose between the four 16-lane rows of a wave and four registers:
+// on return r[t] in row g holds what r[g] held in row t.
+__device__ __forceinline__ void transpose_rows4(uint32_t& r0, uint32_t& r1, uint32_t& r2,
+                                                uint32_t& r3) {
+  // rows {2,3} of r0 <-> rows {0,1} of r2, and of r1 <-> r3
+  auto a = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  // odd rows of the first <-> even rows of the second
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r0 = c[0];
+  r1 = c[1];
+  r2 = e[0];
+  r3 = e[1];
+}
+
+// Four E4M3 codes (one dword, lowest byte first) -> four bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+  return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+template <int D, int NBUF>
+__device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
+  constexpr int B = kBlock;
+  constexpr int KC = D / 64;              // 16-byte K code loads per lane per block
+  constexpr int VC = D / 64;              // 16-byte V code loads per lane per block
+  constexpr int KJ = D / 32;              // q.K MFMAs per block
+  constexpr int NT = D / 16;              // P.V MFMAs per block
+  constexpr uint32_t QROW = D * 2;         // bytes per bf16 q row
+  constexpr uint32_t SOFF = B * D;         // offset of the scales in a K region
+  constexpr uint32_t RBK = B * D + 4 * B;  // K region bytes per (block, kv head)
+  constexpr uint32_t RBV = B * D;          // V region bytes per (block, kv head)
+
+  const int s = u.s, g = u.g, L = u.L;
+  const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // K codes: lane loads token col, dims c*64 + grp*16 .. +16 (c < KC).  MFMA
+  // kj = 2c + h takes the h-th 8 of those 16 dims, so the q operand of step
+  // kj holds q[head col][c*64 + grp*16 + h*8 .. +8].  The order in which
+  // dims meet the MFMA does not change the dot product.
+  bf16x8 qop[KJ];
+  {
+    u32x4 w[KJ];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
+    if (col < G) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                          ((size_t)s * a.num_q_heads + g * G + col) * QROW + grp * 32;
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
+        w[kj] = *reinterpret_cast<const u32x4*>(qp + (kj >> 1) * 128 + (kj & 1) * 16);
+    }
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
+  }
+
+  const size_t kblk_bytes = (size_t)a.num_kv_heads * RBK;
+  const size_t vblk_bytes = (size_t)a.num_kv_heads * RBV;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * RBK;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * RBV;
+  const uint32_t koff = col * D + grp * 16;
+  const uint32_t voff = lane * 16;           // dim h*64 + lane of load h: its 16 tokens
+  const uint32_t soff = SOFF + grp * 16;     // K and V scales of tokens 4*grp .. +4
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 kring[NBUF][KC];
+  u32x4 sring[NBUF];
+  u32x4 vring[NBUF][VC];
+
+  const int nblk = je - jb;
+  for (int c0 = 0; c0 < nblk; c0 += 64) {
+    const int cnt = min(64, nblk - c0);
+    const int tab = trow[jb + c0 + min(lane, cnt - 1)];
+
+    auto load = [&](int i, auto slot) {
+      const size_t b = (size_t)__builtin_amdgcn_readlane(tab, i);
+      const gptr kblk = uniform_ptr(kpool + b * kblk_bytes);
+      const gptr vblk = uniform_ptr(vpool + b * vblk_bytes);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kring[slot][c] = ldg_stream<u32x4>(kblk + koff + c * 64);
+      sring[slot] = ldg_stream<u32x4>(kblk + soff);
+#pragma unroll
+      for (int h = 0; h < VC; ++h) vring[slot][h] = ldg_stream<u32x4>(vblk + voff + h * 1024);
+    };
+
+    auto compute = [&](int i, auto slot) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 w = kring[slot][c];
+        const u32x2 k0 = e4m3x4_to_bf16(w.x), k1 = e4m3x4_to_bf16(w.y);
+        const u32x2 k2 = e4m3x4_to_bf16(w.z), k3 = e4m3x4_to_bf16(w.w);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{k0.x, k0.y, k1.x, k1.y}), qop[2 * c], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{k2.x, k2.y, k3.x, k3.y}), qop[2 * c + 1], sc, 0, 0,
+            0);
+      }
+      // scales of tokens 4*grp + r: bf16 pairs, K in words x, y and V in z, w
+      const u32x4 sw = sring[slot];
+      const f32x4 ks = {__uint_as_float(sw.x << 16), bf16_hi(sw.x), __uint_as_float(sw.y << 16),
+                        bf16_hi(sw.y)};
+      f32x4 vs = {__uint_as_float(sw.z << 16), bf16_hi(sw.z), __uint_as_float(sw.w << 16),
+                  bf16_hi(sw.w)};
+      // load h, row r held dim h*64 + r*16 + col (tile 4h + r), token group j
+      // in word j; after the transpose word t of row g is tile 4h + t, tokens
+      // 4g .. 4g + 3 of dim col: the B operand layout of P.V
+      uint32_t vb[NT];
+#pragma unroll
+      for (int h = 0; h < VC; ++h) {
+        uint32_t w0 = vring[slot][h].x, w1 = vring[slot][h].y, w2 = vring[slot][h].z,
+                 w3 = vring[slot][h].w;
+        transpose_rows4(w0, w1, w2, w3);
+        vb[4 * h + 0] = w0;
+        vb[4 * h + 1] = w1;
+        vb[4 * h + 2] = w2;
+        vb[4 * h + 3] = w3;
+      }
+      // sc[r] = code-level score of token 4*grp + r for head col
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks[r] * a.scale_log2;
+      const int valid = L - (jb + c0 + i) * B;
+      if (valid < B) {
+        // slots past the context: score -inf, V codes and scale zeroed
+        const int t = 4 * grp;
+        uint32_t m = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (t + r >= valid) {
+            x[r] = kNegInf;
+            vs[r] = 0.f;
+          } else {
+            m |= 0xffu << (8 * r);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) vb[nt] &= m;
+      }
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, swap16(bm));
+      bm = fmaxf(bm, swap32(bm));
+      if (__ballot(bm > m_ref + kSlack)) {
+        const float m_new = fmaxf(m_ref, bm);
+        const float alpha = fexp2(m_ref - m_new);
+        l_run *= alpha;
+        m_ref = m_new;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      // the V scale rides on the probability: o += (p * s_v) * code
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] *= vs[r];
+      uint32_t pb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
+      const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
+                           static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
+      const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
+                           static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
+      const i16x4 phi = __builtin_bit_cast(
+          i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
+      const i16x4 plo = __builtin_bit_cast(
+          i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+      i16x4 vop[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vop[nt] = __builtin_bit_cast(i16x4, e4m3x4_to_bf16(vb[nt]));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vop[nt], acc[nt], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop[nt], acc[nt], 0, 0, 0);
+    };
+
+    block_ring<NBUF>(cnt, load, compute);
+  }
+
+  float l_tot = l_run + swap16(l_run);
+  l_tot += swap32(l_tot);
+  finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
+}
+
+template <int D, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan(a, plan_lds);
@@ -498,7 +733,21 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kerne
   const int lane = threadIdx.x & 63;
   const int g = hg * kWaves + wave;
   if (g >= a.num_kv_heads) return;
-  walk_range(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, GM, NBUF>(a, G, u, lane); });
+  walk_range(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, NBUF>(a, G, u, lane); });
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
+  extern __shared__ int plan_lds[];
+  const Plan pl = build_plan(a, plan_lds);
+  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
+  if (r >= pl.R) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = hg * kWaves + wave;
+  if (g >= a.num_kv_heads) return;
+  walk_range(a, pl, r, g, [&](const Unit& u) { mfma8_unit<D, NBUF>(a, G, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -794,18 +1043,22 @@ Launch decode_launch(const DecodeArgs& a, K kernel) {
   return {dim3((unsigned)(ranges * hg)), dim3(kWaves * 64), lds};
 }
 
-template <int D, int GM>
-hipError_t launch_mfma_g(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_mfma_kernel<D, GM, kNBuf>);
-  decode_mfma_kernel<D, GM, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
-  return hipGetLastError();
+// The head group (1..16) fills the 16 head slots of the MFMA tiles at run
+// time, so one instantiation per head_dim serves every group size.
+template <int D>
+hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
+  const Launch l = decode_launch(a, decode_mfma_kernel<D, kNBuf>);
+  decode_mfma_kernel<D, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce<__bf16, D>(a, st);
 }
 
 template <int D>
-hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
-  hipError_t e = G <= 4 ? launch_mfma_g<D, 4>(a, G, st)
-               : G <= 8 ? launch_mfma_g<D, 8>(a, G, st)
-                        : launch_mfma_g<D, 16>(a, G, st);
+hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
+  const Launch l = decode_launch(a, decode_mfma8_kernel<D, kNBuf8>);
+  decode_mfma8_kernel<D, kNBuf8><<<l.grid, l.block, l.lds, st>>>(a, G);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
 }
@@ -840,6 +1093,7 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group) {
     if (group <= kMaxMfmaGroup) return DecodePath::kMfma;
     return DecodePath::kUnsupported;
   }
+  if (dtype == PA_FP8_E4M3 && group <= kMaxMfmaGroup) return DecodePath::kMfma8;
   if (dtype == PA_F32 && group <= 4) return DecodePath::kValu;
   return DecodePath::kUnsupported;
 }
@@ -850,6 +1104,8 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
   switch (decode_path(dtype, head_dim, group)) {
     case DecodePath::kMfma:
       return head_dim == 128 ? launch_mfma<128>(a, group, st) : launch_mfma<64>(a, group, st);
+    case DecodePath::kMfma8:
+      return head_dim == 128 ? launch_mfma8<128>(a, group, st) : launch_mfma8<64>(a, group, st);
     case DecodePath::kValu:
       return head_dim == 128 ? launch_valu<128>(a, group, st) : launch_valu<64>(a, group, st);
     default:
@@ -863,7 +1119,7 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
 // is offset to the slice.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
                          hipStream_t st) {
-  const size_t es = dtype == PA_BF16 ? 2 : 4;
+  const size_t es = dtype == PA_F32 ? 4 : 2;  // q / out element (bf16 for 8-bit pools)
   for (int32_t s0 = 0; s0 < a.num_seqs; s0 += kMaxPlanSeqs) {
     DecodeArgs b = a;
     b.num_seqs = std::min(kMaxPlanSeqs, a.num_seqs - s0);

@@ -21,6 +21,9 @@ namespace pakv {
 #ifndef PA_MFMA_MIN_WG
 #define PA_MFMA_MIN_WG 2  // MFMA decode: workgroups per CU the register budget must allow
 #endif
+#ifndef PA_NBUF8
+#define PA_NBUF8 4   // register buffers per wave for 8-bit pools (half the bytes per block)
+#endif
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1  // 1: K/V loads carry the non-temporal hint
 #endif
@@ -28,6 +31,7 @@ namespace pakv {
 constexpr int kBlock = 16;       // tokens per block supported by decode
 constexpr int kWaves = PA_WAVES;
 constexpr int kNBuf = PA_NBUF;
+constexpr int kNBuf8 = PA_NBUF8;
 constexpr int kMaxMfmaGroup = 16;
 constexpr int kMaxSlots = 1 << 20;  // partial slots per (sequence, head)
 constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan)
@@ -53,22 +57,24 @@ struct DecodeArgs {
 };
 
 // Which decode kernel family handles a shape.
-enum class DecodePath { kUnsupported, kValu, kMfma };
+enum class DecodePath { kUnsupported, kValu, kMfma, kMfma8 };
 DecodePath decode_path(pa_dtype dtype, int head_dim, int group);
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
                          hipStream_t stream);
 
-// block_tables == nullptr: no table update (plain slot write).
+// block_tables == nullptr: no table update (plain slot write).  For
+// PA_FP8_E4M3 pools k_new / v_new are bf16 and are quantised.
 hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new,
                            const void* v_new, const int64_t* slots, int32_t T,
                            int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
-                           int32_t elem_bytes, int32_t* block_tables, int32_t max_blocks,
+                           pa_dtype dtype, int32_t* block_tables, int32_t max_blocks,
                            const int32_t* seq_ids, const int32_t* positions,
                            hipStream_t stream);
 
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
-                             int32_t num_pairs, size_t block_bytes, hipStream_t stream);
+                             int32_t num_pairs, size_t k_block_bytes, size_t v_block_bytes,
+                             hipStream_t stream);
 
 hipError_t launch_table_update(int32_t* block_tables, int32_t max_blocks,
                                int32_t block_size, const int32_t* seq_ids,

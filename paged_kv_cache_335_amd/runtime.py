@@ -19,8 +19,8 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (PA_OK, PagedKVError, pa_block_copy, pa_decode, pa_decode_partition_tokens,
-               pa_decode_workspace_bytes, pa_kv_append)
+from . import (PA_OK, PagedKVError, alloc_pools, pa_block_copy, pa_decode,
+               pa_decode_partition_tokens, pa_decode_workspace_bytes, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -103,10 +103,9 @@ class PagedKVCache:
         self.dtype = dtype
         self.device = torch.device(device)
         self.bm = BlockManager(num_blocks, block_size, shuffle_seed)
-        self.k_pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
-                                  device=self.device)
-        self.v_pool = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype,
-                                  device=self.device)
+        # dtype torch.uint8: 8-bit pools (E4M3 codes + per-token scales)
+        self.k_pool, self.v_pool = alloc_pools(num_blocks, num_kv_heads, head_dim, block_size,
+                                               dtype, self.device)
         self.tables = torch.zeros((max_seqs, table_width), dtype=torch.int32, device=self.device)
         # device lengths of the latest step (a view into its staging buffer)
         self.lens = torch.zeros(max_seqs, dtype=torch.int32, device=self.device)

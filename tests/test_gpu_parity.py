@@ -15,7 +15,7 @@ import torch
 import oracle
 from oracle.bm_model import BlockManagerModel
 from workloads import (CONFIGS, POISON_V, block_copy_case, decode_case, kv_write_case)
-from workloads.gen import from_numpy_storage, to_numpy_storage
+from workloads.gen import fp8_poison, fp8_region_bytes, from_numpy_storage, to_numpy_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -307,10 +307,11 @@ def test_kv_append_bit_exact(pk):
 
 # --- the whole path: block manager -> copy -> write -> decode -----------------
 def _run_path_both(pk, prompts, samples, shared, private_lo, private_hi, Hq, Hkv, d, seed,
-                   decode_steps=3):
+                   decode_steps=3, kv="bf16"):
     """Each side runs its own block manager and kernels from the same seeded
     token K/V; tables/slots/pairs must match exactly, pools bit for bit, and
-    attention within tolerance."""
+    attention within tolerance.  kv="fp8": 8-bit pools (tokens stay bf16 and
+    are quantised by each side's slot write)."""
     B = 16
     rng = np.random.default_rng(seed)
     privs = rng.integers(private_lo, private_hi, prompts * samples, endpoint=True)
@@ -319,10 +320,18 @@ def _run_path_both(pk, prompts, samples, shared, private_lo, private_hi, Hq, Hkv
     cbm = pk.BlockManager(nb, B, bm_seed)
     mbm = BlockManagerModel(nb, B, bm_seed)
     dt = torch.bfloat16
-    k_dev = torch.full((nb, Hkv, B, d), 64.0, dtype=dt, device="cuda")
-    v_dev = torch.full((nb, Hkv, d, B), POISON_V, dtype=dt, device="cuda")
-    k_host = to_numpy_storage(k_dev)
-    v_host = to_numpy_storage(v_dev)
+    if kv == "fp8":
+        rk, rv = fp8_region_bytes(B, d)
+        k_host = np.zeros((nb, Hkv, rk), np.uint8)
+        v_host = np.zeros((nb, Hkv, rv), np.uint8)
+        fp8_poison(k_host, v_host, np.ones((nb, B), bool), B, d)
+        k_dev = torch.from_numpy(k_host).cuda()
+        v_dev = torch.from_numpy(v_host).cuda()
+    else:
+        k_dev = torch.full((nb, Hkv, B, d), 64.0, dtype=dt, device="cuda")
+        v_dev = torch.full((nb, Hkv, d, B), POISON_V, dtype=dt, device="cuda")
+        k_host = to_numpy_storage(k_dev)
+        v_host = to_numpy_storage(v_dev)
 
     def tokens(n):
         kn = torch.from_numpy(rng.standard_normal((n, Hkv, d), dtype=np.float32)).to(dt)
@@ -408,6 +417,12 @@ def test_full_path_full_shared_tail_no_copy(pk):
 def test_full_path_mha(pk):
     _run_path_both(pk, prompts=6, samples=1, shared=200, private_lo=1, private_hi=300, Hq=8,
                    Hkv=8, d=128, seed=13)
+
+
+def test_full_path_fp8_cache_with_copy_on_write(pk):
+    n_cow = _run_path_both(pk, prompts=4, samples=4, shared=104, private_lo=1, private_hi=40,
+                           Hq=32, Hkv=8, d=128, seed=14, kv="fp8")
+    assert n_cow == 4 * 3
 
 
 # --- error paths ---------------------------------------------------------------

@@ -137,3 +137,56 @@ def test_event_helper_uses_the_hip_runtime_torch_loaded():
     maps = open("/proc/self/maps").read().splitlines()
     copies = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(copies) == 1, copies
+
+
+def test_fp8_pool_geometry_and_dtypes_checked_on_the_host():
+    """8-bit pools are a uint8 pair, K [nb][H][B*(d+4)] and V [nb][H][B*d]:
+    block size and head dim follow from the two; their q and new tokens must
+    be bf16.  Rejected before any device call."""
+    import paged_kv_cache_335_amd as pk
+    rk, rv = pk.fp8_region_bytes(16, 64)
+    k = torch.zeros(4, 2, rk, dtype=torch.uint8)
+    v = torch.zeros(4, 2, rv, dtype=torch.uint8)
+    d = pk.pool_desc(k, v)
+    assert (d.num_blocks, d.block_size, d.num_kv_heads, d.head_dim, d.dtype) == \
+        (4, 16, 2, 64, pk.PA_FP8_E4M3)
+    with pytest.raises(ValueError):
+        pk.pool_desc(k, k)                                   # V region must be smaller
+    with pytest.raises(ValueError):
+        pk.pool_desc(k, torch.zeros(4, 2, rv + 4, dtype=torch.uint8))
+    q = torch.zeros(1, 2, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        pk.pa_decode(q, k, v, torch.zeros(1, 1, dtype=torch.int32),
+                     torch.ones(1, dtype=torch.int32), 0.1)
+    kn = torch.zeros(1, 2, 64, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        pk.pa_kv_write(k, v, kn, kn, torch.zeros(1, dtype=torch.int64))
+    a, b = pk.alloc_pools(3, 2, 64, 16, torch.uint8, device="cpu")
+    assert tuple(a.shape) == (3, 2, rk) and tuple(b.shape) == (3, 2, rv)
+
+
+def test_fp8_host_checks_in_the_c_abi():
+    """The C entry points accept PA_FP8_E4M3 pools and reject unsupported
+    decode shapes for them without a launch."""
+    import paged_kv_cache_335_amd as pk
+    L = pk.lib()
+    null = ctypes.c_void_p(0)
+    dummy = ctypes.c_void_p(0x1000)
+    d8 = pk.PoolDesc(64, 16, 8, 128, pk.PA_FP8_E4M3)
+    ws = L.pa_decode_workspace_bytes(ctypes.byref(d8), 4, 32, 64, 0)
+    assert ws > 0
+    bad_dim = pk.PoolDesc(64, 16, 8, 96, pk.PA_FP8_E4M3)
+    st = L.pa_decode(ctypes.byref(bad_dim), dummy, dummy, dummy, 1, 32, dummy, 4, dummy, 0.1,
+                     dummy, 0, dummy, 1 << 20, null)
+    assert st == pk.PA_EUNSUPPORTED
+    group17 = pk.PoolDesc(64, 16, 1, 128, pk.PA_FP8_E4M3)
+    st = L.pa_decode(ctypes.byref(group17), dummy, dummy, dummy, 1, 17, dummy, 4, dummy, 0.1,
+                     dummy, 0, dummy, 1 << 20, null)
+    assert st == pk.PA_EUNSUPPORTED
+    odd_block = pk.PoolDesc(64, 6, 8, 128, pk.PA_FP8_E4M3)    # scale groups of 4 slots
+    assert L.pa_kv_write(ctypes.byref(odd_block), dummy, dummy, dummy, dummy, dummy, 4,
+                         null) == pk.PA_EINVAL
+    bad_type = pk.PoolDesc(64, 16, 8, 128, 3)
+    assert L.pa_kv_write(ctypes.byref(bad_type), dummy, dummy, dummy, dummy, dummy, 4,
+                         null) == pk.PA_EINVAL
+    assert L.pa_block_copy(ctypes.byref(d8), null, null, null, 0, null) == pk.PA_OK
