@@ -158,8 +158,9 @@ def main():
     ones = np.ones(S, np.int32)
     P = cache.partition_tokens(Hq, args.partition)
     cache.workspace(Hq, args.partition)
-    # bytes of one token's K and V rows for every kv head (8-bit: codes + scale)
-    kv_per_token = 2 * Hkv * (d + 4 if fp8 else d * 2)
+    # bytes of one token's K and V rows for every kv head (8-bit: d codes and
+    # one bf16 scale per side)
+    kv_per_token = 2 * Hkv * (d + 2 if fp8 else d * 2)
 
     # decode timing: events without a system-scope fence, so recording them
     # does not write back and invalidate the caches between the step's kernels

@@ -230,9 +230,9 @@ class DecodeCase:
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes one decode reads: sum_s L_s * 2 * H_kv * (bytes
-        per token row: d * e, or d codes + one 4-byte scale for 8-bit pools)."""
+        per token row: d * e, or d codes + one bf16 scale for 8-bit pools)."""
         c = self.cfg
-        row = c.head_dim + 4 if self.dtype == "fp8" else \
+        row = c.head_dim + 2 if self.dtype == "fp8" else \
             c.head_dim * (2 if self.dtype == "bf16" else 4)
         return int(self.lens.astype(np.int64).sum()) * 2 * c.num_kv_heads * row
 
