@@ -82,6 +82,9 @@ def parse():
                     help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--swap-blocks", type=int, default=1024,
+                    help="after timing, swap this many resident blocks out to pinned host memory "
+                         "and back, timed (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a kernel of known traffic, to scale the HBM byte counters)")
@@ -219,6 +222,10 @@ def main():
     cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
     torch.cuda.synchronize()
 
+    swap = None
+    if args.swap_blocks > 0:
+        swap = swap_probe(pk, cache, args.swap_blocks, stream)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -260,6 +267,7 @@ def main():
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(kv_avg)
                      if args.partition == 0 and not fp8 else None},
+        "block_swap": swap,
         "block_manager": {"tail_waste_pct": round(tail_waste, 3),
                           "contiguous_reservation_utilisation_pct": round(contiguous_util, 2),
                           "cow_copies": stats["cow_copies"]},
@@ -273,6 +281,39 @@ def main():
             cache, qs[-1], out, lens_now, S, Hq, d, kv_per_token, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def swap_probe(pk, cache, n, stream):
+    """Swap n resident blocks (K and V, every kv head) out to pinned host
+    memory and back into the same device blocks, each direction one
+    pa_block_swap launch timed with HIP events; the pools end unchanged."""
+    from paged_kv_cache_335_amd.runtime import DeviceEvent
+    k, v = cache.k_pool, cache.v_pool
+    n = min(n, k.shape[0])
+    hk, hv = pk.alloc_host_pools(n, k, v)
+    rng = np.random.default_rng(1)
+    dev = torch.from_numpy(rng.permutation(k.shape[0])[:n].astype(np.int32))
+    host = torch.arange(n, dtype=torch.int32)
+    out_pairs = torch.stack([dev, host], 1).contiguous().to(k.device)
+    in_pairs = torch.stack([host, dev], 1).contiguous().to(k.device)
+    block_bytes = (k[0].numel() * k.element_size() + v[0].numel() * v.element_size())
+    res = {}
+    for name, pairs, direction in (("out", out_pairs, pk.PA_SWAP_OUT),
+                                   ("in", in_pairs, pk.PA_SWAP_IN)):
+        best = None
+        for _ in range(3):
+            a, b = DeviceEvent(timing=True), DeviceEvent(timing=True)
+            a.record(stream)
+            pk.pa_block_swap(k, v, hk, hv, pairs, direction, stream=stream)
+            b.record(stream)
+            b.synchronize()
+            ms = a.elapsed_ms(b)
+            best = ms if best is None else min(best, ms)
+        res[name] = {"us": round(best * 1e3, 1),
+                     "GBps": round(n * block_bytes / (best * 1e-3) / 1e9, 2)}
+    log(f"block swap of {n} blocks ({n * block_bytes / 2**20:.0f} MiB): out "
+        f"{res['out']['GBps']} GB/s, in {res['in']['GBps']} GB/s")
+    return {"blocks": n, "bytes": int(n * block_bytes), **res}
 
 
 def cpu_baseline(cache, q, out, lens, S, Hq, d, kv_per_token, seconds):

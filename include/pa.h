@@ -177,6 +177,29 @@ pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool,
                         const int32_t* pairs, int32_t num_pairs, void* stream);
 
 /*
+ * Block swap between the device pools and host memory (preemption by
+ * swapping, vLLM post "Where it bites"; glossary entry "Flexible
+ * Management": pages can be swapped out, spilling to CPU RAM).
+ *   host_k, host_v: caller-owned PINNED host buffers (hipHostMalloc, or a
+ *       pinned torch tensor) of num_host_blocks blocks each, laid out like
+ *       k_pool / v_pool (same bytes per block); host pointers.
+ *   pairs: int32 [num_pairs][2] = (src, dst), device-accessible memory:
+ *       PA_SWAP_OUT copies device block src to host block dst,
+ *       PA_SWAP_IN copies host block src to device block dst, bitwise,
+ *       every kv head and slot of K and of V.  Destinations must be
+ *       distinct; src in [0, num_blocks) and dst in [0, num_host_blocks) for
+ *       SWAP_OUT, the other way round for SWAP_IN.
+ * One launch on `stream` moves every pair over the host link.  PA_EINVAL if
+ * the host buffers are not pinned host memory; nothing is launched then.
+ * num_pairs = 0 is a no-op.
+ */
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_dir;
+
+pa_status pa_block_swap(const pa_pool* pool, void* k_pool, void* v_pool, void* host_k,
+                        void* host_v, int32_t num_host_blocks, const int32_t* pairs,
+                        int32_t num_pairs, pa_swap_dir dir, void* stream);
+
+/*
  * Device-side mirror of table growth ("PagedAttention: paging, borrowed from
  * the operating system": a growing sequence appends an entry to its block
  * table).  For every i with slot_mapping[i] >= 0:

@@ -16,7 +16,10 @@
  *    copy-on-write": growing past a full shared block needs only a new block.
  *  - same page, section "Where it bites" of the vLLM page: a full pool forces
  *    the engine to preempt; this library reports the condition (PA_ENOMEM)
- *    and leaves the policy to the caller.
+ *    and leaves the policy to the caller.  One preemption it supports is
+ *    swapping a sequence's blocks out to host memory and back (same section;
+ *    glossary entry, "Flexible Management": pages can be swapped out or
+ *    spilled to CPU RAM).
  *
  * Deterministic choices (the pages leave them open):
  *  - The free pool is a stack initialised to [N-1, ..., 1, 0] (so the first
@@ -30,6 +33,15 @@
  *    copy (pa_block_copy) before writing, and drops one reference to the old
  *    block; the last holder writes in place.
  *  - Appends are all or nothing: on PA_ENOMEM no state changes.
+ *  - Host swap space is a second pool of num_host_blocks blocks whose free
+ *    stack starts as [H-1, ..., 1, 0] (first pop yields 0), unshuffled.
+ *    Swapping a sequence out gives each table entry, in table order, a host
+ *    block popped from that stack and reports (device block, host block);
+ *    then the device references are dropped last entry first, exactly as
+ *    freeing would (a block still shared by another sequence stays resident
+ *    and the swapped sequence keeps its own copy).  Swapping in pops device
+ *    blocks in table order, reports (host block, device block), and pushes
+ *    the host blocks back last entry first.  Both are all or nothing.
  *
  * All pointers are HOST pointers owned by the caller.  A pa_bm is not
  * thread-safe; use one per thread or lock around it.
@@ -60,7 +72,13 @@ typedef struct {
   int64_t allocated_slots;  /* used_blocks * block_size                      */
   int64_t cow_copies;       /* copy-on-write pairs emitted so far            */
   int64_t enomem_events;    /* appends refused for lack of blocks            */
+  int64_t swapped_seqs;     /* live sequences whose blocks are in host memory */
+  int64_t host_blocks;      /* size of the host swap space                   */
+  int64_t host_free_blocks;
+  int64_t swapped_out_blocks; /* blocks copied to host so far                */
+  int64_t swapped_in_blocks;  /* blocks copied back so far                   */
 } pa_bm_stats_t;
+/* live_seqs, logical_tokens and logical_blocks count resident sequences only. */
 
 /* New manager over blocks [0, num_blocks); NULL on bad sizes or host OOM. */
 pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed);
@@ -97,12 +115,48 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_to
                              int32_t n_seqs, int64_t* slots_out, int32_t* seq_out,
                              int32_t* pos_out, int32_t* cow_pairs_out, int32_t* n_cow);
 
-/* Return every block of `seq` (refcount - 1; pushed when it reaches 0). */
+/* Return every block of `seq` (refcount - 1; pushed when it reaches 0); the
+ * host blocks of a swapped-out sequence go back to the host free stack. */
 pa_status pa_bm_free_seq(pa_bm* bm, int32_t seq);
+
+/*
+ * Give the manager a host swap space of num_host_blocks blocks (block ids
+ * 0..num_host_blocks-1 of a caller-owned pinned host buffer laid out like
+ * the pools).  Allowed while no block is swapped out; replaces any previous
+ * size.  PA_EINVAL on a negative size or blocks in use.
+ */
+pa_status pa_bm_set_host_blocks(pa_bm* bm, int32_t num_host_blocks);
+
+/*
+ * Swap `seq` out: pairs_out[2 * len] receives (device block, host block) for
+ * each table entry in order (*n_pairs = len, the caller copies them with
+ * pa_block_swap(PA_SWAP_OUT) before reusing the freed device blocks); the
+ * sequence keeps its token count and becomes swapped: append, fork and
+ * export refuse it until it is swapped in.  PA_ENOMEM: fewer free host
+ * blocks than table entries; nothing changed.  PA_EINVAL: unknown, freed or
+ * already swapped sequence.
+ */
+pa_status pa_bm_swap_out(pa_bm* bm, int32_t seq, int32_t* pairs_out, int32_t* n_pairs);
+
+/*
+ * Swap `seq` back in: pairs_out[2 * len] receives (host block, device block)
+ * per table entry in order (the caller copies them with
+ * pa_block_swap(PA_SWAP_IN) before decoding it).  PA_ENOMEM: fewer free
+ * device blocks than table entries; nothing changed.  PA_EINVAL: the
+ * sequence is not swapped out.
+ */
+pa_status pa_bm_swap_in(pa_bm* bm, int32_t seq, int32_t* pairs_out, int32_t* n_pairs);
+
+/* 1 if `seq` is swapped out, 0 if resident, -1 if unknown or freed. */
+int32_t pa_bm_is_swapped(const pa_bm* bm, int32_t seq);
+
+/* Copy the host free stack, bottom first, into out[cap]; returns its length. */
+int32_t pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap);
 
 /*
  * Copy seq's table into out[cap] (as many entries as fit); *n_blocks and
  * *n_tokens receive the table length and token count (either may be NULL).
+ * For a swapped-out sequence the entries are host block ids.
  */
 pa_status pa_bm_block_table(const pa_bm* bm, int32_t seq, int32_t* out, int32_t cap,
                             int32_t* n_blocks, int32_t* n_tokens);
@@ -110,7 +164,8 @@ pa_status pa_bm_block_table(const pa_bm* bm, int32_t seq, int32_t* out, int32_t 
 /*
  * Dense export for a decode batch: row i of tables_out[n_seqs][width] gets
  * seqs[i]'s table, entries past its length set to pad_block; lens_out[i] its
- * token count.  PA_EINVAL if a table is longer than width.
+ * token count.  PA_EINVAL if a table is longer than width or a sequence is
+ * swapped out.
  */
 pa_status pa_bm_export(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
                        int32_t* tables_out, int32_t width, int32_t pad_block,

@@ -45,6 +45,9 @@ def lib():
         L.oracle_kv_write.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
         L.oracle_block_copy.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32]
         L.oracle_max_threads.argtypes = []
+        L.oracle_block_swap.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, i32,
+                                        i32]
+        L.oracle_block_swap.restype = ctypes.c_int
         L.oracle_e4m3_encode.argtypes = [vp, vp, i32]
         L.oracle_e4m3_decode.argtypes = [vp, vp, i32]
         L.oracle_e4m3_encode.restype = None
@@ -233,6 +236,31 @@ def block_copy(k_pool, v_pool, pairs):
                                  vp_.ctypes.data_as(ctypes.c_void_p), prp, pr.shape[0])
     _check(rc, "oracle_block_copy")
     return kp, vp_
+
+
+SWAP_OUT, SWAP_IN = 0, 1
+
+
+def block_swap(k_pool, v_pool, host_k, host_v, pairs, direction):
+    """Return copies (k_pool, v_pool, host_k, host_v) after moving each
+    (src, dst) block: device -> host for SWAP_OUT, host -> device for SWAP_IN.
+    Host pools have the device pools' per-block layout."""
+    nb, B, nkv, d = _geom(k_pool, v_pool)
+    kp = np.array(k_pool, copy=True, order="C")
+    vp_ = np.array(v_pool, copy=True, order="C")
+    hk = np.array(host_k, copy=True, order="C")
+    hv = np.array(host_v, copy=True, order="C")
+    if hk.shape[1:] != kp.shape[1:] or hv.shape[1:] != vp_.shape[1:] or hk.dtype != kp.dtype:
+        raise ValueError("host pools must have the device pools' block layout")
+    pr, prp = _c(np.asarray(pairs).reshape(-1, 2), np.int32)
+    rc = lib().oracle_block_swap(_dtype_code(kp), nb, B, nkv, d,
+                                 kp.ctypes.data_as(ctypes.c_void_p),
+                                 vp_.ctypes.data_as(ctypes.c_void_p),
+                                 hk.ctypes.data_as(ctypes.c_void_p),
+                                 hv.ctypes.data_as(ctypes.c_void_p), hk.shape[0], prp,
+                                 pr.shape[0], int(direction))
+    _check(rc, "oracle_block_swap")
+    return kp, vp_, hk, hv
 
 
 def e4m3_encode(x):

@@ -37,6 +37,18 @@ block manager):
   * An append is all or nothing: if the pool lacks the blocks it needs
     (new blocks plus a copy-on-write block) nothing changes and ENOMEM is
     returned.
+  * Swap to host (vLLM post, "Where it bites": a full pool preempts sequences
+    and swaps their blocks out to CPU memory; glossary entry, "Flexible
+    Management": pages can be swapped out, spilling to CPU RAM).  A host
+    pool of H blocks has the free stack [H-1, ..., 0], unshuffled.  Swapping
+    a sequence out takes one host block per table entry in table order,
+    pairing (device block, host block), then drops the sequence's device
+    references from its last entry to its first, as freeing would; a block
+    another sequence still holds stays resident, and the swapped sequence
+    keeps its own copy.  Swapping in takes one device block per entry in
+    table order, pairing (host block, device block), then returns the host
+    blocks from the last entry to the first.  A swapped sequence cannot be
+    appended to or forked until it is swapped in.  Both are all or nothing.
 """
 from dataclasses import dataclass, field
 from typing import List, Tuple
@@ -73,6 +85,7 @@ class _Seq:
     table: List[int] = field(default_factory=list)
     n_tokens: int = 0
     alive: bool = True
+    swapped: bool = False
 
 
 class BlockManagerModel:
@@ -86,6 +99,10 @@ class BlockManagerModel:
         self.seqs: List[_Seq] = []
         self.cow_copies = 0
         self.enomem_events = 0
+        self.num_host_blocks = 0
+        self.host_free: List[int] = []
+        self.swapped_out_blocks = 0
+        self.swapped_in_blocks = 0
 
     # --- operations -------------------------------------------------------
     def add_seq(self) -> int:
@@ -95,9 +112,12 @@ class BlockManagerModel:
     def _live(self, s: int) -> bool:
         return 0 <= s < len(self.seqs) and self.seqs[s].alive
 
+    def _resident(self, s: int) -> bool:
+        return self._live(s) and not self.seqs[s].swapped
+
     def fork(self, parent: int) -> Tuple[int, int]:
         """Child shares every block of the parent (refcount + 1 each)."""
-        if not self._live(parent):
+        if not self._resident(parent):
             return EINVAL, -1
         p = self.seqs[parent]
         child = _Seq(table=list(p.table), n_tokens=p.n_tokens)
@@ -108,7 +128,7 @@ class BlockManagerModel:
 
     def append(self, s: int, n: int):
         """Returns (status, slots, cow_pairs)."""
-        if not self._live(s) or n < 0:
+        if not self._resident(s) or n < 0:
             return EINVAL, [], []
         if n == 0:
             return OK, [], []
@@ -138,21 +158,68 @@ class BlockManagerModel:
         seq.n_tokens = pend
         return OK, slots, pairs
 
-    def free_seq(self, s: int) -> int:
-        if not self._live(s):
-            return EINVAL
-        seq = self.seqs[s]
-        for b in reversed(seq.table):
-            if self.refcount[b] <= 0:
-                return EINVAL
+    def _drop_device_refs(self, seq: _Seq):
         for b in reversed(seq.table):
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.free.append(b)
+
+    def free_seq(self, s: int) -> int:
+        if not self._live(s):
+            return EINVAL
+        seq = self.seqs[s]
+        if seq.swapped:
+            self.host_free.extend(reversed(seq.table))
+        else:
+            if any(self.refcount[b] <= 0 for b in seq.table):
+                return EINVAL
+            self._drop_device_refs(seq)
         seq.table = []
         seq.n_tokens = 0
         seq.alive = False
+        seq.swapped = False
         return OK
+
+    def set_host_blocks(self, n: int) -> int:
+        if n < 0 or len(self.host_free) != self.num_host_blocks:
+            return EINVAL
+        self.num_host_blocks = n
+        self.host_free = list(range(n - 1, -1, -1))
+        return OK
+
+    def swap_out(self, s: int):
+        """Returns (status, [(device block, host block), ...])."""
+        if not self._resident(s):
+            return EINVAL, []
+        seq = self.seqs[s]
+        if len(seq.table) > len(self.host_free):
+            return ENOMEM, []
+        host = [self.host_free.pop() for _ in seq.table]
+        pairs = list(zip(seq.table, host))
+        self._drop_device_refs(seq)
+        seq.table = host
+        seq.swapped = True
+        self.swapped_out_blocks += len(host)
+        return OK, pairs
+
+    def swap_in(self, s: int):
+        """Returns (status, [(host block, device block), ...])."""
+        if not self._live(s) or not self.seqs[s].swapped:
+            return EINVAL, []
+        seq = self.seqs[s]
+        if len(seq.table) > len(self.free):
+            return ENOMEM, []
+        dev = []
+        for _ in seq.table:
+            d = self.free.pop()
+            self.refcount[d] = 1
+            dev.append(d)
+        pairs = list(zip(seq.table, dev))
+        self.host_free.extend(reversed(seq.table))
+        seq.table = dev
+        seq.swapped = False
+        self.swapped_in_blocks += len(dev)
+        return OK, pairs
 
     # --- queries ----------------------------------------------------------
     def block_table(self, s: int):
@@ -165,9 +232,12 @@ class BlockManagerModel:
         used = sum(1 for r in self.refcount if r > 0)
         shared = sum(1 for r in self.refcount if r > 1)
         fill = [0] * self.num_blocks
-        live = logical_tokens = logical_blocks = 0
+        live = logical_tokens = logical_blocks = swapped = 0
         for seq in self.seqs:
             if not seq.alive:
+                continue
+            if seq.swapped:
+                swapped += 1
                 continue
             live += 1
             logical_tokens += seq.n_tokens
@@ -187,6 +257,11 @@ class BlockManagerModel:
             "allocated_slots": used * B,
             "cow_copies": self.cow_copies,
             "enomem_events": self.enomem_events,
+            "swapped_seqs": swapped,
+            "host_blocks": self.num_host_blocks,
+            "host_free_blocks": len(self.host_free),
+            "swapped_out_blocks": self.swapped_out_blocks,
+            "swapped_in_blocks": self.swapped_in_blocks,
         }
 
 

@@ -562,6 +562,42 @@ int oracle_block_copy(int dtype, int num_blocks, int block_size, int num_kv_head
   return 0;
 }
 
+/*
+ * Block swap between a device pool and a host pool (preemption by swapping:
+ * vLLM post, "Where it bites"; glossary entry, "Flexible Management").  For
+ * each (src, dst) pair, the whole block src of the source pools (the device
+ * pools for dir 0, the host pools for dir 1) is copied bit for bit to block
+ * dst of the other pools, K and V.  Returns 2 on an index out of range.
+ */
+int oracle_block_swap(int dtype, int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                      void* k_pool, void* v_pool, void* host_k, void* host_v,
+                      int num_host_blocks, const int32_t* pairs, int num_pairs, int dir) {
+  if (check_geometry(dtype, num_blocks, block_size, num_kv_heads, head_dim, num_kv_heads))
+    return 1;
+  if (dir != 0 && dir != 1) return 1;
+  const size_t plain = (size_t)num_kv_heads * block_size * head_dim * orc_elem_size(dtype);
+  const size_t k_bytes =
+      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_k_region(block_size, head_dim) : plain;
+  const size_t v_bytes =
+      dtype == ORC_FP8 ? (size_t)num_kv_heads * orc_fp8_v_region(block_size, head_dim) : plain;
+  const int n_src = dir == 0 ? num_blocks : num_host_blocks;
+  const int n_dst = dir == 0 ? num_host_blocks : num_blocks;
+  for (int p = 0; p < num_pairs; ++p)
+    if (pairs[2 * p] < 0 || pairs[2 * p] >= n_src || pairs[2 * p + 1] < 0 ||
+        pairs[2 * p + 1] >= n_dst)
+      return 2;
+  char* sk = (char*)(dir == 0 ? k_pool : host_k);
+  char* sv = (char*)(dir == 0 ? v_pool : host_v);
+  char* dk = (char*)(dir == 0 ? host_k : k_pool);
+  char* dv = (char*)(dir == 0 ? host_v : v_pool);
+  for (int p = 0; p < num_pairs; ++p) {
+    const size_t src = (size_t)pairs[2 * p], dst = (size_t)pairs[2 * p + 1];
+    memcpy(dk + dst * k_bytes, sk + src * k_bytes, k_bytes);
+    memcpy(dv + dst * v_bytes, sv + src * v_bytes, v_bytes);
+  }
+  return 0;
+}
+
 /* The E4M3 codec over arrays (for pinning it against the format). */
 void oracle_e4m3_encode(const float* x, uint8_t* codes, int n) {
   for (int i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(x[i]);

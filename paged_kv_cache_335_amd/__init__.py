@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 
 PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_EUNSUPPORTED = range(5)
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
 
 class PagedKVError(RuntimeError):
@@ -45,7 +46,8 @@ class BMStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_blocks", "block_size", "free_blocks", "used_blocks", "shared_blocks",
         "live_seqs", "logical_tokens", "logical_blocks", "stored_tokens",
-        "allocated_slots", "cow_copies", "enomem_events")]
+        "allocated_slots", "cow_copies", "enomem_events", "swapped_seqs", "host_blocks",
+        "host_free_blocks", "swapped_out_blocks", "swapped_in_blocks")]
 
 
 def _load():
@@ -65,6 +67,7 @@ def _load():
         "pa_block_copy": (i32, [P, vp, vp, vp, i32, vp]),
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
         "pa_kv_append": (i32, [P, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]),
+        "pa_block_swap": (i32, [P, vp, vp, vp, vp, i32, vp, i32, i32, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_version": (ctypes.c_char_p, []),
         "pa_bm_create": (vp, [i32, i32, ctypes.c_uint64]),
@@ -79,6 +82,11 @@ def _load():
         "pa_bm_refcount": (i32, [vp, i32]),
         "pa_bm_free_list": (i32, [vp, vp, i32]),
         "pa_bm_stats": (i32, [vp, ctypes.POINTER(BMStats)]),
+        "pa_bm_set_host_blocks": (i32, [vp, i32]),
+        "pa_bm_swap_out": (i32, [vp, i32, vp, vp]),
+        "pa_bm_swap_in": (i32, [vp, i32, vp, vp]),
+        "pa_bm_is_swapped": (i32, [vp, i32]),
+        "pa_bm_host_free_list": (i32, [vp, vp, i32]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -90,10 +98,12 @@ def _load():
 _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
-    "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_status_str", "pa_version", "pa_bm_create",
+    "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_status_str",
+    "pa_version", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch",
     "pa_bm_free_seq", "pa_bm_block_table", "pa_bm_export", "pa_bm_refcount",
-    "pa_bm_free_list", "pa_bm_stats")
+    "pa_bm_free_list", "pa_bm_stats", "pa_bm_set_host_blocks", "pa_bm_swap_out",
+    "pa_bm_swap_in", "pa_bm_is_swapped", "pa_bm_host_free_list")
 
 
 def lib():
@@ -262,6 +272,40 @@ def pa_block_copy(k_pool, v_pool, pairs, stream=None):
     st = _lib.pa_block_copy(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                             _dev(pairs, "pairs"), n, _stream(stream))
     _check(st, "pa_block_copy")
+
+
+def alloc_host_pools(num_host_blocks, k_pool, v_pool):
+    """Pinned host pools of num_host_blocks blocks with k_pool / v_pool's
+    per-block layout (swap space for pa_block_swap)."""
+    return (torch.empty((num_host_blocks,) + tuple(k_pool.shape[1:]), dtype=k_pool.dtype,
+                        pin_memory=True),
+            torch.empty((num_host_blocks,) + tuple(v_pool.shape[1:]), dtype=v_pool.dtype,
+                        pin_memory=True))
+
+
+def pa_block_swap(k_pool, v_pool, host_k, host_v, pairs, direction, stream=None):
+    """Move whole blocks between the device pools and pinned host pools:
+    PA_SWAP_OUT copies device block src to host block dst, PA_SWAP_IN host
+    block src to device block dst, for each (src, dst) row of ``pairs``."""
+    desc = pool_desc(k_pool, v_pool)
+    for t, pool, name in ((host_k, k_pool, "host_k"), (host_v, v_pool, "host_v")):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+            raise TypeError(f"{name} must be a pinned host tensor")
+        if not t.is_contiguous() or t.dtype != pool.dtype or \
+                tuple(t.shape[1:]) != tuple(pool.shape[1:]):
+            raise ValueError(f"{name} must be contiguous with the pool's block layout")
+    if host_k.shape[0] != host_v.shape[0]:
+        raise ValueError("host_k and host_v must hold the same number of blocks")
+    if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise ValueError("pairs must be int32 [P][2]")
+    n = pairs.numel() // 2
+    if n == 0:
+        return
+    st = _lib.pa_block_swap(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                            ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
+                            int(host_k.shape[0]), _dev(pairs, "pairs"), n, int(direction),
+                            _stream(stream))
+    _check(st, "pa_block_swap")
 
 
 def pa_table_update(block_tables, block_size, seq_ids, positions, slot_mapping, stream=None):

@@ -103,6 +103,36 @@ class BlockManager:
             raise PagedKVError(st, "pa_bm_export")
         return tables, lens
 
+    def set_host_blocks(self, n: int) -> int:
+        return self._lib.pa_bm_set_host_blocks(self._h, int(n))
+
+    def _swap(self, fn, seq: int):
+        nb = ctypes.c_int32(0)
+        self._lib.pa_bm_block_table(self._h, int(seq), None, 0, ctypes.byref(nb), None)
+        pairs = np.empty((max(nb.value, 1), 2), np.int32)
+        n = ctypes.c_int32(0)
+        st = fn(self._h, int(seq), _ptr(pairs), ctypes.byref(n))
+        if st != PA_OK:
+            return st, np.empty((0, 2), np.int32)
+        return st, pairs[:n.value]
+
+    def swap_out(self, seq: int):
+        """Returns (status, pairs int32 [n][2] = (device block, host block))."""
+        return self._swap(self._lib.pa_bm_swap_out, seq)
+
+    def swap_in(self, seq: int):
+        """Returns (status, pairs int32 [n][2] = (host block, device block))."""
+        return self._swap(self._lib.pa_bm_swap_in, seq)
+
+    def is_swapped(self, seq: int) -> int:
+        return int(self._lib.pa_bm_is_swapped(self._h, int(seq)))
+
+    def host_free_list(self):
+        n = self._lib.pa_bm_host_free_list(self._h, None, 0)
+        out = np.empty(max(n, 1), np.int32)
+        self._lib.pa_bm_host_free_list(self._h, _ptr(out), n)
+        return out[:n].tolist()
+
     def refcount(self, block: int) -> int:
         return int(self._lib.pa_bm_refcount(self._h, int(block)))
 

@@ -16,11 +16,12 @@
 #include "pa_bm.h"
 
 typedef struct {
-  int32_t* table;
+  int32_t* table;   /* device block ids, or host block ids while swapped */
   int32_t len;
   int32_t cap;
   int32_t n_tokens;
   int32_t alive;
+  int32_t swapped;
 } bm_seq;
 
 struct pa_bm {
@@ -37,6 +38,11 @@ struct pa_bm {
   uint32_t epoch;
   int64_t cow_copies;
   int64_t enomem_events;
+  int32_t num_host_blocks;
+  int32_t* host_free; /* capacity num_host_blocks */
+  int32_t n_host_free;
+  int64_t swapped_out_blocks;
+  int64_t swapped_in_blocks;
 };
 
 /* SplitMix64 (Steele, Lea, Flood 2014): Weyl step then a 64-bit mixer. */
@@ -82,12 +88,16 @@ void pa_bm_destroy(pa_bm* bm) {
   free(bm->free_stack);
   free(bm->refcount);
   free(bm->scratch);
+  free(bm->host_free);
   free(bm);
 }
 
 static int live(const pa_bm* bm, int32_t s) {
   return s >= 0 && s < bm->n_seqs && bm->seqs[s].alive;
 }
+
+/* A live sequence whose blocks are on the device. */
+static int resident(const pa_bm* bm, int32_t s) { return live(bm, s) && !bm->seqs[s].swapped; }
 
 static pa_status new_seq(pa_bm* bm, int32_t* id) {
   if (bm->n_seqs == INT32_MAX) return PA_ENOMEM;
@@ -127,7 +137,7 @@ pa_status pa_bm_add_seq(pa_bm* bm, int32_t* seq_id) {
 }
 
 pa_status pa_bm_fork(pa_bm* bm, int32_t parent, int32_t* child) {
-  if (!bm || !child || !live(bm, parent)) return PA_EINVAL;
+  if (!bm || !child || !resident(bm, parent)) return PA_EINVAL;
   int32_t id;
   pa_status st = new_seq(bm, &id);
   if (st != PA_OK) return st;
@@ -185,7 +195,7 @@ static void apply_append(pa_bm* bm, int32_t s, int32_t n, int cow, int64_t* slot
 
 pa_status pa_bm_append(pa_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
                        int32_t* cow_pairs_out, int32_t* n_cow) {
-  if (!bm || !live(bm, seq) || n_tokens < 0 || !n_cow) return PA_EINVAL;
+  if (!bm || !resident(bm, seq) || n_tokens < 0 || !n_cow) return PA_EINVAL;
   if (n_tokens > 0 && (!slots_out || !cow_pairs_out)) return PA_EINVAL;
   *n_cow = 0;
   if (n_tokens == 0) return PA_OK;
@@ -220,7 +230,7 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_to
   int64_t need_total = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     int32_t s = seqs[i];
-    if (!live(bm, s) || n_tokens[i] < 0 || bm->stamp[s] == bm->epoch) return PA_EINVAL;
+    if (!resident(bm, s) || n_tokens[i] < 0 || bm->stamp[s] == bm->epoch) return PA_EINVAL;
     if ((int64_t)bm->seqs[s].n_tokens + n_tokens[i] > INT32_MAX) return PA_EINVAL;
     bm->stamp[s] = bm->epoch;
     int cow;
@@ -251,20 +261,101 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_to
   return PA_OK;
 }
 
-pa_status pa_bm_free_seq(pa_bm* bm, int32_t seq) {
-  if (!bm || !live(bm, seq)) return PA_EINVAL;
-  bm_seq* q = &bm->seqs[seq];
+/* Drop seq's device references, last table entry first (freed blocks are
+ * pushed on the free stack); PA_EINVAL if a refcount is already 0. */
+static pa_status release_device_blocks(pa_bm* bm, bm_seq* q) {
   for (int32_t j = q->len - 1; j >= 0; --j)
     if (bm->refcount[q->table[j]] <= 0) return PA_EINVAL;
   for (int32_t j = q->len - 1; j >= 0; --j) {
     int32_t b = q->table[j];
     if (--bm->refcount[b] == 0) bm->free_stack[bm->n_free++] = b;
   }
+  return PA_OK;
+}
+
+pa_status pa_bm_free_seq(pa_bm* bm, int32_t seq) {
+  if (!bm || !live(bm, seq)) return PA_EINVAL;
+  bm_seq* q = &bm->seqs[seq];
+  if (q->swapped) {
+    for (int32_t j = q->len - 1; j >= 0; --j) bm->host_free[bm->n_host_free++] = q->table[j];
+  } else {
+    pa_status st = release_device_blocks(bm, q);
+    if (st != PA_OK) return st;
+  }
   free(q->table);
   q->table = NULL;
   q->len = q->cap = q->n_tokens = 0;
   q->alive = 0;
+  q->swapped = 0;
   return PA_OK;
+}
+
+pa_status pa_bm_set_host_blocks(pa_bm* bm, int32_t num_host_blocks) {
+  if (!bm || num_host_blocks < 0) return PA_EINVAL;
+  if (bm->n_host_free != bm->num_host_blocks) return PA_EINVAL; /* blocks in use */
+  int32_t* hf = NULL;
+  if (num_host_blocks > 0) {
+    hf = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_host_blocks);
+    if (!hf) return PA_ENOMEM;
+    for (int32_t i = 0; i < num_host_blocks; ++i) hf[i] = num_host_blocks - 1 - i;
+  }
+  free(bm->host_free);
+  bm->host_free = hf;
+  bm->num_host_blocks = num_host_blocks;
+  bm->n_host_free = num_host_blocks;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_out(pa_bm* bm, int32_t seq, int32_t* pairs_out, int32_t* n_pairs) {
+  if (!bm || !n_pairs || !resident(bm, seq)) return PA_EINVAL;
+  bm_seq* q = &bm->seqs[seq];
+  if (q->len > 0 && !pairs_out) return PA_EINVAL;
+  if (q->len > bm->n_host_free) return PA_ENOMEM;
+  for (int32_t j = 0; j < q->len; ++j)
+    if (bm->refcount[q->table[j]] <= 0) return PA_EINVAL;
+  int32_t* host = bm->scratch; /* len <= num_blocks */
+  for (int32_t j = 0; j < q->len; ++j) {
+    host[j] = bm->host_free[--bm->n_host_free];
+    pairs_out[2 * j] = q->table[j];
+    pairs_out[2 * j + 1] = host[j];
+  }
+  release_device_blocks(bm, q); /* refcounts checked above */
+  for (int32_t j = 0; j < q->len; ++j) q->table[j] = host[j];
+  q->swapped = 1;
+  bm->swapped_out_blocks += q->len;
+  *n_pairs = q->len;
+  return PA_OK;
+}
+
+pa_status pa_bm_swap_in(pa_bm* bm, int32_t seq, int32_t* pairs_out, int32_t* n_pairs) {
+  if (!bm || !n_pairs || !live(bm, seq) || !bm->seqs[seq].swapped) return PA_EINVAL;
+  bm_seq* q = &bm->seqs[seq];
+  if (q->len > 0 && !pairs_out) return PA_EINVAL;
+  if (q->len > bm->n_free) return PA_ENOMEM;
+  for (int32_t j = 0; j < q->len; ++j) {
+    int32_t d = bm->free_stack[--bm->n_free];
+    bm->refcount[d] = 1;
+    pairs_out[2 * j] = q->table[j];
+    pairs_out[2 * j + 1] = d;
+  }
+  for (int32_t j = q->len - 1; j >= 0; --j) bm->host_free[bm->n_host_free++] = q->table[j];
+  for (int32_t j = 0; j < q->len; ++j) q->table[j] = pairs_out[2 * j + 1];
+  q->swapped = 0;
+  bm->swapped_in_blocks += q->len;
+  *n_pairs = q->len;
+  return PA_OK;
+}
+
+int32_t pa_bm_is_swapped(const pa_bm* bm, int32_t seq) {
+  if (!bm || !live(bm, seq)) return -1;
+  return bm->seqs[seq].swapped ? 1 : 0;
+}
+
+int32_t pa_bm_host_free_list(const pa_bm* bm, int32_t* out, int32_t cap) {
+  if (!bm) return -1;
+  int32_t n = bm->n_host_free < cap ? bm->n_host_free : cap;
+  if (n > 0 && out) memcpy(out, bm->host_free, sizeof(int32_t) * (size_t)n);
+  return bm->n_host_free;
 }
 
 pa_status pa_bm_block_table(const pa_bm* bm, int32_t seq, int32_t* out, int32_t cap,
@@ -285,7 +376,7 @@ pa_status pa_bm_export(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
   if (n_seqs == 0) return PA_OK;
   if (!seqs || !tables_out || !lens_out) return PA_EINVAL;
   for (int32_t i = 0; i < n_seqs; ++i)
-    if (!live(bm, seqs[i]) || bm->seqs[seqs[i]].len > width) return PA_EINVAL;
+    if (!resident(bm, seqs[i]) || bm->seqs[seqs[i]].len > width) return PA_EINVAL;
   for (int32_t i = 0; i < n_seqs; ++i) {
     const bm_seq* q = &bm->seqs[seqs[i]];
     int32_t* row = tables_out + (size_t)i * width;
@@ -324,6 +415,10 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   for (int32_t s = 0; s < bm->n_seqs; ++s) {
     const bm_seq* q = &bm->seqs[s];
     if (!q->alive) continue;
+    if (q->swapped) {
+      out->swapped_seqs += 1;
+      continue;
+    }
     out->live_seqs += 1;
     out->logical_tokens += q->n_tokens;
     out->logical_blocks += q->len;
@@ -337,5 +432,9 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   out->allocated_slots = out->used_blocks * B;
   out->cow_copies = bm->cow_copies;
   out->enomem_events = bm->enomem_events;
+  out->host_blocks = bm->num_host_blocks;
+  out->host_free_blocks = bm->n_host_free;
+  out->swapped_out_blocks = bm->swapped_out_blocks;
+  out->swapped_in_blocks = bm->swapped_in_blocks;
   return PA_OK;
 }

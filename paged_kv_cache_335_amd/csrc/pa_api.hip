@@ -255,6 +255,43 @@ pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool, const i
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
+pa_status pa_block_swap(const pa_pool* pool, void* k_pool, void* v_pool, void* host_k,
+                        void* host_v, int32_t num_host_blocks, const int32_t* pairs,
+                        int32_t num_pairs, pa_swap_dir dir, void* stream) {
+  if (!pool_ok(pool) || num_pairs < 0 || num_host_blocks < 0) return PA_EINVAL;
+  if (dir != PA_SWAP_OUT && dir != PA_SWAP_IN) return PA_EINVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !host_k || !host_v || !pairs || num_host_blocks == 0)
+    return PA_EINVAL;
+  // the kernel reaches host memory through its device mapping; memory that is
+  // not pinned host memory has none, and is refused before any launch
+  void* dk = nullptr;
+  void* dv = nullptr;
+  if (hipHostGetDevicePointer(&dk, host_k, 0) != hipSuccess || !dk ||
+      hipHostGetDevicePointer(&dv, host_v, 0) != hipSuccess || !dv) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return PA_EINVAL;
+  }
+  hipStream_t st = as_stream(stream);
+  const int32_t n_src = dir == PA_SWAP_OUT ? pool->num_blocks : num_host_blocks;
+  const int32_t n_dst = dir == PA_SWAP_OUT ? num_host_blocks : pool->num_blocks;
+  if (debug_checks()) {
+    std::vector<int32_t> pr;
+    if (!fetch(pr, pairs, (size_t)num_pairs * 2, st)) return PA_EHIP;
+    std::vector<uint8_t> seen((size_t)n_dst, 0);
+    for (int32_t p = 0; p < num_pairs; ++p) {
+      const int32_t s = pr[2 * p], d = pr[2 * p + 1];
+      if (s < 0 || s >= n_src || d < 0 || d >= n_dst || seen[(size_t)d]) return PA_EINVAL;
+      seen[(size_t)d] = 1;
+    }
+  }
+  const size_t kb = block_bytes(pool, false), vb = block_bytes(pool, true);
+  hipError_t e = dir == PA_SWAP_OUT
+                     ? pakv::launch_block_move(k_pool, v_pool, dk, dv, pairs, num_pairs, kb, vb, st)
+                     : pakv::launch_block_move(dk, dv, k_pool, v_pool, pairs, num_pairs, kb, vb, st);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
 pa_status pa_table_update(int32_t* block_tables, int32_t max_blocks_per_seq,
                           int32_t block_size, const int32_t* seq_ids, const int32_t* positions,
                           const int64_t* slot_mapping, int32_t T, void* stream) {

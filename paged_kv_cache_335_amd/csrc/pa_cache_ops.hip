@@ -17,6 +17,8 @@
 //    codes with one scale, scale = bf16(max |x| / 448), code = x / scale
 //    rounded to nearest even.  Not bitwise: the one kernel here with
 //    arithmetic.
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace pakv {
@@ -183,6 +185,38 @@ __global__ __launch_bounds__(kThreads) void block_copy_bytes_kernel(
   for (size_t c = threadIdx.x; c < block_bytes; c += kThreads) st_pool(pool + dst + c, pool[src + c]);
 }
 
+// Block move between different buffers (device pool <-> host-mapped pool):
+// grid (num_pairs, 2, chunks); y = 0 moves K, y = 1 V; z splits a block into
+// chunks so that enough 16-byte requests are in flight over the host link.
+__global__ __launch_bounds__(kThreads) void block_move16_kernel(
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const int32_t* __restrict__ pairs,
+    size_t k_bytes, size_t v_bytes) {
+  const int p = blockIdx.x;
+  const bool is_v = blockIdx.y == 1;
+  const size_t bytes = is_v ? v_bytes : k_bytes;
+  const uint8_t* src = (is_v ? src_v : src_k) + (size_t)pairs[2 * p] * bytes;
+  uint8_t* dst = (is_v ? dst_v : dst_k) + (size_t)pairs[2 * p + 1] * bytes;
+  const size_t n16 = bytes / 16;
+  for (size_t c = (size_t)blockIdx.z * kThreads + threadIdx.x; c < n16;
+       c += (size_t)gridDim.z * kThreads)
+    st_pool(reinterpret_cast<u32x4*>(dst + c * 16), *reinterpret_cast<const u32x4*>(src + c * 16));
+}
+
+__global__ __launch_bounds__(kThreads) void block_move_bytes_kernel(
+    const uint8_t* __restrict__ src_k, const uint8_t* __restrict__ src_v,
+    uint8_t* __restrict__ dst_k, uint8_t* __restrict__ dst_v, const int32_t* __restrict__ pairs,
+    size_t k_bytes, size_t v_bytes) {
+  const int p = blockIdx.x;
+  const bool is_v = blockIdx.y == 1;
+  const size_t bytes = is_v ? v_bytes : k_bytes;
+  const uint8_t* src = (is_v ? src_v : src_k) + (size_t)pairs[2 * p] * bytes;
+  uint8_t* dst = (is_v ? dst_v : dst_k) + (size_t)pairs[2 * p + 1] * bytes;
+  for (size_t c = (size_t)blockIdx.z * kThreads + threadIdx.x; c < bytes;
+       c += (size_t)gridDim.z * kThreads)
+    st_pool(dst + c, src[c]);
+}
+
 __global__ __launch_bounds__(kThreads) void table_update_kernel(
     int32_t* __restrict__ tables, int32_t max_blocks, int32_t block_size,
     const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
@@ -232,6 +266,25 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
     block_copy16_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, k_bytes, v_bytes);
   else
     block_copy_bytes_kernel<<<grid, kThreads, 0, st>>>(kp, vp, pairs, k_bytes, v_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_move(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int32_t* pairs, int32_t num_pairs, size_t k_bytes,
+                             size_t v_bytes, hipStream_t st) {
+  if (num_pairs <= 0) return hipSuccess;
+  // chunks of 4 KiB per workgroup pass, at most 8 workgroups per block
+  const size_t big = k_bytes > v_bytes ? k_bytes : v_bytes;
+  const unsigned chunks = (unsigned)std::min<size_t>(8, (big + 4095) / 4096);
+  const dim3 grid(num_pairs, 2, chunks);
+  auto sk = static_cast<const uint8_t*>(src_k);
+  auto sv = static_cast<const uint8_t*>(src_v);
+  auto dk = static_cast<uint8_t*>(dst_k);
+  auto dv = static_cast<uint8_t*>(dst_v);
+  if (k_bytes % 16 == 0 && v_bytes % 16 == 0)
+    block_move16_kernel<<<grid, kThreads, 0, st>>>(sk, sv, dk, dv, pairs, k_bytes, v_bytes);
+  else
+    block_move_bytes_kernel<<<grid, kThreads, 0, st>>>(sk, sv, dk, dv, pairs, k_bytes, v_bytes);
   return hipGetLastError();
 }
 

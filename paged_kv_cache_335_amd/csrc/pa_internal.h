@@ -76,6 +76,12 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
                              int32_t num_pairs, size_t k_block_bytes, size_t v_block_bytes,
                              hipStream_t stream);
 
+// Copy whole blocks between two pool pairs (device and host-mapped):
+// dst_*[pairs[i][1]] <- src_*[pairs[i][0]].
+hipError_t launch_block_move(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                             const int32_t* pairs, int32_t num_pairs, size_t k_block_bytes,
+                             size_t v_block_bytes, hipStream_t stream);
+
 hipError_t launch_table_update(int32_t* block_tables, int32_t max_blocks,
                                int32_t block_size, const int32_t* seq_ids,
                                const int32_t* positions, const int64_t* slots, int32_t T,

@@ -13,14 +13,20 @@ A decode step for a batch of live sequences:
   4. pa_kv_append: device table rows follow the growth and the new tokens'
      K/V go into their slots, in one launch;
   5. pa_decode: attention over the grown contexts.
+
+Preemption by swapping: swap_out(seq) moves a sequence's blocks to a pinned
+host pool and frees them on the device; swap_in(seq) brings them back into
+new device blocks and rewrites the sequence's table row.  While any
+sequence is swapped out, decode takes the list of resident sequences.
 """
 import ctypes
 
 import numpy as np
 import torch
 
-from . import (PA_OK, PagedKVError, alloc_pools, pa_block_copy, pa_decode,
-               pa_decode_partition_tokens, pa_decode_workspace_bytes, pa_kv_append)
+from . import (PA_OK, PA_SWAP_IN, PA_SWAP_OUT, PagedKVError, alloc_host_pools, alloc_pools,
+               pa_block_copy, pa_block_swap, pa_decode, pa_decode_partition_tokens,
+               pa_decode_workspace_bytes, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -94,7 +100,8 @@ class DeviceEvent:
 
 class PagedKVCache:
     def __init__(self, num_blocks, num_kv_heads, head_dim, max_seqs, table_width,
-                 block_size=16, dtype=torch.bfloat16, shuffle_seed=0, device="cuda"):
+                 block_size=16, dtype=torch.bfloat16, shuffle_seed=0, device="cuda",
+                 host_blocks=0):
         self.B = block_size
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -110,7 +117,14 @@ class PagedKVCache:
         # device lengths of the latest step (a view into its staging buffer)
         self.lens = torch.zeros(max_seqs, dtype=torch.int32, device=self.device)
         self.host_lens = np.zeros(max_seqs, dtype=np.int32)
+        self.host_k = self.host_v = None
+        if host_blocks:
+            self.host_k, self.host_v = alloc_host_pools(host_blocks, self.k_pool, self.v_pool)
+            st = self.bm.set_host_blocks(host_blocks)
+            if st != PA_OK:
+                raise PagedKVError(st, "pa_bm_set_host_blocks")
         self.rows = {}          # sequence id -> row of the device table
+        self.swapped = set()    # sequences whose blocks are in the host pool
         self._ring = None
         self._ring_events = [None] * (_RING // _GROUP)
         self._ring_pos = 0
@@ -200,6 +214,36 @@ class PagedKVCache:
                          d_pos, stream=stream)
         return len(pairs)
 
+    # --- preemption by swapping ------------------------------------------------
+    def _swap(self, seq, out, stream):
+        st, pairs = (self.bm.swap_out if out else self.bm.swap_in)(seq)
+        if st != PA_OK:
+            raise PagedKVError(st, "pa_bm_swap_out" if out else "pa_bm_swap_in")
+        stream = stream or torch.cuda.current_stream(self.device)
+        if len(pairs):
+            d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device)
+            with torch.cuda.stream(stream):
+                pa_block_swap(self.k_pool, self.v_pool, self.host_k, self.host_v, d_pairs,
+                              PA_SWAP_OUT if out else PA_SWAP_IN, stream=stream)
+        return pairs
+
+    def swap_out(self, seq, stream=None):
+        """Copy seq's blocks to the host pool and free them on the device.
+        Returns the (device block, host block) pairs."""
+        pairs = self._swap(seq, True, stream)
+        self.swapped.add(seq)
+        return pairs
+
+    def swap_in(self, seq, stream=None):
+        """Bring seq's blocks back into new device blocks and rewrite its
+        table row.  Returns the (host block, device block) pairs."""
+        pairs = self._swap(seq, False, stream)
+        self.swapped.discard(seq)
+        st, table, n = self.bm.block_table(seq)
+        row = self.rows[seq]
+        self.tables[row, :len(table)].copy_(torch.tensor(table, dtype=torch.int32))
+        return pairs
+
     # --- decode -------------------------------------------------------------
     def workspace(self, num_q_heads, partition_tokens=0):
         S = len(self.rows)
@@ -213,9 +257,23 @@ class PagedKVCache:
         return pa_decode_partition_tokens(self.k_pool, self.v_pool, len(self.rows), num_q_heads,
                                           self.width, partition_tokens)
 
+    def decode_seqs(self, q, seqs, out=None, scale=None, partition_tokens=0, stream=None):
+        """Attention of q [len(seqs)][Hq][d] over the contexts of the given
+        resident sequences (tables exported by the block manager and copied
+        to the device for this call)."""
+        tables, lens = self.bm.export(np.asarray(seqs, np.int32), self.width, pad_block=0)
+        d_tables = torch.from_numpy(tables).to(self.device)
+        d_lens = torch.from_numpy(lens).to(self.device)
+        scale = self.head_dim ** -0.5 if scale is None else scale
+        return pa_decode(q, self.k_pool, self.v_pool, d_tables, d_lens, scale, out=out,
+                         partition_tokens=partition_tokens, stream=stream)
+
     def decode(self, q, out=None, scale=None, partition_tokens=0, stream=None):
         """Attention of q [S][Hq][d] (rows in table order) over every live
-        sequence's context."""
+        sequence's context (none may be swapped out: use decode_seqs)."""
+        if self.swapped:
+            raise ValueError("sequences are swapped out; decode the resident ones with "
+                             "decode_seqs")
         S = len(self.rows)
         scale = self.head_dim ** -0.5 if scale is None else scale
         ws = self.workspace(q.shape[1], partition_tokens)

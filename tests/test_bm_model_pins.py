@@ -232,3 +232,49 @@ def test_free_stack_is_a_permutation_and_seed_zero_pops_in_order():
     assert m.block_table(s)[1] == [0, 1, 2]
     b = initial_free_stack(1000, 42)
     assert sorted(b) == list(range(1000)) and b != list(range(999, -1, -1))
+
+
+def test_swap_rules_by_hand():
+    """Swap to a host pool, worked out from the stated rules: pool of 6
+    unshuffled blocks (pops 0, 1, 2, ...), 4 host blocks (pops 0, 1, ...),
+    block size 4."""
+    m = BlockManagerModel(6, 4, 0)
+    assert m.set_host_blocks(4) == OK
+    a = m.add_seq()
+    assert m.append(a, 10)[0] == OK              # blocks 0, 1, 2
+    st, b = m.fork(a)                            # shares all three
+    assert st == OK
+    st, pairs = m.swap_out(a)
+    assert st == OK and pairs == [(0, 0), (1, 1), (2, 2)]
+    assert m.refcount[:3] == [1, 1, 1]           # b still holds them: none freed
+    assert m.free == [5, 4, 3] and m.host_free == [3]
+    assert m.append(a, 1)[0] == EINVAL           # swapped: no appends, no forks
+    assert m.fork(a)[0] == EINVAL
+    assert m.swap_out(b) == (ENOMEM, [])         # 3 entries, 1 free host block
+    assert m.free_seq(b) == OK                   # pushes 2, 1, 0
+    assert m.free == [5, 4, 3, 2, 1, 0]
+    st, pairs = m.swap_in(a)                     # pops 0, 1, 2 again
+    assert st == OK and pairs == [(0, 0), (1, 1), (2, 2)]
+    assert m.host_free == [3, 2, 1, 0] and m.seqs[a].table == [0, 1, 2]
+    assert m.swap_in(a) == (EINVAL, [])
+    s = m.stats()
+    assert (s["swapped_out_blocks"], s["swapped_in_blocks"], s["swapped_seqs"]) == (3, 3, 0)
+    # a swapped sequence that is freed returns its host blocks
+    assert m.swap_out(a)[0] == OK and m.host_free == [3]
+    assert m.free_seq(a) == OK and m.host_free == [3, 2, 1, 0]
+    assert m.free == [5, 4, 3, 2, 1, 0]
+    assert m.set_host_blocks(2) == OK and m.host_free == [1, 0]
+
+
+def test_swap_out_then_in_restores_the_tokens_table_shape():
+    """After swapping out and back in, a sequence has the same number of
+    blocks and tokens, and appends continue from where it stopped."""
+    m = BlockManagerModel(50, 16, 7)
+    m.set_host_blocks(20)
+    s = m.add_seq()
+    m.append(s, 37)
+    before = (len(m.seqs[s].table), m.seqs[s].n_tokens)
+    assert m.swap_out(s)[0] == OK and m.swap_in(s)[0] == OK
+    assert (len(m.seqs[s].table), m.seqs[s].n_tokens) == before
+    st, slots, pairs = m.append(s, 1)
+    assert st == OK and slots == [m.seqs[s].table[2] * 16 + 5] and pairs == []

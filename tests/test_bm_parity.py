@@ -13,14 +13,17 @@ from workloads import CONFIGS, draw_lengths
 
 def assert_same_state(c: BlockManager, m: BlockManagerModel):
     assert c.free_list() == m.free
+    assert c.host_free_list() == m.host_free
     assert c.refcounts() == m.refcount
     assert c.stats() == m.stats()
     for s, seq in enumerate(m.seqs):
         if seq.alive:
             st, table, n = c.block_table(s)
             assert st == PA_OK and table == seq.table and n == seq.n_tokens
+            assert c.is_swapped(s) == int(seq.swapped)
         else:
             assert c.block_table(s)[0] == PA_EINVAL
+            assert c.is_swapped(s) == -1
 
 
 @pytest.mark.parametrize("seed", [0, 1, 0xDEADBEEF, 2**64 - 1])
@@ -152,3 +155,60 @@ def test_export_matches_tables():
     for i, s in enumerate(seqs):
         t = c.block_table(s)[1]
         assert tables[i, :len(t)].tolist() == t and (tables[i, len(t):] == 99).all()
+
+
+def test_random_streams_with_swaps_match():
+    """Appends, forks, frees and swaps to and from a host pool, in random
+    order: pairs, tables, both free lists, refcounts and statistics agree."""
+    rnd = random.Random(11)
+    for trial in range(4):
+        nb, B, H = rnd.choice([(64, 4, 40), (300, 16, 120), (17, 8, 9)])
+        seed = rnd.randrange(2**64)
+        c, m = BlockManager(nb, B, seed), BlockManagerModel(nb, B, seed)
+        assert c.set_host_blocks(H) == m.set_host_blocks(H) == OK
+        resident, swapped = [], []
+        for step in range(1500):
+            op = rnd.random()
+            if op < 0.1 or not (resident or swapped):
+                a, b = c.add_seq(), m.add_seq()
+                assert a == b
+                resident.append(a)
+            elif op < 0.2 and resident:
+                p = rnd.choice(resident)
+                (s1, k1), (s2, k2) = c.fork(p), m.fork(p)
+                assert s1 == s2 and (s1 != OK or k1 == k2)
+                if s1 == OK:
+                    resident.append(k1)
+            elif op < 0.28:
+                pool = resident + swapped
+                s = rnd.choice(pool)
+                assert c.free_seq(s) == m.free_seq(s) == OK
+                (resident if s in resident else swapped).remove(s)
+            elif op < 0.4 and resident:
+                s = rnd.choice(resident)
+                (st, pairs), (st2, pairs2) = c.swap_out(s), m.swap_out(s)
+                assert st == st2
+                assert [tuple(x) for x in pairs.tolist()] == pairs2
+                if st == PA_OK:
+                    resident.remove(s)
+                    swapped.append(s)
+            elif op < 0.52 and swapped:
+                s = rnd.choice(swapped)
+                (st, pairs), (st2, pairs2) = c.swap_in(s), m.swap_in(s)
+                assert st == st2
+                assert [tuple(x) for x in pairs.tolist()] == pairs2
+                if st == PA_OK:
+                    swapped.remove(s)
+                    resident.append(s)
+            elif swapped and op < 0.56:
+                s = rnd.choice(swapped)   # a swapped sequence refuses appends and forks
+                assert c.append(s, 1)[0] == m.append(s, 1)[0] == PA_EINVAL
+                assert c.fork(s)[0] == m.fork(s)[0] == PA_EINVAL
+            elif resident:
+                s = rnd.choice(resident)
+                n = rnd.randint(0, 2 * B + 3)
+                assert c.append(s, n) == m.append(s, n)
+            if step % 50 == 0:
+                assert_same_state(c, m)
+        assert_same_state(c, m)
+        assert c.stats()["swapped_out_blocks"] > 0 and c.stats()["swapped_in_blocks"] > 0

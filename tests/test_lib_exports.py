@@ -190,3 +190,25 @@ def test_fp8_host_checks_in_the_c_abi():
     assert L.pa_kv_write(ctypes.byref(bad_type), dummy, dummy, dummy, dummy, dummy, 4,
                          null) == pk.PA_EINVAL
     assert L.pa_block_copy(ctypes.byref(d8), null, null, null, 0, null) == pk.PA_OK
+
+
+def test_block_swap_host_checks():
+    """pa_block_swap refuses non-pinned or mis-shaped host pools in the
+    binding, and bad scalars in the C ABI, before any device call."""
+    import paged_kv_cache_335_amd as pk
+    k = torch.zeros(4, 1, 16, 64, dtype=torch.bfloat16)
+    v = torch.zeros(4, 1, 64, 16, dtype=torch.bfloat16)
+    host = torch.zeros(2, 1, 16, 64, dtype=torch.bfloat16)      # not pinned
+    with pytest.raises(TypeError):
+        pk.pa_block_swap(k, v, host, host, torch.zeros(1, 2, dtype=torch.int32),
+                         pk.PA_SWAP_OUT)
+    L = pk.lib()
+    d = pk.PoolDesc(4, 16, 1, 64, pk.PA_BF16)
+    dummy = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(0)
+    assert L.pa_block_swap(ctypes.byref(d), dummy, dummy, dummy, dummy, 2, dummy, 1, 7,
+                           null) == pk.PA_EINVAL                 # bad direction
+    assert L.pa_block_swap(ctypes.byref(d), dummy, dummy, dummy, dummy, 2, dummy, -1, 0,
+                           null) == pk.PA_EINVAL
+    assert L.pa_block_swap(ctypes.byref(d), null, null, null, null, 0, null, 0, 0,
+                           null) == pk.PA_OK                     # nothing to move

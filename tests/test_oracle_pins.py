@@ -337,3 +337,37 @@ def test_block_copy_gives_sharers_identical_prefix():
             assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     for blk in (1, 2, 3, 4):
         assert np.array_equal(k2[blk], k[blk]) and np.array_equal(v2[blk], v[blk])
+
+
+# --- block swap to host -------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_swap_round_trip_equals_a_block_copy(dtype):
+    """Swapping blocks out to host slots and back in to other device blocks
+    moves exactly what a device-to-device copy of the same blocks would; no
+    other byte of either pool changes."""
+    rng = np.random.default_rng(60)
+    nb, nkv, B, d, H = 12, 2, 4, 8, 5
+    k, v = _pools(nb, nkv, B, d, rng, dtype)
+    hk, hv = _pools(H, nkv, B, d, rng, dtype)
+    out_pairs = np.array([[3, 0], [7, 4], [2, 1]], np.int32)
+    k1, v1, hk1, hv1 = oracle.block_swap(k, v, hk, hv, out_pairs, oracle.SWAP_OUT)
+    assert np.array_equal(k1, k) and np.array_equal(v1, v)      # the source is untouched
+    for src, dst in out_pairs:
+        assert np.array_equal(hk1[dst], k[src]) and np.array_equal(hv1[dst], v[src])
+    untouched = [h for h in range(H) if h not in out_pairs[:, 1]]
+    assert np.array_equal(hk1[untouched], hk[untouched])
+    in_pairs = np.array([[0, 9], [4, 10], [1, 11]], np.int32)
+    k2, v2, hk2, hv2 = oracle.block_swap(k1, v1, hk1, hv1, in_pairs, oracle.SWAP_IN)
+    kc, vc = oracle.block_copy(k, v, np.array([[3, 9], [7, 10], [2, 11]], np.int32))
+    assert np.array_equal(k2, kc) and np.array_equal(v2, vc)
+    assert np.array_equal(hk2, hk1) and np.array_equal(hv2, hv1)
+
+
+def test_block_swap_rejects_out_of_range_pairs():
+    rng = np.random.default_rng(61)
+    k, v = _pools(4, 1, 4, 8, rng)
+    hk, hv = _pools(2, 1, 4, 8, rng)
+    with pytest.raises(oracle.OracleError):
+        oracle.block_swap(k, v, hk, hv, np.array([[0, 2]], np.int32), oracle.SWAP_OUT)
+    with pytest.raises(oracle.OracleError):
+        oracle.block_swap(k, v, hk, hv, np.array([[2, 0]], np.int32), oracle.SWAP_IN)
