@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="cfg3", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0: library)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="tokens per block (the table/tail-waste trade-off)")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache storage: bf16, or 8-bit E4M3 codes + per-token scales")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -106,6 +108,8 @@ def main():
     from workloads import CONFIGS, draw_lengths
 
     cfg = CONFIGS[args.config]
+    if args.block_size != cfg.block_size:
+        cfg = cfg.scaled(block_size=args.block_size)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(dev)

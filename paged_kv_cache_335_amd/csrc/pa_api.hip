@@ -185,8 +185,8 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
     return PA_EINVAL;
   const int group = num_q_heads / pool->num_kv_heads;
-  if (pool->block_size != pakv::kBlock) return PA_EUNSUPPORTED;
-  if (pakv::decode_path(pool->dtype, pool->head_dim, group) == pakv::DecodePath::kUnsupported)
+  if (pakv::decode_path(pool->dtype, pool->head_dim, group, pool->block_size) ==
+      pakv::DecodePath::kUnsupported)
     return PA_EUNSUPPORTED;
   if (!workspace || workspace_bytes < ws) return PA_EINVAL;
   hipStream_t hs = as_stream(stream);
@@ -225,7 +225,7 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
   a.min_seg_blocks = P / pool->block_size;
   a.max_slots = slots;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, hs);
+  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, pool->block_size, hs);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 

@@ -80,6 +80,11 @@ __device__ __forceinline__ V ldg_stream(gptr p) {
 #endif
 }
 
+// A generic pointer known to point into global memory, as a global pointer.
+__device__ __forceinline__ gptr to_global(const uint8_t* p) {
+  return reinterpret_cast<gptr>(reinterpret_cast<uint64_t>(p));
+}
+
 // A global pointer that is the same in every lane, moved to SGPRs so that
 // loads can take the scalar-base + 32-bit-vector-offset form.
 __device__ __forceinline__ gptr uniform_ptr(const uint8_t* p) {
@@ -188,7 +193,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
 }
 static_assert(kWaves >= 1 && kWaves <= 8, "the plan scan keeps one sum per wave, 8 at most");
 
-// Collective over the workgroup (256 threads); ends with a barrier.
+// Collective over the workgroup; ends with a barrier.  B = tokens per block.
+template <int B>
 __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
   const int S = a.num_seqs;
   int* pre = lds;            // S + 1
@@ -199,18 +205,18 @@ __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
   const int s0 = min(S, t * C), s1 = min(S, s0 + C);
   // lengths outside [0, table capacity] violate the contract; clamping them
   // keeps every LDS and table index in range whatever the device data says
-  const int cap = a.max_blocks * kBlock;
+  const int cap = a.max_blocks * B;
   int nb = 0;
   for (int s = s0; s < s1; ++s) {
     const int L = min(max(a.context_lens[s], 0), cap);
     lens[s] = L;
-    nb += (L + kBlock - 1) / kBlock;
+    nb += (L + B - 1) / B;
   }
   int T;
   int run = block_excl_scan(nb, wsum, &T);
   for (int s = s0; s < s1; ++s) {
     pre[s] = run;
-    run += (lens[s] + kBlock - 1) / kBlock;
+    run += (lens[s] + B - 1) / B;
   }
   if (t == 0) pre[S] = T;
   __syncthreads();
@@ -237,7 +243,7 @@ __device__ void write_seg_counts(const DecodeArgs& a, const Plan& pl) {
 }
 
 // Walk this workgroup's range for kv head g, calling f(unit) per piece.
-template <typename F>
+template <int B, typename F>
 __device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, int r, int g, F&& f) {
   int b0 = r * pl.q;
   const int b1 = min(pl.T, b0 + pl.q);
@@ -258,8 +264,8 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, 
     u.s = s;
     u.g = g;
     u.L = pl.lens[s];
-    u.t0 = (b0 - sb) * kBlock;
-    u.t1 = min(u.L, (e - sb) * kBlock);
+    u.t0 = (b0 - sb) * B;
+    u.t1 = min(u.L, (e - sb) * B);
     u.part = r - sb / pl.q;
     u.nparts = (se - 1) / pl.q - sb / pl.q + 1;
     f(u);
@@ -355,17 +361,35 @@ __device__ __forceinline__ void finish_mfma_unit(const DecodeArgs& a, int G, con
   }
 }
 
+// The MFMA tiles cover 16 tokens.  A unit walks its tokens [t0, t1) in
+// 16-token tiles: with 16-token blocks a tile is a block; with B = 32 it is
+// one half of a block; with B = 8 it is two consecutive blocks of the unit
+// (the second one clamped to the first past the unit's last block, and
+// masked).  Table entries arrive 64 per lane load ("chunks" of 64 blocks).
+template <int B>
+struct TileGeom {
+  static_assert(B == 8 || B == 16 || B == 32, "block sizes 8, 16 and 32");
+  static constexpr int kSub = B >= 16 ? B / 16 : 1;  // tiles per block
+  static constexpr int kPer = B >= 16 ? 1 : 16 / B;  // blocks per tile
+  // tiles of the chunk of blocks [c0, c0 + cnt) of a unit starting at t0
+  __device__ static int tiles(const Unit& u, int c0, int cnt) {
+    const int lo = u.t0 + c0 * B;
+    const int hi = min(u.t1, u.t0 + (c0 + cnt) * B);
+    return (hi - lo + 15) >> 4;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA kernel: bf16 pools, 1..16 query heads per kv head.
 // ---------------------------------------------------------------------------
-template <int D, int NBUF>
+template <int D, int B, int NBUF>
 __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
-  constexpr int B = kBlock;
-  constexpr int KJ = D / 32;  // q.K MFMAs per block (32 dims each)
-  constexpr int NT = D / 16;  // P.V MFMAs per block (16 output dims each)
+  using TG = TileGeom<B>;
+  constexpr int KJ = D / 32;  // q.K MFMAs per tile (32 dims each)
+  constexpr int NT = D / 16;  // P.V MFMAs per tile (16 output dims each)
   constexpr uint32_t ROW = D * 2;  // bytes per K row
 
-  const int s = u.s, g = u.g, L = u.L;
+  const int s = u.s, g = u.g;
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
   const int col = lane & 15, grp = lane >> 4;
 
@@ -390,8 +414,10 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
   const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
-  const uint32_t koff = col * ROW + grp * 16;
-  const uint32_t voff = col * (B * 2) + grp * 8;
+  // lane offsets inside a tile's block: K row (token) col, V dim col, tokens
+  // 4*grp..+4 (with B = 8, rows and tokens are taken modulo the block)
+  const uint32_t koff = (B >= 16 ? col : col % 8) * ROW + grp * 16;
+  const uint32_t voff = col * (B * 2) + (B >= 16 ? grp : grp % 2) * 8;
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
 
   float m_ref = kNegInf, l_run = 0.f;
@@ -408,18 +434,36 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
     // physical block ids of up to 64 blocks, one per lane (every lane loads a
     // valid entry)
     const int tab = trow[jb + c0 + min(lane, cnt - 1)];
+    const int ntile = TG::tiles(u, c0, cnt);
 
     auto load = [&](int i, auto slot) {
-      const size_t off = (size_t)__builtin_amdgcn_readlane(tab, i) * blk_bytes;
-      const gptr kblk = uniform_ptr(kpool + off);
-      const gptr vblk = uniform_ptr(vpool + off);
+      if constexpr (B >= 16) {
+        // tile i: part i % kSub of block i / kSub (tokens 16 * part ...)
+        const int part = i % TG::kSub;
+        const size_t off = (size_t)__builtin_amdgcn_readlane(tab, i / TG::kSub) * blk_bytes;
+        const gptr kblk = uniform_ptr(kpool + off + part * 16 * ROW);
+        const gptr vblk = uniform_ptr(vpool + off + part * 32);
 #pragma unroll
-      for (int kj = 0; kj < KJ; ++kj) kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
+        for (int kj = 0; kj < KJ; ++kj)
+          kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
+        for (int nt = 0; nt < NT; ++nt)
+          vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
+      } else {
+        // tile i: blocks 2i and 2i + 1; K row col and V tokens 4*grp.. come
+        // from the block that holds them
+        const int b0 = __builtin_amdgcn_readlane(tab, 2 * i);
+        const int b1 = __builtin_amdgcn_readlane(tab, min(2 * i + 1, cnt - 1));
+        const gptr kblk = to_global(kpool) + (size_t)(col < 8 ? b0 : b1) * blk_bytes;
+        const gptr vblk = to_global(vpool) + (size_t)(grp < 2 ? b0 : b1) * blk_bytes;
+#pragma unroll
+        for (int kj = 0; kj < KJ; ++kj)
+          kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
+      }
     };
-
     auto compute = [&](int i, auto slot) {
       u32x4* kb = kring[slot];
       u32x2* vb = vring[slot];
@@ -432,10 +476,11 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = sc[r] * a.scale_log2;
-      const int valid = L - (jb + c0 + i) * B;  // tokens of this block in the context
-      if (valid < B) {
-        // slots past the context: score -inf, V zeroed, so stale bits in an
-        // unused tail slot never reach the output
+      // tokens of this tile inside the unit; the rest (past the context, or
+      // a second block that belongs to another unit) get score -inf and zero
+      // V, so stale bits in an unused slot never reach the output
+      const int valid = u.t1 - (u.t0 + c0 * B + i * 16);
+      if (valid < 16) {
         const int t = 4 * grp;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -494,7 +539,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
                                                             acc[nt], 0, 0, 0);
     };
 
-    block_ring<NBUF>(cnt, load, compute);
+    block_ring<NBUF>(ntile, load, compute);
   }
 
   // l over the four lane groups holding the same head; m_ref is uniform
@@ -544,9 +589,9 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-template <int D, int NBUF>
+template <int D, int B, int NBUF>
 __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
-  constexpr int B = kBlock;
+  using TG = TileGeom<B>;
   constexpr int KC = D / 64;              // 16-byte K code loads per lane per block
   constexpr int VC = D / 64;              // 16-byte V code loads per lane per block
   constexpr int KJ = D / 32;              // q.K MFMAs per block
@@ -556,7 +601,7 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   constexpr uint32_t RBK = B * D + 4 * B;  // K region bytes per (block, kv head)
   constexpr uint32_t RBV = B * D;          // V region bytes per (block, kv head)
 
-  const int s = u.s, g = u.g, L = u.L;
+  const int s = u.s, g = u.g;
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
   const int col = lane & 15, grp = lane >> 4;
 
@@ -584,9 +629,12 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   const size_t vblk_bytes = (size_t)a.num_kv_heads * RBV;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * RBK;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * RBV;
-  const uint32_t koff = col * D + grp * 16;
-  const uint32_t voff = lane * 16;           // dim h*64 + lane of load h: its 16 tokens
-  const uint32_t soff = SOFF + grp * 16;     // K and V scales of tokens 4*grp .. +4
+  // K row (token) col; scales of tokens 4*grp..+4 (with B = 8, rows and
+  // scale groups are taken modulo the block); V: load h gives lane l the 16
+  // tokens of dim h*64 + l (two 8-token halves with B = 8)
+  const uint32_t koff = (B >= 16 ? col : col % 8) * D + grp * 16;
+  const uint32_t soff = SOFF + (B >= 16 ? grp : grp % 2) * 16;
+  const uint32_t voff = lane * B;
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
 
   float m_ref = kNegInf, l_run = 0.f;
@@ -603,15 +651,39 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
     const int cnt = min(64, nblk - c0);
     const int tab = trow[jb + c0 + min(lane, cnt - 1)];
 
+    const int ntile = TG::tiles(u, c0, cnt);
+
     auto load = [&](int i, auto slot) {
-      const size_t b = (size_t)__builtin_amdgcn_readlane(tab, i);
-      const gptr kblk = uniform_ptr(kpool + b * kblk_bytes);
-      const gptr vblk = uniform_ptr(vpool + b * vblk_bytes);
+      if constexpr (B >= 16) {
+        // tile i: part i % kSub of block i / kSub
+        const int part = i % TG::kSub;
+        const size_t b = (size_t)__builtin_amdgcn_readlane(tab, i / TG::kSub);
+        const gptr kblk = uniform_ptr(kpool + b * kblk_bytes + part * 16 * D);
+        const gptr vblk = uniform_ptr(vpool + b * vblk_bytes + part * 16);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) kring[slot][c] = ldg_stream<u32x4>(kblk + koff + c * 64);
-      sring[slot] = ldg_stream<u32x4>(kblk + soff);
+        for (int c = 0; c < KC; ++c) kring[slot][c] = ldg_stream<u32x4>(kblk + koff + c * 64);
+        sring[slot] = ldg_stream<u32x4>(kblk - part * 16 * D + soff + part * 64);
 #pragma unroll
-      for (int h = 0; h < VC; ++h) vring[slot][h] = ldg_stream<u32x4>(vblk + voff + h * 1024);
+        for (int h = 0; h < VC; ++h)
+          vring[slot][h] = ldg_stream<u32x4>(vblk + voff + h * 64 * B);
+      } else {
+        // tile i: blocks 2i and 2i + 1
+        const int b0 = __builtin_amdgcn_readlane(tab, 2 * i);
+        const int b1 = __builtin_amdgcn_readlane(tab, min(2 * i + 1, cnt - 1));
+        const gptr kblk = to_global(kpool) + (size_t)(col < 8 ? b0 : b1) * kblk_bytes;
+        const gptr sblk = to_global(kpool) + (size_t)(grp < 2 ? b0 : b1) * kblk_bytes;
+        const gptr vb0 = uniform_ptr(vpool + (size_t)b0 * vblk_bytes);
+        const gptr vb1 = uniform_ptr(vpool + (size_t)b1 * vblk_bytes);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kring[slot][c] = ldg_stream<u32x4>(kblk + koff + c * 64);
+        sring[slot] = ldg_stream<u32x4>(sblk + soff);
+#pragma unroll
+        for (int h = 0; h < VC; ++h) {
+          const u32x2 lo = ldg_stream<u32x2>(vb0 + voff + h * 64 * B);
+          const u32x2 hi = ldg_stream<u32x2>(vb1 + voff + h * 64 * B);
+          vring[slot][h] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
     };
 
     auto compute = [&](int i, auto slot) {
@@ -651,8 +723,8 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks[r] * a.scale_log2;
-      const int valid = L - (jb + c0 + i) * B;
-      if (valid < B) {
+      const int valid = u.t1 - (u.t0 + c0 * B + i * 16);  // tokens of the tile in the unit
+      if (valid < 16) {
         // slots past the context: score -inf, V codes and scale zeroed
         const int t = 4 * grp;
         uint32_t m = 0;
@@ -713,7 +785,7 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop[nt], acc[nt], 0, 0, 0);
     };
 
-    block_ring<NBUF>(cnt, load, compute);
+    block_ring<NBUF>(ntile, load, compute);
   }
 
   float l_tot = l_run + swap16(l_run);
@@ -721,10 +793,10 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
 }
 
-template <int D, int NBUF>
+template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan(a, plan_lds);
+  const Plan pl = build_plan<B>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
   const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
   if (r >= pl.R) return;
@@ -733,13 +805,13 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kerne
   const int lane = threadIdx.x & 63;
   const int g = hg * kWaves + wave;
   if (g >= a.num_kv_heads) return;
-  walk_range(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, NBUF>(a, G, u, lane); });
+  walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
-template <int D, int NBUF>
+template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan(a, plan_lds);
+  const Plan pl = build_plan<B>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
   const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
   if (r >= pl.R) return;
@@ -747,7 +819,7 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kern
   const int lane = threadIdx.x & 63;
   const int g = hg * kWaves + wave;
   if (g >= a.num_kv_heads) return;
-  walk_range(a, pl, r, g, [&](const Unit& u) { mfma8_unit<D, NBUF>(a, G, u, lane); });
+  walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma8_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -924,7 +996,7 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
 template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan(a, plan_lds);
+  const Plan pl = build_plan<kBlock>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
   const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
   if (r >= pl.R) return;
@@ -932,7 +1004,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) 
   const int lane = threadIdx.x & 63;
   const int g = hg * kWaves + wave;
   if (g >= a.num_kv_heads) return;
-  walk_range(a, pl, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
+  walk_range<kBlock>(a, pl, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -1045,19 +1117,19 @@ Launch decode_launch(const DecodeArgs& a, K kernel) {
 
 // The head group (1..16) fills the 16 head slots of the MFMA tiles at run
 // time, so one instantiation per head_dim serves every group size.
-template <int D>
+template <int D, int B>
 hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_mfma_kernel<D, kNBuf>);
-  decode_mfma_kernel<D, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
+  const Launch l = decode_launch(a, decode_mfma_kernel<D, B, kNBuf>);
+  decode_mfma_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
 }
 
-template <int D>
+template <int D, int B>
 hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_mfma8_kernel<D, kNBuf8>);
-  decode_mfma8_kernel<D, kNBuf8><<<l.grid, l.block, l.lds, st>>>(a, G);
+  const Launch l = decode_launch(a, decode_mfma8_kernel<D, B, kNBuf8>);
+  decode_mfma8_kernel<D, B, kNBuf8><<<l.grid, l.block, l.lds, st>>>(a, G);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
@@ -1086,9 +1158,11 @@ hipError_t launch_valu(const DecodeArgs& a, int G, hipStream_t st) {
 
 }  // namespace
 
-DecodePath decode_path(pa_dtype dtype, int head_dim, int group) {
+DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size) {
   if (head_dim != 64 && head_dim != 128) return DecodePath::kUnsupported;
   if (group < 1) return DecodePath::kUnsupported;
+  if (block_size != 8 && block_size != 16 && block_size != 32) return DecodePath::kUnsupported;
+  if (dtype == PA_F32 && block_size != kBlock) return DecodePath::kUnsupported;
   if (dtype == PA_BF16) {
     if (group <= kMaxMfmaGroup) return DecodePath::kMfma;
     return DecodePath::kUnsupported;
@@ -1099,13 +1173,34 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group) {
 }
 
 namespace {
+// One instantiation per (head_dim, block size) of each MFMA kernel.
+template <template <int, int> class K, int D>
+hipError_t by_block(int block_size, const DecodeArgs& a, int group, hipStream_t st) {
+  switch (block_size) {
+    case 8: return K<D, 8>::run(a, group, st);
+    case 16: return K<D, 16>::run(a, group, st);
+    case 32: return K<D, 32>::run(a, group, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <int D, int B>
+struct MfmaLaunch {
+  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st) { return launch_mfma<D, B>(a, G, st); }
+};
+template <int D, int B>
+struct Mfma8Launch {
+  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st) { return launch_mfma8<D, B>(a, G, st); }
+};
+
 hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
-                               hipStream_t st) {
-  switch (decode_path(dtype, head_dim, group)) {
+                               int block_size, hipStream_t st) {
+  switch (decode_path(dtype, head_dim, group, block_size)) {
     case DecodePath::kMfma:
-      return head_dim == 128 ? launch_mfma<128>(a, group, st) : launch_mfma<64>(a, group, st);
+      return head_dim == 128 ? by_block<MfmaLaunch, 128>(block_size, a, group, st)
+                             : by_block<MfmaLaunch, 64>(block_size, a, group, st);
     case DecodePath::kMfma8:
-      return head_dim == 128 ? launch_mfma8<128>(a, group, st) : launch_mfma8<64>(a, group, st);
+      return head_dim == 128 ? by_block<Mfma8Launch, 128>(block_size, a, group, st)
+                             : by_block<Mfma8Launch, 64>(block_size, a, group, st);
     case DecodePath::kValu:
       return head_dim == 128 ? launch_valu<128>(a, group, st) : launch_valu<64>(a, group, st);
     default:
@@ -1118,7 +1213,7 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
 // sequences (the per-workgroup plan lives in LDS); every per-sequence array
 // is offset to the slice.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
-                         hipStream_t st) {
+                         int block_size, hipStream_t st) {
   const size_t es = dtype == PA_F32 ? 4 : 2;  // q / out element (bf16 for 8-bit pools)
   for (int32_t s0 = 0; s0 < a.num_seqs; s0 += kMaxPlanSeqs) {
     DecodeArgs b = a;
@@ -1133,7 +1228,7 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int 
     b.part_l = a.part_l + pr;
     b.part_o = a.part_o + pr * head_dim;
     b.seg_count = a.seg_count + s0;
-    const hipError_t e = launch_decode_slice(b, dtype, head_dim, group, st);
+    const hipError_t e = launch_decode_slice(b, dtype, head_dim, group, block_size, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -28,7 +28,7 @@ namespace pakv {
 #define PA_NT_LOADS 1  // 1: K/V loads carry the non-temporal hint
 #endif
 
-constexpr int kBlock = 16;       // tokens per block supported by decode
+constexpr int kBlock = 16;       // tokens per block of the fp32 decode (MFMA paths: 8, 16, 32)
 constexpr int kWaves = PA_WAVES;
 constexpr int kNBuf = PA_NBUF;
 constexpr int kNBuf8 = PA_NBUF8;
@@ -58,9 +58,10 @@ struct DecodeArgs {
 
 // Which decode kernel family handles a shape.
 enum class DecodePath { kUnsupported, kValu, kMfma, kMfma8 };
-DecodePath decode_path(pa_dtype dtype, int head_dim, int group);
+DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size);
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
+                         int block_size,
                          hipStream_t stream);
 
 // block_tables == nullptr: no table update (plain slot write).  For
