@@ -101,10 +101,10 @@ def test_host_checks_reject_before_any_launch():
     st = L.pa_decode(ctypes.byref(d96), dummy, dummy, dummy, 1, 32, dummy, 4, dummy, 0.1,
                      dummy, 0, null, 0, null)
     assert st == pk.PA_EUNSUPPORTED
-    d8 = _desc(B=8)
-    st = L.pa_decode(ctypes.byref(d8), dummy, dummy, dummy, 1, 32, dummy, 4, dummy, 0.1,
-                     dummy, 0, null, 0, null)
-    assert st == pk.PA_EUNSUPPORTED
+    for bad in (_desc(B=12), _desc(B=8, dt=pk.PA_F32)):   # sizes 8/16/32; fp32 only 16
+        st = L.pa_decode(ctypes.byref(bad), dummy, dummy, dummy, 1, 32, dummy, 4, dummy, 0.1,
+                         dummy, 0, null, 0, null)
+        assert st == pk.PA_EUNSUPPORTED
     # no workspace given (every decode needs one)
     st = L.pa_decode(ctypes.byref(d), dummy, dummy, dummy, 4, 32, dummy, 8192, dummy, 0.1,
                      dummy, 512, null, 0, null)
