@@ -80,6 +80,22 @@ __device__ __forceinline__ V ldg_stream(gptr p) {
 #endif
 }
 
+// A load that leaves its lines to the caches' normal policy: used where the
+// other half of the lines is read by the next tile (V rows of 32-token
+// blocks), which a non-temporal load would make HBM fetch again.
+template <typename V>
+__device__ __forceinline__ V ldg_keep(gptr p) {
+  typedef const V __attribute__((address_space(1)))* vptr;
+  return *reinterpret_cast<vptr>(p);
+}
+
+// V loads of a tile: non-temporal unless the tile reads half of each row.
+template <int B, typename V>
+__device__ __forceinline__ V ldg_v(gptr p) {
+  if constexpr (B > 16) return ldg_keep<V>(p);
+  else return ldg_stream<V>(p);
+}
+
 // A generic pointer known to point into global memory, as a global pointer.
 __device__ __forceinline__ gptr to_global(const uint8_t* p) {
   return reinterpret_cast<gptr>(reinterpret_cast<uint64_t>(p));
@@ -448,7 +464,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
           kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
+          vring[slot][nt] = ldg_v<B, u32x2>(vblk + voff + nt * 16 * (B * 2));
       } else {
         // tile i: blocks 2i and 2i + 1; K row col and V tokens 4*grp.. come
         // from the block that holds them
@@ -664,8 +680,7 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
         for (int c = 0; c < KC; ++c) kring[slot][c] = ldg_stream<u32x4>(kblk + koff + c * 64);
         sring[slot] = ldg_stream<u32x4>(kblk - part * 16 * D + soff + part * 64);
 #pragma unroll
-        for (int h = 0; h < VC; ++h)
-          vring[slot][h] = ldg_stream<u32x4>(vblk + voff + h * 64 * B);
+        for (int h = 0; h < VC; ++h) vring[slot][h] = ldg_v<B, u32x4>(vblk + voff + h * 64 * B);
       } else {
         // tile i: blocks 2i and 2i + 1
         const int b0 = __builtin_amdgcn_readlane(tab, 2 * i);
