@@ -45,6 +45,9 @@ def lib():
         L.oracle_kv_write.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
         L.oracle_block_copy.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32]
         L.oracle_max_threads.argtypes = []
+        L.oracle_extend.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, vp, i32,
+                                    vp, f64, vp, i32]
+        L.oracle_extend.restype = ctypes.c_int
         L.oracle_block_swap.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, i32,
                                         i32]
         L.oracle_block_swap.restype = ctypes.c_int
@@ -236,6 +239,29 @@ def block_copy(k_pool, v_pool, pairs):
                                  vp_.ctypes.data_as(ctypes.c_void_p), prp, pr.shape[0])
     _check(rc, "oracle_block_copy")
     return kp, vp_
+
+
+def extend(k_pool, v_pool, q, q_start, block_tables, context_lens, scale, threads=0):
+    """Multi-token causal attention: q [total][Hq][d] rows of the sequences
+    given by q_start [S+1]; query j of sequence s sits at position
+    context_lens[s] - n_s + j and attends to tokens 0..that position.
+    Returns float64 [total][Hq][d]."""
+    nb, B, nkv, d = _geom(k_pool, v_pool)
+    T, Hq, _ = q.shape
+    kp, kpp = _c(k_pool)
+    vp_, vpp = _c(v_pool)
+    qq, qp = _c(q)
+    qs, qsp = _c(q_start, np.int32)
+    bt, btp = _c(block_tables, np.int32)
+    cl, clp = _c(context_lens, np.int32)
+    if qs[-1] != T:
+        raise ValueError("q_start[-1] must equal the number of query rows")
+    out = np.empty((T, Hq, d), np.float64)
+    rc = lib().oracle_extend(_dtype_code(k_pool), nb, B, nkv, d, kpp, vpp, qp, qsp,
+                             len(qs) - 1, Hq, btp, bt.shape[1], clp, float(scale),
+                             out.ctypes.data_as(ctypes.c_void_p), int(threads))
+    _check(rc, "oracle_extend")
+    return out
 
 
 SWAP_OUT, SWAP_IN = 0, 1

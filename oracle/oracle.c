@@ -563,6 +563,66 @@ int oracle_block_copy(int dtype, int num_blocks, int block_size, int num_kv_head
 }
 
 /*
+ * Multi-token attention with a causal mask (extend / chunked prefill):
+ * sequence s brings n_s = q_start[s+1] - q_start[s] query rows whose tokens
+ * are already counted in L = context_lens[s]; query j is at position
+ * p = L - n_s + j and attends to tokens [0, p] exactly as decode attends to
+ * [0, L) (gather through the table, textbook softmax in double).  The pages
+ * describe the table-driven gather for any logical order (glossary entry,
+ * "Complex Attention Patterns"); the causal range is the plainest reading of
+ * appending tokens one by one ("Dynamic Growth").  q, out: [total][nq][d].
+ */
+int oracle_extend(int dtype, int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                  const void* k_pool, const void* v_pool, const void* q,
+                  const int32_t* q_start, int num_seqs, int num_q_heads,
+                  const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* context_lens, double scale, double* out, int num_threads) {
+  if (check_geometry(dtype, num_blocks, block_size, num_kv_heads, head_dim, num_q_heads))
+    return 1;
+  const int B = block_size, d = head_dim, nkv = num_kv_heads, G = num_q_heads / num_kv_heads;
+  if (num_seqs < 0 || q_start[0] != 0) return 2;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = q_start[s + 1] - q_start[s], L = context_lens[s];
+    if (n < 0 || (n > 0 && (L < n || L > max_blocks_per_seq * B))) return 2;
+    for (int j = 0; n > 0 && j < (L + B - 1) / B; ++j) {
+      int32_t b = block_tables[(size_t)s * max_blocks_per_seq + j];
+      if (b < 0 || b >= num_blocks) return 2;
+    }
+  }
+  const int total = q_start[num_seqs];
+  set_threads(num_threads);
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int p = 0; p < total * num_q_heads; ++p) {
+    const int row = p / num_q_heads, h = p % num_q_heads, g = h / G;
+    int s = 0;
+    while (q_start[s + 1] <= row) ++s;
+    const int n = q_start[s + 1] - q_start[s], L = context_lens[s];
+    const int pos = L - n + (row - q_start[s]);
+    const int len = pos + 1;
+    double* Kc = (double*)malloc(sizeof(double) * (size_t)len * d);
+    double* Vc = (double*)malloc(sizeof(double) * (size_t)len * d);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)len);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!Kc || !Vc || !sc || !qd) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      for (int i = 0; i < d; ++i)
+        qd[i] = orc_load(orc_q_dtype(dtype), q, ((size_t)row * num_q_heads + h) * d + i);
+      orc_gather(dtype, nkv, B, d, k_pool, v_pool,
+                 block_tables + (size_t)s * max_blocks_per_seq, g, len, Kc, Vc);
+      orc_attend(qd, Kc, Vc, d, len, scale, sc, out + (size_t)p * d);
+    }
+    free(Kc);
+    free(Vc);
+    free(sc);
+    free(qd);
+  }
+  return failed ? 3 : 0;
+}
+
+/*
  * Block swap between a device pool and a host pool (preemption by swapping:
  * vLLM post, "Where it bites"; glossary entry, "Flexible Management").  For
  * each (src, dst) pair, the whole block src of the source pools (the device

@@ -371,3 +371,79 @@ def test_block_swap_rejects_out_of_range_pairs():
         oracle.block_swap(k, v, hk, hv, np.array([[0, 2]], np.int32), oracle.SWAP_OUT)
     with pytest.raises(oracle.OracleError):
         oracle.block_swap(k, v, hk, hv, np.array([[2, 0]], np.int32), oracle.SWAP_IN)
+
+
+# --- multi-token (extend) attention ---------------------------------------------------
+def _extend_case(rng, lens, ns, nb=40, nkv=2, Hq=4, B=4, d=8, dtype="f32"):
+    k, v = _pools(nb, nkv, B, d, rng, dtype)
+    S = len(lens)
+    width = max(-(-L // B) for L in lens)
+    tables = np.stack([rng.permutation(nb)[:width] for _ in range(S)]).astype(np.int32)
+    q_start = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    q = rng.standard_normal((int(q_start[-1]), Hq, d)).astype(np.float32)
+    if dtype == "bf16":
+        q = f32_to_bf16_bits(q)
+    return k, v, q, q_start, tables, np.array(lens, np.int32)
+
+
+def test_extend_with_one_query_per_sequence_is_decode():
+    """One new token per sequence sits at position L - 1 and sees the whole
+    context: the extend oracle must equal the decode oracle bit for bit."""
+    rng = np.random.default_rng(70)
+    k, v, q, qs, tables, lens = _extend_case(rng, [5, 17, 1, 40], [1, 1, 1, 1])
+    ext = oracle.extend(k, v, q, qs, tables, lens, 0.3)
+    dec = oracle.decode(k, v, q, tables, lens, 0.3)
+    assert np.array_equal(ext, dec)
+
+
+def test_extend_equal_keys_give_causal_means():
+    """All keys zero: query j of a sequence averages V over tokens 0..p_j,
+    p_j = L - n + j -- a different prefix for every query."""
+    rng = np.random.default_rng(71)
+    k, v, q, qs, tables, lens = _extend_case(rng, [13, 9], [5, 9])
+    k[...] = 0
+    out = oracle.extend(k, v, q, qs, tables, lens, 1.0)
+    B = 4
+    for s in range(2):
+        n, L = qs[s + 1] - qs[s], lens[s]
+        Kc, Vc = oracle.gather(k, v, tables[s], 1, L)
+        for j in range(n):
+            p = L - n + j
+            assert np.allclose(out[qs[s] + j, 2:4], Vc[:p + 1].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_extend_is_blind_to_tokens_after_each_position():
+    """Changing every token after position p changes no output of a query at
+    p or before."""
+    rng = np.random.default_rng(72)
+    k, v, q, qs, tables, lens = _extend_case(rng, [21], [7], B=4)
+    out = oracle.extend(k, v, q, qs, tables, lens, 0.5)
+    L, n, B = 21, 7, 4
+    p_cut = L - n + 3                          # query 3's position
+    k2, v2 = k.copy(), v.copy()
+    for t in range(p_cut + 1, L):              # overwrite the later tokens
+        b, r = tables[0, t // B], t % B
+        k2[b, :, r, :] = 1e3
+        v2[b, :, :, r] = -1e3
+    out2 = oracle.extend(k2, v2, q, qs, tables, lens, 0.5)
+    assert np.array_equal(out[:4], out2[:4])
+    assert not np.array_equal(out[4:], out2[4:])
+
+
+def test_extend_chunks_compose():
+    """Prefilling n tokens in one call equals two calls on consecutive chunks
+    (the first with the context ending at the chunk boundary)."""
+    rng = np.random.default_rng(73)
+    k, v, q, qs, tables, lens = _extend_case(rng, [30], [12], dtype="bf16")
+    whole = oracle.extend(k, v, q, qs, tables, lens, 0.4)
+    first = oracle.extend(k, v, q[:5], np.array([0, 5], np.int32), tables,
+                          np.array([23], np.int32), 0.4)
+    second = oracle.extend(k, v, q[5:], np.array([0, 7], np.int32), tables, lens, 0.4)
+    assert np.array_equal(whole, np.concatenate([first, second]))
+
+
+def test_extend_rejects_more_queries_than_context():
+    rng = np.random.default_rng(74)
+    k, v, q, qs, tables, lens = _extend_case(rng, [3], [4])
+    with pytest.raises(oracle.OracleError):
+        oracle.extend(k, v, q, qs, tables, lens, 1.0)
