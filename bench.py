@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0: library)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="tokens per block (the table/tail-waste trade-off)")
+    ap.add_argument("--mode", default="decode", choices=["decode", "extend"],
+                    help="decode (default) or extend: chunked prefill over paged prefixes")
+    ap.add_argument("--extend-seqs", type=int, default=32)
+    ap.add_argument("--chunk", type=int, default=256, help="new tokens per sequence per step")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache storage: bf16, or 8-bit E4M3 codes + per-token scales")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -106,6 +110,9 @@ def main():
     import paged_kv_cache_335_amd as pk
     from paged_kv_cache_335_amd.runtime import DeviceEvent, PagedKVCache
     from workloads import CONFIGS, draw_lengths
+
+    if args.mode == "extend":
+        return bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths)
 
     cfg = CONFIGS[args.config]
     if args.block_size != cfg.block_size:
@@ -284,6 +291,101 @@ def main():
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(
             cache, qs[-1], out, lens_now, S, Hq, d, kv_per_token, args.cpu_seconds)
 
+    print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
+    """Chunked prefill: `extend_seqs` sequences with cached prefixes drawn like
+    the decode workload's lengths; every step appends `chunk` new tokens to
+    each (block manager, slot write) and runs causal attention of those
+    queries over the whole paged context.  Reports attention TFLOP/s against
+    the bf16 MFMA peak (the path is matrix-bound at these chunk sizes)."""
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
+    S, Hq, Hkv, d, B = (args.extend_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                        cfg.block_size)
+    W, K, C = args.warmup, args.steps, args.chunk
+    rng = np.random.default_rng(cfg.seed)
+    lens0 = draw_lengths(cfg, rng)[:S].astype(np.int64)
+    final = lens0 + (W + K) * C
+    need = int(((final + B - 1) // B).sum())
+    num_blocks = int(math.ceil(1.1 * need))
+    width = int((final.max() + B - 1) // B)
+    cache = PagedKVCache(num_blocks, Hkv, d, S, width, block_size=B, shuffle_seed=cfg.seed,
+                         device=dev)
+    seqs = np.array([cache.add_sequence() for _ in range(S)], dtype=np.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    log(f"extend: S={S} chunk={C} prefix sum={int(lens0.sum())} pool={num_blocks} blocks")
+    for i in range(S):  # prefixes through the slot write
+        n = int(lens0[i])
+        kn = torch.randn((n, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        vn = torch.randn((n, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        cache.append(seqs[i:i + 1], np.array([n], np.int32), kn, vn, stream=stream)
+    torch.cuda.synchronize()
+    steps = W + K
+    T = S * C
+    qs = [torch.randn((T, Hq, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(steps)]
+    kns = [torch.randn((T, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(steps)]
+    vns = [torch.randn((T, Hkv, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(steps)]
+    out = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    ns = np.full(S, C, np.int32)
+    flops, kv_bytes = [], []
+    ev = [(DeviceEvent(timing=True), DeviceEvent(timing=True)) for _ in range(steps)]
+    scale = d ** -0.5
+    q_start = torch.from_numpy(np.arange(S + 1, dtype=np.int32) * C).to(dev)
+
+    def step(i):
+        cache.append(seqs, ns, kns[i], vns[i], stream=stream)
+        tables, lens = cache.bm.export(seqs, width, pad_block=0)
+        d_tables = torch.from_numpy(tables).to(dev, non_blocking=False)
+        d_lens = torch.from_numpy(lens).to(dev, non_blocking=False)
+        ev[i][0].record(stream)
+        pk.pa_extend(qs[i], cache.k_pool, cache.v_pool, q_start, d_tables, d_lens, scale,
+                     out=out, stream=stream)
+        ev[i][1].record(stream)
+        L = lens.astype(np.int64)
+        # sum over queries of (position + 1): query j of a sequence sees L - C + j + 1 tokens
+        seen = (C * (L - C) + C * (C + 1) // 2).sum()
+        flops.append(int(seen) * Hq * 4 * d)
+        kv_bytes.append(int(L.sum()) * 2 * Hkv * d * 2)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(W, steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    ext_ms = [ev[i][0].elapsed_ms(ev[i][1]) for i in range(W, steps)]
+    ext_avg = float(np.mean(ext_ms))
+    fl = float(np.mean(flops[W:]))
+    tflops = fl / (ext_avg * 1e-3) / 1e12
+    log(f"extend step {ms_step:.3f} ms; attention {ext_avg * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": "paged extend (chunked prefill) attention: TFLOP/s + query tokens/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.key} shape, {S} sequences with cached prefixes, "
+                               f"{C}-token chunks", "num_seqs": S, "chunk": C,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d, "block_size": B,
+                   "mean_context_tokens": round(float(np.mean(lens0)) + (W + K) * C / 2, 1)},
+        "extend": {"us_mean": round(ext_avg * 1e3, 2), "us_min": round(min(ext_ms) * 1e3, 2),
+                   "query_tokens_per_s": round(T / (ext_avg * 1e-3), 1),
+                   "kv_GBps_unique": round(float(np.mean(kv_bytes[W:])) / (ext_avg * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -163,6 +163,32 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     void* stream);
 
 /*
+ * Multi-token paged attention: extend / chunked prefill over a paged prefix
+ * with a causal mask (glossary entry, "Complex Attention Patterns" and
+ * "Dynamic Growth": attention reads the cache through the block table
+ * whatever the logical order, and new tokens are appended on demand).
+ * Sequence s brings n_s = q_start[s+1] - q_start[s] new query tokens, rows
+ * q_start[s] .. q_start[s+1] - 1 of q; their K/V are already in the cache
+ * (pa_kv_write first), so context_lens[s] = L_s counts them and n_s <= L_s.
+ * Query j of sequence s is at position p = L_s - n_s + j and attends to the
+ * sequence's tokens 0..p:
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t,
+ * with K_t, V_t read as in pa_decode (kv head h / (num_q_heads / H_kv)).
+ *   q, out:      [total_q][num_q_heads][head_dim] bf16, total_q = q_start[S].
+ *   q_start:     int32 [num_seqs + 1], q_start[0] = 0, non-decreasing;
+ *                sequences with no queries are allowed.
+ *   block_tables, context_lens: as for pa_decode.
+ * Requires bf16 pools, block_size 16, head_dim 64 or 128 and at most 16
+ * query heads per kv head (PA_EUNSUPPORTED otherwise).  No workspace.
+ * With PA_DEBUG=1, q_start, lengths and table entries are validated first.
+ */
+pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                    const void* q, int32_t total_q, const int32_t* q_start, int32_t num_seqs,
+                    int32_t num_q_heads, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                    void* out, void* stream);
+
+/*
  * Copy-on-write block copy ("The bonus contiguous storage can't give you:
  * sharing" on the vLLM KV-cache page; "Shared blocks and copy-on-write" on
  * the attention-lab page): for each (src, dst) pair, every KV head and slot

@@ -68,6 +68,7 @@ def _load():
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
         "pa_kv_append": (i32, [P, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]),
         "pa_block_swap": (i32, [P, vp, vp, vp, vp, i32, vp, i32, i32, vp]),
+        "pa_extend": (i32, [P, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, f32, vp, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_version": (ctypes.c_char_p, []),
         "pa_bm_create": (vp, [i32, i32, ctypes.c_uint64]),
@@ -98,7 +99,8 @@ def _load():
 _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
-    "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_status_str",
+    "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
+    "pa_status_str",
     "pa_version", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch",
     "pa_bm_free_seq", "pa_bm_block_table", "pa_bm_export", "pa_bm_refcount",
@@ -258,6 +260,36 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
                         _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
                         int(partition_tokens), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def pa_extend(q, k_pool, v_pool, q_start, block_tables, context_lens, scale, out=None,
+              stream=None):
+    """Multi-token causal attention (extend / chunked prefill); returns out
+    [total_q][num_q_heads][head_dim].  Query j of sequence s (rows
+    q_start[s] .. q_start[s+1]) sits at position context_lens[s] - n_s + j
+    and attends to the sequence's tokens up to it."""
+    desc = pool_desc(k_pool, v_pool)
+    T, Hq, d = q.shape
+    if d != desc.head_dim or q.dtype != io_dtype(k_pool):
+        raise ValueError("q must be [total][Hq][head_dim] in the pool's element type")
+    for t, name in ((q_start, "q_start"), (block_tables, "block_tables"),
+                    (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    S = context_lens.numel()
+    if q_start.numel() != S + 1 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("q_start must be [S+1] and block_tables [S][max_blocks]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = _lib.pa_extend(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                        _dev(q, "q"), T, _dev(q_start, "q_start"), S, Hq,
+                        _dev(block_tables, "block_tables"), block_tables.shape[1],
+                        _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
+                        _stream(stream))
+    _check(st, "pa_extend")
     return out
 
 

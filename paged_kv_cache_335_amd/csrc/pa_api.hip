@@ -229,6 +229,60 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
+pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                    const void* q, int32_t total_q, const int32_t* q_start, int32_t num_seqs,
+                    int32_t num_q_heads, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
+                    void* out, void* stream) {
+  if (!pool_ok(pool) || num_seqs < 0 || total_q < 0 || num_q_heads <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_EINVAL;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_EINVAL;
+  if ((int64_t)max_blocks_per_seq * pool->block_size > INT32_MAX) return PA_EINVAL;
+  if (num_seqs == 0 || total_q == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !q_start || !block_tables || !context_lens || !out)
+    return PA_EINVAL;
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return PA_EINVAL;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (!pakv::extend_supported(pool->dtype, pool->head_dim, group, pool->block_size))
+    return PA_EUNSUPPORTED;
+  hipStream_t hs = as_stream(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> qs, lens, tab;
+    if (!fetch(qs, q_start, (size_t)num_seqs + 1, hs) ||
+        !fetch(lens, context_lens, (size_t)num_seqs, hs) ||
+        !fetch(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, hs))
+      return PA_EHIP;
+    if (qs[0] != 0 || qs[num_seqs] != total_q) return PA_EINVAL;
+    const int64_t max_len = (int64_t)max_blocks_per_seq * pool->block_size;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t n = qs[s + 1] - qs[s];
+      if (n < 0 || (n > 0 && (lens[s] < n || lens[s] > max_len))) return PA_EINVAL;
+      const int32_t nb = n > 0 ? (lens[s] + pool->block_size - 1) / pool->block_size : 0;
+      for (int32_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= pool->num_blocks) return PA_EINVAL;
+      }
+    }
+  }
+  pakv::ExtendArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.q = q;
+  a.out = out;
+  a.q_start = q_start;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pakv::launch_extend(a, pool->head_dim, group, hs);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
 pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool, const int32_t* pairs,
                         int32_t num_pairs, void* stream) {
   if (!pool_ok(pool) || num_pairs < 0) return PA_EINVAL;

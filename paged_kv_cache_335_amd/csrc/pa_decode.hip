@@ -50,115 +50,11 @@
 #include <type_traits>
 #include <utility>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pakv {
 namespace {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Global-memory (address space 1) byte pointer.
-typedef const uint8_t __attribute__((address_space(1)))* gptr;
-
-template <typename V>
-__device__ __forceinline__ V ldg_stream(gptr p) {
-  typedef const V __attribute__((address_space(1)))* vptr;
-#if PA_NT_LOADS
-  return __builtin_nontemporal_load(reinterpret_cast<vptr>(p));
-#else
-  return *reinterpret_cast<vptr>(p);
-#endif
-}
-
-// A load that leaves its lines to the caches' normal policy: used where the
-// other half of the lines is read by the next tile (V rows of 32-token
-// blocks), which a non-temporal load would make HBM fetch again.
-template <typename V>
-__device__ __forceinline__ V ldg_keep(gptr p) {
-  typedef const V __attribute__((address_space(1)))* vptr;
-  return *reinterpret_cast<vptr>(p);
-}
-
-// V loads of a tile: non-temporal unless the tile reads half of each row.
-template <int B, typename V>
-__device__ __forceinline__ V ldg_v(gptr p) {
-  if constexpr (B > 16) return ldg_keep<V>(p);
-  else return ldg_stream<V>(p);
-}
-
-// A generic pointer known to point into global memory, as a global pointer.
-__device__ __forceinline__ gptr to_global(const uint8_t* p) {
-  return reinterpret_cast<gptr>(reinterpret_cast<uint64_t>(p));
-}
-
-// A global pointer that is the same in every lane, moved to SGPRs so that
-// loads can take the scalar-base + 32-bit-vector-offset form.
-__device__ __forceinline__ gptr uniform_ptr(const uint8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<gptr>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1]; row rotate right by 4, 8.
-constexpr int kQuadXor1 = 0xB1;
-constexpr int kQuadXor2 = 0x4E;
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-
-// Lane i <-> lane i^16 (ds_swizzle bit mode: and 0x1F, xor 0x10).
-__device__ __forceinline__ float swap16(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-}
-// Lane i <-> lane i^32.
-__device__ __forceinline__ float swap32(float x) {
-  const int lane = __lane_id();
-  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(x)));
-}
-__device__ __forceinline__ float lane_bcast(float x, int src) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kQuadXor1>(x));
-  x = fmaxf(x, dpp<kQuadXor2>(x));
-  x = fmaxf(x, dpp<kRowRor4>(x));
-  x = fmaxf(x, dpp<kRowRor8>(x));
-  x = fmaxf(x, swap16(x));
-  return fmaxf(x, swap32(x));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp<kQuadXor1>(x);
-  x += dpp<kQuadXor2>(x);
-  x += dpp<kRowRor4>(x);
-  x += dpp<kRowRor8>(x);
-  x += swap16(x);
-  return x + swap32(x);
-}
-
-template <typename T>
-__device__ __forceinline__ void store_out(void* out, size_t idx, float v);
-template <>
-__device__ __forceinline__ void store_out<float>(void* out, size_t idx, float v) {
-  static_cast<float*>(out)[idx] = v;
-}
-template <>
-__device__ __forceinline__ void store_out<__bf16>(void* out, size_t idx, float v) {
-  static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(v);  // v_cvt_pk_bf16_f32, RNE
-}
 
 // A piece of work for one wave: tokens [t0, t1) of sequence s, kv head g;
 // `part` is the piece's slot among the sequence's `nparts` pieces.
@@ -179,35 +75,6 @@ struct Plan {
 __host__ __device__ constexpr size_t plan_lds_bytes(int S) {
   return ((size_t)2 * S + 1 + 8) * sizeof(int);
 }
-
-// Inclusive scan of one value per lane over a wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __builtin_amdgcn_ds_bpermute((lane - d) << 2, v);
-    if (lane >= d) v += y;
-  }
-  return v;
-}
-
-// Exclusive scan of one value per thread over the workgroup (at most 8
-// waves: wsum holds one partial sum per wave).
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int inc = wave_incl_scan(v, lane);
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  int off = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) off += wsum[w];
-    tot += wsum[w];
-  }
-  *total = tot;
-  __syncthreads();
-  return off + inc - v;
-}
-static_assert(kWaves >= 1 && kWaves <= 8, "the plan scan keeps one sum per wave, 8 at most");
 
 // Collective over the workgroup; ends with a barrier.  B = tokens per block.
 template <int B>
@@ -292,50 +159,6 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, 
 // Index of (sequence, query head, piece) in the partial buffers.
 __device__ __forceinline__ size_t part_index(const DecodeArgs& a, int s, int hq, int part) {
   return ((size_t)s * a.num_q_heads + hq) * a.max_slots + part;
-}
-
-// Online softmax with a lazy reference: probabilities are 2^(x - m_ref) for a
-// per-head reference m_ref that only moves when some head's block maximum
-// exceeds it by more than kSlack (log2 units).  Until then the accumulators
-// need no rescaling; probabilities stay below 2^kSlack, far from fp32 range
-// limits, and the final (or split) normalisation divides the reference out
-// exactly as it would a running maximum.
-constexpr float kSlack = 8.f;
-
-template <int... I, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Software pipeline over `cnt` blocks with a ring of NBUF register buffers:
-// load(i, slot) issues block i's loads into ring slot `slot`; compute(i, slot)
-// consumes it.  NBUF - 1 blocks are in flight while one is consumed.  The
-// steady-state loop issues a load at every step, so the wait before each
-// compute only covers the oldest buffer; the drain (at most 2*NBUF - 2
-// blocks) is separate code, so its shorter waits do not leak into the loop.
-// The prologue clamps its block indices so that it is unconditional (a unit
-// shorter than the ring re-reads its last block into unused slots).
-template <int NBUF, typename LoadF, typename ComputeF>
-__device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& compute) {
-  static_for<NBUF - 1>([&](auto b) { load(min((int)b, cnt - 1), b); });
-  int i = 0;
-  for (; i + 2 * NBUF - 2 < cnt; i += NBUF) {
-    static_for<NBUF>([&](auto b) {
-      load(i + b + NBUF - 1, std::integral_constant<int, (b + NBUF - 1) % NBUF>{});
-      compute(i + b, b);
-    });
-  }
-  static_for<2 * NBUF - 2>([&](auto b) {
-    if (i + b < cnt) {
-      if (i + b + NBUF - 1 < cnt)
-        load(i + b + NBUF - 1, std::integral_constant<int, (b + NBUF - 1) % NBUF>{});
-      compute(i + b, std::integral_constant<int, b % NBUF>{});
-    }
-  });
 }
 
 // Epilogue of an MFMA unit: acc[nt][r] holds head 4*grp + r, dim nt*16 + col

@@ -1,0 +1,280 @@
+// Multi-token paged attention: extend / chunked prefill over a paged prefix
+// with a causal mask.  The glossary entry's "Complex Attention Patterns" and
+// "Dynamic Growth" (the cache is read through the block table whatever the
+// logical order; new tokens are appended on demand) and the vLLM post's
+// "The bonus contiguous storage can't give you: sharing" (several sequences
+// reading one prefix) make the same gather serve more than one query per
+// sequence.
+//
+// What is computed: sequence s brings n_s new query tokens (rows
+// q_start[s] .. q_start[s+1] of q), whose K/V are already in the cache, so
+// its context length L_s counts them.  Query j of s sits at position
+// p = L_s - n_s + j and attends to tokens 0..p of the sequence:
+//   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t,
+// K_t, V_t read from block_tables[s][t / 16], slot t % 16, kv head h / G.
+//
+// Decomposition: the 16 "head slots" of the decode kernel's MFMA tiles hold
+// (query, head) pairs here: a row tile is QPT = 16 / G consecutive queries
+// of one sequence times the G query heads of one kv head.  Each wave takes
+// row tiles in turn (tile k, kv head g), streams blocks 0 .. p_max of the
+// sequence through the same register ring, and masks each row at its own
+// position.  Consecutive waves take the kv heads of one tile, so a
+// workgroup reads adjacent regions of the same blocks together.  No
+// context split: every row tile finishes in place.
+#include <algorithm>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pakv {
+namespace {
+
+constexpr int kExtBlock = 16;
+
+// Plan in LDS: tiles before each sequence (prefix sums of ceil(n_s / QPT)).
+__device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* wsum) {
+  const int S = a.num_seqs, T_ = blockDim.x, t = threadIdx.x;
+  const int C = (S + T_ - 1) / T_;
+  const int s0 = min(S, t * C), s1 = min(S, s0 + C);
+  int nt = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
+    nt += (n + qpt - 1) / qpt;
+  }
+  int total;
+  int run = block_excl_scan(nt, wsum, &total);
+  for (int s = s0; s < s1; ++s) {
+    pre[s] = run;
+    const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
+    run += (n + qpt - 1) / qpt;
+  }
+  if (t == 0) pre[S] = total;
+  __syncthreads();
+  return total;
+}
+
+template <int D, int NBUF>
+__device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt, int s, int tile,
+                                            int g, int lane) {
+  constexpr int B = kExtBlock;
+  constexpr int KJ = D / 32;
+  constexpr int NT = D / 16;
+  constexpr uint32_t ROW = D * 2;
+  const int col = lane & 15, grp = lane >> 4;
+
+  const int q0 = a.q_start[s];
+  const int n = a.q_start[s + 1] - q0;
+  const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
+  const int first = tile * qpt;                 // first query of the tile
+  const int last = min(n - 1, first + qpt - 1); // last query of the tile
+  // this lane's slot: query first + col / G, head col % G
+  const int qi = first + col / G;
+  const bool row_ok = col < qpt * G && qi <= last;
+  const int p_max = L - n + last;
+  const int p_row = row_ok ? L - n + qi : p_max;  // padding slots behave like the last row
+
+  bf16x8 qop[KJ];
+  {
+    u32x4 w[KJ];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
+    if (row_ok) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                          ((size_t)(q0 + qi) * a.num_q_heads + g * G + col % G) * ROW + grp * 16;
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + kj * 64);
+    }
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
+  }
+
+  const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
+  const uint32_t koff = col * ROW + grp * 16;
+  const uint32_t voff = col * (B * 2) + grp * 8;
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 kring[NBUF][KJ];
+  u32x2 vring[NBUF][NT];
+
+  const int nblk = p_max / B + 1;  // blocks holding tokens 0 .. p_max
+  for (int c0 = 0; c0 < nblk; c0 += 64) {
+    const int cnt = min(64, nblk - c0);
+    const int tab = trow[c0 + min(lane, cnt - 1)];
+
+    auto load = [&](int i, auto slot) {
+      const size_t off = (size_t)__builtin_amdgcn_readlane(tab, i) * blk_bytes;
+      const gptr kblk = uniform_ptr(kpool + off);
+      const gptr vblk = uniform_ptr(vpool + off);
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj) kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
+    };
+
+    auto compute = [&](int i, auto slot) {
+      u32x4* kb = kring[slot];
+      u32x2* vb = vring[slot];
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
+                                                     qop[kj], sc, 0, 0, 0);
+      // sc[r]: token t0 + 4*grp + r against the row of slot col
+      const int t0 = (c0 + i) * B + 4 * grp;
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = t0 + r <= p_row ? sc[r] * a.scale_log2 : kNegInf;
+      if ((c0 + i + 1) * B > p_max + 1) {
+        // tokens past every row of the tile (including slots past the
+        // context): zero V so stale bits never reach the output
+        const uint32_t m0 = (t0 + 0 <= p_max ? 0x0000ffffu : 0u) | (t0 + 1 <= p_max ? 0xffff0000u : 0u);
+        const uint32_t m1 = (t0 + 2 <= p_max ? 0x0000ffffu : 0u) | (t0 + 3 <= p_max ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          vb[nt].x &= m0;
+          vb[nt].y &= m1;
+        }
+      }
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, swap16(bm));
+      bm = fmaxf(bm, swap32(bm));
+      if (__ballot(bm > m_ref + kSlack)) {
+        const float m_new = fmaxf(m_ref, bm);
+        const float alpha = fexp2(m_ref - m_new);
+        l_run *= alpha;
+        m_ref = m_new;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      uint32_t pb[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
+      const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
+                           static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
+      const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
+                           static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
+      const i16x4 phi = __builtin_bit_cast(
+          i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
+      const i16x4 plo = __builtin_bit_cast(
+          i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, __builtin_bit_cast(i16x4, vb[nt]),
+                                                            acc[nt], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, __builtin_bit_cast(i16x4, vb[nt]),
+                                                            acc[nt], 0, 0, 0);
+    };
+
+    block_ring<NBUF>(cnt, load, compute);
+  }
+
+  float l_tot = l_run + swap16(l_run);
+  l_tot += swap32(l_tot);
+  // acc[nt][r] holds slot 4*grp + r (query first + slot / G, head slot % G),
+  // dim nt*16 + col
+  float den[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = 4 * grp + r;
+    const int q = first + slot / G;
+    if (slot >= qpt * G || q > last) continue;
+    const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[nt][r] / den[r]);
+  }
+}
+
+template <int D, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void extend_kernel(ExtendArgs a, int G,
+                                                                             int qpt) {
+  extern __shared__ int ext_lds[];
+  int* pre = ext_lds;                 // [S + 1]
+  int* wsum = ext_lds + a.num_seqs + 1;
+  const int tiles = build_extend_plan(a, qpt, pre, wsum);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int units = tiles * a.num_kv_heads;
+  const int stride = gridDim.x * kWaves;
+  for (int u = blockIdx.x * kWaves + wave; u < units; u += stride) {
+    const int g = u % a.num_kv_heads, k = u / a.num_kv_heads;
+    // sequence holding tile k: largest s with pre[s] <= k (pre[s + 1] > k)
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    int s = lo;
+    while (pre[s + 1] <= k) ++s;  // skip sequences without queries
+    extend_tile<D, NBUF>(a, G, qpt, s, k - pre[s], g, lane);
+  }
+}
+
+int cu_count_ext() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached = n;
+  }
+  return cached;
+}
+
+template <int D>
+hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
+  const int qpt = std::max(1, 16 / G);
+  // grid: enough workgroups for every unit, at most two per CU
+  const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
+  const int grid = std::max(1, std::min(cu_count_ext() * 2, 1 << 16));
+  extend_kernel<D, kNBuf><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool extend_supported(pa_dtype dtype, int head_dim, int group, int block_size) {
+  return dtype == PA_BF16 && block_size == kExtBlock && (head_dim == 64 || head_dim == 128) &&
+         group >= 1 && group <= 16;
+}
+
+// Batches larger than kMaxPlanSeqs sequences run in slices (the plan lives
+// in LDS); q_start holds absolute row indices, so only the per-sequence
+// arrays move.
+hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream_t st) {
+  for (int32_t s0 = 0; s0 < a.num_seqs; s0 += kMaxPlanSeqs) {
+    ExtendArgs b = a;
+    b.num_seqs = std::min(kMaxPlanSeqs, a.num_seqs - s0);
+    b.q_start = a.q_start + s0;
+    b.block_tables = a.block_tables + (size_t)s0 * a.max_blocks;
+    b.context_lens = a.context_lens + s0;
+    const hipError_t e =
+        head_dim == 128 ? launch_extend_d<128>(b, group, st) : launch_extend_d<64>(b, group, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pakv

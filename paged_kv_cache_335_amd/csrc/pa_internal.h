@@ -56,6 +56,26 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
 };
 
+// Multi-token (extend / chunked prefill) attention over paged contexts.
+struct ExtendArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const void* q;               // [total_q][Hq][D] bf16
+  void* out;                   // [total_q][Hq][D] bf16
+  const int32_t* q_start;      // [S + 1] first query row of each sequence
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  float scale_log2;
+};
+
+// Supported: bf16 pools, 16-token blocks, head_dim 64 / 128, group <= 16.
+bool extend_supported(pa_dtype dtype, int head_dim, int group, int block_size);
+hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream_t stream);
+
 // Which decode kernel family handles a shape.
 enum class DecodePath { kUnsupported, kValu, kMfma, kMfma8 };
 DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size);

@@ -26,7 +26,7 @@ import torch
 
 from . import (PA_OK, PA_SWAP_IN, PA_SWAP_OUT, PagedKVError, alloc_host_pools, alloc_pools,
                pa_block_copy, pa_block_swap, pa_decode, pa_decode_partition_tokens,
-               pa_decode_workspace_bytes, pa_kv_append)
+               pa_decode_workspace_bytes, pa_extend, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -267,6 +267,22 @@ class PagedKVCache:
         scale = self.head_dim ** -0.5 if scale is None else scale
         return pa_decode(q, self.k_pool, self.v_pool, d_tables, d_lens, scale, out=out,
                          partition_tokens=partition_tokens, stream=stream)
+
+    def extend(self, seqs, n_tokens, q, k_new, v_new, out=None, scale=None, stream=None):
+        """Chunked prefill / extend: append n_tokens[i] tokens to seqs[i]
+        (slot write), then causal attention of their queries q [sum n][Hq][d]
+        over each sequence's context.  Returns out like q."""
+        stream = stream or torch.cuda.current_stream(self.device)
+        self.append(seqs, n_tokens, k_new, v_new, stream=stream)
+        tables, lens = self.bm.export(np.asarray(seqs, np.int32), self.width, pad_block=0)
+        q_start = np.concatenate([[0], np.cumsum(n_tokens)]).astype(np.int32)
+        scale = self.head_dim ** -0.5 if scale is None else scale
+        with torch.cuda.stream(stream):
+            d_tables = torch.from_numpy(tables).to(self.device)
+            d_lens = torch.from_numpy(lens).to(self.device)
+            d_qs = torch.from_numpy(q_start).to(self.device)
+            return pa_extend(q, self.k_pool, self.v_pool, d_qs, d_tables, d_lens, scale,
+                             out=out, stream=stream)
 
     def decode(self, q, out=None, scale=None, partition_tokens=0, stream=None):
         """Attention of q [S][Hq][d] (rows in table order) over every live
