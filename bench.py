@@ -42,6 +42,7 @@ def log(msg):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_cfg3_hbm_traffic.md")
 DECODE_SOURCES = ("paged_kv_cache_335_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_335_amd/csrc/pa_device.h",
                   "paged_kv_cache_335_amd/csrc/pa_internal.h")
 
 
