@@ -30,8 +30,17 @@ namespace pakv {
 namespace {
 
 constexpr int kExtBlock = 16;
+#ifndef PA_EXT_ROWS
+#define PA_EXT_ROWS 4
+#endif
+constexpr int kExtRows = PA_EXT_ROWS;  // row tiles per wave sharing each K/V load
+#ifndef PA_EXT_MIN_WG
+#define PA_EXT_MIN_WG 1
+#endif
+constexpr int kExtWgPerCu = PA_EXT_MIN_WG;  // workgroups per CU (register budget 512 / this)
 
-// Plan in LDS: tiles before each sequence (prefix sums of ceil(n_s / QPT)).
+// Plan in LDS: units before each sequence (prefix sums of ceil(n_s / qpt),
+// with qpt the queries of one unit).
 __device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* wsum) {
   const int S = a.num_seqs, T_ = blockDim.x, t = threadIdx.x;
   const int C = (S + T_ - 1) / T_;
@@ -53,7 +62,14 @@ __device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* ws
   return total;
 }
 
-template <int D, int NBUF>
+// R row tiles of one (sequence, kv head) share every K/V tile a wave
+// loads: tile rr holds queries first + rr*qpt .. + qpt - 1.  Each loaded
+// 16-token K/V tile feeds R score MFMA groups and R P.V groups, so the
+// flops per byte read from the caches grow R-fold.  Measured on 32
+// sequences x 256-token chunks (GQA 32/8, d 128): 112 TFLOP/s with one row
+// tile per wave, 186 with two (two workgroups per CU), 211 with four (one
+// workgroup per CU, accumulators in AGPRs; no spills).
+template <int D, int NBUF, int R>
 __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt, int s, int tile,
                                             int g, int lane) {
   constexpr int B = kExtBlock;
@@ -65,16 +81,21 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
   const int q0 = a.q_start[s];
   const int n = a.q_start[s + 1] - q0;
   const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
-  const int first = tile * qpt;                 // first query of the tile
-  const int last = min(n - 1, first + qpt - 1); // last query of the tile
-  // this lane's slot: query first + col / G, head col % G
-  const int qi = first + col / G;
-  const bool row_ok = col < qpt * G && qi <= last;
+  const int first = tile * R * qpt;               // first query of the row tiles
+  const int last = min(n - 1, first + R * qpt - 1);
   const int p_max = L - n + last;
-  const int p_row = row_ok ? L - n + qi : p_max;  // padding slots behave like the last row
 
-  bf16x8 qop[KJ];
-  {
+  int p_row[R];
+  bool live[R];                                    // row tile rr has a query (uniform)
+  bf16x8 qop[R][KJ];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int f = first + rr * qpt;
+    live[rr] = f <= last;
+    const int qi = f + col / G;
+    const bool row_ok = col < qpt * G && qi <= last;
+    // padding slots behave like the last row of the tiles
+    p_row[rr] = row_ok ? L - n + qi : p_max;
     u32x4 w[KJ];
 #pragma unroll
     for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
@@ -85,7 +106,7 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
       for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + kj * 64);
     }
 #pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
+    for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
   }
 
   const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
@@ -95,10 +116,15 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
   const uint32_t voff = col * (B * 2) + grp * 8;
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
 
-  float m_ref = kNegInf, l_run = 0.f;
-  f32x4 acc[NT];
+  float m_ref[R], l_run[R];
+  f32x4 acc[R][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = 0; rr < R; ++rr) {
+    m_ref[rr] = kNegInf;
+    l_run[rr] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   u32x4 kring[NBUF][KJ];
   u32x2 vring[NBUF][NT];
 
@@ -121,19 +147,10 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
     auto compute = [&](int i, auto slot) {
       u32x4* kb = kring[slot];
       u32x2* vb = vring[slot];
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
-                                                     qop[kj], sc, 0, 0, 0);
-      // sc[r]: token t0 + 4*grp + r against the row of slot col
-      const int t0 = (c0 + i) * B + 4 * grp;
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = t0 + r <= p_row ? sc[r] * a.scale_log2 : kNegInf;
+      const int t0 = (c0 + i) * B + 4 * grp;       // this lane's first token of the tile
       if ((c0 + i + 1) * B > p_max + 1) {
-        // tokens past every row of the tile (including slots past the
-        // context): zero V so stale bits never reach the output
+        // tokens past every row (including slots past the context): zero V
+        // so stale bits never reach the output
         const uint32_t m0 = (t0 + 0 <= p_max ? 0x0000ffffu : 0u) | (t0 + 1 <= p_max ? 0xffff0000u : 0u);
         const uint32_t m1 = (t0 + 2 <= p_max ? 0x0000ffffu : 0u) | (t0 + 3 <= p_max ? 0xffff0000u : 0u);
 #pragma unroll
@@ -142,76 +159,94 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
           vb[nt].y &= m1;
         }
       }
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, swap16(bm));
-      bm = fmaxf(bm, swap32(bm));
-      if (__ballot(bm > m_ref + kSlack)) {
-        const float m_new = fmaxf(m_ref, bm);
-        const float alpha = fexp2(m_ref - m_new);
-        l_run *= alpha;
-        m_ref = m_new;
-        float ar[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+      for (int rr = 0; rr < R; ++rr) {
+        if (!live[rr]) continue;
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kj = 0; kj < KJ; ++kj)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
+                                                       qop[rr][kj], sc, 0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[r] = t0 + r <= p_row[rr] ? sc[r] * a.scale_log2 : kNegInf;
+        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        bm = fmaxf(bm, swap16(bm));
+        bm = fmaxf(bm, swap32(bm));
+        if (__ballot(bm > m_ref[rr] + kSlack)) {
+          const float m_new = fmaxf(m_ref[rr], bm);
+          const float alpha = fexp2(m_ref[rr] - m_new);
+          l_run[rr] *= alpha;
+          m_ref[rr] = m_new;
+          float ar[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
+        }
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref[rr]);
+        l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
+        uint32_t pb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
+        const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
+                             static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
+        const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
+                             static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
+        const i16x4 phi = __builtin_bit_cast(
+            i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
+        const i16x4 plo = __builtin_bit_cast(
+            i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
+          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              phi, __builtin_bit_cast(i16x4, vb[nt]), acc[rr][nt], 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+        for (int nt = 0; nt < NT; ++nt)
+          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              plo, __builtin_bit_cast(i16x4, vb[nt]), acc[rr][nt], 0, 0, 0);
       }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      uint32_t pb[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
-      const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
-                           static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
-      const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
-                           static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
-      const i16x4 phi = __builtin_bit_cast(
-          i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
-      const i16x4 plo = __builtin_bit_cast(
-          i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, __builtin_bit_cast(i16x4, vb[nt]),
-                                                            acc[nt], 0, 0, 0);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, __builtin_bit_cast(i16x4, vb[nt]),
-                                                            acc[nt], 0, 0, 0);
     };
 
     block_ring<NBUF>(cnt, load, compute);
   }
 
-  float l_tot = l_run + swap16(l_run);
-  l_tot += swap32(l_tot);
-  // acc[nt][r] holds slot 4*grp + r (query first + slot / G, head slot % G),
-  // dim nt*16 + col
-  float den[4];
+  // acc[rr][nt][r] holds slot 4*grp + r of row tile rr (query first + rr*qpt
+  // + slot / G, head slot % G), dim nt*16 + col
 #pragma unroll
-  for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
+  for (int rr = 0; rr < R; ++rr) {
+    if (!live[rr]) continue;
+    float l_tot = l_run[rr] + swap16(l_run[rr]);
+    l_tot += swap32(l_tot);
+    float den[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int slot = 4 * grp + r;
-    const int q = first + slot / G;
-    if (slot >= qpt * G || q > last) continue;
-    const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
+    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[nt][r] / den[r]);
+    for (int r = 0; r < 4; ++r) {
+      const int slot = 4 * grp + r;
+      const int q = first + rr * qpt + slot / G;
+      if (slot >= qpt * G || q > last) continue;
+      const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] / den[r]);
+    }
   }
 }
 
-template <int D, int NBUF>
-__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void extend_kernel(ExtendArgs a, int G,
+template <int D, int NBUF, int R>
+__global__ __launch_bounds__(kWaves * 64, PA_EXT_MIN_WG) void extend_kernel(ExtendArgs a, int G,
                                                                              int qpt) {
   extern __shared__ int ext_lds[];
   int* pre = ext_lds;                 // [S + 1]
   int* wsum = ext_lds + a.num_seqs + 1;
-  const int tiles = build_extend_plan(a, qpt, pre, wsum);
+  // a unit is R row tiles of qpt queries each
+  const int tiles = build_extend_plan(a, R * qpt, pre, wsum);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int units = tiles * a.num_kv_heads;
@@ -226,7 +261,7 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void extend_kernel(Ext
     }
     int s = lo;
     while (pre[s + 1] <= k) ++s;  // skip sequences without queries
-    extend_tile<D, NBUF>(a, G, qpt, s, k - pre[s], g, lane);
+    extend_tile<D, NBUF, R>(a, G, qpt, s, k - pre[s], g, lane);
   }
 }
 
@@ -246,10 +281,10 @@ int cu_count_ext() {
 template <int D>
 hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   const int qpt = std::max(1, 16 / G);
-  // grid: enough workgroups for every unit, at most two per CU
+  // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
-  const int grid = std::max(1, std::min(cu_count_ext() * 2, 1 << 16));
-  extend_kernel<D, kNBuf><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
+  extend_kernel<D, kNBuf, kExtRows><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
   return hipGetLastError();
 }
 
