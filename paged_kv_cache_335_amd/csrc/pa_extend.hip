@@ -38,6 +38,14 @@ constexpr int kExtRows = PA_EXT_ROWS;  // row tiles per wave sharing each K/V lo
 #define PA_EXT_MIN_WG 1
 #endif
 constexpr int kExtWgPerCu = PA_EXT_MIN_WG;  // workgroups per CU (register budget 512 / this)
+#ifndef PA_EXT_NBUF
+#define PA_EXT_NBUF 2
+#endif
+constexpr int kExtNBuf = PA_EXT_NBUF;  // K/V tiles in the register ring (in flight: NBUF - 1)
+#ifndef PA_EXT_GROUP
+#define PA_EXT_GROUP 1
+#endif
+constexpr int kExtGroup = PA_EXT_GROUP;  // row tiles interleaved stage by stage
 
 // Plan in LDS: units before each sequence (prefix sums of ceil(n_s / qpt),
 // with qpt the queries of one unit).
@@ -69,11 +77,12 @@ __device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* ws
 // sequences x 256-token chunks (GQA 32/8, d 128): 112 TFLOP/s with one row
 // tile per wave, 186 with two (two workgroups per CU), 211 with four (one
 // workgroup per CU, accumulators in AGPRs; no spills).
-template <int D, int NBUF, int R>
+template <int D, int NBUF, int R, int RG = kExtGroup>
 __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt, int s, int tile,
                                             int g, int lane) {
   constexpr int B = kExtBlock;
   constexpr int KJ = D / 32;
+  static_assert(R % RG == 0, "row tiles come in whole groups");
   constexpr int NT = D / 16;
   constexpr uint32_t ROW = D * 2;
   const int col = lane & 15, grp = lane >> 4;
@@ -159,23 +168,40 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
           vb[nt].y &= m1;
         }
       }
+      // Row tiles advance RG at a time, stage by stage (scores, maxima, one
+      // shared rescale check, probabilities, P.V), so that their independent
+      // MFMA and VALU chains interleave; a row tile without queries computes
+      // on zero q and is never stored.
 #pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
-        if (!live[rr]) continue;
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 0; r0 < R; r0 += RG) {
+      f32x4 sc[RG];
 #pragma unroll
-        for (int kj = 0; kj < KJ; ++kj)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
-                                                       qop[rr][kj], sc, 0, 0, 0);
-        float x[4];
+      for (int rr = r0; rr < r0 + RG; ++rr) sc[rr - r0] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
+#pragma unroll
+        for (int rr = r0; rr < r0 + RG; ++rr)
+          sc[rr - r0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
+                                                           qop[rr][kj], sc[rr - r0], 0, 0, 0);
+      float x[RG][4], bm[RG];
+#pragma unroll
+      for (int rr = r0; rr < r0 + RG; ++rr) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          x[r] = t0 + r <= p_row[rr] ? sc[r] * a.scale_log2 : kNegInf;
-        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = fmaxf(bm, swap16(bm));
-        bm = fmaxf(bm, swap32(bm));
-        if (__ballot(bm > m_ref[rr] + kSlack)) {
-          const float m_new = fmaxf(m_ref[rr], bm);
+          x[rr - r0][r] = t0 + r <= p_row[rr] ? sc[rr - r0][r] * a.scale_log2 : kNegInf;
+        bm[rr - r0] = fmaxf(fmaxf(x[rr - r0][0], x[rr - r0][1]), fmaxf(x[rr - r0][2], x[rr - r0][3]));
+      }
+#pragma unroll
+      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = fmaxf(bm[rr - r0], swap16(bm[rr - r0]));
+#pragma unroll
+      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = fmaxf(bm[rr - r0], swap32(bm[rr - r0]));
+      bool grow = false;
+#pragma unroll
+      for (int rr = r0; rr < r0 + RG; ++rr) grow = grow || bm[rr - r0] > m_ref[rr] + kSlack;
+      if (__ballot(grow)) {  // rare: move the references that grew, rescale
+#pragma unroll
+        for (int rr = r0; rr < r0 + RG; ++rr) {
+          const float m_new = fmaxf(m_ref[rr], bm[rr - r0] > m_ref[rr] + kSlack ? bm[rr - r0] : m_ref[rr]);
           const float alpha = fexp2(m_ref[rr] - m_new);
           l_run[rr] *= alpha;
           m_ref[rr] = m_new;
@@ -187,9 +213,17 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
         }
+      }
+      // P.V in one 16x16x32 MFMA per dim tile: its 32-long k runs over this
+      // lane's four tokens twice, the first time with the high (truncated)
+      // bf16 part of each probability, the second time with the bf16
+      // residual, against the same four V values.
+      bf16x8 pp[RG];
+#pragma unroll
+      for (int rr = r0; rr < r0 + RG; ++rr) {
         float p[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref[rr]);
+        for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr - r0][r] - m_ref[rr]);
         l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
         uint32_t pb[4];
 #pragma unroll
@@ -198,18 +232,17 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
                              static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
         const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
                              static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
-        const i16x4 phi = __builtin_bit_cast(
-            i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
-        const i16x4 plo = __builtin_bit_cast(
-            i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+        pp[rr - r0] = __builtin_bit_cast(
+            bf16x8, u32x4{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u),
+                          __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+      }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              phi, __builtin_bit_cast(i16x4, vb[nt]), acc[rr][nt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{vb[nt].x, vb[nt].y, vb[nt].x, vb[nt].y});
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              plo, __builtin_bit_cast(i16x4, vb[nt]), acc[rr][nt], 0, 0, 0);
+        for (int rr = r0; rr < r0 + RG; ++rr)
+          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[rr - r0], vv, acc[rr][nt], 0, 0, 0);
+      }
       }
     };
 
@@ -284,7 +317,7 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
   const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
-  extend_kernel<D, kNBuf, kExtRows><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  extend_kernel<D, kExtNBuf, kExtRows><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
   return hipGetLastError();
 }
 
