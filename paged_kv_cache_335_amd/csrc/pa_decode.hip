@@ -352,30 +352,12 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
       l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      // P.V on v_mfma_f32_16x16x16_bf16: A = P (16 head slots x 16 tokens;
-      // this lane's 4 tokens are exactly its 4 scores), B = V (16 tokens x 16
-      // dims; the lane's 8-byte V^T load).  P goes in twice: its high bf16
-      // part (truncation), then the low part (p - high, rounded to nearest
-      // even), which carries P to about 16 significant bits.
-      uint32_t pb[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
-      const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
-                           static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
-      const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
-                           static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
-      const i16x4 phi = __builtin_bit_cast(
-          i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
-      const i16x4 plo = __builtin_bit_cast(
-          i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+      // P.V: A = P (16 head slots x this lane's 4 tokens, which are exactly
+      // its 4 scores), B = V (the lane's 8-byte V^T load: 4 tokens of one dim)
+      const bf16x8 pp = p_split(p);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, __builtin_bit_cast(i16x4, vb[nt]),
-                                                            acc[nt], 0, 0, 0);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, __builtin_bit_cast(i16x4, vb[nt]),
-                                                            acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[nt], 0, 0, 0);
     };
 
     block_ring<NBUF>(ntile, load, compute);
@@ -601,26 +583,11 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
       // the V scale rides on the probability: o += (p * s_v) * code
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] *= vs[r];
-      uint32_t pb[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
-      const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
-                           static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
-      const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
-                           static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
-      const i16x4 phi = __builtin_bit_cast(
-          i16x4, u32x2{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u)});
-      const i16x4 plo = __builtin_bit_cast(
-          i16x4, u32x2{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
-      i16x4 vop[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vop[nt] = __builtin_bit_cast(i16x4, e4m3x4_to_bf16(vb[nt]));
+      const bf16x8 pp = p_split(p);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vop[nt], acc[nt], 0, 0, 0);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vop[nt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(e4m3x4_to_bf16(vb[nt])),
+                                                          acc[nt], 0, 0, 0);
     };
 
     block_ring<NBUF>(ntile, load, compute);

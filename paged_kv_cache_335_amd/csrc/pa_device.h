@@ -27,6 +27,28 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// P.V on v_mfma_f32_16x16x32_bf16 with P carried to about 16 significant
+// bits: the instruction's 32-long k runs over a lane's four tokens twice.
+// In A (p_split) the first four entries are the high bf16 part of each
+// probability (truncation), the last four the residual p - high rounded to
+// nearest even; in B (v_twice) the same four V values appear twice.  A and B
+// place their entries at the same k, so the sum is (high + low) . V.
+__device__ __forceinline__ bf16x8 p_split(const float (&p)[4]) {
+  uint32_t pb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
+  const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
+                       static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
+  const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
+                       static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
+  return __builtin_bit_cast(
+      bf16x8, u32x4{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u),
+                    __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+}
+__device__ __forceinline__ bf16x8 v_twice(u32x2 v) {
+  return __builtin_bit_cast(bf16x8, u32x4{v.x, v.y, v.x, v.y});
+}
+
 // Global-memory (address space 1) byte pointer.
 typedef const uint8_t __attribute__((address_space(1)))* gptr;
 

@@ -214,10 +214,6 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
             for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
         }
       }
-      // P.V in one 16x16x32 MFMA per dim tile: its 32-long k runs over this
-      // lane's four tokens twice, the first time with the high (truncated)
-      // bf16 part of each probability, the second time with the bf16
-      // residual, against the same four V values.
       bf16x8 pp[RG];
 #pragma unroll
       for (int rr = r0; rr < r0 + RG; ++rr) {
@@ -225,20 +221,11 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr - r0][r] - m_ref[rr]);
         l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
-        uint32_t pb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pb[r] = __float_as_uint(p[r]);
-        const bf16x2 lo01 = {static_cast<__bf16>(p[0] - bf16_hi(pb[0])),
-                             static_cast<__bf16>(p[1] - bf16_hi(pb[1]))};
-        const bf16x2 lo23 = {static_cast<__bf16>(p[2] - bf16_hi(pb[2])),
-                             static_cast<__bf16>(p[3] - bf16_hi(pb[3]))};
-        pp[rr - r0] = __builtin_bit_cast(
-            bf16x8, u32x4{(pb[0] >> 16) | (pb[1] & 0xffff0000u), (pb[2] >> 16) | (pb[3] & 0xffff0000u),
-                          __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+        pp[rr - r0] = p_split(p);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 vv = __builtin_bit_cast(bf16x8, u32x4{vb[nt].x, vb[nt].y, vb[nt].x, vb[nt].y});
+        const bf16x8 vv = v_twice(vb[nt]);
 #pragma unroll
         for (int rr = r0; rr < r0 + RG; ++rr)
           acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[rr - r0], vv, acc[rr][nt], 0, 0, 0);
