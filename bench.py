@@ -7,7 +7,7 @@ context lengths lognormal (median 1024, sigma 1) clipped to [16, 8192], a
 shuffled pool sized to the blocks needed plus 10%.
 
 With --kv fp8 the same workload runs on an 8-bit cache (E4M3 codes with one
-fp32 scale per token and kv head; queries and new tokens stay bf16).
+bf16 scale per token and kv head; queries and new tokens stay bf16).
 
 One step = the whole hot path for one batch: the host block manager appends
 one token to every sequence (slots, new blocks, copy-on-write decisions), one
@@ -40,7 +40,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_cfg3_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_gqa_hbm_traffic.md")
 DECODE_SOURCES = ("paged_kv_cache_335_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_335_amd/csrc/pa_device.h",
                   "paged_kv_cache_335_amd/csrc/pa_internal.h")
@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="cfg3", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
+    ap.add_argument("--config", default="llama3_8b_gqa", choices=["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0: library)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="tokens per block (the table/tail-waste trade-off)")
@@ -269,7 +269,7 @@ def main():
         "dtype": "fp8e4m3 kv, bf16 mfma" if fp8 else "bf16", "data": "synthetic",
         "config": {
             "workload": f"{cfg.key}: {cfg.description}" + (
-                "; 8-bit cache (E4M3 + per-token fp32 scales)" if fp8 else ""),
+                "; 8-bit cache (E4M3 + per-token bf16 scales)" if fp8 else ""),
             "kv_storage": args.kv,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
             "block_size": B, "pool_blocks": num_blocks, "partition_tokens": P,

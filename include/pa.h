@@ -54,7 +54,7 @@ typedef enum {
 typedef enum {
   PA_F32 = 0,       /* IEEE fp32 elements                                        */
   PA_BF16 = 1,      /* bf16 elements                                             */
-  PA_FP8_E4M3 = 2   /* 8-bit cache: OCP E4M3 codes + one fp32 scale per token    */
+  PA_FP8_E4M3 = 2   /* 8-bit cache: OCP E4M3 codes + one bf16 scale per token    */
 } pa_dtype;
 
 /*

@@ -68,7 +68,7 @@ def _dtype_code(arr):
         return F32
     if arr.dtype == np.uint16:  # bf16 bit patterns
         return BF16
-    if arr.dtype == np.uint8:  # 8-bit regions: E4M3 codes then per-token fp32 scales
+    if arr.dtype == np.uint8:  # 8-bit regions: E4M3 codes (K: then per-token bf16 scales)
         return FP8
     raise TypeError(f"pool dtype must be float32, uint16 (bf16 bits) or uint8 (8-bit "
                     f"regions), got {arr.dtype}")

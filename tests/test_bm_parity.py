@@ -106,7 +106,7 @@ def test_exhaustion_leaves_state_unchanged():
     assert_same_state(c, m)
 
 
-@pytest.mark.parametrize("key", ["cfg4", "cfg4cow"])
+@pytest.mark.parametrize("key", ["prefix_sharing", "prefix_sharing_cow"])
 def test_prefix_sharing_workload_matches(key):
     """64 prompts fanned out to 4 samples, then each sample's private tokens:
     with a partly filled shared tail every sample but the last copies it

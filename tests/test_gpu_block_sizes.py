@@ -30,13 +30,13 @@ def pk():
 
 def _small(key, B, dtype):
     base = {
-        "cfg2": dict(num_seqs=6, lengths=("uniform", 128, 700), pool=("fixed", 512 * 16 // B),
+        "llama2_7b_mha": dict(num_seqs=6, lengths=("uniform", 128, 700), pool=("fixed", 512 * 16 // B),
                      table_width=48 * 16 // B),
-        "cfg3": dict(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
+        "llama3_8b_gqa": dict(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
                      table_width=128 * 16 // B),
-        "cfg4": dict(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
+        "prefix_sharing": dict(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
                      table_width=9 * 16 // B + 1),
-        "cfg5": dict(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512 * 16 // B),
+        "long_context_128k": dict(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512 * 16 // B),
                      table_width=256 * 16 // B),
     }[key]
     return CONFIGS[key].scaled(block_size=B, dtype=dtype, **base)
@@ -44,7 +44,7 @@ def _small(key, B, dtype):
 
 @pytest.mark.parametrize("B", [8, 32])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("key", ["cfg2", "cfg3", "cfg4", "cfg5"])
+@pytest.mark.parametrize("key", ["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"])
 def test_decode_block_sizes_all_elements(pk, key, dtype, B):
     cfg = _small(key, B, dtype)
     c = decode_case(cfg, payload="numpy", device="cuda")
@@ -63,7 +63,7 @@ def test_decode_block_sizes_odd_lengths_and_groups(pk, B):
     """Lengths around tile and block edges (a tile of 8-token blocks can end
     mid-range), group sizes 1 and 16."""
     for G, d in ((1, 128), (16, 64)):
-        cfg = CONFIGS["cfg3"].scaled(num_seqs=12, num_q_heads=2 * G, num_kv_heads=2, head_dim=d,
+        cfg = CONFIGS["llama3_8b_gqa"].scaled(num_seqs=12, num_q_heads=2 * G, num_kv_heads=2, head_dim=d,
                                      block_size=B, lengths=("uniform", 1, 300),
                                      table_width=300 // B + 2, seed=40 + B + G)
         c = decode_case(cfg, payload="numpy", device="cuda")

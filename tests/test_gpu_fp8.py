@@ -53,13 +53,13 @@ def _check(got, ref, what):
 
 
 SMALL = {
-    "cfg2": CONFIGS["cfg2"].scaled(num_seqs=6, lengths=("uniform", 128, 700),
+    "llama2_7b_mha": CONFIGS["llama2_7b_mha"].scaled(num_seqs=6, lengths=("uniform", 128, 700),
                                    pool=("fixed", 512), table_width=48, dtype="fp8"),
-    "cfg3": CONFIGS["cfg3"].scaled(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
+    "llama3_8b_gqa": CONFIGS["llama3_8b_gqa"].scaled(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
                                    table_width=128, dtype="fp8"),
-    "cfg4": CONFIGS["cfg4"].scaled(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
+    "prefix_sharing": CONFIGS["prefix_sharing"].scaled(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
                                    table_width=9, dtype="fp8"),
-    "cfg5": CONFIGS["cfg5"].scaled(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512),
+    "long_context_128k": CONFIGS["long_context_128k"].scaled(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512),
                                    table_width=256, dtype="fp8"),
 }
 
@@ -103,7 +103,7 @@ def test_fp8_decode_group_sizes_and_head_dims(pk, G, d):
 def test_fp8_nan_codes_and_scales_in_unused_slots_never_reach_output(pk):
     """Dead slots hold NaN codes (0x7F) and NaN scales: masked tokens must
     contribute exactly nothing."""
-    cfg = SMALL["cfg3"]
+    cfg = SMALL["llama3_8b_gqa"]
     c = decode_case(cfg, payload="numpy", device="cuda")
     ref = oracle.decode(*c.oracle_inputs(), c.scale)
     B, d = cfg.block_size, cfg.head_dim
@@ -117,7 +117,7 @@ def test_fp8_nan_codes_and_scales_in_unused_slots_never_reach_output(pk):
 
 
 def test_fp8_decode_deterministic(pk):
-    c = decode_case(SMALL["cfg3"], payload="numpy", device="cuda")
+    c = decode_case(SMALL["llama3_8b_gqa"], payload="numpy", device="cuda")
     a = _decode(pk, c, 64).clone()
     assert torch.equal(a, _decode(pk, c, 64))
 
@@ -214,15 +214,15 @@ def test_fp8_decode_full_size_all_outputs(pk):
     """The 256-sequence GQA workload with an 8-bit cache at full size, in the
     benchmark's launch configuration: every output against the oracle, and a
     second call bit-identical."""
-    cfg = CONFIGS["cfg3"].scaled(dtype="fp8")
-    _log("fp8 cfg3: generating on the GPU")
+    cfg = CONFIGS["llama3_8b_gqa"].scaled(dtype="fp8")
+    _log("fp8 llama3_8b_gqa: generating on the GPU")
     c = decode_case(cfg, payload="torch", device="cuda")
     got = _decode(pk, c).clone()
     assert torch.equal(got, _decode(pk, c))
     S, Hq = cfg.num_seqs, cfg.num_q_heads
     pairs = np.array([[s, h] for s in range(S) for h in range(Hq)], np.int32)
-    _log(f"fp8 cfg3: copying pools to the host for all {len(pairs)} outputs")
+    _log(f"fp8 llama3_8b_gqa: copying pools to the host for all {len(pairs)} outputs")
     ref = oracle.decode_pairs(*c.oracle_inputs(), c.scale, pairs)
-    _check(_to64(got)[pairs[:, 0], pairs[:, 1]], ref, "fp8 cfg3 full size, all outputs")
+    _check(_to64(got)[pairs[:, 0], pairs[:, 1]], ref, "fp8 llama3_8b_gqa full size, all outputs")
     del c
     torch.cuda.empty_cache()

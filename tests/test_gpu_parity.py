@@ -54,16 +54,16 @@ def _check(got, ref, dtype, what):
 
 # --- reduced-size configs, every output element -----------------------------
 SMALL = {
-    "cfg1": CONFIGS["cfg1"],
-    "cfg2": CONFIGS["cfg2"].scaled(num_seqs=6, lengths=("uniform", 128, 700), pool=("fixed", 512),
+    "tiny_f32": CONFIGS["tiny_f32"],
+    "llama2_7b_mha": CONFIGS["llama2_7b_mha"].scaled(num_seqs=6, lengths=("uniform", 128, 700), pool=("fixed", 512),
                                    table_width=48),
-    "cfg3": CONFIGS["cfg3"].scaled(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
+    "llama3_8b_gqa": CONFIGS["llama3_8b_gqa"].scaled(num_seqs=24, lengths=("lognormal", 256, 1.0, 16, 2048),
                                    table_width=128),
-    "cfg4": CONFIGS["cfg4"].scaled(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
+    "prefix_sharing": CONFIGS["prefix_sharing"].scaled(num_seqs=16, prompts=4, lengths=("shared", 96, 1, 40),
                                    table_width=9),
-    "cfg4cow": CONFIGS["cfg4cow"].scaled(num_seqs=16, prompts=4, lengths=("shared", 104, 1, 40),
+    "prefix_sharing_cow": CONFIGS["prefix_sharing_cow"].scaled(num_seqs=16, prompts=4, lengths=("shared", 104, 1, 40),
                                          table_width=10),
-    "cfg5": CONFIGS["cfg5"].scaled(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512),
+    "long_context_128k": CONFIGS["long_context_128k"].scaled(num_seqs=2, lengths=("fixed", 4096), pool=("fixed", 512),
                                    table_width=256),
 }
 
@@ -114,7 +114,7 @@ def test_decode_group_sizes_and_head_dims(pk, G, d):
 
 def test_decode_fp32_group_sizes(pk):
     for G in (1, 2, 4):
-        cfg = CONFIGS["cfg1"].scaled(num_seqs=5, num_q_heads=G, num_kv_heads=1, head_dim=128,
+        cfg = CONFIGS["tiny_f32"].scaled(num_seqs=5, num_q_heads=G, num_kv_heads=1, head_dim=128,
                                      lengths=("uniform", 1, 200), pool=("fixed", 80),
                                      table_width=16, seed=30 + G, key="f32g")
         c = decode_case(cfg, payload="numpy", device="cuda")
@@ -124,7 +124,7 @@ def test_decode_fp32_group_sizes(pk):
 
 
 def test_nan_in_unused_tail_slots_never_reaches_output(pk):
-    cfg = SMALL["cfg3"]
+    cfg = SMALL["llama3_8b_gqa"]
     c = decode_case(cfg, payload="numpy", device="cuda")
     ref = oracle.decode(*c.oracle_inputs(), c.scale)
     dead = torch.from_numpy(~c.live).cuda()
@@ -136,7 +136,7 @@ def test_nan_in_unused_tail_slots_never_reaches_output(pk):
 def test_deterministic_and_placement_invariant(pk):
     """Same inputs twice: identical bits.  Same logical data moved to other
     physical blocks (tables renumbered): identical bits."""
-    cfg = SMALL["cfg3"]
+    cfg = SMALL["llama3_8b_gqa"]
     c = decode_case(cfg, payload="numpy", device="cuda")
     a = _gpu_decode(pk, c, 64).clone()
     b = _gpu_decode(pk, c, 64)
@@ -182,7 +182,7 @@ def test_decode_batch_beyond_one_launch(pk):
 
 
 # --- full-size configs: every output ------------------------------------------
-FULL = ["cfg2", "cfg3", "cfg4", "cfg5"]
+FULL = ["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"]
 
 
 @pytest.mark.slow
@@ -427,7 +427,7 @@ def test_full_path_fp8_cache_with_copy_on_write(pk):
 
 # --- error paths ---------------------------------------------------------------
 def test_debug_validation_rejects_bad_device_indices(pk, monkeypatch):
-    cfg = SMALL["cfg3"]
+    cfg = SMALL["llama3_8b_gqa"]
     c = decode_case(cfg, payload="numpy", device="cuda")
     monkeypatch.setenv("PA_DEBUG", "1")
     bad = c.context_lens.clone()

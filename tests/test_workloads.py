@@ -9,7 +9,7 @@ from workloads.gen import to_numpy_storage
 
 
 def test_same_seed_same_bytes():
-    cfg = CONFIGS["cfg3"].scaled(num_seqs=8, lengths=("lognormal", 128, 1.0, 16, 512),
+    cfg = CONFIGS["llama3_8b_gqa"].scaled(num_seqs=8, lengths=("lognormal", 128, 1.0, 16, 512),
                                  table_width=32)
     a, b = decode_case(cfg), decode_case(cfg)
     for x, y in zip(a.oracle_inputs(), b.oracle_inputs()):
@@ -18,7 +18,7 @@ def test_same_seed_same_bytes():
     assert not np.array_equal(a.oracle_inputs()[2], c.oracle_inputs()[2])
 
 
-@pytest.mark.parametrize("key", ["cfg1", "cfg2", "cfg3", "cfg4", "cfg4cow", "cfg5"])
+@pytest.mark.parametrize("key", ["tiny_f32", "llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "prefix_sharing_cow", "long_context_128k"])
 def test_full_size_structure(key):
     cfg = CONFIGS[key]
     lens, nb, tables, live = decode_structure(cfg)
@@ -31,14 +31,14 @@ def test_full_size_structure(key):
         used = np.concatenate([tables[s, :nblk[s]] for s in range(cfg.num_seqs)])
         assert len(np.unique(used)) == len(used)       # no block used twice
     assert live.sum() == (lens.sum() if cfg.lengths[0] != "shared" else live.sum())
-    if key == "cfg5":
+    if key == "long_context_128k":
         assert nb == 32768 and lens.sum() == 4 * 131072 and live.all()
-    if key == "cfg3":
+    if key == "llama3_8b_gqa":
         assert lens.min() >= 16 and lens.max() <= 8192
         assert nb == int(np.ceil(1.1 * nblk.sum()))
-    if key == "cfg2":
+    if key == "llama2_7b_mha":
         assert nb == 16384 and lens.min() >= 128 and lens.max() <= 2048
-    if key.startswith("cfg4"):
+    if key.startswith("prefix_sharing"):
         shared = cfg.lengths[1] // B
         for p in range(cfg.prompts):
             rows = tables[p * cfg.samples:(p + 1) * cfg.samples, :shared]
@@ -46,7 +46,7 @@ def test_full_size_structure(key):
 
 
 def test_poison_fills_exactly_the_dead_slots():
-    cfg = CONFIGS["cfg1"]
+    cfg = CONFIGS["tiny_f32"]
     c = decode_case(cfg)
     k, v = to_numpy_storage(c.k_pool), to_numpy_storage(c.v_pool)
     dead = ~c.live

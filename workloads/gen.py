@@ -280,7 +280,7 @@ def build_tables(cfg: Config, lens: np.ndarray, perm: np.ndarray):
     for s in range(S):
         n = int(nblk[s])
         tables[s, n:] = pad if pad is not None else tables[s, 0]
-    if cfg.key == "cfg1":
+    if cfg.key == "tiny_f32":
         # the tiny config's tables are consecutive chunks of one permutation
         # of the whole pool; entries past a sequence's blocks are its padding
         tables = perm[: S * W].reshape(S, W).astype(np.int32)
