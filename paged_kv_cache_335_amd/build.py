@@ -26,6 +26,11 @@ HIPCC_FLAGS = [
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Extra hipcc flags per source.  pa_extend.hip: MFMAs in the VGPR form.  Its
+# accumulators need more registers than the 256 VGPRs leave; in the AGPR
+# form the compiler copied every accumulator out to VGPRs and back around
+# each K/V block (for the softmax rescale), which doubled the VALU work.
+SOURCE_FLAGS = {"pa_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 
 
@@ -51,8 +56,9 @@ def build(verbose: bool = False) -> str:
     jobs = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+        jobs.append([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in C_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")

@@ -333,8 +333,8 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
         }
       }
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, swap16(bm));
-      bm = fmaxf(bm, swap32(bm));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
       if (__ballot(bm > m_ref + kSlack)) {  // rare: move the reference, rescale
         const float m_new = fmaxf(m_ref, bm);
         const float alpha = fexp2(m_ref - m_new);
@@ -364,8 +364,8 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
   }
 
   // l over the four lane groups holding the same head; m_ref is uniform
-  float l_tot = l_run + swap16(l_run);
-  l_tot += swap32(l_tot);
+  float l_tot = sum_xor16(l_run);
+  l_tot = sum_xor32(l_tot);
   finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
 }
 
@@ -561,8 +561,8 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
         for (int nt = 0; nt < NT; ++nt) vb[nt] &= m;
       }
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, swap16(bm));
-      bm = fmaxf(bm, swap32(bm));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
       if (__ballot(bm > m_ref + kSlack)) {
         const float m_new = fmaxf(m_ref, bm);
         const float alpha = fexp2(m_ref - m_new);
@@ -593,8 +593,8 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
     block_ring<NBUF>(ntile, load, compute);
   }
 
-  float l_tot = l_run + swap16(l_run);
-  l_tot += swap32(l_tot);
+  float l_tot = sum_xor16(l_run);
+  l_tot = sum_xor32(l_tot);
   finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
 }
 
@@ -737,8 +737,8 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
       for (int h = 0; h < G; ++h) {
         bm[h] = fmaxf(sc[h], dpp<kRowRor4>(sc[h]));
         bm[h] = fmaxf(bm[h], dpp<kRowRor8>(bm[h]));
-        bm[h] = fmaxf(bm[h], swap16(bm[h]));
-        bm[h] = fmaxf(bm[h], swap32(bm[h]));
+        bm[h] = max_xor16(bm[h]);
+        bm[h] = max_xor32(bm[h]);
         move |= bm[h] > m_ref[h] + kSlack;
       }
       if (__ballot(move)) {  // rare: move the references, rescale

@@ -102,14 +102,28 @@ constexpr int kQuadXor2 = 0x4E;
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
-// Lane i <-> lane i^16 (ds_swizzle bit mode: and 0x1F, xor 0x10).
-__device__ __forceinline__ float swap16(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+// Reductions across the four 16-lane rows of a wave, on the VALU.
+// v_permlane32_swap(x, x) returns x with rows {2,3} replaced by rows {0,1}
+// and x with rows {0,1} replaced by rows {2,3}: in every lane the pair is
+// x[i] and x[i ^ 32] in some order.  v_permlane16_swap(x, x) does the same
+// for odd and even rows: x[i] and x[i ^ 16].  Max and sum are symmetric, so
+// combining the pair reduces over the partner lane.  (An exchange through
+// the LDS unit would wait behind every LDS access in flight.)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-// Lane i <-> lane i^32.
-__device__ __forceinline__ float swap32(float x) {
-  const int lane = __lane_id();
-  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(x)));
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 __device__ __forceinline__ float lane_bcast(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
@@ -119,16 +133,14 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kQuadXor2>(x));
   x = fmaxf(x, dpp<kRowRor4>(x));
   x = fmaxf(x, dpp<kRowRor8>(x));
-  x = fmaxf(x, swap16(x));
-  return fmaxf(x, swap32(x));
+  return max_xor32(max_xor16(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
   x += dpp<kQuadXor1>(x);
   x += dpp<kQuadXor2>(x);
   x += dpp<kRowRor4>(x);
   x += dpp<kRowRor8>(x);
-  x += swap16(x);
-  return x + swap32(x);
+  return sum_xor32(sum_xor16(x));
 }
 
 template <typename T>

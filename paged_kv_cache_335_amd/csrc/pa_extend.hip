@@ -46,6 +46,14 @@ constexpr int kExtNBuf = PA_EXT_NBUF;  // K/V tiles in the register ring (in fli
 #define PA_EXT_GROUP 1
 #endif
 constexpr int kExtGroup = PA_EXT_GROUP;  // row tiles interleaved stage by stage
+#ifndef PA_EXT_WG
+#define PA_EXT_WG 1
+#endif
+#ifndef PA_EXT_PREFETCH
+#define PA_EXT_PREFETCH 2
+#endif
+constexpr int kExtPrefetch = PA_EXT_PREFETCH;  // blocks in flight per workgroup (shared K/V)
+constexpr int kExtTabWindow = 1024;             // table entries staged in LDS at a time
 
 // Plan in LDS: units before each sequence (prefix sums of ceil(n_s / qpt),
 // with qpt the queries of one unit).
@@ -192,9 +200,9 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
         bm[rr - r0] = fmaxf(fmaxf(x[rr - r0][0], x[rr - r0][1]), fmaxf(x[rr - r0][2], x[rr - r0][3]));
       }
 #pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = fmaxf(bm[rr - r0], swap16(bm[rr - r0]));
+      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = max_xor16(bm[rr - r0]);
 #pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = fmaxf(bm[rr - r0], swap32(bm[rr - r0]));
+      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = max_xor32(bm[rr - r0]);
       bool grow = false;
 #pragma unroll
       for (int rr = r0; rr < r0 + RG; ++rr) grow = grow || bm[rr - r0] > m_ref[rr] + kSlack;
@@ -241,8 +249,8 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (!live[rr]) continue;
-    float l_tot = l_run[rr] + swap16(l_run[rr]);
-    l_tot += swap32(l_tot);
+    float l_tot = sum_xor16(l_run[rr]);
+    l_tot = sum_xor32(l_tot);
     float den[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
@@ -256,6 +264,254 @@ __device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt,
       for (int nt = 0; nt < NT; ++nt)
         static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] / den[r]);
     }
+  }
+}
+
+// Workgroup-shared K/V: the four waves of a workgroup take 4R row tiles of
+// the same (sequence, kv head), and each 16-token K/V tile is loaded once
+// per workgroup into LDS (every thread fetches 16-byte chunks of it) and read
+// by all four waves, so one load feeds 4R row tiles.  Global loads run NPF
+// blocks ahead in a small per-thread register ring; LDS holds two tiles, so
+// one barrier per block separates the store of tile i + 1 from its readers
+// and the readers of tile i - 1 from its overwrite.
+template <int D>
+struct WgTile {
+  static constexpr int kStrideK = D * 2 + 16;   // padded K row: 16 lanes of a 16-byte read hit 64 banks
+  static constexpr int kBytesK = 16 * kStrideK;
+  static constexpr int kBytesV = D * 32;        // V as [dim tile][token quad][dim][4 tokens]
+  static constexpr int kBytes = kBytesK + kBytesV;
+  // each thread fetches one chunk of K and one of V: 32 D / 256 bytes each
+  static constexpr int kChunk = D * 32 / (kWaves * 64);
+  static_assert(kChunk == 8 || kChunk == 16, "8- or 16-byte chunks");
+};
+
+template <int D, int R, int NPF>
+__device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int qpt, int s, int unit,
+                                               int g, int wave, int lane, uint8_t* lds, int* tab) {
+  using T = WgTile<D>;
+  constexpr int B = kExtBlock;
+  constexpr int KJ = D / 32;
+  constexpr int NT = D / 16;
+  constexpr uint32_t ROW = D * 2;
+  const int col = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x;
+
+  const int q0 = a.q_start[s];
+  const int n = a.q_start[s + 1] - q0;
+  const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
+  const int ufirst = unit * kWaves * R * qpt;      // first query of the workgroup's row tiles
+  const int ulast = min(n - 1, ufirst + kWaves * R * qpt - 1);
+  const int p_max = L - n + ulast;                 // furthest position any row attends
+  const int first = ufirst + wave * R * qpt;       // this wave's first query
+  const int last = min(ulast, first + R * qpt - 1);
+
+  int p_row[R];
+  bool live[R];
+  bf16x8 qop[R][KJ];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int f = first + rr * qpt;
+    live[rr] = f <= last;
+    const int qi = f + col / G;
+    const bool row_ok = col < qpt * G && qi <= last;
+    p_row[rr] = row_ok ? L - n + qi : p_max;       // padding slots: harmless finite rows
+    u32x4 w[KJ];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
+    if (row_ok) {
+      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                          ((size_t)(q0 + qi) * a.num_q_heads + g * G + col % G) * ROW + grp * 16;
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + kj * 64);
+    }
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
+  }
+
+  // this thread's chunks: global byte offsets inside a block and LDS offsets
+  const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
+  // this thread's chunks: byte offset inside the K (and V) tile of a block,
+  // and LDS offsets.  A 16-byte V chunk is 8 tokens of one dim: two 4-token
+  // quads, stored 128 bytes apart; an 8-byte chunk is one quad.
+  constexpr int CB = T::kChunk;
+  const uint32_t goff = tid * CB;
+  const uint32_t lk = (goff / ROW) * T::kStrideK + goff % ROW;
+  const int vdim = goff / 32, vquad = (goff % 32) / 8;
+  const uint32_t lv = T::kBytesK + (vdim >> 4) * 512 + vquad * 128 + (vdim & 15) * 8;
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+  // blocks holding tokens 0 .. p_max (at least one, so that lengths shorter
+  // than the query count, which the caller must not pass, still read in bounds)
+  const int nblk = max(1, p_max / B + 1);
+
+  // Block ids come from a window of the table row staged in LDS: a table
+  // read from global memory would be counted with the K/V loads, and
+  // waiting for it would drain every K/V load in flight.
+  using Chunk = std::conditional_t<CB == 16, u32x4, u32x2>;
+  Chunk kring[NPF], vring[NPF];
+  int cn = 1;                                      // blocks in the current window
+  auto gload = [&](int i, auto slot) {
+    const size_t off = (size_t)tab[min(i, cn - 1)] * blk_bytes + goff;
+    kring[slot] = *reinterpret_cast<const Chunk*>(kpool + off);
+    vring[slot] = *reinterpret_cast<const Chunk*>(vpool + off);
+  };
+  auto lstore = [&](auto slot, int buf) {
+    uint8_t* t = lds + buf * T::kBytes;
+    *reinterpret_cast<Chunk*>(t + lk) = kring[slot];
+    if constexpr (CB == 16) {
+      *reinterpret_cast<u32x2*>(t + lv) = u32x2{vring[slot].x, vring[slot].y};
+      *reinterpret_cast<u32x2*>(t + lv + 128) = u32x2{vring[slot].z, vring[slot].w};
+    } else {
+      *reinterpret_cast<u32x2*>(t + lv) = vring[slot];
+    }
+  };
+
+  float m_ref[R], l_run[R];
+  f32x4 acc[R][NT];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    m_ref[rr] = kNegInf;
+    l_run[rr] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int i, int buf) {
+    const uint8_t* t = lds + buf * T::kBytes;
+    u32x4 kb[KJ];
+    u32x2 vb[NT];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj)
+      kb[kj] = *reinterpret_cast<const u32x4*>(t + col * T::kStrideK + kj * 64 + grp * 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      vb[nt] = *reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8);
+    const int t0 = i * B + 4 * grp;                // this lane's first token of the tile
+    // tokens past every row (and slots past the context) get zero V, so stale
+    // bits never reach the output
+    const uint32_t m0 = (t0 + 0 <= p_max ? 0x0000ffffu : 0u) | (t0 + 1 <= p_max ? 0xffff0000u : 0u);
+    const uint32_t m1 = (t0 + 2 <= p_max ? 0x0000ffffu : 0u) | (t0 + 3 <= p_max ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      vb[nt].x &= m0;
+      vb[nt].y &= m1;
+    }
+    f32x4 sc[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      sc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
+        sc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
+                                                         qop[rr][kj], sc[rr], 0, 0, 0);
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = t0 + r <= p_row[rr] ? sc[rr][r] * a.scale_log2 : kNegInf;
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
+      if (__ballot(bm > m_ref[rr] + kSlack)) {     // rare: move the reference, rescale
+        const float m_new = fmaxf(m_ref[rr], bm > m_ref[rr] + kSlack ? bm : m_ref[rr]);
+        const float alpha = fexp2(m_ref[rr] - m_new);
+        l_run[rr] *= alpha;
+        m_ref[rr] = m_new;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref[rr]);
+      l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
+      const bf16x8 pp = p_split(p);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[rr][nt], 0, 0, 0);
+    }
+  };
+
+  for (int w0 = 0; w0 < nblk; w0 += kExtTabWindow) {
+    cn = min(kExtTabWindow, nblk - w0);
+    for (int e = tid; e < cn; e += kWaves * 64) tab[e] = trow[w0 + e];
+    __syncthreads();
+    // prologue: the window's blocks 0 .. NPF - 1 in flight, block 0 staged
+    static_for<NPF>([&](auto j) { gload(j, j); });
+    lstore(std::integral_constant<int, 0>{}, 0);
+    gload(NPF, std::integral_constant<int, 0>{});
+    __syncthreads();
+    // block i of the window is in LDS buffer i & 1 and block i + 1 in ring
+    // slot (i + 1) % NPF.  Steps run in whole groups of NPF without a
+    // branch (so the compiler counts the loads in flight exactly): loads
+    // past the window's last block re-read it, and a step past it computes
+    // on that block with every token beyond p_max, so its scores are masked
+    // and its V is zeroed.  The barrier closing each step also guards the
+    // reuse of both buffers and of the table window.
+    for (int i0 = 0; i0 < cn; i0 += NPF) {
+      static_for<NPF>([&](auto j) {
+        const int i = i0 + j;
+        constexpr int nxt = (j + 1) % NPF;
+        compute(w0 + i, i & 1);
+        lstore(std::integral_constant<int, nxt>{}, (i + 1) & 1);
+        gload(i + 1 + NPF, std::integral_constant<int, nxt>{});
+        __syncthreads();
+      });
+    }
+  }
+
+  // acc[rr][nt][r] holds slot 4*grp + r of row tile rr (query first + rr*qpt
+  // + slot / G, head slot % G), dim nt*16 + col
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (!live[rr]) continue;
+    float l_tot = sum_xor16(l_run[rr]);
+    l_tot = sum_xor32(l_tot);
+    float den[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int slot = 4 * grp + r;
+      const int q = first + rr * qpt + slot / G;
+      if (slot >= qpt * G || q > last) continue;
+      const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] / den[r]);
+    }
+  }
+}
+
+template <int D, int R, int NPF>
+__global__ __launch_bounds__(kWaves * 64, 1) void extend_wg_kernel(ExtendArgs a, int G, int qpt) {
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * WgTile<D>::kBytes];
+  __shared__ int tab_lds[kExtTabWindow];
+  extern __shared__ int ext_lds[];
+  int* pre = ext_lds;                 // [S + 1]
+  int* wsum = ext_lds + a.num_seqs + 1;
+  // a unit is the workgroup's 4R row tiles of qpt queries each
+  const int tiles = build_extend_plan(a, kWaves * R * qpt, pre, wsum);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int units = tiles * a.num_kv_heads;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    const int g = u % a.num_kv_heads, k = u / a.num_kv_heads;
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    int s = lo;
+    while (pre[s + 1] <= k) ++s;  // skip sequences without queries
+    s = __builtin_amdgcn_readfirstlane(s);
+    extend_wg_unit<D, R, NPF>(a, G, qpt, s, k - pre[s], g, wave, lane, kv_lds, tab_lds);
   }
 }
 
@@ -304,7 +560,11 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
   const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
+#if PA_EXT_WG
+  extend_wg_kernel<D, kExtRows, kExtPrefetch><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+#else
   extend_kernel<D, kExtNBuf, kExtRows><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+#endif
   return hipGetLastError();
 }
 
