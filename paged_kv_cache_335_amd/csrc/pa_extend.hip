@@ -15,13 +15,14 @@
 //
 // Decomposition: the 16 "head slots" of the decode kernel's MFMA tiles hold
 // (query, head) pairs here: a row tile is QPT = 16 / G consecutive queries
-// of one sequence times the G query heads of one kv head.  Each wave takes
-// row tiles in turn (tile k, kv head g), streams blocks 0 .. p_max of the
-// sequence through the same register ring, and masks each row at its own
-// position.  Consecutive waves take the kv heads of one tile, so a
-// workgroup reads adjacent regions of the same blocks together.  No
-// context split: every row tile finishes in place.
+// of one sequence times the G query heads of one kv head.  A workgroup's
+// four waves take 4R consecutive row tiles of one (sequence, kv head) and
+// stream blocks 0 .. p_max of the sequence: each 16-token K/V tile is
+// loaded once per workgroup into LDS and read by all four waves, and each
+// wave masks its rows at their own positions.  No context split: every row
+// tile finishes in place.
 #include <algorithm>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -30,29 +31,24 @@ namespace pakv {
 namespace {
 
 constexpr int kExtBlock = 16;
+// Tuning (measured on 32 sequences x 256-token chunks, GQA 32/8, d 128):
+// two row tiles per wave and two workgroups per CU (two waves per SIMD, so
+// one wave's MFMAs hide the other's softmax) ran at 458-479 TFLOP/s; four
+// row tiles at one workgroup per CU at 332-337, one row tile at four
+// workgroups per CU at 438.  One block in flight beyond the staged one was
+// best at two workgroups per CU (a deeper ring spills).
 #ifndef PA_EXT_ROWS
-#define PA_EXT_ROWS 4
+#define PA_EXT_ROWS 2
 #endif
-constexpr int kExtRows = PA_EXT_ROWS;  // row tiles per wave sharing each K/V load
+constexpr int kExtRows = PA_EXT_ROWS;  // row tiles per wave
 #ifndef PA_EXT_MIN_WG
-#define PA_EXT_MIN_WG 1
+#define PA_EXT_MIN_WG 2
 #endif
 constexpr int kExtWgPerCu = PA_EXT_MIN_WG;  // workgroups per CU (register budget 512 / this)
-#ifndef PA_EXT_NBUF
-#define PA_EXT_NBUF 2
-#endif
-constexpr int kExtNBuf = PA_EXT_NBUF;  // K/V tiles in the register ring (in flight: NBUF - 1)
-#ifndef PA_EXT_GROUP
-#define PA_EXT_GROUP 1
-#endif
-constexpr int kExtGroup = PA_EXT_GROUP;  // row tiles interleaved stage by stage
-#ifndef PA_EXT_WG
-#define PA_EXT_WG 1
-#endif
 #ifndef PA_EXT_PREFETCH
-#define PA_EXT_PREFETCH 2
+#define PA_EXT_PREFETCH 1
 #endif
-constexpr int kExtPrefetch = PA_EXT_PREFETCH;  // blocks in flight per workgroup (shared K/V)
+constexpr int kExtPrefetch = PA_EXT_PREFETCH;  // blocks in flight beyond the staged one
 constexpr int kExtTabWindow = 1024;             // table entries staged in LDS at a time
 
 // Plan in LDS: units before each sequence (prefix sums of ceil(n_s / qpt),
@@ -78,202 +74,14 @@ __device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* ws
   return total;
 }
 
-// R row tiles of one (sequence, kv head) share every K/V tile a wave
-// loads: tile rr holds queries first + rr*qpt .. + qpt - 1.  Each loaded
-// 16-token K/V tile feeds R score MFMA groups and R P.V groups, so the
-// flops per byte read from the caches grow R-fold.  Measured on 32
-// sequences x 256-token chunks (GQA 32/8, d 128): 112 TFLOP/s with one row
-// tile per wave, 186 with two (two workgroups per CU), 211 with four (one
-// workgroup per CU, accumulators in AGPRs; no spills).
-template <int D, int NBUF, int R, int RG = kExtGroup>
-__device__ __forceinline__ void extend_tile(const ExtendArgs& a, int G, int qpt, int s, int tile,
-                                            int g, int lane) {
-  constexpr int B = kExtBlock;
-  constexpr int KJ = D / 32;
-  static_assert(R % RG == 0, "row tiles come in whole groups");
-  constexpr int NT = D / 16;
-  constexpr uint32_t ROW = D * 2;
-  const int col = lane & 15, grp = lane >> 4;
-
-  const int q0 = a.q_start[s];
-  const int n = a.q_start[s + 1] - q0;
-  const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
-  const int first = tile * R * qpt;               // first query of the row tiles
-  const int last = min(n - 1, first + R * qpt - 1);
-  const int p_max = L - n + last;
-
-  int p_row[R];
-  bool live[R];                                    // row tile rr has a query (uniform)
-  bf16x8 qop[R][KJ];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int f = first + rr * qpt;
-    live[rr] = f <= last;
-    const int qi = f + col / G;
-    const bool row_ok = col < qpt * G && qi <= last;
-    // padding slots behave like the last row of the tiles
-    p_row[rr] = row_ok ? L - n + qi : p_max;
-    u32x4 w[KJ];
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
-    if (row_ok) {
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                          ((size_t)(q0 + qi) * a.num_q_heads + g * G + col % G) * ROW + grp * 16;
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + kj * 64);
-    }
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
-  }
-
-  const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
-  const uint32_t koff = col * ROW + grp * 16;
-  const uint32_t voff = col * (B * 2) + grp * 8;
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
-
-  float m_ref[R], l_run[R];
-  f32x4 acc[R][NT];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    m_ref[rr] = kNegInf;
-    l_run[rr] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[rr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  u32x4 kring[NBUF][KJ];
-  u32x2 vring[NBUF][NT];
-
-  const int nblk = p_max / B + 1;  // blocks holding tokens 0 .. p_max
-  for (int c0 = 0; c0 < nblk; c0 += 64) {
-    const int cnt = min(64, nblk - c0);
-    const int tab = trow[c0 + min(lane, cnt - 1)];
-
-    auto load = [&](int i, auto slot) {
-      const size_t off = (size_t)__builtin_amdgcn_readlane(tab, i) * blk_bytes;
-      const gptr kblk = uniform_ptr(kpool + off);
-      const gptr vblk = uniform_ptr(vpool + off);
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj) kring[slot][kj] = ldg_stream<u32x4>(kblk + koff + kj * 64);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        vring[slot][nt] = ldg_stream<u32x2>(vblk + voff + nt * 16 * (B * 2));
-    };
-
-    auto compute = [&](int i, auto slot) {
-      u32x4* kb = kring[slot];
-      u32x2* vb = vring[slot];
-      const int t0 = (c0 + i) * B + 4 * grp;       // this lane's first token of the tile
-      if ((c0 + i + 1) * B > p_max + 1) {
-        // tokens past every row (including slots past the context): zero V
-        // so stale bits never reach the output
-        const uint32_t m0 = (t0 + 0 <= p_max ? 0x0000ffffu : 0u) | (t0 + 1 <= p_max ? 0xffff0000u : 0u);
-        const uint32_t m1 = (t0 + 2 <= p_max ? 0x0000ffffu : 0u) | (t0 + 3 <= p_max ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          vb[nt].x &= m0;
-          vb[nt].y &= m1;
-        }
-      }
-      // Row tiles advance RG at a time, stage by stage (scores, maxima, one
-      // shared rescale check, probabilities, P.V), so that their independent
-      // MFMA and VALU chains interleave; a row tile without queries computes
-      // on zero q and is never stored.
-#pragma unroll
-      for (int r0 = 0; r0 < R; r0 += RG) {
-      f32x4 sc[RG];
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) sc[rr - r0] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj)
-#pragma unroll
-        for (int rr = r0; rr < r0 + RG; ++rr)
-          sc[rr - r0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
-                                                           qop[rr][kj], sc[rr - r0], 0, 0, 0);
-      float x[RG][4], bm[RG];
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[rr - r0][r] = t0 + r <= p_row[rr] ? sc[rr - r0][r] * a.scale_log2 : kNegInf;
-        bm[rr - r0] = fmaxf(fmaxf(x[rr - r0][0], x[rr - r0][1]), fmaxf(x[rr - r0][2], x[rr - r0][3]));
-      }
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = max_xor16(bm[rr - r0]);
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) bm[rr - r0] = max_xor32(bm[rr - r0]);
-      bool grow = false;
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) grow = grow || bm[rr - r0] > m_ref[rr] + kSlack;
-      if (__ballot(grow)) {  // rare: move the references that grew, rescale
-#pragma unroll
-        for (int rr = r0; rr < r0 + RG; ++rr) {
-          const float m_new = fmaxf(m_ref[rr], bm[rr - r0] > m_ref[rr] + kSlack ? bm[rr - r0] : m_ref[rr]);
-          const float alpha = fexp2(m_ref[rr] - m_new);
-          l_run[rr] *= alpha;
-          m_ref[rr] = m_new;
-          float ar[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
-        }
-      }
-      bf16x8 pp[RG];
-#pragma unroll
-      for (int rr = r0; rr < r0 + RG; ++rr) {
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr - r0][r] - m_ref[rr]);
-        l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
-        pp[rr - r0] = p_split(p);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 vv = v_twice(vb[nt]);
-#pragma unroll
-        for (int rr = r0; rr < r0 + RG; ++rr)
-          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[rr - r0], vv, acc[rr][nt], 0, 0, 0);
-      }
-      }
-    };
-
-    block_ring<NBUF>(cnt, load, compute);
-  }
-
-  // acc[rr][nt][r] holds slot 4*grp + r of row tile rr (query first + rr*qpt
-  // + slot / G, head slot % G), dim nt*16 + col
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    if (!live[rr]) continue;
-    float l_tot = sum_xor16(l_run[rr]);
-    l_tot = sum_xor32(l_tot);
-    float den[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int slot = 4 * grp + r;
-      const int q = first + rr * qpt + slot / G;
-      if (slot >= qpt * G || q > last) continue;
-      const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] / den[r]);
-    }
-  }
-}
-
 // Workgroup-shared K/V: the four waves of a workgroup take 4R row tiles of
 // the same (sequence, kv head), and each 16-token K/V tile is loaded once
-// per workgroup into LDS (every thread fetches 16-byte chunks of it) and read
-// by all four waves, so one load feeds 4R row tiles.  Global loads run NPF
-// blocks ahead in a small per-thread register ring; LDS holds two tiles, so
-// one barrier per block separates the store of tile i + 1 from its readers
-// and the readers of tile i - 1 from its overwrite.
+// per workgroup into LDS (every thread fetches one chunk of K and one of V)
+// and read by all four waves, so one load feeds 4R row tiles.  Global loads
+// run NPF blocks ahead of the staged one in a small per-thread register
+// ring; LDS holds two tiles, so one barrier per block separates the store
+// of tile i + 1 from its readers and the readers of tile i - 1 from its
+// overwrite.
 template <int D>
 struct WgTile {
   static constexpr int kStrideK = D * 2 + 16;   // padded K row: 16 lanes of a 16-byte read hit 64 banks
@@ -328,7 +136,6 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
   }
 
-  // this thread's chunks: global byte offsets inside a block and LDS offsets
   const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
@@ -340,6 +147,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   const uint32_t lk = (goff / ROW) * T::kStrideK + goff % ROW;
   const int vdim = goff / 32, vquad = (goff % 32) / 8;
   const uint32_t lv = T::kBytesK + (vdim >> 4) * 512 + vquad * 128 + (vdim & 15) * 8;
+  const int vtok = vquad * 4;                      // first token of the chunk in its block
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
   // blocks holding tokens 0 .. p_max (at least one, so that lengths shorter
   // than the query count, which the caller must not pass, still read in bounds)
@@ -356,15 +164,26 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     kring[slot] = *reinterpret_cast<const Chunk*>(kpool + off);
     vring[slot] = *reinterpret_cast<const Chunk*>(vpool + off);
   };
-  auto lstore = [&](auto slot, int buf) {
+  // Stages block `blk` (index in the sequence) from ring slot `slot`.  V of
+  // tokens past p_max (past every row, or past the context) is zeroed, so
+  // stale bits never meet a zero probability.
+  auto lstore = [&](auto slot, int buf, int blk) {
     uint8_t* t = lds + buf * T::kBytes;
     *reinterpret_cast<Chunk*>(t + lk) = kring[slot];
+    uint32_t v[CB / 4];
     if constexpr (CB == 16) {
-      *reinterpret_cast<u32x2*>(t + lv) = u32x2{vring[slot].x, vring[slot].y};
-      *reinterpret_cast<u32x2*>(t + lv + 128) = u32x2{vring[slot].z, vring[slot].w};
+      v[0] = vring[slot].x; v[1] = vring[slot].y; v[2] = vring[slot].z; v[3] = vring[slot].w;
     } else {
-      *reinterpret_cast<u32x2*>(t + lv) = vring[slot];
+      v[0] = vring[slot].x; v[1] = vring[slot].y;
     }
+    const int tok = blk * B + vtok;
+    if (tok + 2 * CB / 4 > p_max + 1) {            // uniform in practice: the block holds p_max
+#pragma unroll
+      for (int e = 0; e < CB / 2; ++e)
+        if (tok + e > p_max) v[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+    }
+    *reinterpret_cast<u32x2*>(t + lv) = u32x2{v[0], v[1]};
+    if constexpr (CB == 16) *reinterpret_cast<u32x2*>(t + lv + 128) = u32x2{v[2], v[3]};
   };
 
   float m_ref[R], l_run[R];
@@ -380,23 +199,14 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   auto compute = [&](int i, int buf) {
     const uint8_t* t = lds + buf * T::kBytes;
     u32x4 kb[KJ];
-    u32x2 vb[NT];
+    bf16x8 vb[NT];
 #pragma unroll
     for (int kj = 0; kj < KJ; ++kj)
       kb[kj] = *reinterpret_cast<const u32x4*>(t + col * T::kStrideK + kj * 64 + grp * 16);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      vb[nt] = *reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8);
+      vb[nt] = v_twice(*reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8));
     const int t0 = i * B + 4 * grp;                // this lane's first token of the tile
-    // tokens past every row (and slots past the context) get zero V, so stale
-    // bits never reach the output
-    const uint32_t m0 = (t0 + 0 <= p_max ? 0x0000ffffu : 0u) | (t0 + 1 <= p_max ? 0xffff0000u : 0u);
-    const uint32_t m1 = (t0 + 2 <= p_max ? 0x0000ffffu : 0u) | (t0 + 3 <= p_max ? 0xffff0000u : 0u);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      vb[nt].x &= m0;
-      vb[nt].y &= m1;
-    }
     f32x4 sc[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
@@ -406,16 +216,26 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
         sc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
                                                          qop[rr][kj], sc[rr], 0, 0, 0);
     }
+    // Softmax of the R row tiles, stage by stage so that one wave-wide
+    // branch covers the (rare) moves of any tile's reference and the rest
+    // of the step is one basic block in which the compiler can interleave
+    // the tiles' VALU work with their MFMAs.
+    float x[R][4], bm[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = t0 + r <= p_row[rr] ? sc[rr][r] * a.scale_log2 : kNegInf;
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = max_xor16(bm);
-      bm = max_xor32(bm);
-      if (__ballot(bm > m_ref[rr] + kSlack)) {     // rare: move the reference, rescale
-        const float m_new = fmaxf(m_ref[rr], bm > m_ref[rr] + kSlack ? bm : m_ref[rr]);
+      for (int r = 0; r < 4; ++r) {
+        x[rr][r] = t0 + r <= p_row[rr] ? sc[rr][r] * a.scale_log2 : kNegInf;
+      }
+      bm[rr] = max_xor32(max_xor16(fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]))));
+    }
+    bool grow = false;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) grow = grow || bm[rr] > m_ref[rr] + kSlack;
+    if (__ballot(grow)) {                          // rare: move references that grew, rescale
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const float m_new = bm[rr] > m_ref[rr] + kSlack ? bm[rr] : m_ref[rr];
         const float alpha = fexp2(m_ref[rr] - m_new);
         l_run[rr] *= alpha;
         m_ref[rr] = m_new;
@@ -427,14 +247,17 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
       }
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref[rr]);
+      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr][r] - m_ref[rr]);
       l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
       const bf16x8 pp = p_split(p);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[rr][nt], 0, 0, 0);
+        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, vb[nt], acc[rr][nt], 0, 0, 0);
     }
   };
 
@@ -444,7 +267,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     __syncthreads();
     // prologue: the window's blocks 0 .. NPF - 1 in flight, block 0 staged
     static_for<NPF>([&](auto j) { gload(j, j); });
-    lstore(std::integral_constant<int, 0>{}, 0);
+    lstore(std::integral_constant<int, 0>{}, 0, w0);
     gload(NPF, std::integral_constant<int, 0>{});
     __syncthreads();
     // block i of the window is in LDS buffer i & 1 and block i + 1 in ring
@@ -459,7 +282,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
         const int i = i0 + j;
         constexpr int nxt = (j + 1) % NPF;
         compute(w0 + i, i & 1);
-        lstore(std::integral_constant<int, nxt>{}, (i + 1) & 1);
+        lstore(std::integral_constant<int, nxt>{}, (i + 1) & 1, w0 + i + 1);
         gload(i + 1 + NPF, std::integral_constant<int, nxt>{});
         __syncthreads();
       });
@@ -490,7 +313,8 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
 }
 
 template <int D, int R, int NPF>
-__global__ __launch_bounds__(kWaves * 64, 1) void extend_wg_kernel(ExtendArgs a, int G, int qpt) {
+__global__ __launch_bounds__(kWaves * 64, kExtWgPerCu) void extend_wg_kernel(ExtendArgs a, int G,
+                                                                             int qpt) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * WgTile<D>::kBytes];
   __shared__ int tab_lds[kExtTabWindow];
   extern __shared__ int ext_lds[];
@@ -515,32 +339,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void extend_wg_kernel(ExtendArgs a,
   }
 }
 
-template <int D, int NBUF, int R>
-__global__ __launch_bounds__(kWaves * 64, PA_EXT_MIN_WG) void extend_kernel(ExtendArgs a, int G,
-                                                                             int qpt) {
-  extern __shared__ int ext_lds[];
-  int* pre = ext_lds;                 // [S + 1]
-  int* wsum = ext_lds + a.num_seqs + 1;
-  // a unit is R row tiles of qpt queries each
-  const int tiles = build_extend_plan(a, R * qpt, pre, wsum);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int units = tiles * a.num_kv_heads;
-  const int stride = gridDim.x * kWaves;
-  for (int u = blockIdx.x * kWaves + wave; u < units; u += stride) {
-    const int g = u % a.num_kv_heads, k = u / a.num_kv_heads;
-    // sequence holding tile k: largest s with pre[s] <= k (pre[s + 1] > k)
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= k) lo = mid; else hi = mid - 1;
-    }
-    int s = lo;
-    while (pre[s + 1] <= k) ++s;  // skip sequences without queries
-    extend_tile<D, NBUF, R>(a, G, qpt, s, k - pre[s], g, lane);
-  }
-}
-
 int cu_count_ext() {
   static int cached = 0;
   if (cached == 0) {
@@ -560,11 +358,7 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
   const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
-#if PA_EXT_WG
   extend_wg_kernel<D, kExtRows, kExtPrefetch><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
-#else
-  extend_kernel<D, kExtNBuf, kExtRows><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
-#endif
   return hipGetLastError();
 }
 

@@ -67,6 +67,21 @@ def test_extend_matches_oracle(pk, G, d):
     assert np.isfinite(got).all() and err.max() <= 2e-2
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_extend_contexts_longer_than_one_table_window(pk, d):
+    """Contexts of 1250 and 1025 blocks: the kernel stages the block table
+    1024 entries at a time, so these rows read through a second window (and
+    the second one holds a single block).  Every output against the oracle."""
+    rng = np.random.default_rng(77 + d)
+    lens, ns = [20000, 16400, 300], [70, 5, 33]
+    k, v, q, qs, tables, lens = _case(rng, lens, ns, 8, 2, d, nb=1300)
+    ref = oracle.extend(k, v, q, qs, tables, lens, d ** -0.5)
+    got = _run(pk, k, v, q, qs, tables, lens, d ** -0.5)
+    err = np.abs(got - ref)
+    _log(f"long contexts d={d}: max|err| {err.max():.3e}")
+    assert np.isfinite(got).all() and err.max() <= 2e-2
+
+
 def test_extend_many_sequences_and_determinism(pk):
     rng = np.random.default_rng(310)
     S = 200
