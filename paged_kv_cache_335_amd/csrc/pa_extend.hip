@@ -33,10 +33,11 @@ namespace {
 constexpr int kExtBlock = 16;
 // Tuning (measured on 32 sequences x 256-token chunks, GQA 32/8, d 128):
 // two row tiles per wave and two workgroups per CU (two waves per SIMD, so
-// one wave's MFMAs hide the other's softmax) ran at 458-479 TFLOP/s; four
-// row tiles at one workgroup per CU at 332-337, one row tile at four
-// workgroups per CU at 438.  One block in flight beyond the staged one was
-// best at two workgroups per CU (a deeper ring spills).
+// one wave's MFMAs hide the other's softmax) ran at 530-537 TFLOP/s; three
+// row tiles at 409, four at one workgroup per CU at about 330 (the last two
+// with P carried to 16 bits: 332-337 and 458-479 for two row tiles), and
+// one row tile at four workgroups per CU at 438.  One block in flight beyond
+// the staged one is what fits two workgroups per CU (a deeper ring spills).
 #ifndef PA_EXT_ROWS
 #define PA_EXT_ROWS 2
 #endif
@@ -84,7 +85,9 @@ __device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* ws
 // overwrite.
 template <int D>
 struct WgTile {
-  static constexpr int kStrideK = D * 2 + 16;   // padded K row: 16 lanes of a 16-byte read hit 64 banks
+  // K rows padded by 32 bytes: the LDS bank-conflict counter read a third of
+  // what it read with 16 or 64 bytes of padding (8 times less than unpadded)
+  static constexpr int kStrideK = D * 2 + 32;
   static constexpr int kBytesK = 16 * kStrideK;
   static constexpr int kBytesV = D * 32;        // V as [dim tile][token quad][dim][4 tokens]
   static constexpr int kBytes = kBytesK + kBytesV;
@@ -199,13 +202,13 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   auto compute = [&](int i, int buf) {
     const uint8_t* t = lds + buf * T::kBytes;
     u32x4 kb[KJ];
-    bf16x8 vb[NT];
+    u32x2 vq[NT];
 #pragma unroll
     for (int kj = 0; kj < KJ; ++kj)
       kb[kj] = *reinterpret_cast<const u32x4*>(t + col * T::kStrideK + kj * 64 + grp * 16);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      vb[nt] = v_twice(*reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8));
+      vq[nt] = *reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8);
     const int t0 = i * B + 4 * grp;                // this lane's first token of the tile
     f32x4 sc[R];
 #pragma unroll
@@ -254,10 +257,20 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr][r] - m_ref[rr]);
       l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
-      const bf16x8 pp = p_split(p);
+      // P rounded to bf16 (nearest even) is the A operand of a 16x16x16
+      // MFMA whose B operand is the lane's V quad as read.  The softmax VALU
+      // work, not the MFMAs, bounds this kernel: carrying P to 16 bits as the
+      // decode does (a high and a low part, with V duplicated into a
+      // 16x16x32 operand) cost 15%.  Its error stays within the bf16 bar: a
+      // weight is off by at most 2^-9 of itself.
+      const bf16x2 p01 = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1])};
+      const bf16x2 p23 = {static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+      const i16x4 pq = __builtin_bit_cast(
+          i16x4, u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)});
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, vb[nt], acc[rr][nt], 0, 0, 0);
+        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pq, __builtin_bit_cast(i16x4, vq[nt]),
+                                                                acc[rr][nt], 0, 0, 0);
     }
   };
 
