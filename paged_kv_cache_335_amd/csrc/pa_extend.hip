@@ -33,7 +33,8 @@ namespace {
 constexpr int kExtBlock = 16;
 // Tuning (measured on 32 sequences x 256-token chunks, GQA 32/8, d 128):
 // two row tiles per wave and two workgroups per CU (two waves per SIMD, so
-// one wave's MFMAs hide the other's softmax) ran at 530-537 TFLOP/s; three
+// one wave's MFMAs hide the other's softmax) ran at 530-537 TFLOP/s before
+// the mask-free interior blocks and the fused scale (590 with both); three
 // row tiles at 409, four at one workgroup per CU at about 330 (the last two
 // with P carried to 16 bits: 332-337 and 458-479 for two row tiles), and
 // one row tile at four workgroups per CU at 438.  One block in flight beyond
@@ -96,7 +97,7 @@ struct WgTile {
   static_assert(kChunk == 8 || kChunk == 16, "8- or 16-byte chunks");
 };
 
-template <int D, int R, int NPF>
+template <int D, int R, int NPF, bool kPos>
 __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int qpt, int s, int unit,
                                                int g, int wave, int lane, uint8_t* lds, int* tab) {
   using T = WgTile<D>;
@@ -115,6 +116,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   const int p_max = L - n + ulast;                 // furthest position any row attends
   const int first = ufirst + wave * R * qpt;       // this wave's first query
   const int last = min(ulast, first + R * qpt - 1);
+  const int p_lo = first <= last ? L - n + first : p_max;  // nearest position of the wave's rows
 
   int p_row[R];
   bool live[R];
@@ -223,14 +225,29 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     // branch covers the (rare) moves of any tile's reference and the rest
     // of the step is one basic block in which the compiler can interleave
     // the tiles' VALU work with their MFMAs.
+    // With a positive scale (kPos) the scores stay unscaled until the
+    // exponent: x = masked raw score, the block max is scaled once, and
+    // p = exp2(fma(x, scale, -m)).  Otherwise x is the scaled score.
     float x[R][4], bm[R];
+    // A block whose tokens every row of the wave sees (all but the blocks
+    // near the diagonal and steps past the last block) skips the mask.
+    const bool seen = i * B + B - 1 <= p_lo;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[rr][r] = kPos ? sc[rr][r] : sc[rr][r] * a.scale_log2;
+    if (!seen) {
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int lim = p_row[rr] - t0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[rr][r] = r <= lim ? x[rr][r] : kNegInf;
+      }
+    }
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[rr][r] = t0 + r <= p_row[rr] ? sc[rr][r] * a.scale_log2 : kNegInf;
-      }
       bm[rr] = max_xor32(max_xor16(fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]))));
+      if constexpr (kPos) bm[rr] *= a.scale_log2;
     }
     bool grow = false;
 #pragma unroll
@@ -255,7 +272,8 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     for (int rr = 0; rr < R; ++rr) {
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[rr][r] - m_ref[rr]);
+      for (int r = 0; r < 4; ++r)
+        p[r] = kPos ? fexp2(fmaf(x[rr][r], a.scale_log2, -m_ref[rr])) : fexp2(x[rr][r] - m_ref[rr]);
       l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
       // P rounded to bf16 (nearest even) is the A operand of a 16x16x16
       // MFMA whose B operand is the lane's V quad as read.  The softmax VALU
@@ -325,7 +343,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   }
 }
 
-template <int D, int R, int NPF>
+template <int D, int R, int NPF, bool kPos>
 __global__ __launch_bounds__(kWaves * 64, kExtWgPerCu) void extend_wg_kernel(ExtendArgs a, int G,
                                                                              int qpt) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * WgTile<D>::kBytes];
@@ -348,7 +366,7 @@ __global__ __launch_bounds__(kWaves * 64, kExtWgPerCu) void extend_wg_kernel(Ext
     int s = lo;
     while (pre[s + 1] <= k) ++s;  // skip sequences without queries
     s = __builtin_amdgcn_readfirstlane(s);
-    extend_wg_unit<D, R, NPF>(a, G, qpt, s, k - pre[s], g, wave, lane, kv_lds, tab_lds);
+    extend_wg_unit<D, R, NPF, kPos>(a, G, qpt, s, k - pre[s], g, wave, lane, kv_lds, tab_lds);
   }
 }
 
@@ -371,7 +389,12 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
   const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
-  extend_wg_kernel<D, kExtRows, kExtPrefetch><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  // a positive scale folds into the exponent's fma; any other takes the
+  // plain form
+  if (a.scale_log2 > 0.f)
+    extend_wg_kernel<D, kExtRows, kExtPrefetch, true><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  else
+    extend_wg_kernel<D, kExtRows, kExtPrefetch, false><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
   return hipGetLastError();
 }
 

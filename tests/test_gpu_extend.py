@@ -67,6 +67,21 @@ def test_extend_matches_oracle(pk, G, d):
     assert np.isfinite(got).all() and err.max() <= 2e-2
 
 
+@pytest.mark.parametrize("scale", [-0.1, 0.0])
+def test_extend_non_positive_scale(pk, scale):
+    """A positive scale takes the kernel's fused scale-and-subtract form; a
+    negative or zero scale takes the plain one (zero: uniform weights over
+    each row's visible tokens)."""
+    rng = np.random.default_rng(91)
+    lens, ns = [37, 300, 64, 17], [37, 77, 1, 16]
+    k, v, q, qs, tables, lens = _case(rng, lens, ns, 8, 2, 128)
+    ref = oracle.extend(k, v, q, qs, tables, lens, scale)
+    got = _run(pk, k, v, q, qs, tables, lens, scale)
+    err = np.abs(got - ref)
+    _log(f"scale {scale}: max|err| {err.max():.3e}")
+    assert np.isfinite(got).all() and err.max() <= 2e-2
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_extend_contexts_longer_than_one_table_window(pk, d):
     """Contexts of 1250 and 1025 blocks: the kernel stages the block table
