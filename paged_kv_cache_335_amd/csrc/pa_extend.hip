@@ -165,9 +165,10 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
   Chunk kring[NPF], vring[NPF];
   int cn = 1;                                      // blocks in the current window
   auto gload = [&](int i, auto slot) {
-    const size_t off = (size_t)tab[min(i, cn - 1)] * blk_bytes + goff;
-    kring[slot] = *reinterpret_cast<const Chunk*>(kpool + off);
-    vring[slot] = *reinterpret_cast<const Chunk*>(vpool + off);
+    // the block id is the same in every lane: its offset is scalar work
+    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tab[min(i, cn - 1)]) * blk_bytes;
+    kring[slot] = *reinterpret_cast<const Chunk*>(kpool + off + goff);
+    vring[slot] = *reinterpret_cast<const Chunk*>(vpool + off + goff);
   };
   // Stages block `blk` (index in the sequence) from ring slot `slot`.  V of
   // tokens past p_max (past every row, or past the context) is zeroed, so
@@ -181,8 +182,8 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     } else {
       v[0] = vring[slot].x; v[1] = vring[slot].y;
     }
-    const int tok = blk * B + vtok;
-    if (tok + 2 * CB / 4 > p_max + 1) {            // uniform in practice: the block holds p_max
+    if (blk * B + B - 1 > p_max) {                 // uniform: the block reaches past p_max
+      const int tok = blk * B + vtok;
 #pragma unroll
       for (int e = 0; e < CB / 2; ++e)
         if (tok + e > p_max) v[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
@@ -191,11 +192,12 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     if constexpr (CB == 16) *reinterpret_cast<u32x2*>(t + lv + 128) = u32x2{v[2], v[3]};
   };
 
-  float m_ref[R], l_run[R];
+  float m_ref[R], thr[R], l_run[R];               // thr = m_ref + kSlack
   f32x4 acc[R][NT];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     m_ref[rr] = kNegInf;
+    thr[rr] = kNegInf;
     l_run[rr] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[rr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -251,14 +253,15 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     }
     bool grow = false;
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) grow = grow || bm[rr] > m_ref[rr] + kSlack;
+    for (int rr = 0; rr < R; ++rr) grow = grow || bm[rr] > thr[rr];
     if (__ballot(grow)) {                          // rare: move references that grew, rescale
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        const float m_new = bm[rr] > m_ref[rr] + kSlack ? bm[rr] : m_ref[rr];
+        const float m_new = bm[rr] > thr[rr] ? bm[rr] : m_ref[rr];
         const float alpha = fexp2(m_ref[rr] - m_new);
         l_run[rr] *= alpha;
         m_ref[rr] = m_new;
+        thr[rr] = m_new + kSlack;
         float ar[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
