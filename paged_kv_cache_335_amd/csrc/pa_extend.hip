@@ -228,7 +228,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     // of the step is one basic block in which the compiler can interleave
     // the tiles' VALU work with their MFMAs.
     // With a positive scale (kPos) the scores stay unscaled until the
-    // exponent: x = masked raw score, the block max is scaled once, and
+    // exponent: x = masked raw score, the lane's max is scaled once, and
     // p = exp2(fma(x, scale, -m)).  Otherwise x is the scaled score.
     float x[R][4], bm[R];
     // A block whose tokens every row of the wave sees (all but the blocks
@@ -246,9 +246,13 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
         for (int r = 0; r < 4; ++r) x[rr][r] = r <= lim ? x[rr][r] : kNegInf;
       }
     }
+    // bm: this lane's max of each row's scores.  A row's max passes its
+    // threshold exactly when some lane's does, so the common path needs no
+    // exchange between lanes; the (rare) branch that moves references takes
+    // the max over the row's four lanes first.
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      bm[rr] = max_xor32(max_xor16(fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]))));
+      bm[rr] = fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]));
       if constexpr (kPos) bm[rr] *= a.scale_log2;
     }
     bool grow = false;
@@ -257,6 +261,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     if (__ballot(grow)) {                          // rare: move references that grew, rescale
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
+        bm[rr] = max_xor32(max_xor16(bm[rr]));
         const float m_new = bm[rr] > thr[rr] ? bm[rr] : m_ref[rr];
         const float alpha = fexp2(m_ref[rr] - m_new);
         l_run[rr] *= alpha;
