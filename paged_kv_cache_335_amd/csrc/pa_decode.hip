@@ -332,10 +332,11 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
           vb[nt].y &= m1;
         }
       }
+      // A head's max passes m_ref + kSlack exactly when some lane's own max
+      // does, so only the (rare) rescale exchanges values between lanes.
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = max_xor16(bm);
-      bm = max_xor32(bm);
       if (__ballot(bm > m_ref + kSlack)) {  // rare: move the reference, rescale
+        bm = max_xor32(max_xor16(bm));
         const float m_new = fmaxf(m_ref, bm);
         const float alpha = fexp2(m_ref - m_new);
         l_run *= alpha;
@@ -561,9 +562,8 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
         for (int nt = 0; nt < NT; ++nt) vb[nt] &= m;
       }
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = max_xor16(bm);
-      bm = max_xor32(bm);
-      if (__ballot(bm > m_ref + kSlack)) {
+      if (__ballot(bm > m_ref + kSlack)) {  // rare: as in mfma_unit
+        bm = max_xor32(max_xor16(bm));
         const float m_new = fmaxf(m_ref, bm);
         const float alpha = fexp2(m_ref - m_new);
         l_run *= alpha;
@@ -731,20 +731,18 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
           }
         }
       }
-      float bm[G];
+      // a head's max passes m_ref + kSlack exactly when some lane's score
+      // does; the max over the wave is taken only in the rare branch
       bool move = false;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        bm[h] = fmaxf(sc[h], dpp<kRowRor4>(sc[h]));
-        bm[h] = fmaxf(bm[h], dpp<kRowRor8>(bm[h]));
-        bm[h] = max_xor16(bm[h]);
-        bm[h] = max_xor32(bm[h]);
-        move |= bm[h] > m_ref[h] + kSlack;
-      }
+      for (int h = 0; h < G; ++h) move |= sc[h] > m_ref[h] + kSlack;
       if (__ballot(move)) {  // rare: move the references, rescale
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float m_new = fmaxf(m_ref[h], bm[h]);
+          float bm = fmaxf(sc[h], dpp<kRowRor4>(sc[h]));
+          bm = fmaxf(bm, dpp<kRowRor8>(bm));
+          bm = max_xor32(max_xor16(bm));
+          const float m_new = fmaxf(m_ref[h], bm);
           const float alpha = fexp2(m_ref[h] - m_new);
           m_ref[h] = m_new;
           l_run[h] *= alpha;
