@@ -9,6 +9,13 @@ shuffled pool sized to the blocks needed plus 10%.
 With --kv fp8 the same workload runs on an 8-bit cache (E4M3 codes with one
 bf16 scale per token and kv head; queries and new tokens stay bf16).
 
+With --config prefix_sharing (or prefix_sharing_cow) 64 prompts are written
+once and forked into 4 samples each, which share the prompt's blocks (the
+copy-on-write variant's partly filled shared tail is copied on the first
+private append).  `value` counts every sequence's context (logical bytes);
+the roofline uses the distinct token slots read (a shared prefix once),
+since repeated reads of shared blocks can hit in the caches.
+
 One step = the whole hot path for one batch: the host block manager appends
 one token to every sequence (slots, new blocks, copy-on-write decisions), one
 packed host-to-device metadata copy, the device table update, the slot write
@@ -20,6 +27,7 @@ Prints one JSON line.  `value` is KV bytes read per step / step time (GB/s);
 the same batch.
 """
 import argparse
+import gc
 import json
 import math
 import os
@@ -75,7 +83,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama3_8b_gqa", choices=["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"])
+    ap.add_argument("--config", default="llama3_8b_gqa",
+                    choices=["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing",
+                             "prefix_sharing_cow", "long_context_128k"])
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0: library)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="tokens per block (the table/tail-waste trade-off)")
@@ -111,6 +121,7 @@ def main():
     import paged_kv_cache_335_amd as pk
     from paged_kv_cache_335_amd.runtime import DeviceEvent, PagedKVCache
     from workloads import CONFIGS, draw_lengths
+    from workloads.gen import unique_blocks
 
     if args.mode == "extend":
         return bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths)
@@ -128,10 +139,11 @@ def main():
 
     rng = np.random.default_rng(cfg.seed)
     lens0 = draw_lengths(cfg, rng)           # context length at the first step
-    if cfg.lengths[0] == "shared":
-        raise SystemExit("prefix-sharing workloads are exercised by the tests, not timed here")
+    # prefix sharing: prompts x samples sequences; each prompt's first
+    # `shared` tokens are written once and shared by its samples (forks)
+    shared = int(cfg.lengths[1]) if cfg.lengths[0] == "shared" else 0
     final = lens0.astype(np.int64) + steps
-    need_blocks = int(((final + B - 1) // B).sum())
+    need_blocks = unique_blocks(cfg, final) if shared else int(((final + B - 1) // B).sum())
     num_blocks = int(math.ceil(1.1 * need_blocks)) if cfg.pool[0] == "plus" else max(
         int(cfg.pool[1]), need_blocks)
     width = int((final.max() + B - 1) // B)
@@ -141,12 +153,27 @@ def main():
     fp8 = args.kv == "fp8"
     cache = PagedKVCache(num_blocks, Hkv, d, S, width, block_size=B, shuffle_seed=cfg.seed,
                          dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-    seqs = np.array([cache.add_sequence() for _ in range(S)], dtype=np.int32)
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed)
+    if shared:
+        # each prompt's shared tokens once, then its forks (so a prompt's
+        # samples take adjacent table rows)
+        log(f"prefill {cfg.prompts} prompts x {shared} shared tokens, {cfg.samples} samples each")
+        seq_list = []
+        for _ in range(cfg.prompts):
+            s0 = cache.add_sequence()
+            kn = torch.randn((shared, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+            vn = torch.randn((shared, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+            cache.append(np.array([s0], np.int32), np.array([shared], np.int32), kn, vn,
+                         stream=stream)
+            seq_list += [s0] + [cache.fork(s0) for _ in range(cfg.samples - 1)]
+        seqs = np.array(seq_list, dtype=np.int32)
+    else:
+        seqs = np.array([cache.add_sequence() for _ in range(S)], dtype=np.int32)
 
-    # prefill: every context token but the one each first step appends
-    pre = (lens0 - 1).astype(np.int32)
+    # prefill: every context token but the one each first step appends (past
+    # the shared prefix, which is already in place)
+    pre = (lens0 - 1 - shared).astype(np.int32)
     log(f"prefill {int(pre.sum())} tokens through the slot write")
     chunk = 16384
     start = 0
@@ -178,6 +205,12 @@ def main():
     kv_per_token = 2 * Hkv * (d + 2 if fp8 else d * 2)
 
     step_bytes = []
+    step_unique = []  # bytes of distinct token slots read (a shared prefix counts once)
+    base = (shared // B) * B  # tokens of each prompt's shared full blocks
+
+    def unique_tokens(lens):
+        lens = lens.astype(np.int64)
+        return int(cfg.prompts * base + (lens - base).sum()) if shared else int(lens.sum())
 
     def step(i):
         cache.append(seqs, ones, kns[i], vns[i], stream=stream)
@@ -187,18 +220,27 @@ def main():
     for i in range(W):
         step(i)
         step_bytes.append(int(cache.host_lens[:S].sum()) * kv_per_token)
+        step_unique.append(unique_tokens(cache.host_lens[:S]) * kv_per_token)
     torch.cuda.synchronize()
     # the timed steps carry no events: recording one leaves the GPU idle for
     # a few microseconds before the next kernel, which is instrumentation,
     # not part of the path
     log(f"timing {K} steps")
+    # Python's cyclic garbage collector: a full collection takes tens of
+    # milliseconds in this process and, when one fell inside the timed steps,
+    # left the GPU idle for a few steps' worth of time; collect now and keep
+    # it off while the steps are enqueued
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(W, steps):
         step(i)
         step_bytes.append(int(cache.host_lens[:S].sum()) * kv_per_token)
+        step_unique.append(unique_tokens(cache.host_lens[:S]) * kv_per_token)
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     host_ms = (t_enq - t0) * 1e3 / K
     ms_step = (t1 - t0) * 1e3 / K
     timed_bytes = step_bytes[W:]
@@ -209,14 +251,19 @@ def main():
     # same stream, over the last step's batch, between two fence-free HIP
     # events (each call = the decode kernel and its reduce kernel)
     ea, eb = DeviceEvent(timing=True), DeviceEvent(timing=True)
+    gc.disable()
     ea.record(stream)
     for _ in range(K):
         cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
     eb.record(stream)
     eb.synchronize()
+    gc.enable()
     dec_ms_avg = ea.elapsed_ms(eb) / K
     last_bytes = step_bytes[-1]
     dec_gbps = last_bytes / (dec_ms_avg * 1e-3) / 1e9
+    # with a shared prefix, the bytes that must come from HBM are the
+    # distinct slots; repeated reads of shared blocks can hit in the caches
+    dec_gbps_unique = step_unique[-1] / (dec_ms_avg * 1e-3) / 1e9
     log(f"step {ms_step:.3f} ms ({value:.0f} GB/s); decode {dec_ms_avg * 1e3:.1f} us "
         f"({dec_gbps:.0f} GB/s); host enqueue {host_ms:.3f} ms/step")
 
@@ -275,16 +322,20 @@ def main():
             "block_size": B, "pool_blocks": num_blocks, "partition_tokens": P,
             "mean_context_tokens": round(float(lens_now.mean()), 1),
             "kv_bytes_per_step": int(kv_avg),
+            "kv_bytes_unique_per_step": int(np.mean(step_unique[W:])),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "host_enqueue_ms_per_step": round(host_ms, 4),
         "decode": {"us_mean": round(dec_ms_avg * 1e3, 2), "GBps": round(dec_gbps, 1),
                    "kv_bytes": int(last_bytes), "calls": K,
-                   "tokens_per_s": round(S / (dec_ms_avg * 1e-3), 1)},
+                   "tokens_per_s": round(S / (dec_ms_avg * 1e-3), 1),
+                   "GBps_unique": round(dec_gbps_unique, 1),
+                   "kv_bytes_unique": int(step_unique[-1])},
         "decode_cold": cold,
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps_unique, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps_unique / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(kv_avg)
                      if args.partition == 0 and not fp8 else None},
         "block_swap": swap,
@@ -368,11 +419,14 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    gc.collect()  # no collector pause inside the timed steps (as for decode)
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(W, steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     ms_step = (t1 - t0) * 1e3 / K
     ext_ms = [ev[i][0].elapsed_ms(ev[i][1]) for i in range(W, steps)]
     ext_avg = float(np.mean(ext_ms))
