@@ -216,6 +216,13 @@ def main():
         cache.append(seqs, ones, kns[i], vns[i], stream=stream)
         cache.decode(qs[i], out=out, partition_tokens=args.partition, stream=stream)
 
+    # Python's cyclic garbage collector: a full collection takes tens of
+    # milliseconds in this process and, when one fell inside the timed steps,
+    # left the GPU idle for a few steps' worth of time.  Collect before the
+    # warm-up (whose steps then also warm the host path) and keep it off
+    # until the timed steps and the roofline calls have run.
+    gc.collect()
+    gc.disable()
     log(f"warmup {W} steps (partition {P} tokens)")
     for i in range(W):
         step(i)
@@ -226,12 +233,6 @@ def main():
     # a few microseconds before the next kernel, which is instrumentation,
     # not part of the path
     log(f"timing {K} steps")
-    # Python's cyclic garbage collector: a full collection takes tens of
-    # milliseconds in this process and, when one fell inside the timed steps,
-    # left the GPU idle for a few steps' worth of time; collect now and keep
-    # it off while the steps are enqueued
-    gc.collect()
-    gc.disable()
     t0 = time.perf_counter()
     for i in range(W, steps):
         step(i)
@@ -240,7 +241,6 @@ def main():
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gc.enable()
     host_ms = (t_enq - t0) * 1e3 / K
     ms_step = (t1 - t0) * 1e3 / K
     timed_bytes = step_bytes[W:]
@@ -251,13 +251,12 @@ def main():
     # same stream, over the last step's batch, between two fence-free HIP
     # events (each call = the decode kernel and its reduce kernel)
     ea, eb = DeviceEvent(timing=True), DeviceEvent(timing=True)
-    gc.disable()
     ea.record(stream)
     for _ in range(K):
         cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
     eb.record(stream)
     eb.synchronize()
-    gc.enable()
+    gc.enable()  # off since before the warm-up
     dec_ms_avg = ea.elapsed_ms(eb) / K
     last_bytes = step_bytes[-1]
     dec_gbps = last_bytes / (dec_ms_avg * 1e-3) / 1e9
@@ -416,11 +415,11 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
         flops.append(int(seen) * Hq * 4 * d)
         kv_bytes.append(int(L.sum()) * 2 * Hkv * d * 2)
 
+    gc.collect()  # no collector pause inside the timed steps (as for decode)
+    gc.disable()
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
-    gc.collect()  # no collector pause inside the timed steps (as for decode)
-    gc.disable()
     t0 = time.perf_counter()
     for i in range(W, steps):
         step(i)
