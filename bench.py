@@ -288,6 +288,8 @@ def main():
     cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
     torch.cuda.synchronize()
 
+    copy_write = copy_write_probe(pk, cache, kns[-1], vns[-1], stream)
+
     swap = None
     if args.swap_blocks > 0:
         swap = swap_probe(pk, cache, args.swap_blocks, stream)
@@ -337,6 +339,7 @@ def main():
                      "frac": round(dec_gbps_unique / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(kv_avg)
                      if args.partition == 0 and not fp8 else None},
+        "cache_ops": copy_write,
         "block_swap": swap,
         "block_manager": {"tail_waste_pct": round(tail_waste, 3),
                           "contiguous_reservation_utilisation_pct": round(contiguous_util, 2),
@@ -449,6 +452,52 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
                      "traffic": None},
     }
     print(json.dumps(result), flush=True)
+
+
+def copy_write_probe(pk, cache, k_new, v_new, stream, calls=20, pairs_n=192):
+    """The two cache-maintenance calls on their own, each timed over `calls`
+    back-to-back launches between HIP events: pa_block_copy of `pairs_n`
+    (live block, free block) pairs -- the copy-on-write count of the
+    prefix-sharing workload -- and pa_kv_write of the step's tokens into
+    slots of free blocks.  Only free blocks are written, so the live contexts
+    are untouched.  Latency-bound at these sizes: no roofline claim."""
+    from paged_kv_cache_335_amd.runtime import DeviceEvent
+    k, v = cache.k_pool, cache.v_pool
+    B = cache.B
+    T = k_new.shape[0]
+    free = np.asarray(cache.bm.free_list(), dtype=np.int64)
+    n_wblk = (T + B - 1) // B
+    if len(free) < pairs_n + n_wblk:
+        return None
+    S = len(cache.rows)
+    live = np.unique(cache.tables[:S, 0].cpu().numpy())  # first block of every sequence
+    src = np.resize(live, pairs_n)
+    pairs = torch.from_numpy(np.stack([src, free[:pairs_n]], 1).astype(np.int32)).to(k.device)
+    slots = (free[pairs_n:pairs_n + n_wblk, None] * B + np.arange(B)).reshape(-1)[:T]
+    d_slots = torch.from_numpy(slots.astype(np.int64)).to(k.device)
+    block_bytes = k[0].numel() * k.element_size() + v[0].numel() * v.element_size()
+    row_bytes = block_bytes // B  # one token's K and V rows, every kv head, in the pool
+    res = {}
+    for name, fn, moved in (
+            ("block_copy", lambda: pk.pa_block_copy(k, v, pairs, stream=stream),
+             2 * pairs_n * block_bytes),
+            ("kv_write", lambda: pk.pa_kv_write(k, v, k_new, v_new, d_slots, stream=stream),
+             T * row_bytes + (k_new.numel() + v_new.numel()) * k_new.element_size())):
+        fn()
+        a, b = DeviceEvent(timing=True), DeviceEvent(timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        us = a.elapsed_ms(b) * 1e3 / calls
+        res[name] = {"us": round(us, 2), "bytes_read_and_written": int(moved),
+                     "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+    res["block_copy"]["pairs"] = pairs_n
+    res["kv_write"]["tokens"] = int(T)
+    log(f"block copy of {pairs_n} pairs {res['block_copy']['us']} us; "
+        f"slot write of {T} tokens {res['kv_write']['us']} us")
+    return res
 
 
 def swap_probe(pk, cache, n, stream):
