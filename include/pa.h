@@ -140,8 +140,11 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *                  never read.
  *   context_lens:  int32 [num_seqs], 1 <= L <= max_blocks_per_seq*block_size.
  *   partition_tokens: smallest piece of a sequence one workgroup streams
- *                  (0: the library's choice, 256 tokens); otherwise a
- *                  positive multiple of block_size.  The work is split by
+ *                  (0: the library's choice, 256 tokens, or less for a
+ *                  table shorter than 8192 tokens: its capacity
+ *                  max_blocks_per_seq * block_size in 32 pieces, rounded up
+ *                  to whole blocks); otherwise a positive multiple of
+ *                  block_size.  The work is split by
  *                  blocks, not by sequence: per group of 4 kv heads the
  *                  batch's blocks, sequence after sequence, are cut into
  *                  equal contiguous ranges, one per workgroup of a grid that

@@ -48,10 +48,21 @@ bool fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
 }
 
 // Smallest piece a workgroup streams when the library chooses: 256 tokens
-// (16 blocks).  Ranges are normally much longer (the batch's blocks divided
-// evenly over the grid); the floor only matters for small batches, where it
-// bounds the number of partials.
+// (16 blocks), or for a short table its capacity in 32 pieces (whole
+// blocks, at least one).  Ranges are normally much longer (the batch's
+// blocks divided evenly over the grid); the floor only matters for small
+// batches, where it bounds the number of partials -- and, set too high,
+// crowds many short sequences into few ranges that each walk them one
+// after another (256 one-token sequences: 42 us a call with a 256-token
+// floor).
 constexpr int32_t kDefaultMinPiece = 256;
+constexpr int32_t kDefaultPiecesPerTable = 32;
+
+int32_t default_piece(int64_t max_len, int32_t block_size) {
+  int64_t p = (max_len + kDefaultPiecesPerTable - 1) / kDefaultPiecesPerTable;
+  p = (p + block_size - 1) / block_size * block_size;
+  return static_cast<int32_t>(std::min<int64_t>(kDefaultMinPiece, std::max<int64_t>(block_size, p)));
+}
 
 pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
                        int32_t req_piece, int32_t* P_out, int32_t* slots_out,
@@ -60,8 +71,8 @@ pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
   if (Hq % pool->num_kv_heads != 0) return PA_EINVAL;
   if (req_piece < 0 || (req_piece > 0 && req_piece % pool->block_size != 0)) return PA_EINVAL;
   if ((int64_t)maxB * pool->block_size > INT32_MAX) return PA_EINVAL;
-  const int32_t P = req_piece > 0 ? req_piece : kDefaultMinPiece;
   const int64_t max_len = (int64_t)maxB * pool->block_size;
+  const int32_t P = req_piece > 0 ? req_piece : default_piece(max_len, pool->block_size);
   // a sequence of n blocks meets at most ceil(n / min piece) + 1 ranges
   const int64_t slots = (max_len + P - 1) / P + 1;
   if (slots > pakv::kMaxSlots) return PA_EINVAL;

@@ -67,8 +67,16 @@ def test_workspace_and_partition_sizing():
     slots = 8192 * 16 // 512 + 1
     n = 4 * 32 * slots
     assert ws >= n * 4 * 2 + n * 128 * 4 + 4 * 4
-    # library choice: 256-token minimum pieces
+    # library choice: 256-token minimum pieces, or for a table shorter than
+    # 8192 tokens its capacity in 32 pieces rounded up to whole blocks
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 0) == 256
+    assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 516, 0) == 256
+    assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 129, 0) == 80   # 2064 / 32 -> 5 blocks
+    assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8, 0) == 16     # at least one block
+    # at most 33 partial slots per sequence with the library's choice
+    for w in (1, 7, 64, 129, 511):
+        P0 = L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, w, 0)
+        assert P0 % 16 == 0 and (w * 16 + P0 - 1) // P0 + 1 <= 33
     # even short sequences can be cut by a range boundary: never 0 for S > 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8, 256) > 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 0, 32, 8, 256) == 0
