@@ -451,7 +451,58 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None},
     }
+    if not args.no_cpu_baseline:
+        tables, lens = cache.bm.export(seqs, width, pad_block=0)
+        result["cpu_baseline"], result["parity_sample"] = extend_cpu_baseline(
+            cache, qs[-1], out, tables, lens, C, Hq, d, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def extend_cpu_baseline(cache, q, out, tables, lens, C, Hq, d, scale, seconds):
+    """Time the CPU oracle's extend (as it stands) on whole sequences of the
+    last timed step's batch: one sequence first, then as many as fit in about
+    `seconds` of CPU work (in a fixed order).  Also compares the sampled rows
+    with the GPU's."""
+    import oracle
+    from workloads.gen import to_numpy_storage
+    log("cpu baseline (extend): copying the pool to the host")
+    k = to_numpy_storage(cache.k_pool)
+    v = to_numpy_storage(cache.v_pool)
+    qn = to_numpy_storage(q)
+    got_all = out.float().cpu().numpy().astype(np.float64)
+    lens = lens.astype(np.int32)
+    threads = oracle.max_threads()
+
+    def run(sel):
+        sel = np.asarray(sel)
+        rows = (sel[:, None] * C + np.arange(C)[None, :]).reshape(-1)
+        q_start = (np.arange(len(sel) + 1) * C).astype(np.int32)
+        t = time.perf_counter()
+        ref = oracle.extend(k, v, np.ascontiguousarray(qn[rows]), q_start,
+                            np.ascontiguousarray(tables[sel]), np.ascontiguousarray(lens[sel]),
+                            scale)
+        return time.perf_counter() - t, ref, rows
+
+    def flops_of(sel):
+        L = lens[np.asarray(sel)].astype(np.int64)
+        return int((C * (L - C) + C * (C + 1) // 2).sum()) * Hq * 4 * d
+
+    order = np.random.default_rng(0).permutation(len(lens))
+    t1, _, _ = run(order[:1])
+    n = int(max(1, min(len(lens), seconds // max(t1, 1e-3))))
+    sel = order[:n]
+    dt, ref, rows = run(sel)
+    err = float(np.abs(got_all[rows] - ref).max())
+    fl = flops_of(sel)
+    log(f"cpu baseline (extend): {n} sequences x {C} queries on {threads} threads, {dt:.2f} s, "
+        f"{fl / dt / 1e12:.4f} TFLOP/s; sampled parity max|err| {err:.3e}")
+    base = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {len(lens)} sequences of the last timed step's batch, all {C} "
+                      f"queries and {Hq} query heads each ({dt:.1f} s); fp64 C oracle, OpenMP",
+            "seconds": round(dt, 3), "query_tokens_per_s": round(n * C / dt, 2)}
+    return base, {"rows": int(len(rows)), "max_abs_err": err, "tolerance": 2e-2,
+                  "pass": bool(err <= 2e-2)}
 
 
 def copy_write_probe(pk, cache, k_new, v_new, stream, calls=20, pairs_n=192):
