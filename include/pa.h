@@ -87,9 +87,9 @@ typedef enum {
  */
 typedef struct {
   int32_t num_blocks;
-  int32_t block_size;    /* tokens per block; decode supports 16 */
+  int32_t block_size;    /* tokens per block; decode: 8, 16 or 32 (fp32: 16) */
   int32_t num_kv_heads;
-  int32_t head_dim;      /* decode supports 64 and 128 */
+  int32_t head_dim;      /* decode and extend: 64 or 128 */
   pa_dtype dtype;        /* element type of both pools (PA_FP8_E4M3: regions) */
 } pa_pool;
 
@@ -154,9 +154,11 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *                  go to `workspace` and are combined by a second kernel.
  *   workspace:     device buffer of at least pa_decode_workspace_bytes(...)
  *                  bytes; contents on entry are irrelevant.
- * Requires num_q_heads % num_kv_heads == 0, block_size 16, head_dim 64 or
- * 128.  The result does not depend on where blocks sit in the pool, and two
- * calls with the same inputs give identical bits.
+ * Requires num_q_heads % num_kv_heads == 0 and head_dim 64 or 128; bf16 and
+ * 8-bit pools: block_size 8, 16 or 32 and at most 16 query heads per kv
+ * head; fp32 pools: block_size 16 and at most 4 query heads per kv head
+ * (PA_EUNSUPPORTED otherwise).  The result does not depend on where blocks
+ * sit in the pool, and two calls with the same inputs give identical bits.
  */
 pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const void* q, int32_t num_seqs, int32_t num_q_heads,
