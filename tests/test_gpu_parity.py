@@ -181,6 +181,22 @@ def test_decode_batch_beyond_one_launch(pk):
         _check(_to64(_gpu_decode(pk, c, P)), ref, "bf16", f"S=4100 P={P}")
 
 
+def test_decode_short_tables_default_partition(pk):
+    """Short tables take a floor below 256 tokens by default (one block for
+    a 1- or 3-block table): hundreds of short sequences then spread over many
+    ranges and are cut across range boundaries.  Every output against the
+    oracle, with the library's choice and with an explicit 256."""
+    rng = np.random.default_rng(93)
+    for width, hi in ((1, 16), (3, 40)):
+        lens = rng.integers(1, hi + 1, 600)
+        c = _custom_case(lens, Hq=8, Hkv=2, d=128, nb=400, width=width, seed=94 + width)
+        P0 = pk.pa_decode_partition_tokens(c.k_pool, c.v_pool, 600, 8, width)
+        assert P0 == 16, P0
+        ref = oracle.decode(*c.oracle_inputs(), c.scale)
+        for P in (0, 256):
+            _check(_to64(_gpu_decode(pk, c, P)), ref, "bf16", f"width={width} P={P}")
+
+
 # --- full-size configs: every output ------------------------------------------
 FULL = ["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"]
 
