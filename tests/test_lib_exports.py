@@ -124,6 +124,14 @@ def test_host_checks_reject_before_any_launch():
     assert L.pa_block_copy(ctypes.byref(d), dummy, dummy, null, 3, null) == pk.PA_EINVAL
     assert L.pa_block_copy(ctypes.byref(d), null, null, null, 0, null) == pk.PA_OK
     assert L.pa_table_update(dummy, 0, 16, dummy, dummy, dummy, 4, null) == pk.PA_EINVAL
+    # empty inputs are no-ops that touch no memory (null pointers accepted)
+    assert L.pa_decode(ctypes.byref(d), null, null, null, 0, 32, null, 4, null, 0.1, null, 0,
+                       null, 0, null) == pk.PA_OK
+    assert L.pa_extend(ctypes.byref(d), null, null, null, 0, null, 0, 32, null, 4, null, 0.1,
+                       null, null) == pk.PA_OK
+    assert L.pa_extend(ctypes.byref(d), null, null, null, 0, null, 3, 32, null, 4, null, 0.1,
+                       null, null) == pk.PA_OK
+    assert L.pa_block_swap(ctypes.byref(d), null, null, null, null, 0, null, 0, 0, null) == pk.PA_OK
 
 
 def test_binding_rejects_cpu_tensors():
