@@ -197,6 +197,69 @@ def test_decode_short_tables_default_partition(pk):
             _check(_to64(_gpu_decode(pk, c, P)), ref, "bf16", f"width={width} P={P}")
 
 
+def test_pools_beyond_4_gib(pk):
+    """Pools of 4.1 GiB each, every block the test touches above the 4 GiB
+    mark (byte offsets past 2^32 in both pools): decode, slot write and
+    block copy against the oracle on compact host copies of the touched
+    blocks."""
+    Hkv, d, B, Hq = 8, 128, 16, 32
+    blk = Hkv * B * d * 2                      # bytes of one block in each pool
+    lo_n = (4 << 30) // blk                    # blocks below the 4 GiB mark
+    nb = lo_n + 4096
+    dev = torch.device("cuda")
+    k = torch.empty((nb, Hkv, B, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((nb, Hkv, d, B), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    k.normal_(generator=g)
+    v.normal_(generator=g)
+    rng = np.random.default_rng(8)
+    hi = np.arange(lo_n, nb)
+
+    def host(pool, ids):
+        return to_numpy_storage(pool[torch.from_numpy(np.asarray(ids, np.int64)).to(dev)])
+
+    # decode over tables of high blocks
+    lens = np.array([1, 100, 777, 1500], np.int32)
+    width = int((lens.max() + B - 1) // B)
+    ids = rng.permutation(hi)[:len(lens) * width].reshape(len(lens), width).astype(np.int32)
+    q = torch.randn((len(lens), Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    out = pk.pa_decode(q, k, v, torch.from_numpy(ids).to(dev), torch.from_numpy(lens).to(dev),
+                       d ** -0.5)
+    torch.cuda.synchronize()
+    used = np.unique(ids)
+    ref = oracle.decode(host(k, used), host(v, used), to_numpy_storage(q),
+                        np.searchsorted(used, ids).astype(np.int32), lens, d ** -0.5)
+    _check(_to64(out), ref, "bf16", "decode over blocks past 4 GiB")
+
+    # slot write into high blocks (one slot per block, so slots are distinct)
+    T = 64
+    wblk = rng.permutation(hi)[:T]
+    rows = rng.integers(0, B, T)
+    kn = torch.randn((T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((T, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    kref, vref = oracle.kv_write(host(k, wblk), host(v, wblk), to_numpy_storage(kn),
+                                 to_numpy_storage(vn), (np.arange(T) * B + rows).astype(np.int64))
+    pk.pa_kv_write(k, v, kn, vn, torch.from_numpy((wblk * B + rows).astype(np.int64)).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(k, wblk), kref)
+    assert np.array_equal(host(v, wblk), vref)
+
+    # block copy across the mark both ways: no destination is a source
+    P = 16
+    src_hi, dst_hi = np.split(rng.permutation(hi)[:2 * P], 2)
+    src_lo, dst_lo = np.split(rng.permutation(lo_n)[:2 * P], 2)
+    src = np.concatenate([src_hi, src_lo])
+    dst = np.concatenate([dst_lo, dst_hi])
+    k_src, v_src = host(k, src), host(v, src)
+    pk.pa_block_copy(k, v, torch.from_numpy(np.stack([src, dst], 1).astype(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(k, dst), k_src)
+    assert np.array_equal(host(v, dst), v_src)
+    del k, v
+    torch.cuda.empty_cache()
+
+
 # --- full-size configs: every output ------------------------------------------
 FULL = ["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"]
 
