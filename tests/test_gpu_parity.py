@@ -199,8 +199,8 @@ def test_decode_short_tables_default_partition(pk):
 
 def test_pools_beyond_4_gib(pk):
     """Pools of 4.1 GiB each, every block the test touches above the 4 GiB
-    mark (byte offsets past 2^32 in both pools): decode, slot write and
-    block copy against the oracle on compact host copies of the touched
+    mark (byte offsets past 2^32 in both pools): decode, extend, slot write
+    and block copy against the oracle on compact host copies of the touched
     blocks."""
     Hkv, d, B, Hq = 8, 128, 16, 32
     blk = Hkv * B * d * 2                      # bytes of one block in each pool
@@ -231,6 +231,16 @@ def test_pools_beyond_4_gib(pk):
     ref = oracle.decode(host(k, used), host(v, used), to_numpy_storage(q),
                         np.searchsorted(used, ids).astype(np.int32), lens, d ** -0.5)
     _check(_to64(out), ref, "bf16", "decode over blocks past 4 GiB")
+    # extend (the last n tokens of each context as queries) over the same tables
+    n = np.minimum(lens, 24).astype(np.int32)
+    q_start = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    qe = torch.randn((int(q_start[-1]), Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    oute = pk.pa_extend(qe, k, v, torch.from_numpy(q_start).to(dev), torch.from_numpy(ids).to(dev),
+                        torch.from_numpy(lens).to(dev), d ** -0.5)
+    torch.cuda.synchronize()
+    refe = oracle.extend(host(k, used), host(v, used), to_numpy_storage(qe), q_start,
+                         np.searchsorted(used, ids).astype(np.int32), lens, d ** -0.5)
+    _check(_to64(oute), refe, "bf16", "extend over blocks past 4 GiB")
 
     # slot write into high blocks (one slot per block, so slots are distinct)
     T = 64
