@@ -112,6 +112,21 @@ def test_decode_group_sizes_and_head_dims(pk, G, d):
         _check(_to64(_gpu_decode(pk, c, P)), ref, "bf16", f"G={G} d={d} P={P}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.3, 4.0])
+def test_decode_extreme_scales(pk, scale):
+    """Zero scale (plain mean of V), a negative scale, and a large one whose
+    scores spread over dozens of log2 units, so the running reference moves
+    often: MFMA kernel with 1 and 4 query heads per kv head, and the fp32
+    VALU kernel, against the oracle."""
+    lens = (1, 2, 15, 16, 17, 200, 513, 1000)
+    for Hq, Hkv, dtype in ((8, 2, "bf16"), (2, 2, "bf16"), (4, 2, "f32")):
+        c = _custom_case(lens, Hq=Hq, Hkv=Hkv, d=128, nb=300, width=63, seed=7, dtype=dtype)
+        ref = oracle.decode(*c.oracle_inputs(), scale)
+        out = pk.pa_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, scale)
+        torch.cuda.synchronize()
+        _check(_to64(out), ref, dtype, f"scale={scale} Hq={Hq} {dtype}")
+
+
 def test_decode_fp32_group_sizes(pk):
     for G in (1, 2, 4):
         cfg = CONFIGS["tiny_f32"].scaled(num_seqs=5, num_q_heads=G, num_kv_heads=1, head_dim=128,
