@@ -91,6 +91,19 @@ def _custom_fp8_case(lens, Hq, Hkv, d, nb, width, seed):
     return c
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.3, 4.0])
+def test_fp8_decode_extreme_scales(pk, scale):
+    """Zero, negative and large attention scales on the 8-bit kernel, whose
+    per-token K scales multiply the scores and V scales the probabilities."""
+    lens = (1, 2, 16, 17, 200, 1000)
+    for G in (1, 4):
+        c = _custom_fp8_case(lens, Hq=2 * G, Hkv=2, d=128, nb=300, width=63, seed=300 + G)
+        ref = oracle.decode(*c.oracle_inputs(), scale)
+        out = pk.pa_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, scale)
+        torch.cuda.synchronize()
+        _check(_to64(out), ref, f"fp8 scale={scale} G={G}")
+
+
 @pytest.mark.parametrize("G,d", [(1, 64), (1, 128), (4, 128), (5, 64), (8, 128), (16, 128)])
 def test_fp8_decode_group_sizes_and_head_dims(pk, G, d):
     lens = (1, 15, 16, 17, 63, 64, 65, 511, 512, 513)
