@@ -31,12 +31,13 @@
 //    v_mfma_f32_16x16x32_bf16 with A = the 16 tokens of a block x 32 dims and
 //    B = 32 dims x 16 head slots (the group's heads, zero padded).  Its
 //    output layout (lane holds tokens 4*(lane/16)+i of head lane%16) is
-//    exactly the A layout of P.V on v_mfma_f32_16x16x16_bf16, so
-//    probabilities never leave the lane.  P goes in twice, as its bf16 high
-//    part (truncation) and then its low part (p - high, rounded to nearest
-//    even), which carries P to about 16 significant bits.  V is stored
-//    dim-major in the pool so each lane's 4 tokens of one dim are one 8-byte
-//    load.
+//    the A layout P.V needs, so probabilities never leave the lane.  P.V is
+//    one v_mfma_f32_16x16x32_bf16 per 16 output dims whose 32-long k runs
+//    over the lane's 4 tokens twice: A holds P's bf16 high part
+//    (truncation) and then its low part (p - high, rounded to nearest even),
+//    which carries P to about 16 significant bits, and B the lane's V values
+//    twice.  V is stored dim-major in the pool so each lane's 4 tokens of
+//    one dim are one 8-byte load.
 //    With a single query head per kv head (MHA) the 16 head slots hold one
 //    real head; the instruction count per block does not depend on the group
 //    size, and measured against a VALU kernel on the 32/32-head workload the
