@@ -12,7 +12,8 @@
 // and so on.  The grid is persistent (as many workgroups as fit on the chip
 // at once) and every workgroup takes one equal, contiguous range of that
 // list for one head group; its 4 waves each stream the range for one kv head
-// of the group.  Every workgroup thus reads the same number of blocks
+// of the group (with fewer than 4 kv heads, the spare waves stream further,
+// adjacent ranges of the same heads).  Every workgroup thus reads the same number of blocks
 // whatever the length mix, and a range spans only a few sequences.  Inside
 // the range a wave walks piece by piece (a piece is the part of one
 // sequence inside the range), keeping a ring of register buffers so that
@@ -70,6 +71,7 @@ struct Plan {
   const int* pre;   // [S + 1] blocks before sequence s; pre[S] = T
   const int* lens;  // [S] context lengths (clamped to the table capacity)
   int S, T, q, R, HG;
+  int SUB;          // waves per kv head in a workgroup (fewer kv heads than waves)
 };
 
 // Dynamic LDS bytes for a plan over S sequences.
@@ -110,9 +112,32 @@ __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
   pl.S = S;
   pl.T = T;
   pl.HG = (a.num_kv_heads + kWaves - 1) / kWaves;
-  pl.R = max(1, (int)gridDim.x / pl.HG);
+  // With fewer kv heads than waves, the spare waves of a workgroup take
+  // further ranges of the same heads instead of idling: SUB adjacent ranges
+  // per head and workgroup.
+  pl.SUB = a.num_kv_heads >= kWaves ? 1 : kWaves / a.num_kv_heads;
+  pl.R = max(1, (int)gridDim.x / pl.HG) * pl.SUB;
   pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
   return pl;
+}
+
+// The kv head and range of one wave: wave w of head group hg takes head
+// hg * kWaves + w; with fewer kv heads than waves (SUB > 1), head w % H_kv
+// and range rw * SUB + w / H_kv of the workgroup's SUB adjacent ranges.
+// False for a wave with nothing to do.
+__device__ __forceinline__ bool wave_work(const DecodeArgs& a, const Plan& pl, int wave, int* g,
+                                          int* r) {
+  const int hg = blockIdx.x % pl.HG, rw = blockIdx.x / pl.HG;
+  if (pl.SUB == 1) {
+    *g = hg * kWaves + wave;
+    *r = rw;
+  } else {
+    const int sr = wave / a.num_kv_heads;
+    if (sr >= pl.SUB) return false;
+    *g = wave % a.num_kv_heads;
+    *r = rw * pl.SUB + sr;
+  }
+  return *g < a.num_kv_heads && *r < pl.R;
 }
 
 // Pieces sequence s is cut into (0 for an empty sequence).
@@ -604,13 +629,11 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kerne
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
-  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
-  if (r >= pl.R) return;
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = hg * kWaves + wave;
-  if (g >= a.num_kv_heads) return;
+  int g, r;
+  if (!wave_work(a, pl, wave, &g, &r)) return;
   walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
@@ -619,12 +642,10 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kern
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
-  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
-  if (r >= pl.R) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = hg * kWaves + wave;
-  if (g >= a.num_kv_heads) return;
+  int g, r;
+  if (!wave_work(a, pl, wave, &g, &r)) return;
   walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma8_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
@@ -802,12 +823,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) 
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<kBlock>(a, plan_lds);
   if (blockIdx.x == 0) write_seg_counts(a, pl);
-  const int hg = blockIdx.x % pl.HG, r = blockIdx.x / pl.HG;
-  if (r >= pl.R) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = hg * kWaves + wave;
-  if (g >= a.num_kv_heads) return;
+  int g, r;
+  if (!wave_work(a, pl, wave, &g, &r)) return;
   walk_range<kBlock>(a, pl, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
 }
 
