@@ -145,11 +145,12 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  *                  max_blocks_per_seq * block_size in 32 pieces, rounded up
  *                  to whole blocks); otherwise a positive multiple of
  *                  block_size.  The work is split by
- *                  blocks, not by sequence: per group of 4 kv heads the
- *                  batch's blocks, sequence after sequence, are cut into
- *                  equal contiguous ranges, one per workgroup of a grid that
- *                  fills the chip, each range at least partition_tokens
- *                  long.  A sequence cut by range boundaries is processed in
+ *                  blocks, not by sequence: for each kv head the batch's
+ *                  blocks, sequence after sequence, are cut into equal
+ *                  contiguous ranges, each streamed by one wave of a grid
+ *                  that fills the chip (a workgroup's waves take
+ *                  consecutive (kv head, range) pairs), each range at least
+ *                  partition_tokens long.  A sequence cut by range boundaries is processed in
  *                  pieces whose (max, sum-exp, unnormalised output) partials
  *                  go to `workspace` and are combined by a second kernel.
  *   workspace:     device buffer of at least pa_decode_workspace_bytes(...)

@@ -12,8 +12,9 @@
 // and so on.  The grid is persistent (as many workgroups as fit on the chip
 // at once) and every workgroup takes one equal, contiguous range of that
 // list for one head group; its 4 waves each stream the range for one kv head
-// of the group (with fewer than 4 kv heads, the spare waves stream further,
-// adjacent ranges of the same heads).  Every workgroup thus reads the same number of blocks
+// of the group (with fewer kv heads, or a count that is not a multiple of 4,
+// the waves take the next (head, range) pairs in turn, so none idles).
+// Every workgroup thus reads the same number of blocks
 // whatever the length mix, and a range spans only a few sequences.  Inside
 // the range a wave walks piece by piece (a piece is the part of one
 // sequence inside the range), keeping a ring of register buffers so that
@@ -70,8 +71,7 @@ struct Unit {
 struct Plan {
   const int* pre;   // [S + 1] blocks before sequence s; pre[S] = T
   const int* lens;  // [S] context lengths (clamped to the table capacity)
-  int S, T, q, R, HG;
-  int SUB;          // waves per kv head in a workgroup (fewer kv heads than waves)
+  int S, T, q, R;   // R: ranges per kv head
 };
 
 // Dynamic LDS bytes for a plan over S sequences.
@@ -111,33 +111,24 @@ __device__ Plan build_plan(const DecodeArgs& a, int* lds) {
   pl.lens = lens;
   pl.S = S;
   pl.T = T;
-  pl.HG = (a.num_kv_heads + kWaves - 1) / kWaves;
-  // With fewer kv heads than waves, the spare waves of a workgroup take
-  // further ranges of the same heads instead of idling: SUB adjacent ranges
-  // per head and workgroup.
-  pl.SUB = a.num_kv_heads >= kWaves ? 1 : kWaves / a.num_kv_heads;
-  pl.R = max(1, (int)gridDim.x / pl.HG) * pl.SUB;
+  // every wave of the grid streams one (kv head, range) pair: R ranges per head
+  pl.R = max(1, (int)(gridDim.x * kWaves) / a.num_kv_heads);
   pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
   return pl;
 }
 
-// The kv head and range of one wave: wave w of head group hg takes head
-// hg * kWaves + w; with fewer kv heads than waves (SUB > 1), head w % H_kv
-// and range rw * SUB + w / H_kv of the workgroup's SUB adjacent ranges.
-// False for a wave with nothing to do.
+// The kv head and range of one wave.  The grid's waves, numbered
+// blockIdx * kWaves + wave, take the (head, range) pairs in order, heads
+// fastest: with a multiple of kWaves kv heads a workgroup streams one range
+// for kWaves consecutive heads (their blocks sit next to each other in the
+// pool); with fewer kv heads, or a count that does not divide evenly, no
+// wave idles but the last few.  False for a wave with nothing to do.
 __device__ __forceinline__ bool wave_work(const DecodeArgs& a, const Plan& pl, int wave, int* g,
                                           int* r) {
-  const int hg = blockIdx.x % pl.HG, rw = blockIdx.x / pl.HG;
-  if (pl.SUB == 1) {
-    *g = hg * kWaves + wave;
-    *r = rw;
-  } else {
-    const int sr = wave / a.num_kv_heads;
-    if (sr >= pl.SUB) return false;
-    *g = wave % a.num_kv_heads;
-    *r = rw * pl.SUB + sr;
-  }
-  return *g < a.num_kv_heads && *r < pl.R;
+  const int slot = blockIdx.x * kWaves + wave;
+  *g = slot % a.num_kv_heads;
+  *r = slot / a.num_kv_heads;
+  return *r < pl.R;
 }
 
 // Pieces sequence s is cut into (0 for an empty sequence).
@@ -933,9 +924,9 @@ Launch decode_launch(const DecodeArgs& a, K kernel) {
       n = 1;
     per_cu = std::min(n, kMaxWgPerCu);
   }
-  const int hg = (a.num_kv_heads + kWaves - 1) / kWaves;
-  const int ranges = std::max(1, cu_count() * per_cu / hg);
-  return {dim3((unsigned)(ranges * hg)), dim3(kWaves * 64), lds};
+  // at least one wave per kv head, so that every head has a range
+  const int grid = std::max(cu_count() * per_cu, (a.num_kv_heads + kWaves - 1) / kWaves);
+  return {dim3((unsigned)grid), dim3(kWaves * 64), lds};
 }
 
 // The head group (1..16) fills the 16 head slots of the MFMA tiles at run

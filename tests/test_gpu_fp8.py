@@ -91,6 +91,16 @@ def _custom_fp8_case(lens, Hq, Hkv, d, nb, width, seed):
     return c
 
 
+@pytest.mark.parametrize("Hkv", [1, 3, 6])
+def test_fp8_decode_kv_head_counts(pk, Hkv):
+    """Kv-head counts that are not a multiple of four on the 8-bit kernel."""
+    lens = (1, 16, 17, 300, 1000)
+    c = _custom_fp8_case(lens, Hq=4 * Hkv, Hkv=Hkv, d=128, nb=300, width=63, seed=600 + Hkv)
+    ref = oracle.decode(*c.oracle_inputs(), c.scale)
+    for P in (0, 64):
+        _check(_to64(_decode(pk, c, P)), ref, f"fp8 Hkv={Hkv} P={P}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.3, 4.0])
 def test_fp8_decode_extreme_scales(pk, scale):
     """Zero, negative and large attention scales on the 8-bit kernel, whose

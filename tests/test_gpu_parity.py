@@ -127,6 +127,21 @@ def test_decode_extreme_scales(pk, scale):
         _check(_to64(out), ref, dtype, f"scale={scale} Hq={Hq} {dtype}")
 
 
+@pytest.mark.parametrize("Hkv", [1, 3, 5, 6, 12])
+def test_decode_kv_head_counts(pk, Hkv):
+    """Kv-head counts that are not a multiple of a workgroup's four waves:
+    the grid's waves take (kv head, range) pairs in turn, so a workgroup can
+    mix heads and ranges.  MFMA and fp32 VALU kernels, two partition
+    floors, every output against the oracle."""
+    lens = (1, 16, 17, 100, 511, 1200)
+    for G, dtype in ((2, "bf16"), (3, "f32")):
+        c = _custom_case(lens, Hq=G * Hkv, Hkv=Hkv, d=64, nb=300, width=80, seed=500 + Hkv,
+                         dtype=dtype)
+        ref = oracle.decode(*c.oracle_inputs(), c.scale)
+        for P in (0, 64):
+            _check(_to64(_gpu_decode(pk, c, P)), ref, dtype, f"Hkv={Hkv} G={G} {dtype} P={P}")
+
+
 def test_decode_fp32_group_sizes(pk):
     for G in (1, 2, 4):
         cfg = CONFIGS["tiny_f32"].scaled(num_seqs=5, num_q_heads=G, num_kv_heads=1, head_dim=128,
