@@ -300,6 +300,63 @@ def test_pools_beyond_4_gib(pk):
     torch.cuda.empty_cache()
 
 
+def test_write_and_decode_replayed_from_a_hip_graph(pk):
+    """A decode step's device work -- slot write, then decode with a caller
+    workspace -- captured once in a HIP graph (the calls allocate, memset
+    and synchronize nothing) and replayed three times.  Between replays the
+    program writes new queries, new token rows and new slots eagerly; every
+    replay must equal the same two calls run eagerly on a second copy of the
+    pools, bit for bit."""
+    rng = np.random.default_rng(77)
+    lens = (5, 16, 17, 200, 700)
+    c = _custom_case(lens, Hq=8, Hkv=2, d=128, nb=300, width=44, seed=78)
+    k, v = c.k_pool, c.v_pool
+    kr, vr = k.clone(), v.clone()
+    T = 8
+    kn = torch.empty((T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    slots = torch.empty(T, dtype=torch.int64, device="cuda")
+    q = c.q.clone()
+    out = torch.empty_like(q)
+    S, maxB = len(lens), c.block_tables.shape[1]
+    ws = torch.empty(pk.pa_decode_workspace_bytes(k, v, S, 8, maxB), dtype=torch.uint8,
+                     device="cuda")
+
+    def fill(i):
+        g = torch.Generator().manual_seed(1000 + i)
+        q.copy_(torch.randn(q.shape, generator=g).to(torch.bfloat16))
+        kn.copy_(torch.randn(kn.shape, generator=g).to(torch.bfloat16))
+        vn.copy_(torch.randn(vn.shape, generator=g).to(torch.bfloat16))
+        slots.copy_(torch.from_numpy(rng.permutation(300 * 16)[:T].astype(np.int64)))
+
+    def step(kp, vp, o, w):
+        pk.pa_kv_write(kp, vp, kn, vn, slots)
+        pk.pa_decode(q, kp, vp, c.block_tables, c.context_lens, c.scale, out=o, workspace=w)
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(k, v, out, ws)            # warm-up before capture (launch set-up done once)
+        step(kr, vr, torch.empty_like(out), ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(k, v, out, ws)
+    ws_ref = torch.empty_like(ws)
+    for i in range(1, 4):
+        fill(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        ref = torch.empty_like(out)
+        step(kr, vr, ref, ws_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(k, kr) and torch.equal(v, vr), f"replay {i}: pools differ"
+        assert torch.equal(out, ref), f"replay {i}: decode output differs"
+        assert torch.isfinite(out.float()).all()
+
+
 # --- full-size configs: every output ------------------------------------------
 FULL = ["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing", "long_context_128k"]
 
