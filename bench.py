@@ -93,6 +93,9 @@ def parse():
                     help="decode (default) or extend: chunked prefill over paged prefixes")
     ap.add_argument("--extend-seqs", type=int, default=32)
     ap.add_argument("--chunk", type=int, default=256, help="new tokens per sequence per step")
+    ap.add_argument("--no-share", action="store_true",
+                    help="prefix-sharing configs: read shared blocks once per sequence, not "
+                         "once per prefix group")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache storage: bf16, or 8-bit E4M3 codes + per-token scales")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -151,8 +154,10 @@ def main():
         f"pool={num_blocks} blocks width={width}")
 
     fp8 = args.kv == "fp8"
+    share = bool(shared) and not args.no_share
     cache = PagedKVCache(num_blocks, Hkv, d, S, width, block_size=B, shuffle_seed=cfg.seed,
-                         dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+                         dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev,
+                         share_prefixes=share, max_group=max(1, 16 // (Hq // Hkv)))
     g = torch.Generator(device=dev)
     g.manual_seed(cfg.seed)
     if shared:

@@ -109,10 +109,13 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool,
                       const int64_t* slot_mapping, int32_t T, void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for these sizes (non-zero for
- * num_seqs > 0: per-piece partials and per-sequence piece counts).
- * partition_tokens as for pa_decode.  Returns 0 also for invalid arguments;
- * pa_decode reports those.
+ * Bytes of device workspace pa_decode (and pa_decode_shared) need for these
+ * sizes: per-piece partials and per-sequence piece locations.  The partials
+ * are bounded by the launch grid, not by the batch or the table width: each
+ * (range, kv head) wave of the persistent grid leaves at most two cut
+ * pieces, so for 256 CUs, 128-dim heads and 4 query heads per kv head about
+ * 17 MB, and 4 KiB more per 256 sequences (at most 64 KiB).  Returns 0 for
+ * num_seqs = 0 and for invalid arguments; pa_decode reports those.
  */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq,
@@ -167,6 +170,54 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const int32_t* context_lens, float scale, void* out,
                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * pa_decode over prefix groups: sequences that share the blocks of a common
+ * prefix (vLLM post, "The bonus contiguous storage can't give you: sharing":
+ * parallel samples of one prompt point their tables at the same physical
+ * blocks; glossary entry, "Sampling Algorithms": the shared prompt's pages
+ * are stored once and not recomputed).  Each shared block is streamed from
+ * HBM once for all of its group's members, whose query heads fill the head
+ * slots of one MFMA tile; each member's remaining blocks are read as in
+ * pa_decode, and the two parts combine through the split-context partials.
+ * The result is the same attention as pa_decode's (up to the order of fp32
+ * sums).
+ *   group_start:   int32 [num_groups + 1], device: the groups partition the
+ *                  batch into runs of consecutive sequences, group i being
+ *                  sequences group_start[i] .. group_start[i+1] - 1
+ *                  (group_start[0] = 0, strictly increasing,
+ *                  group_start[num_groups] = num_seqs).
+ *   shared_blocks: int32 [num_groups], device: the first shared_blocks[i]
+ *                  table entries of every member of group i name the same
+ *                  physical blocks, and each of those blocks is full (below
+ *                  every member's context length).  0: nothing shared.
+ * pa_bm_prefix_groups produces both.  A group shares only when its members'
+ * query heads fit one tile (members * heads per kv head <= 16) and the pool
+ * is bf16 or 8-bit; otherwise its blocks are read per sequence.
+ * num_groups = 0 is pa_decode.  The workspace must hold at least
+ * pa_decode_shared_workspace_bytes(...) bytes (contents on entry are
+ * irrelevant).  With
+ * PA_DEBUG=1 the groups are validated too (PA_EINVAL if they break the
+ * rules above).
+ */
+pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                           const void* q, int32_t num_seqs, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, float scale, void* out,
+                           int32_t partition_tokens, int32_t num_groups,
+                           const int32_t* group_start, const int32_t* shared_blocks,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode_shared needs: pa_decode's, plus two
+ * partial rows (fp32 max, sum and head_dim outputs) per query head of each
+ * sequence of one launch (up to 2048 sequences), since a grouped sequence's
+ * own blocks and its share of the group's blocks always combine.  0 for
+ * num_seqs = 0 and for invalid arguments.
+ */
+size_t pa_decode_shared_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                        int32_t partition_tokens);
 
 /*
  * Multi-token paged attention: extend / chunked prefill over a paged prefix

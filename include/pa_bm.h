@@ -171,6 +171,28 @@ pa_status pa_bm_export(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
                        int32_t* tables_out, int32_t width, int32_t pad_block,
                        int32_t* lens_out);
 
+/*
+ * Prefix groups of a decode batch, for pa_decode_shared (vLLM post, "The
+ * bonus contiguous storage can't give you: sharing": parallel samples of
+ * one prompt point their block tables at the same physical blocks, which
+ * are stored once; glossary entry, "Sampling Algorithms": the shared
+ * prompt's pages need not be read or computed again per sample).  Walks
+ * seqs[0..n_seqs) in order and cuts it into runs of consecutive sequences.
+ * A run starts at sequence i with S = the number of full blocks (below the
+ * token count) of i; the next sequence joins while the run has fewer than
+ * max_members members and its first c >= 1 table entries equal i's, c
+ * counted among the first min(S, its own full blocks) entries; then S = c.
+ * The run shares S blocks (0 for a run of one).  Outputs:
+ *   group_start_out[n_seqs + 1]  batch index of each group's first member,
+ *                                then n_seqs (caller-allocated, host),
+ *   shared_blocks_out[n_seqs]    full blocks each group shares,
+ *   *n_groups_out                number of groups.
+ * PA_EINVAL for an unknown, freed or swapped-out sequence.  Read only.
+ */
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
+                              int32_t max_members, int32_t* group_start_out,
+                              int32_t* shared_blocks_out, int32_t* n_groups_out);
+
 /* Refcount of one block (-1 if out of range). */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
 

@@ -158,6 +158,56 @@ class BlockManagerModel:
         seq.n_tokens = pend
         return OK, slots, pairs
 
+    def append_batch(self, seqs, ns):
+        """Appends to several sequences as one all-or-nothing step: the
+        appends run one after another in the order given; if any lacks
+        blocks, nothing changes.  Returns (status, slots, cow_pairs)."""
+        if len(set(seqs)) != len(seqs) or any(not self._resident(s) or n < 0
+                                               for s, n in zip(seqs, ns)):
+            return EINVAL, [], []
+        snap = ([list(q.table) for q in self.seqs], [q.n_tokens for q in self.seqs],
+                list(self.free), list(self.refcount), self.cow_copies)
+        slots, pairs = [], []
+        for s, n in zip(seqs, ns):
+            st, sl, pr = self.append(s, n)
+            if st != OK:
+                for q, t, n_tok in zip(self.seqs, snap[0], snap[1]):
+                    q.table, q.n_tokens = t, n_tok
+                self.free, self.refcount, self.cow_copies = snap[2], snap[3], snap[4]
+                return st, [], []
+            slots += sl
+            pairs += pr
+        return OK, slots, pairs
+
+    def prefix_groups(self, seqs, max_members: int):
+        """Runs of consecutive batch entries that share leading full blocks:
+        a run starting at sequence i may share its S full blocks; the next
+        sequence joins (while the run has fewer than max_members) if its
+        first c >= 1 entries among the first min(S, its full blocks) equal
+        i's, and then S = c.  Returns (group_start, shared_blocks)."""
+        B = self.B
+        gs, sb = [], []
+        i = 0
+        while i < len(seqs):
+            first = self.seqs[seqs[i]]
+            shared = first.n_tokens // B
+            j = i + 1
+            while j < len(seqs) and j - i < max_members:
+                q = self.seqs[seqs[j]]
+                lim = min(shared, q.n_tokens // B)
+                c = 0
+                while c < lim and q.table[c] == first.table[c]:
+                    c += 1
+                if c == 0:
+                    break
+                shared = c
+                j += 1
+            gs.append(i)
+            sb.append(shared if j - i > 1 else 0)
+            i = j
+        gs.append(len(seqs))
+        return gs, sb
+
     def _drop_device_refs(self, seq: _Seq):
         for b in reversed(seq.table):
             self.refcount[b] -= 1

@@ -64,11 +64,16 @@ def _load():
         "pa_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_decode_partition_tokens": (i32, [P, i32, i32, i32, i32]),
         "pa_decode": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp, sz, vp]),
+        "pa_decode_shared": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, i32, vp,
+                                   vp, vp, sz, vp]),
+        "pa_decode_shared_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_block_copy": (i32, [P, vp, vp, vp, i32, vp]),
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
         "pa_kv_append": (i32, [P, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]),
         "pa_block_swap": (i32, [P, vp, vp, vp, vp, i32, vp, i32, i32, vp]),
         "pa_extend": (i32, [P, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, f32, vp, vp]),
+        "pa_probe_sink_bytes": (sz, [i32]),
+        "pa_probe_read": (i32, [vp, vp, i32, ctypes.c_uint32, i32, vp, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_version": (ctypes.c_char_p, []),
         "pa_bm_create": (vp, [i32, i32, ctypes.c_uint64]),
@@ -82,6 +87,7 @@ def _load():
         "pa_bm_export": (i32, [vp, vp, i32, vp, i32, i32, vp]),
         "pa_bm_refcount": (i32, [vp, i32]),
         "pa_bm_free_list": (i32, [vp, vp, i32]),
+        "pa_bm_prefix_groups": (i32, [vp, vp, i32, i32, vp, vp, vp]),
         "pa_bm_stats": (i32, [vp, ctypes.POINTER(BMStats)]),
         "pa_bm_set_host_blocks": (i32, [vp, i32]),
         "pa_bm_swap_out": (i32, [vp, i32, vp, vp]),
@@ -99,12 +105,13 @@ def _load():
 _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
+    "pa_decode_shared", "pa_decode_shared_workspace_bytes",
     "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
-    "pa_status_str",
+    "pa_status_str", "pa_probe_sink_bytes", "pa_probe_read",
     "pa_version", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch",
     "pa_bm_free_seq", "pa_bm_block_table", "pa_bm_export", "pa_bm_refcount",
-    "pa_bm_free_list", "pa_bm_stats", "pa_bm_set_host_blocks", "pa_bm_swap_out",
+    "pa_bm_free_list", "pa_bm_prefix_groups", "pa_bm_stats", "pa_bm_set_host_blocks", "pa_bm_swap_out",
     "pa_bm_swap_in", "pa_bm_is_swapped", "pa_bm_host_free_list")
 
 
@@ -222,11 +229,44 @@ def pa_decode_workspace_bytes(k_pool, v_pool, num_seqs, num_q_heads, max_blocks_
                                               max_blocks_per_seq, partition_tokens))
 
 
+def pa_decode_shared_workspace_bytes(k_pool, v_pool, num_seqs, num_q_heads,
+                                     max_blocks_per_seq, partition_tokens=0):
+    desc = pool_desc(k_pool, v_pool)
+    return int(_lib.pa_decode_shared_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                                     max_blocks_per_seq, partition_tokens))
+
+
 def pa_decode_partition_tokens(k_pool, v_pool, num_seqs, num_q_heads, max_blocks_per_seq,
                                partition_tokens=0):
     desc = pool_desc(k_pool, v_pool)
     return int(_lib.pa_decode_partition_tokens(ctypes.byref(desc), num_seqs, num_q_heads,
                                                max_blocks_per_seq, partition_tokens))
+
+
+def _decode_args(q, k_pool, v_pool, block_tables, context_lens, out):
+    S, Hq, d = q.shape
+    desc = pool_desc(k_pool, v_pool)
+    if d != desc.head_dim or q.dtype != io_dtype(k_pool):
+        raise ValueError("q must be [S][Hq][head_dim] in the pool's element type")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    return desc, S, Hq, block_tables.shape[1], out
+
+
+def _workspace(desc, S, Hq, maxB, partition_tokens, workspace, device, shared=False):
+    query = _lib.pa_decode_shared_workspace_bytes if shared else _lib.pa_decode_workspace_bytes
+    need = int(query(ctypes.byref(desc), S, Hq, maxB, partition_tokens))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return ws_ptr, ws_bytes
 
 
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
@@ -236,30 +276,37 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
     ``workspace`` is a uint8 GPU tensor of at least pa_decode_workspace_bytes
     bytes; when None one is allocated here with torch (the library itself
     never allocates)."""
-    S, Hq, d = q.shape
-    desc = pool_desc(k_pool, v_pool)
-    if d != desc.head_dim or q.dtype != io_dtype(k_pool):
-        raise ValueError("q must be [S][Hq][head_dim] in the pool's element type")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise TypeError("block_tables and context_lens must be int32")
-    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.numel() != S:
-        raise ValueError("block_tables must be [S][max_blocks] and context_lens [S]")
-    maxB = block_tables.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
-        raise ValueError("out must match q")
-    need = int(_lib.pa_decode_workspace_bytes(ctypes.byref(desc), S, Hq, maxB,
-                                              partition_tokens))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device)
     st = _lib.pa_decode(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                         _dev(q, "q"), S, Hq, _dev(block_tables, "block_tables"), maxB,
                         _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
                         int(partition_tokens), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def pa_decode_shared(q, k_pool, v_pool, block_tables, context_lens, scale, group_start,
+                     shared_blocks, out=None, partition_tokens=0, workspace=None, stream=None):
+    """pa_decode over prefix groups (int32 GPU tensors ``group_start``
+    [G+1] and ``shared_blocks`` [G], e.g. from BlockManager.prefix_groups):
+    each group's shared blocks are read once for all of its members."""
+    desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    if group_start.dtype != torch.int32 or shared_blocks.dtype != torch.int32:
+        raise TypeError("group_start and shared_blocks must be int32")
+    n = shared_blocks.numel()
+    if group_start.numel() != n + 1:
+        raise ValueError("group_start must have one entry more than shared_blocks")
+    ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device,
+                                  shared=n > 0)
+    st = _lib.pa_decode_shared(
+        ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(q, "q"), S, Hq,
+        _dev(block_tables, "block_tables"), maxB, _dev(context_lens, "context_lens"),
+        float(scale), _dev(out, "out"), int(partition_tokens), n,
+        _dev(group_start, "group_start") if n else ctypes.c_void_p(0),
+        _dev(shared_blocks, "shared_blocks") if n else ctypes.c_void_p(0),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "pa_decode_shared")
     return out
 
 
@@ -381,6 +428,26 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, seq_i
                            _dev(seq_ids, "seq_ids"), _dev(positions, "positions"),
                            _stream(stream))
     _check(st, "pa_kv_append")
+
+
+def pa_probe_read(buf, order, chunk_bytes, workgroups, sink=None, stream=None):
+    """Read buf's chunks in the given order (pa_probe_read); returns sink."""
+    if order.dtype != torch.int32:
+        raise TypeError("order must be int32")
+    need = int(_lib.pa_probe_sink_bytes(int(workgroups)))
+    if sink is None:
+        sink = torch.empty(need, dtype=torch.uint8, device=buf.device)
+    if sink.numel() * sink.element_size() < need:
+        raise ValueError("sink too small")
+    n = order.numel()
+    if n * int(chunk_bytes) > buf.numel() * buf.element_size():
+        raise ValueError("chunks reach past the buffer")
+    if n and int(order.max()) * int(chunk_bytes) + int(chunk_bytes) > buf.numel() * buf.element_size():
+        raise ValueError("a chunk index reaches past the buffer")
+    st = _lib.pa_probe_read(_dev(buf, "buf"), _dev(order, "order"), n, int(chunk_bytes),
+                            int(workgroups), _dev(sink, "sink"), _stream(stream))
+    _check(st, "pa_probe_read")
+    return sink
 
 
 from .block_manager import BlockManager  # noqa: E402,F401

@@ -133,6 +133,18 @@ class BlockManager:
         self._lib.pa_bm_host_free_list(self._h, _ptr(out), n)
         return out[:n].tolist()
 
+    def prefix_groups(self, seqs, max_members: int):
+        """(status, group_start [n_groups + 1], shared_blocks [n_groups]) for a
+        decode batch in the order given (pa_bm_prefix_groups)."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = len(seqs)
+        gs = np.zeros(n + 1, np.int32)
+        sb = np.zeros(max(n, 1), np.int32)
+        k = ctypes.c_int32()
+        st = self._lib.pa_bm_prefix_groups(self._h, _ptr(seqs), n, int(max_members), _ptr(gs),
+                                           _ptr(sb), ctypes.byref(k))
+        return st, gs[:k.value + 1].copy(), sb[:k.value].copy()
+
     def refcount(self, block: int) -> int:
         return int(self._lib.pa_bm_refcount(self._h, int(block)))
 

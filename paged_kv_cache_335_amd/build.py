@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_extend.hip", "pa_cache_ops.hip"]
+HIP_SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_extend.hip", "pa_cache_ops.hip", "pa_probe.hip"]
 C_SOURCES = ["bm.c"]
 
 HIPCC_FLAGS = [

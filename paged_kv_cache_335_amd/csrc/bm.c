@@ -61,7 +61,7 @@ pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_see
   bm->block_size = block_size;
   bm->free_stack = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_blocks);
   bm->refcount = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
-  bm->scratch = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_blocks);
+  bm->scratch = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t)); /* kept zero between calls */
   if (!bm->free_stack || !bm->refcount || !bm->scratch) {
     pa_bm_destroy(bm);
     return NULL;
@@ -227,14 +227,33 @@ pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* n_to
     memset(bm->stamp, 0, sizeof(uint32_t) * (size_t)bm->seq_cap);
     bm->epoch = 1;
   }
-  int64_t need_total = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     int32_t s = seqs[i];
     if (!resident(bm, s) || n_tokens[i] < 0 || bm->stamp[s] == bm->epoch) return PA_EINVAL;
     if ((int64_t)bm->seqs[s].n_tokens + n_tokens[i] > INT32_MAX) return PA_EINVAL;
     bm->stamp[s] = bm->epoch;
-    int cow;
-    need_total += blocks_needed(bm, &bm->seqs[s], n_tokens[i], &cow);
+  }
+  /* Blocks the batch takes, counted as the appends will run, one after
+   * another: each copy-on-write drops the shared tail's refcount, so of k
+   * sharers of a partly filled tail only the first k - 1 copy and the last
+   * writes in place.  scratch[b] counts the drops of block b so far. */
+  int64_t need_total = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const bm_seq* q = &bm->seqs[seqs[i]];
+    const int32_t n = n_tokens[i];
+    const int64_t end = (int64_t)q->n_tokens + n;
+    need_total += (end + bm->block_size - 1) / bm->block_size - q->len;
+    if (n > 0 && q->n_tokens % bm->block_size != 0) {
+      const int32_t tail = q->table[q->len - 1];
+      if (bm->refcount[tail] - bm->scratch[tail] > 1) {
+        need_total += 1;
+        bm->scratch[tail] += 1;
+      }
+    }
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) { /* scratch back to zero */
+    const bm_seq* q = &bm->seqs[seqs[i]];
+    if (q->len > 0) bm->scratch[q->table[q->len - 1]] = 0;
   }
   if (need_total > bm->n_free) {
     bm->enomem_events += 1;
@@ -320,7 +339,10 @@ pa_status pa_bm_swap_out(pa_bm* bm, int32_t seq, int32_t* pairs_out, int32_t* n_
     pairs_out[2 * j + 1] = host[j];
   }
   release_device_blocks(bm, q); /* refcounts checked above */
-  for (int32_t j = 0; j < q->len; ++j) q->table[j] = host[j];
+  for (int32_t j = 0; j < q->len; ++j) {
+    q->table[j] = host[j];
+    host[j] = 0;
+  }
   q->swapped = 1;
   bm->swapped_out_blocks += q->len;
   *n_pairs = q->len;
@@ -428,7 +450,10 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
       if (f > fill[q->table[j]]) fill[q->table[j]] = f;
     }
   }
-  for (int32_t b = 0; b < bm->num_blocks; ++b) out->stored_tokens += fill[b];
+  for (int32_t b = 0; b < bm->num_blocks; ++b) {
+    out->stored_tokens += fill[b];
+    fill[b] = 0;
+  }
   out->allocated_slots = out->used_blocks * B;
   out->cow_copies = bm->cow_copies;
   out->enomem_events = bm->enomem_events;
@@ -436,5 +461,42 @@ pa_status pa_bm_stats(const pa_bm* bm, pa_bm_stats_t* out) {
   out->host_free_blocks = bm->n_host_free;
   out->swapped_out_blocks = bm->swapped_out_blocks;
   out->swapped_in_blocks = bm->swapped_in_blocks;
+  return PA_OK;
+}
+
+pa_status pa_bm_prefix_groups(const pa_bm* bm, const int32_t* seqs, int32_t n_seqs,
+                              int32_t max_members, int32_t* group_start_out,
+                              int32_t* shared_blocks_out, int32_t* n_groups_out) {
+  if (!bm || n_seqs < 0 || max_members < 1 || !n_groups_out) return PA_EINVAL;
+  *n_groups_out = 0;
+  if (n_seqs == 0) {
+    if (group_start_out) group_start_out[0] = 0;
+    return PA_OK;
+  }
+  if (!seqs || !group_start_out || !shared_blocks_out) return PA_EINVAL;
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (!resident(bm, seqs[i])) return PA_EINVAL;
+  const int32_t B = bm->block_size;
+  int32_t k = 0, i = 0;
+  while (i < n_seqs) {
+    const bm_seq* first = &bm->seqs[seqs[i]];
+    int32_t shared = first->n_tokens / B; /* full blocks of the first member */
+    int32_t j = i + 1;
+    while (j < n_seqs && j - i < max_members) {
+      const bm_seq* q = &bm->seqs[seqs[j]];
+      int32_t lim = q->n_tokens / B < shared ? q->n_tokens / B : shared;
+      int32_t c = 0;
+      while (c < lim && q->table[c] == first->table[c]) ++c;
+      if (c == 0) break;
+      shared = c;
+      ++j;
+    }
+    group_start_out[k] = i;
+    shared_blocks_out[k] = j - i > 1 ? shared : 0;
+    ++k;
+    i = j;
+  }
+  group_start_out[k] = n_seqs;
+  *n_groups_out = k;
   return PA_OK;
 }

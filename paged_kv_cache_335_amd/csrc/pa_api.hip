@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "pa_internal.h"
@@ -64,25 +65,150 @@ int32_t default_piece(int64_t max_len, int32_t block_size) {
   return static_cast<int32_t>(std::min<int64_t>(kDefaultMinPiece, std::max<int64_t>(block_size, p)));
 }
 
+// Head slots of one partial row group: the query heads of one kv head, or
+// with prefix groups as many members' heads as fill the 16-slot MFMA tile.
+int32_t part_slots(int32_t group, bool grouped) {
+  return grouped && group <= pakv::kMaxMfmaGroup ? (pakv::kMaxMfmaGroup / group) * group : group;
+}
+
+// Workspace layout: part_m, part_l [rows], part_o [rows][d] (fp32), then
+// seg_info int32 [min(S, plan size)][4].  rows = 2 * waves of the grid *
+// head slots (each (range, kv head) wave leaves at most two cut pieces);
+// with prefix groups 2 * Hq more per sequence of one launch (segments that
+// are not cut but still combine: a member's own blocks and its share of
+// the group's blocks).
+struct WsLayout {
+  size_t rows, range_rows, off_l, off_o, off_info, bytes;
+};
+
+WsLayout ws_layout(const pa_pool* pool, int32_t S, int32_t Hq, bool grouped) {
+  const int32_t G = Hq / pool->num_kv_heads;
+  WsLayout w{};
+  w.range_rows = (size_t)2 * pakv::decode_grid(pool->num_kv_heads) * pakv::kWaves *
+                 std::max(part_slots(G, true), part_slots(G, false));
+  w.rows = w.range_rows +
+           (grouped ? (size_t)2 * std::min(S, pakv::kMaxPlanSeqs / 2) * Hq : 0);
+  w.off_l = align_up(w.rows * sizeof(float));
+  w.off_o = w.off_l + align_up(w.rows * sizeof(float));
+  w.off_info = w.off_o + align_up(w.rows * pool->head_dim * sizeof(float));
+  w.bytes = w.off_info + align_up((size_t)std::min(S, pakv::kMaxPlanSeqs) * 4 * sizeof(int32_t));
+  return w;
+}
+
 pa_status decode_sizes(const pa_pool* pool, int32_t S, int32_t Hq, int32_t maxB,
-                       int32_t req_piece, int32_t* P_out, int32_t* slots_out,
-                       size_t* ws_out) {
+                       int32_t req_piece, bool grouped, int32_t* P_out, size_t* ws_out) {
   if (!pool_ok(pool) || S < 0 || Hq <= 0 || maxB <= 0) return PA_EINVAL;
   if (Hq % pool->num_kv_heads != 0) return PA_EINVAL;
   if (req_piece < 0 || (req_piece > 0 && req_piece % pool->block_size != 0)) return PA_EINVAL;
   if ((int64_t)maxB * pool->block_size > INT32_MAX) return PA_EINVAL;
+  if (grouped && (int64_t)std::min(S, pakv::kMaxPlanSeqs / 2) * Hq * 2 > INT32_MAX / 4)
+    return PA_EINVAL;
   const int64_t max_len = (int64_t)maxB * pool->block_size;
-  const int32_t P = req_piece > 0 ? req_piece : default_piece(max_len, pool->block_size);
-  // a sequence of n blocks meets at most ceil(n / min piece) + 1 ranges
-  const int64_t slots = (max_len + P - 1) / P + 1;
-  if (slots > pakv::kMaxSlots) return PA_EINVAL;
-  const size_t n = (size_t)S * Hq * slots;
-  *P_out = P;
-  *slots_out = static_cast<int32_t>(slots);
-  *ws_out = S == 0 ? 0
-                   : 2 * align_up(n * sizeof(float)) + align_up(n * pool->head_dim * sizeof(float)) +
-                         align_up((size_t)S * sizeof(int32_t));
+  *P_out = req_piece > 0 ? req_piece : default_piece(max_len, pool->block_size);
+  *ws_out = S == 0 ? 0 : ws_layout(pool, S, Hq, grouped).bytes;
   return PA_OK;
+}
+
+// Prefix groups, validated on the host under PA_DEBUG: they partition the
+// batch into runs of consecutive sequences, and group i's first
+// shared_blocks[i] table entries are the same blocks in every member and
+// full in every member.
+pa_status check_groups(const pa_pool* pool, int32_t S, int32_t maxB, const int32_t* group_start,
+                       const int32_t* shared_blocks, int32_t num_groups,
+                       const std::vector<int32_t>& lens, const std::vector<int32_t>& tab,
+                       hipStream_t st) {
+  std::vector<int32_t> gs, sb;
+  if (!fetch(gs, group_start, (size_t)num_groups + 1, st) ||
+      !fetch(sb, shared_blocks, (size_t)num_groups, st))
+    return PA_EHIP;
+  if (gs[0] != 0 || gs[num_groups] != S) return PA_EINVAL;
+  for (int32_t i = 0; i < num_groups; ++i) {
+    if (gs[i + 1] <= gs[i] || sb[i] < 0 || sb[i] > maxB) return PA_EINVAL;
+    for (int32_t m = gs[i]; m < gs[i + 1]; ++m) {
+      if (sb[i] > lens[m] / pool->block_size) return PA_EINVAL;
+      for (int32_t j = 0; j < sb[i]; ++j)
+        if (tab[(size_t)m * maxB + j] != tab[(size_t)gs[i] * maxB + j]) return PA_EINVAL;
+    }
+  }
+  return PA_OK;
+}
+
+// The decode entry points share this: validation, then the launch over a
+// workspace of ws_bytes at ws.
+pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                      const void* q, int32_t num_seqs, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, float scale, void* out,
+                      int32_t partition_tokens, int32_t num_groups, const int32_t* group_start,
+                      const int32_t* shared_blocks, void* workspace, size_t workspace_bytes,
+                      bool debug, hipStream_t hs) {
+  int32_t P;
+  size_t ws;
+  if (num_groups < 0) return PA_EINVAL;
+  pa_status st = decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                              partition_tokens, num_groups > 0, &P, &ws);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !block_tables || !context_lens || !out) return PA_EINVAL;
+  if (num_groups > 0 && (!group_start || !shared_blocks)) return PA_EINVAL;
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return PA_EINVAL;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (pakv::decode_path(pool->dtype, pool->head_dim, group, pool->block_size) ==
+      pakv::DecodePath::kUnsupported)
+    return PA_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < ws) return PA_EINVAL;
+  if (debug) {
+    std::vector<int32_t> lens, tab;
+    if (!fetch(lens, context_lens, (size_t)num_seqs, hs)) return PA_EHIP;
+    if (!fetch(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, hs)) return PA_EHIP;
+    const int64_t max_len = (int64_t)max_blocks_per_seq * pool->block_size;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 1 || lens[s] > max_len) return PA_EINVAL;
+      const int32_t nb = (lens[s] + pool->block_size - 1) / pool->block_size;
+      for (int32_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= pool->num_blocks) return PA_EINVAL;
+      }
+    }
+    if (num_groups > 0) {
+      st = check_groups(pool, num_seqs, max_blocks_per_seq, group_start, shared_blocks,
+                        num_groups, lens, tab, hs);
+      if (st != PA_OK) return st;
+    }
+  }
+  // prefix groups serve the MFMA kernels; a group that cannot share (fp32
+  // pools, or more query heads per kv head than leave room for a second
+  // member in the tile) reads its blocks per sequence, with the same result
+  const bool grouped = num_groups > 0 && pool->dtype != PA_F32 &&
+                       part_slots(group, true) >= 2 * group;
+  const WsLayout L = ws_layout(pool, num_seqs, num_q_heads, grouped);
+  DecodeArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.group_start = grouped ? group_start : nullptr;
+  a.shared_blocks = grouped ? shared_blocks : nullptr;
+  a.num_groups = grouped ? num_groups : 0;
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  a.part_m = reinterpret_cast<float*>(w);
+  a.part_l = reinterpret_cast<float*>(w + L.off_l);
+  a.part_o = reinterpret_cast<float*>(w + L.off_o);
+  a.seg_info = reinterpret_cast<int32_t*>(w + L.off_info);
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.min_seg_blocks = P / pool->block_size;
+  a.slots = part_slots(group, grouped);
+  a.own_row0 = static_cast<int32_t>(L.range_rows);
+  a.sh_row0 = static_cast<int32_t>(L.range_rows + (L.rows - L.range_rows) / 2);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, pool->block_size, hs);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
 }  // namespace
@@ -162,20 +288,31 @@ pa_status pa_kv_append(const pa_pool* pool, void* k_pool, void* v_pool, const vo
 
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_blocks_per_seq, int32_t partition_tokens) {
-  int32_t P, slots;
+  int32_t P;
   size_t ws;
-  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
-                   &slots, &ws) != PA_OK)
+  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, false, &P,
+                   &ws) != PA_OK)
+    return 0;
+  return ws;
+}
+
+size_t pa_decode_shared_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                        int32_t partition_tokens) {
+  int32_t P;
+  size_t ws;
+  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, true, &P,
+                   &ws) != PA_OK)
     return 0;
   return ws;
 }
 
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_blocks_per_seq, int32_t partition_tokens) {
-  int32_t P, slots;
+  int32_t P;
   size_t ws;
-  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, &P,
-                   &slots, &ws) != PA_OK)
+  if (decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_tokens, false, &P,
+                   &ws) != PA_OK)
     return 0;
   return P;
 }
@@ -186,58 +323,22 @@ pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const int32_t* context_lens, float scale, void* out,
                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                     void* stream) {
-  int32_t P, slots;
-  size_t ws;
-  pa_status st = decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
-                              partition_tokens, &P, &slots, &ws);
-  if (st != PA_OK) return st;
-  if (num_seqs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !q || !block_tables || !context_lens || !out) return PA_EINVAL;
-  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
-    return PA_EINVAL;
-  const int group = num_q_heads / pool->num_kv_heads;
-  if (pakv::decode_path(pool->dtype, pool->head_dim, group, pool->block_size) ==
-      pakv::DecodePath::kUnsupported)
-    return PA_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < ws) return PA_EINVAL;
-  hipStream_t hs = as_stream(stream);
-  if (debug_checks()) {
-    std::vector<int32_t> lens, tab;
-    if (!fetch(lens, context_lens, (size_t)num_seqs, hs)) return PA_EHIP;
-    if (!fetch(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, hs)) return PA_EHIP;
-    const int64_t max_len = (int64_t)max_blocks_per_seq * pool->block_size;
-    for (int32_t s = 0; s < num_seqs; ++s) {
-      if (lens[s] < 1 || lens[s] > max_len) return PA_EINVAL;
-      const int32_t nb = (lens[s] + pool->block_size - 1) / pool->block_size;
-      for (int32_t j = 0; j < nb; ++j) {
-        const int32_t b = tab[(size_t)s * max_blocks_per_seq + j];
-        if (b < 0 || b >= pool->num_blocks) return PA_EINVAL;
-      }
-    }
-  }
-  DecodeArgs a{};
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
-  a.q = q;
-  a.out = out;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  const size_t n = (size_t)num_seqs * num_q_heads * slots;
-  uint8_t* w = static_cast<uint8_t*>(workspace);
-  a.part_m = reinterpret_cast<float*>(w);
-  a.part_l = reinterpret_cast<float*>(w + align_up(n * sizeof(float)));
-  a.part_o = reinterpret_cast<float*>(w + 2 * align_up(n * sizeof(float)));
-  a.seg_count = reinterpret_cast<int32_t*>(w + 2 * align_up(n * sizeof(float)) +
-                                           align_up(n * pool->head_dim * sizeof(float)));
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.max_blocks = max_blocks_per_seq;
-  a.min_seg_blocks = P / pool->block_size;
-  a.max_slots = slots;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, pool->block_size, hs);
-  return e == hipSuccess ? PA_OK : PA_EHIP;
+  return decode_impl(pool, k_pool, v_pool, q, num_seqs, num_q_heads, block_tables,
+                     max_blocks_per_seq, context_lens, scale, out, partition_tokens, 0, nullptr,
+                     nullptr, workspace, workspace_bytes, debug_checks(), as_stream(stream));
+}
+
+pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                           const void* q, int32_t num_seqs, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, float scale, void* out,
+                           int32_t partition_tokens, int32_t num_groups,
+                           const int32_t* group_start, const int32_t* shared_blocks,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(pool, k_pool, v_pool, q, num_seqs, num_q_heads, block_tables,
+                     max_blocks_per_seq, context_lens, scale, out, partition_tokens, num_groups,
+                     group_start, shared_blocks, workspace, workspace_bytes, debug_checks(),
+                     as_stream(stream));
 }
 
 pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,

@@ -59,62 +59,152 @@
 namespace pakv {
 namespace {
 
-// A piece of work for one wave: tokens [t0, t1) of sequence s, kv head g;
-// `part` is the piece's slot among the sequence's `nparts` pieces.
+// A piece of work for one wave: logical tokens [t0, t1) of one segment for
+// kv head g.  The segment's member sequences s .. s + nmem - 1 read the same
+// blocks; member m's query head h of the group takes head slot m * G + h.
+// A piece that is the whole attention of one sequence (in_place) is
+// normalised and stored; any other leaves (m, l, o) for head slot c in
+// partial row prow + (c / G) * mstride + c % G.
 struct Unit {
-  int s, g, part, L, t0, t1, nparts;
+  int s, nmem, g, t0, t1, prow, mstride;
+  bool in_place;
 };
 
-// The plan every workgroup builds in LDS from the context lengths: block
-// prefix sums over the batch and the range length.  Built from scans only,
-// so every workgroup gets the same plan.
+// The plan every workgroup builds in LDS from the context lengths (and the
+// prefix groups): segments in order, and their block prefix sums.  Built
+// from scans only, so every workgroup gets the same plan.
 struct Plan {
-  const int* pre;   // [S + 1] blocks before sequence s; pre[S] = T
-  const int* lens;  // [S] context lengths (clamped to the table capacity)
-  int S, T, q, R;   // R: ranges per kv head
+  const int* pre;    // [K + 1] blocks before segment k; pre[K] = T
+  const int* lens;   // [S] context lengths (clamped to the table capacity)
+  const int* sdesc;  // [K] first member | member count << 16 (nullptr: segment k is sequence k)
+  const int* sj0;    // [K] first logical block of the segment
+  int S, K, T, q, R;  // R: ranges per kv head, q: blocks per range
 };
 
-// Dynamic LDS bytes for a plan over S sequences.
-__host__ __device__ constexpr size_t plan_lds_bytes(int S) {
-  return ((size_t)2 * S + 1 + 8) * sizeof(int);
+// Dynamic LDS bytes for a plan over S sequences (with prefix groups a
+// sequence can add a segment: at most 2S).
+__host__ __device__ constexpr size_t plan_lds_bytes(int S, bool grouped) {
+  return ((size_t)S + (grouped ? 6 * (size_t)S : (size_t)S) + 1 + 8) * sizeof(int);
+}
+
+// Group i of the prefix groups, clipped to this launch's sequences: members
+// [*m0, *m1) (launch-local indices) and the full blocks they share.  A group
+// whose members would not fit the head slots of one tile, or whose shared
+// blocks reach past a member's full blocks (arguments outside the
+// contract), shares nothing, which gives the same result.
+template <int B>
+__device__ __forceinline__ void group_view(const DecodeArgs& a, const int* lens, int G, int i,
+                                           int* m0, int* m1, int* P) {
+  const int lo = max(a.group_start[i], a.seq_base) - a.seq_base;
+  const int hi = min(a.group_start[i + 1], a.seq_base + a.num_seqs) - a.seq_base;
+  *m0 = lo;
+  *m1 = max(lo, hi);
+  int p = min(max(a.shared_blocks[i], 0), a.max_blocks);
+  if (hi - lo < 2 || (hi - lo) * G > a.slots) p = 0;
+  for (int m = lo; m < hi && p > 0; ++m) p = min(p, lens[m] / B);
+  *P = p;
 }
 
 // Collective over the workgroup; ends with a barrier.  B = tokens per block.
 template <int B>
-__device__ Plan build_plan(const DecodeArgs& a, int* lds) {
+__device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   const int S = a.num_seqs;
-  int* pre = lds;            // S + 1
-  int* lens = pre + S + 1;   // S
-  int* wsum = lens + S;      // 8
+  const bool grouped = a.group_start != nullptr;
+  const int Kmax = grouped ? 2 * S : S;
+  int* lens = lds;                          // S
+  int* pre = lens + S;                      // Kmax + 1
+  int* sdesc = pre + Kmax + 1;              // Kmax (grouped only)
+  int* sj0 = sdesc + Kmax;                  // Kmax (grouped only)
+  int* wsum = grouped ? sj0 + Kmax : sdesc; // 8
   const int T_ = blockDim.x, t = threadIdx.x;
-  const int C = (S + T_ - 1) / T_;  // contiguous chunk of sequences per thread
-  const int s0 = min(S, t * C), s1 = min(S, s0 + C);
   // lengths outside [0, table capacity] violate the contract; clamping them
   // keeps every LDS and table index in range whatever the device data says
   const int cap = a.max_blocks * B;
-  int nb = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int L = min(max(a.context_lens[s], 0), cap);
-    lens[s] = L;
-    nb += (L + B - 1) / B;
+  for (int s = t; s < S; s += T_) lens[s] = min(max(a.context_lens[s], 0), cap);
+  __syncthreads();
+  int K = 0, T = 0;
+  bool use_groups = grouped;
+  if (grouped) {
+    // segments of group i: its shared blocks (when it shares any), then
+    // each member's remaining blocks
+    const int NG = a.num_groups;
+    const int C = (NG + T_ - 1) / T_;
+    const int i0 = min(NG, t * C), i1 = min(NG, i0 + C);
+    int nseg = 0, nb = 0;
+    for (int i = i0; i < i1; ++i) {
+      int m0, m1, P;
+      group_view<B>(a, lens, G, i, &m0, &m1, &P);
+      nseg += (P > 0) + (m1 - m0);
+      nb += P;
+      for (int m = m0; m < m1; ++m) nb += (lens[m] + B - 1) / B - P;
+    }
+    int k = block_excl_scan(nseg, wsum, &K);
+    int run = block_excl_scan(nb, wsum, &T);
+    // groups that overlap (outside the contract) could need more segments
+    // than the plan holds: the workgroup-uniform total decides, before any
+    // write, to plan without them
+    use_groups = K <= Kmax;
+    if (use_groups) {
+      for (int i = i0; i < i1; ++i) {
+        int m0, m1, P;
+        group_view<B>(a, lens, G, i, &m0, &m1, &P);
+        if (P > 0) {
+          pre[k] = run;
+          sdesc[k] = m0 | (m1 - m0) << 16;
+          sj0[k] = 0;
+          run += P;
+          ++k;
+        }
+        for (int m = m0; m < m1; ++m) {
+          pre[k] = run;
+          sdesc[k] = m | 1 << 16;
+          sj0[k] = P;
+          run += (lens[m] + B - 1) / B - P;
+          ++k;
+        }
+      }
+    }
   }
-  int T;
-  int run = block_excl_scan(nb, wsum, &T);
-  for (int s = s0; s < s1; ++s) {
-    pre[s] = run;
-    run += (lens[s] + B - 1) / B;
+  if (!use_groups) {
+    const int C = (S + T_ - 1) / T_;  // contiguous chunk of sequences per thread
+    const int s0 = min(S, t * C), s1 = min(S, s0 + C);
+    int nb = 0;
+    for (int s = s0; s < s1; ++s) nb += (lens[s] + B - 1) / B;
+    int run = block_excl_scan(nb, wsum, &T);
+    for (int s = s0; s < s1; ++s) {
+      pre[s] = run;
+      run += (lens[s] + B - 1) / B;
+    }
+    K = S;
   }
-  if (t == 0) pre[S] = T;
+  if (t == 0) pre[K] = T;
   __syncthreads();
   Plan pl;
   pl.pre = pre;
   pl.lens = lens;
+  pl.sdesc = use_groups ? sdesc : nullptr;
+  pl.sj0 = sj0;
   pl.S = S;
+  pl.K = K;
   pl.T = T;
   // every wave of the grid streams one (kv head, range) pair: R ranges per head
   pl.R = max(1, (int)(gridDim.x * kWaves) / a.num_kv_heads);
   pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
   return pl;
+}
+
+// Segment k: first member, member count, first logical block.
+__device__ __forceinline__ void seg_desc(const Plan& pl, int k, int* s, int* nmem, int* j0) {
+  if (pl.sdesc) {
+    const int d = pl.sdesc[k];
+    *s = d & 0xffff;
+    *nmem = d >> 16;
+    *j0 = pl.sj0[k];
+  } else {
+    *s = k;
+    *nmem = 1;
+    *j0 = 0;
+  }
 }
 
 // The kv head and range of one wave.  The grid's waves, numbered
@@ -131,56 +221,90 @@ __device__ __forceinline__ bool wave_work(const DecodeArgs& a, const Plan& pl, i
   return *r < pl.R;
 }
 
-// Pieces sequence s is cut into (0 for an empty sequence).
-__device__ __forceinline__ int seg_count_of(const Plan& pl, int s) {
-  const int b = pl.pre[s], e = pl.pre[s + 1];
-  return e > b ? (e - 1) / pl.q - b / pl.q + 1 : 0;
+// Collective over workgroup 0: where each sequence's cut pieces went, for
+// the reduce kernel.  seg_info[s] = {range of its first piece * 2 + end of
+// that piece, pieces} of the sequence's own segment, then the same for the
+// shared segment of its group (pieces | member index << 16; 0 pieces when
+// it shares none).  Pieces after the first start at their range's first
+// block (end 0).
+__device__ void write_seg_info(const DecodeArgs& a, const Plan& pl) {
+  // every sequence's entry starts empty, so one that no segment names (only
+  // with groups outside the contract) is skipped by the reduce
+  for (int s = threadIdx.x; s < pl.S; s += blockDim.x)
+    *reinterpret_cast<int4*>(a.seg_info + (size_t)s * 4) = int4{0, 0, 0, 0};
+  __syncthreads();
+  for (int k = threadIdx.x; k < pl.K; k += blockDim.x) {
+    int s, nmem, j0;
+    seg_desc(pl, k, &s, &nmem, &j0);
+    const int sb = pl.pre[k], se = pl.pre[k + 1];
+    int first = 0, np = 0;
+    if (se > sb) {
+      const int r0 = sb / pl.q;
+      first = r0 * 2 + (sb != r0 * pl.q);
+      np = (se - 1) / pl.q - r0 + 1;
+    }
+    int* info = a.seg_info + (size_t)s * 4;
+    if (nmem == 1) {
+      info[0] = first;
+      info[1] = np;
+    } else {
+      for (int m = 0; m < nmem; ++m) {
+        info[4 * m + 2] = first;
+        info[4 * m + 3] = np | m << 16;
+      }
+    }
+  }
 }
 
-// Collective over the workgroup: the reduce kernel's per-sequence piece counts.
-__device__ void write_seg_counts(const DecodeArgs& a, const Plan& pl) {
-  for (int s = threadIdx.x; s < pl.S; s += blockDim.x) a.seg_count[s] = seg_count_of(pl, s);
-}
-
-// Walk this workgroup's range for kv head g, calling f(unit) per piece.
+// Walk range r for kv head g, calling f(unit) per piece (the part of one
+// segment inside the range).  G: query heads per kv head.
 template <int B, typename F>
-__device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, int r, int g, F&& f) {
+__device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, int G, int r, int g,
+                                           F&& f) {
   int b0 = r * pl.q;
   const int b1 = min(pl.T, b0 + pl.q);
   if (b0 >= b1) return;
-  // sequence holding block b0: the largest s with pre[s] <= b0 (then
-  // pre[s + 1] > b0 because b0 < T)
-  int lo = 0, hi = pl.S - 1;
+  // segment holding block b0: the largest k with pre[k] <= b0 (then
+  // pre[k + 1] > b0 once empty segments are skipped, because b0 < T)
+  int lo = 0, hi = pl.K - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (pl.pre[mid] <= b0) lo = mid; else hi = mid - 1;
   }
-  int s = lo;
+  int k = lo;
+  int end = 0;  // 0 for the piece that starts at the range's first block
   while (b0 < b1) {
-    while (pl.pre[s + 1] <= b0) ++s;  // skip empty sequences
-    const int sb = pl.pre[s], se = pl.pre[s + 1];
+    while (pl.pre[k + 1] <= b0) ++k;  // skip empty segments
+    const int sb = pl.pre[k], se = pl.pre[k + 1];
     const int e = min(b1, se);
+    int s, nmem, j0;
+    seg_desc(pl, k, &s, &nmem, &j0);
     Unit u;
     u.s = s;
+    u.nmem = nmem;
     u.g = g;
-    u.L = pl.lens[s];
-    u.t0 = (b0 - sb) * B;
-    u.t1 = min(u.L, (e - sb) * B);
-    u.part = r - sb / pl.q;
-    u.nparts = (se - 1) / pl.q - sb / pl.q + 1;
+    u.t0 = (j0 + b0 - sb) * B;
+    const int seg_end = nmem > 1 ? (j0 + se - sb) * B : pl.lens[s];
+    u.t1 = min(seg_end, (j0 + e - sb) * B);
+    const bool cut = (se - 1) / pl.q != sb / pl.q;
+    u.in_place = nmem == 1 && j0 == 0 && !cut;
+    if (cut) {
+      u.prow = ((r * a.num_kv_heads + g) * 2 + end) * a.slots;
+      u.mstride = G;
+    } else {  // one piece: its rows are the sequences' own
+      u.prow = (nmem == 1 ? a.own_row0 : a.sh_row0) + s * a.num_q_heads + g * G;
+      u.mstride = a.num_q_heads;
+    }
     f(u);
     b0 = e;
+    end = 1;
   }
 }
 
-// Index of (sequence, query head, piece) in the partial buffers.
-__device__ __forceinline__ size_t part_index(const DecodeArgs& a, int s, int hq, int part) {
-  return ((size_t)s * a.num_q_heads + hq) * a.max_slots + part;
-}
-
-// Epilogue of an MFMA unit: acc[nt][r] holds head 4*grp + r, dim nt*16 + col
-// (unnormalised); a sequence finished in one piece is normalised and stored
-// as bf16, otherwise (m, l, o) go to the piece's partial slot.
+// Epilogue of an MFMA unit: acc[nt][r] holds head slot 4*grp + r, dim
+// nt*16 + col (unnormalised); m_ref and l_tot belong to head slot col.  A
+// piece that is a sequence's whole attention is normalised and stored as
+// bf16; any other writes (m, l, o) to its partial rows.
 template <int D>
 __device__ __forceinline__ void finish_mfma_unit(const DecodeArgs& a, int G, const Unit& u,
                                                  const f32x4* acc, float m_ref, float l_tot,
@@ -188,7 +312,7 @@ __device__ __forceinline__ void finish_mfma_unit(const DecodeArgs& a, int G, con
   constexpr int NT = D / 16;
   const int s = u.s, g = u.g;
   const int col = lane & 15, grp = lane >> 4;
-  if (u.nparts == 1) {
+  if (u.in_place) {
     float den[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
@@ -201,20 +325,45 @@ __device__ __forceinline__ void finish_mfma_unit(const DecodeArgs& a, int G, con
       for (int nt = 0; nt < NT; ++nt) store_out<__bf16>(a.out, ob + nt * 16, acc[nt][r] / den[r]);
     }
   } else {
+    const int nslot = u.nmem * G;
+    auto row = [&](int c) {
+      const int m = c / G;
+      return u.prow + m * u.mstride + (c - m * G);
+    };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * grp + r;
-      if (h >= G) continue;
-      float* po = a.part_o + part_index(a, s, g * G + h, u.part) * D + col;
+      if (h >= nslot) continue;
+      float* po = a.part_o + (size_t)row(h) * D + col;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) po[nt * 16] = acc[nt][r];
     }
-    if (grp == 0 && col < G) {
-      const size_t pi = part_index(a, s, g * G + col, u.part);
-      a.part_m[pi] = m_ref;
-      a.part_l[pi] = l_tot;
+    if (grp == 0 && col < nslot) {
+      a.part_m[row(col)] = m_ref;
+      a.part_l[row(col)] = l_tot;
     }
   }
+}
+
+// B operand of q.K for an MFMA unit: head slot col of the tile is member
+// col / G's query head g * G + col % G (zero past the unit's slots); lane
+// (col, grp) holds 16 bytes of that row at dims kj * KSTEP + grp * 16 / 2
+// in the caller's arrangement: the bytes at qoff(kj) of the row.
+template <int KJ, typename Off>
+__device__ __forceinline__ void load_q_operand(const DecodeArgs& a, int G, const Unit& u, int col,
+                                               uint32_t row_bytes, Off qoff, bf16x8 (&qop)[KJ]) {
+  u32x4 w[KJ];
+#pragma unroll
+  for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
+  if (col < u.nmem * G) {
+    const int m = col / G, h = col - m * G;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                        ((size_t)(u.s + m) * a.num_q_heads + u.g * G + h) * row_bytes;
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + qoff(kj));
+  }
+#pragma unroll
+  for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
 }
 
 // The MFMA tiles cover 16 tokens.  A unit walks its tokens [t0, t1) in
@@ -249,21 +398,9 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
   const int col = lane & 15, grp = lane >> 4;
 
-  // B operand of q.K: lane holds q[head col][kj*32 + grp*8 .. +8]
+  // B operand of q.K: lane holds q[head slot col][kj*32 + grp*8 .. +8]
   bf16x8 qop[KJ];
-  {
-    u32x4 w[KJ];
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
-    if (col < G) {
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                          ((size_t)s * a.num_q_heads + g * G + col) * ROW + grp * 16;
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj) w[kj] = *reinterpret_cast<const u32x4*>(qp + kj * 64);
-    }
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
-  }
+  load_q_operand<KJ>(a, G, u, col, ROW, [&](int kj) { return grp * 16 + kj * 64; }, qop);
 
   // wave-uniform base of this kv head's slice of block 0, plus 32-bit lane
   // offsets: each load is a scalar block base + vector lane offset
@@ -449,20 +586,8 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   // kj holds q[head col][c*64 + grp*16 + h*8 .. +8].  The order in which
   // dims meet the MFMA does not change the dot product.
   bf16x8 qop[KJ];
-  {
-    u32x4 w[KJ];
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
-    if (col < G) {
-      const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                          ((size_t)s * a.num_q_heads + g * G + col) * QROW + grp * 32;
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj)
-        w[kj] = *reinterpret_cast<const u32x4*>(qp + (kj >> 1) * 128 + (kj & 1) * 16);
-    }
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) qop[kj] = __builtin_bit_cast(bf16x8, w[kj]);
-  }
+  load_q_operand<KJ>(a, G, u, col, QROW,
+                     [&](int kj) { return grp * 32 + (kj >> 1) * 128 + (kj & 1) * 16; }, qop);
 
   const size_t kblk_bytes = (size_t)a.num_kv_heads * RBK;
   const size_t vblk_bytes = (size_t)a.num_kv_heads * RBV;
@@ -618,26 +743,26 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
 template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan<B>(a, plan_lds);
-  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const Plan pl = build_plan<B>(a, G, plan_lds);
+  if (blockIdx.x == 0) write_seg_info(a, pl);
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int g, r;
   if (!wave_work(a, pl, wave, &g, &r)) return;
-  walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma_unit<D, B, NBUF>(a, G, u, lane); });
+  walk_range<B>(a, pl, G, r, g, [&](const Unit& u) { mfma_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
 template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan<B>(a, plan_lds);
-  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const Plan pl = build_plan<B>(a, G, plan_lds);
+  if (blockIdx.x == 0) write_seg_info(a, pl);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int g, r;
   if (!wave_work(a, pl, wave, &g, &r)) return;
-  walk_range<B>(a, pl, r, g, [&](const Unit& u) { mfma8_unit<D, B, NBUF>(a, G, u, lane); });
+  walk_range<B>(a, pl, G, r, g, [&](const Unit& u) { mfma8_unit<D, B, NBUF>(a, G, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
@@ -653,7 +778,7 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
   constexpr int NV = EPL * B * ES / 16;  // 16-byte V loads per lane
   constexpr uint32_t ROW = D * ES;
 
-  const int s = u.s, g = u.g, L = u.L;
+  const int s = u.s, g = u.g, L = u.t1;  // tokens past the piece are masked
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
   const int tok = lane >> 2, qc = lane & 3;
 
@@ -793,12 +918,12 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
   for (int h = 0; h < G; ++h) {
     const float lt = wave_sum(l_run[h]);
     const int hq = g * G + h;
-    if (u.nparts == 1) {
+    if (u.in_place) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         store_out<float>(a.out, ((size_t)s * a.num_q_heads + hq) * D + lane * EPL + e, acc[h][e] / lt);
     } else {
-      const size_t pi = part_index(a, s, hq, u.part);
+      const size_t pi = (size_t)u.prow + h;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a.part_o[pi * D + lane * EPL + e] = acc[h][e];
       if (lane == 0) {
@@ -812,41 +937,66 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
 template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan<kBlock>(a, plan_lds);
-  if (blockIdx.x == 0) write_seg_counts(a, pl);
+  const Plan pl = build_plan<kBlock>(a, G, plan_lds);
+  if (blockIdx.x == 0) write_seg_info(a, pl);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int g, r;
   if (!wave_work(a, pl, wave, &g, &r)) return;
-  walk_range<kBlock>(a, pl, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
+  walk_range<kBlock>(a, pl, G, r, g, [&](const Unit& u) { valu_unit<D, G, NBUF>(a, u, lane); });
 }
 
 // ---------------------------------------------------------------------------
 // Split-context reduce: one wave per (query head, sequence), four query
-// heads per workgroup.  A wave reads its pieces' m values across lanes for
-// the maximum, then walks the pieces 16 at a time (their (m, l) as uniform
-// loads, o as two 256-byte rows per piece) so that a long sequence's pieces
-// are fetched in a few rounds; lanes own output dims.  Sequences finished in
-// place by the decode kernel return at once.
+// heads per workgroup.  A sequence's pieces are those of its own segment
+// and, in a prefix group, those of the group's shared segment; seg_info
+// says in which ranges they lie.  A wave reads the pieces' m values across
+// lanes for the maximum, then walks the pieces 16 at a time (their (m, l)
+// as uniform loads, o as 256-byte rows) so that a long sequence's pieces
+// are fetched in a few rounds; lanes own output dims.  Sequences finished
+// in place by the decode kernel return at once.
 // ---------------------------------------------------------------------------
 constexpr int kReduceHeads = 4;
+
+// Partial row of piece p of a sequence: pieces [0, np_own) are its own
+// segment's (head slot h), the rest the shared segment's (head slot
+// member * G + h).  A segment of one piece left its row among the
+// sequences' own rows.  Of a cut segment, the first piece may end its range
+// (end 1); every later piece starts its range (end 0).
+struct PieceMap {
+  int first_own, np_own, first_sh, np_sh, slot_sh, slot_own, hkv, slots, g;
+  int own_row, sh_row;  // rows of a segment that was not cut
+  __device__ __forceinline__ int row(int p) const {
+    const bool own = p < np_own;
+    if ((own ? np_own : np_sh) == 1) return own ? own_row : sh_row;
+    const int i = own ? p : p - np_own;
+    const int first = own ? first_own : first_sh;
+    const int r = (first >> 1) + i;
+    const int end = i == 0 ? (first & 1) : 0;
+    return ((r * hkv + g) * 2 + end) * slots + (own ? slot_own : slot_sh);
+  }
+};
 
 template <typename T, int D>
 __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(DecodeArgs a) {
   constexpr int EPL = D / 64, UNR = 16;
   const int s = blockIdx.y;
-  const int np = a.seg_count[s];
-  if (np <= 1) return;  // finished in place by the decode kernel (or no context)
+  const int4 info = *reinterpret_cast<const int4*>(a.seg_info + (size_t)s * 4);
+  const int np_sh = info.w & 0xffff;
+  const int np = info.y + np_sh;
+  if (np_sh == 0 && info.y <= 1) return;  // finished in place (or no context)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int hq = blockIdx.x * kReduceHeads + wave;
   if (hq >= a.num_q_heads) return;
-  const size_t base = part_index(a, s, hq, 0);
-  const float* pm = a.part_m + base;
-  const float* pl = a.part_l + base;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int g = hq / G, h = hq - g * G;
+  const int srow = s * a.num_q_heads + hq;
+  const PieceMap pm{info.x, info.y, info.z, np_sh, (info.w >> 16) * G + h, h, a.num_kv_heads,
+                    a.slots, g, a.own_row0 + srow, a.sh_row0 + srow};
 
   float M = kNegInf;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, pm[p]);
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, a.part_m[pm.row(p)]);
   M = wave_max(M);
 
   float den = 0.f, num[EPL];
@@ -856,10 +1006,10 @@ __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(Decode
     float f[UNR], o[UNR][EPL];
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int p = min(p0 + k, np - 1);  // clamped: past-the-end terms get f = 0
-      f[k] = p0 + k < np ? fexp2(pm[p] - M) : 0.f;
-      den = fmaf(f[k], pl[p], den);
-      const float* po = a.part_o + (base + p) * D;
+      const int row = pm.row(min(p0 + k, np - 1));  // clamped: past-the-end terms get f = 0
+      f[k] = p0 + k < np ? fexp2(a.part_m[row] - M) : 0.f;
+      den = fmaf(f[k], a.part_l[row], den);
+      const float* po = a.part_o + (size_t)row * D;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[k][e] = po[e * 64 + lane];
     }
@@ -912,14 +1062,21 @@ struct Launch {
   size_t lds;
 };
 
+// Sequences per launch: the plan lives in LDS (with prefix groups it holds
+// up to two segments per sequence), and stays under 64 KiB.
+constexpr int kMaxPlanSeqsGrouped = kMaxPlanSeqs / 2;
+static_assert(plan_lds_bytes(kMaxPlanSeqs, false) <= 65536 &&
+                  plan_lds_bytes(kMaxPlanSeqsGrouped, true) <= 65536,
+              "decode plan fits 64 KiB of LDS");
+
 template <typename K>
 Launch decode_launch(const DecodeArgs& a, K kernel) {
   static int per_cu = 0;  // per kernel instantiation
-  const size_t lds = plan_lds_bytes(a.num_seqs);
+  const size_t lds = plan_lds_bytes(a.num_seqs, a.group_start != nullptr);
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kWaves * 64,
-                                                     plan_lds_bytes(kMaxPlanSeqs)) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, kernel, kWaves * 64, plan_lds_bytes(kMaxPlanSeqsGrouped, true)) != hipSuccess ||
         n < 1)
       n = 1;
     per_cu = std::min(n, kMaxWgPerCu);
@@ -928,6 +1085,14 @@ Launch decode_launch(const DecodeArgs& a, K kernel) {
   const int grid = std::max(cu_count() * per_cu, (a.num_kv_heads + kWaves - 1) / kWaves);
   return {dim3((unsigned)grid), dim3(kWaves * 64), lds};
 }
+
+}  // namespace
+
+int decode_grid(int num_kv_heads) {
+  return std::max(cu_count() * kMaxWgPerCu, (num_kv_heads + kWaves - 1) / kWaves);
+}
+
+namespace {
 
 // The head group (1..16) fills the 16 head slots of the MFMA tiles at run
 // time, so one instantiation per head_dim serves every group size.
@@ -1023,25 +1188,23 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
 }
 }  // namespace
 
-// Batches larger than kMaxPlanSeqs are launched in slices of that many
-// sequences (the per-workgroup plan lives in LDS); every per-sequence array
-// is offset to the slice.
+// Batches larger than one plan are launched in slices (the per-workgroup
+// plan lives in LDS); every per-sequence array is offset to the slice, the
+// prefix groups are clipped to it, and the slices reuse the partial buffers
+// and seg_info one after another on the stream.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
                          int block_size, hipStream_t st) {
   const size_t es = dtype == PA_F32 ? 4 : 2;  // q / out element (bf16 for 8-bit pools)
-  for (int32_t s0 = 0; s0 < a.num_seqs; s0 += kMaxPlanSeqs) {
+  const int step = a.group_start ? kMaxPlanSeqsGrouped : kMaxPlanSeqs;
+  for (int32_t s0 = 0; s0 < a.num_seqs; s0 += step) {
     DecodeArgs b = a;
-    b.num_seqs = std::min(kMaxPlanSeqs, a.num_seqs - s0);
+    b.num_seqs = std::min(step, a.num_seqs - s0);
+    b.seq_base = s0;
     const size_t qrow = (size_t)a.num_q_heads * head_dim * es;
     b.q = static_cast<const uint8_t*>(a.q) + (size_t)s0 * qrow;
     b.out = static_cast<uint8_t*>(a.out) + (size_t)s0 * qrow;
     b.block_tables = a.block_tables + (size_t)s0 * a.max_blocks;
     b.context_lens = a.context_lens + s0;
-    const size_t pr = (size_t)s0 * a.num_q_heads * a.max_slots;
-    b.part_m = a.part_m + pr;
-    b.part_l = a.part_l + pr;
-    b.part_o = a.part_o + pr * head_dim;
-    b.seg_count = a.seg_count + s0;
     const hipError_t e = launch_decode_slice(b, dtype, head_dim, group, block_size, st);
     if (e != hipSuccess) return e;
   }

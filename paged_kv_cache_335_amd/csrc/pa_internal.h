@@ -32,10 +32,14 @@ constexpr int kBlock = 16;       // tokens per block of the fp32 decode (MFMA pa
 constexpr int kWaves = PA_WAVES;
 constexpr int kNBuf = PA_NBUF;
 constexpr int kNBuf8 = PA_NBUF8;
-constexpr int kMaxMfmaGroup = 16;
-constexpr int kMaxSlots = 1 << 20;  // partial slots per (sequence, head)
-constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan)
+constexpr int kMaxMfmaGroup = 16;   // head slots of one MFMA tile
+constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan; 2048 with groups)
 
+// Work is cut into "segments": the part of one sequence it streams alone, or
+// the full blocks at the head of a prefix group's tables, which every member
+// shares and which one wave streams once for all of them (each member's
+// query heads take their own head slots of the MFMA tile).  Without groups a
+// segment is a whole sequence.
 struct DecodeArgs {
   const void* k_pool;
   const void* v_pool;
@@ -43,18 +47,42 @@ struct DecodeArgs {
   void* out;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* part_m;       // [S][Hq][max_slots]    reference max, log2 units
-  float* part_l;       // [S][Hq][max_slots]    sum of exp2(score - m)
-  float* part_o;       // [S][Hq][max_slots][D] unnormalised output
-  int32_t* seg_count;  // [S] pieces each sequence was cut into
+  // Prefix groups (nullptr: none).  Group i is the consecutive sequences
+  // group_start[i] .. group_start[i+1] - 1, whose first shared_blocks[i]
+  // table entries name the same physical blocks, all full.
+  const int32_t* group_start;   // [num_groups + 1]
+  const int32_t* shared_blocks; // [num_groups]
+  int32_t num_groups;
+  int32_t seq_base;             // index of this launch's first sequence in the groups
+  // Split-context partials.  A segment cut by range boundaries leaves one
+  // row per (wave slot, end, head slot): a wave slot is (range r, kv head g)
+  // = r * num_kv_heads + g; `end` is 0 for the piece that starts at the
+  // range's first block and 1 for the range's last piece when that starts
+  // later, so each (range, head) holds at most two cut pieces and these
+  // rows are sized by the grid, not by the batch.  With prefix groups a
+  // segment that is not cut still leaves a partial (a member's result
+  // combines its own blocks' and the shared blocks'): row own_row0 + s * Hq
+  // + h for sequence s's own segment, sh_row0 + s * Hq + h for its share of
+  // the group's shared segment.
+  float* part_m;       // [rows]    reference max, log2 units
+  float* part_l;       // [rows]    sum of exp2(score - m)
+  float* part_o;       // [rows][D] unnormalised output
+  int32_t* seg_info;   // [S][4] where each sequence's pieces went (reduce input)
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
-  int32_t min_seg_blocks;  // smallest range a workgroup streams (blocks)
-  int32_t max_slots;       // partial slots per (sequence, query head)
+  int32_t min_seg_blocks;  // smallest range a wave streams (blocks)
+  int32_t slots;           // head slots per (wave slot, end): G, or members * G with groups
+  int32_t own_row0;        // first per-sequence row of own segments (groups only)
+  int32_t sh_row0;         // first per-sequence row of shared segments (groups only)
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
 };
+
+// Workgroups of a decode launch for this many kv heads (a persistent grid:
+// one per CU, at least one wave per kv head); partial rows are bounded by
+// 2 * grid * kWaves * slots.
+int decode_grid(int num_kv_heads);
 
 // Multi-token (extend / chunked prefill) attention over paged contexts.
 struct ExtendArgs {

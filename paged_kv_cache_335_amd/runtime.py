@@ -14,6 +14,16 @@ A decode step for a batch of live sequences:
      K/V go into their slots, in one launch;
   5. pa_decode: attention over the grown contexts.
 
+With share_prefixes=True the step also exports the batch's prefix groups
+(runs of table rows whose leading full blocks are the same physical
+blocks, e.g. the samples forked from one prompt) in the same staging copy,
+and decode reads each group's shared blocks once for all of its members
+(pa_decode_shared).
+
+Every device operation of a call, allocations and copies included, runs
+on the stream the call names (the current stream by default), so a caller
+may drive the cache from a side stream.
+
 Preemption by swapping: swap_out(seq) moves a sequence's blocks to a pinned
 host pool and frees them on the device; swap_in(seq) brings them back into
 new device blocks and rewrites the sequence's table row.  While any
@@ -26,7 +36,8 @@ import torch
 
 from . import (PA_OK, PA_SWAP_IN, PA_SWAP_OUT, PagedKVError, alloc_host_pools, alloc_pools,
                pa_block_copy, pa_block_swap, pa_decode, pa_decode_partition_tokens,
-               pa_decode_workspace_bytes, pa_extend, pa_kv_append)
+               pa_decode_shared, pa_decode_shared_workspace_bytes, pa_decode_workspace_bytes,
+               pa_extend, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -101,8 +112,9 @@ class DeviceEvent:
 class PagedKVCache:
     def __init__(self, num_blocks, num_kv_heads, head_dim, max_seqs, table_width,
                  block_size=16, dtype=torch.bfloat16, shuffle_seed=0, device="cuda",
-                 host_blocks=0):
+                 host_blocks=0, share_prefixes=False, max_group=4):
         self.B = block_size
+        self.max_group = max_group  # members per prefix group (16 // query heads per kv head)
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.max_seqs = max_seqs
@@ -124,21 +136,32 @@ class PagedKVCache:
             if st != PA_OK:
                 raise PagedKVError(st, "pa_bm_set_host_blocks")
         self.rows = {}          # sequence id -> row of the device table
+        self.row_seqs = []      # sequence id of each table row
         self.swapped = set()    # sequences whose blocks are in the host pool
+        self.share_prefixes = share_prefixes
+        self.groups = None      # device (group_start, shared_blocks) of the latest step
+        self.num_groups = 0
         self._ring = None
         self._ring_events = [None] * (_RING // _GROUP)
         self._ring_pos = 0
         self._ws = None
 
     # --- sequences ------------------------------------------------------
+    def _stream(self, stream):
+        return stream or torch.cuda.current_stream(self.device)
+
     def add_sequence(self) -> int:
         if len(self.rows) >= self.max_seqs:
             raise ValueError("table rows exhausted")
         s = self.bm.add_seq()
         self.rows[s] = len(self.rows)
+        self.row_seqs.append(s)
         return s
 
-    def fork(self, parent: int) -> int:
+    def fork(self, parent: int, stream=None) -> int:
+        """A new sequence sharing every block of ``parent``: its device table
+        row is copied from the parent's on ``stream``, after any earlier
+        growth of that row enqueued there."""
         st, child = self.bm.fork(parent)
         if st != PA_OK:
             raise PagedKVError(st, "pa_bm_fork")
@@ -146,20 +169,25 @@ class PagedKVCache:
             raise ValueError("table rows exhausted")
         r = len(self.rows)
         self.rows[child] = r
-        self.tables[r].copy_(self.tables[self.rows[parent]])
+        self.row_seqs.append(child)
         self.host_lens[r] = self.host_lens[self.rows[parent]]
-        self.lens = torch.from_numpy(self.host_lens.copy()).to(self.device)
+        stream = self._stream(stream)
+        with torch.cuda.stream(stream):
+            self.tables[r].copy_(self.tables[self.rows[parent]])
+            self.lens = torch.from_numpy(self.host_lens.copy()).to(self.device, non_blocking=False)
         return child
 
     # --- staging ----------------------------------------------------------
-    def _staging(self, T, S):
-        need = T * 8 + T * 4 * 2 + S * 4 + 64
-        if self._ring is None or self._ring[0][0].numel() < need:
+    def _staging(self, nbytes, stream):
+        if self._ring is None or self._ring[0][0].numel() < nbytes:
             if self._ring is not None:
-                torch.cuda.current_stream(self.device).synchronize()  # old buffers idle
-            self._ring = [(torch.empty(need, dtype=torch.uint8, pin_memory=True),
-                           torch.empty(need, dtype=torch.uint8, device=self.device))
-                          for _ in range(_RING)]
+                # the old buffers may still be read by copies and kernels on
+                # any stream a previous call named
+                torch.cuda.synchronize(self.device)
+            with torch.cuda.stream(stream):
+                self._ring = [(torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
+                               torch.empty(nbytes, dtype=torch.uint8, device=self.device))
+                              for _ in range(_RING)]
             self._ring_events = [None] * (_RING // _GROUP)
             self._ring_pos = 0
         i = self._ring_pos
@@ -183,19 +211,31 @@ class PagedKVCache:
         row_of_tok = np.repeat(rows, n_tokens)
         self.host_lens[rows] += n_tokens
         S = len(self.rows)
-        i = self._staging(T, S)
-        host, dev = self._ring[i]
+        gs = sb = None
+        if self.share_prefixes and not self.swapped:
+            st, gs, sb = self.bm.prefix_groups(self.row_seqs, self.max_group)
+            if st != PA_OK:
+                raise PagedKVError(st, "pa_bm_prefix_groups")
+        G = 0 if gs is None else len(sb)
         o_sq = T * 8
         o_pos = o_sq + T * 4
         o_len = o_pos + T * 4
+        o_gs = o_len + S * 4
+        o_sb = o_gs + (G + 1) * 4
+        end = o_sb + G * 4
+        stream = self._stream(stream)
+        i = self._staging(max(end, 64), stream)
+        host, dev = self._ring[i]
         hv = host.numpy()
         hv[:o_sq].view(np.int64)[:] = slots
         hv[o_sq:o_pos].view(np.int32)[:] = row_of_tok
         hv[o_pos:o_len].view(np.int32)[:] = pos
-        hv[o_len:o_len + S * 4].view(np.int32)[:] = self.host_lens[:S]
-        stream = stream or torch.cuda.current_stream(self.device)
+        hv[o_len:o_gs].view(np.int32)[:] = self.host_lens[:S]
+        if G:
+            hv[o_gs:o_sb].view(np.int32)[:] = gs
+            hv[o_sb:end].view(np.int32)[:] = sb
         with torch.cuda.stream(stream):
-            dev[:o_len + S * 4].copy_(host[:o_len + S * 4], non_blocking=True)
+            dev[:end].copy_(host[:end], non_blocking=True)
             if i % _GROUP == _GROUP - 1:
                 # after the group's last copy: the host may refill the group once it fires
                 g = i // _GROUP
@@ -205,7 +245,10 @@ class PagedKVCache:
             d_slots = dev[:o_sq].view(torch.int64)
             d_rows = dev[o_sq:o_pos].view(torch.int32)
             d_pos = dev[o_pos:o_len].view(torch.int32)
-            self.lens = dev[o_len:o_len + S * 4].view(torch.int32)
+            self.lens = dev[o_len:o_gs].view(torch.int32)
+            if G:
+                self.groups = (dev[o_gs:o_sb].view(torch.int32), dev[o_sb:end].view(torch.int32))
+                self.num_groups = G
             if len(pairs):
                 d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device,
                                                                            non_blocking=False)
@@ -241,15 +284,20 @@ class PagedKVCache:
         self.swapped.discard(seq)
         st, table, n = self.bm.block_table(seq)
         row = self.rows[seq]
-        self.tables[row, :len(table)].copy_(torch.tensor(table, dtype=torch.int32))
+        with torch.cuda.stream(self._stream(stream)):
+            self.tables[row, :len(table)].copy_(torch.tensor(table, dtype=torch.int32),
+                                                non_blocking=False)
         return pairs
 
     # --- decode -------------------------------------------------------------
     def workspace(self, num_q_heads, partition_tokens=0):
         S = len(self.rows)
-        need = pa_decode_workspace_bytes(self.k_pool, self.v_pool, S, num_q_heads, self.width,
-                                         partition_tokens)
+        query = pa_decode_shared_workspace_bytes if self.share_prefixes else \
+            pa_decode_workspace_bytes
+        need = query(self.k_pool, self.v_pool, S, num_q_heads, self.width, partition_tokens)
         if need and (self._ws is None or self._ws.numel() < need):
+            if self._ws is not None:
+                torch.cuda.synchronize(self.device)  # the old workspace may still be in use
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws if need else None
 
@@ -262,11 +310,15 @@ class PagedKVCache:
         resident sequences (tables exported by the block manager and copied
         to the device for this call)."""
         tables, lens = self.bm.export(np.asarray(seqs, np.int32), self.width, pad_block=0)
-        d_tables = torch.from_numpy(tables).to(self.device)
-        d_lens = torch.from_numpy(lens).to(self.device)
         scale = self.head_dim ** -0.5 if scale is None else scale
-        return pa_decode(q, self.k_pool, self.v_pool, d_tables, d_lens, scale, out=out,
-                         partition_tokens=partition_tokens, stream=stream)
+        stream = self._stream(stream)
+        # uploads and the workspace belong to `stream`, so their memory is
+        # not reused before the kernels that read it there have run
+        with torch.cuda.stream(stream):
+            d_tables = torch.from_numpy(tables).to(self.device, non_blocking=False)
+            d_lens = torch.from_numpy(lens).to(self.device, non_blocking=False)
+            return pa_decode(q, self.k_pool, self.v_pool, d_tables, d_lens, scale, out=out,
+                             partition_tokens=partition_tokens, stream=stream)
 
     def extend(self, seqs, n_tokens, q, k_new, v_new, out=None, scale=None, stream=None):
         """Chunked prefill / extend: append n_tokens[i] tokens to seqs[i]
@@ -292,6 +344,14 @@ class PagedKVCache:
                              "decode_seqs")
         S = len(self.rows)
         scale = self.head_dim ** -0.5 if scale is None else scale
-        ws = self.workspace(q.shape[1], partition_tokens)
-        return pa_decode(q, self.k_pool, self.v_pool, self.tables[:S], self.lens[:S], scale,
-                         out=out, partition_tokens=partition_tokens, workspace=ws, stream=stream)
+        stream = self._stream(stream)
+        with torch.cuda.stream(stream):
+            ws = self.workspace(q.shape[1], partition_tokens)
+            if self.share_prefixes and self.groups is not None:
+                return pa_decode_shared(q, self.k_pool, self.v_pool, self.tables[:S],
+                                        self.lens[:S], scale, self.groups[0], self.groups[1],
+                                        out=out, partition_tokens=partition_tokens, workspace=ws,
+                                        stream=stream)
+            return pa_decode(q, self.k_pool, self.v_pool, self.tables[:S], self.lens[:S], scale,
+                             out=out, partition_tokens=partition_tokens, workspace=ws,
+                             stream=stream)

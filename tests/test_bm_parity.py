@@ -61,24 +61,9 @@ def test_random_operation_streams_match():
                 seqs = rnd.sample(live, k)
                 ns = [rnd.randint(0, 3 * B) for _ in seqs]
                 st, slots, sq, pos, pairs = c.append_batch(seqs, ns)
-                # the model appends the same sequences in the same order
+                # the model runs the same appends one after another, all or nothing
                 snap = (list(m.free), list(m.refcount))
-                exp_slots, exp_pairs, exp_st = [], [], OK
-                need = 0
-                for s, n in zip(seqs, ns):
-                    seq = m.seqs[s]
-                    need += -(-(seq.n_tokens + n) // B) - len(seq.table)
-                    need += 1 if (n > 0 and seq.n_tokens % B and
-                                  m.refcount[seq.table[-1]] > 1) else 0
-                if need > len(m.free):
-                    exp_st = PA_ENOMEM
-                    m.enomem_events += 1
-                else:
-                    for s, n in zip(seqs, ns):
-                        r = m.append(s, n)
-                        assert r[0] == OK
-                        exp_slots += r[1]
-                        exp_pairs += r[2]
+                exp_st, exp_slots, exp_pairs = m.append_batch(seqs, ns)
                 assert st == exp_st
                 if st == PA_OK:
                     assert slots.tolist() == exp_slots
@@ -95,6 +80,94 @@ def test_random_operation_streams_match():
             if step % 50 == 0:
                 assert_same_state(c, m)
         assert_same_state(c, m)
+
+
+def test_batch_of_sharers_fits_exactly_the_blocks_it_takes():
+    """k sharers of a partly filled tail appended in one batch take k - 1
+    copies (the last writes in place), so a pool with exactly k - 1 free
+    blocks is enough; one block fewer is all-or-nothing ENOMEM.  The model
+    runs the appends one after another."""
+    for k in (2, 3, 4):
+        for spare in (0, -1):
+            B = 4
+            nb = 2 + (k - 1) + spare          # 2 blocks of prefix, then k - 1 copies
+            c, m = BlockManager(nb, B, 3), BlockManagerModel(nb, B, 3)
+            for x in (c, m):
+                root = x.add_seq()
+                assert x.append(root, 6)[0] == OK   # 1 full block + a 2-token tail
+                for _ in range(k - 1):
+                    assert x.fork(root)[0] == OK
+            seqs, ns = list(range(k)), [1] * k
+            st, slots, _, _, pairs = c.append_batch(seqs, ns)
+            exp = m.append_batch(seqs, ns)
+            assert st == exp[0] == (PA_OK if spare == 0 else PA_ENOMEM)
+            if st == PA_OK:
+                assert slots.tolist() == exp[1]
+                assert [tuple(p) for p in pairs.tolist()] == exp[2]
+                assert len(exp[2]) == k - 1
+            assert_same_state(c, m)
+
+
+def test_prefix_groups_match_the_model():
+    """Random fork trees appended in random amounts: the C manager's prefix
+    groups equal the model's for batches in random order and member
+    limits, and every group's shared entries are the same full blocks in
+    every member."""
+    rnd = random.Random(5)
+    for trial in range(30):
+        B = rnd.choice([4, 16])
+        c, m = BlockManager(4000, B, trial + 1), BlockManagerModel(4000, B, trial + 1)
+        seqs = []
+        for p in range(rnd.randint(1, 6)):
+            root = c.add_seq()
+            assert m.add_seq() == root
+            n = rnd.randint(0, 5 * B)
+            assert c.append(root, n) == m.append(root, n)
+            fam = [root]
+            for _ in range(rnd.randint(0, 5)):
+                par = rnd.choice(fam)
+                (s1, k1), (s2, k2) = c.fork(par), m.fork(par)
+                assert s1 == s2 == OK and k1 == k2
+                fam.append(k1)
+            for s in fam:
+                n = rnd.randint(0, 2 * B)
+                assert c.append(s, n) == m.append(s, n)
+            seqs += fam
+        if rnd.random() < 0.3:
+            rnd.shuffle(seqs)
+        mm = rnd.choice([1, 2, 4, 16])
+        st, gs, sb = c.prefix_groups(seqs, mm)
+        egs, esb = m.prefix_groups(seqs, mm)
+        assert st == PA_OK and gs.tolist() == egs and sb.tolist() == esb
+        for i in range(len(sb)):
+            members = seqs[gs[i]:gs[i + 1]]
+            assert 1 <= len(members) <= mm
+            first = m.seqs[members[0]].table
+            for s in members:
+                q = m.seqs[s]
+                assert sb[i] <= q.n_tokens // B and q.table[:sb[i]] == first[:sb[i]]
+
+
+def test_prefix_groups_of_parallel_samples():
+    """Four samples forked from a 1024-token prompt (64 full blocks) form one
+    group sharing all 64 blocks, whatever each sample appended since; with a
+    1032-token prompt the partly filled 65th block is not shared (it is not
+    full), and after the first private append it is copied anyway."""
+    for shared_tokens, expect in ((1024, 64), (1032, 64)):
+        c = BlockManager(2000, 16, 7)
+        root = c.add_seq()
+        c.append(root, shared_tokens)
+        kids = [root] + [c.fork(root)[1] for _ in range(3)]
+        for i, s in enumerate(kids):
+            c.append(s, 1 + 37 * i)
+        st, gs, sb = c.prefix_groups(kids, 4)
+        assert st == PA_OK and gs.tolist() == [0, 4] and sb.tolist() == [expect]
+        st, gs, sb = c.prefix_groups(kids, 2)
+        assert gs.tolist() == [0, 2, 4] and sb.tolist() == [expect, expect]
+        other = c.add_seq()
+        c.append(other, 40)
+        st, gs, sb = c.prefix_groups([other] + kids, 4)
+        assert gs.tolist() == [0, 1, 5] and sb.tolist() == [0, expect]
 
 
 def test_exhaustion_leaves_state_unchanged():
