@@ -48,7 +48,8 @@ typedef enum {
   PA_EINVAL = 1,        /* bad argument; nothing was done                  */
   PA_ENOMEM = 2,        /* block pool exhausted (block manager only)       */
   PA_EHIP = 3,          /* a HIP runtime call or kernel launch failed      */
-  PA_EUNSUPPORTED = 4   /* valid arguments, shape not implemented          */
+  PA_EUNSUPPORTED = 4,  /* valid arguments, shape not implemented          */
+  PA_ESCRATCH = 5       /* pa_decode_noalloc: sizes exceed its fixed scratch */
 } pa_status;
 
 typedef enum {
@@ -218,6 +219,31 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
 size_t pa_decode_shared_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
                                         int32_t num_q_heads, int32_t max_blocks_per_seq,
                                         int32_t partition_tokens);
+
+/*
+ * pa_decode without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * result as for pa_decode.  The workspace is a fixed device array inside
+ * the library, pa_decode_noalloc_max_bytes() bytes per GPU, taken when the
+ * library's code is loaded on that GPU and held until the process ends;
+ * its address is looked up on the first call on each device.  Sizes whose
+ * pa_decode_workspace_bytes exceeds it return PA_ESCRATCH (nothing is
+ * launched).  Every call on one GPU uses that GPU's array: calls that
+ * overlap on one GPU (different streams, no ordering) race and give wrong
+ * results; calls ordered on one stream are fine.  Nothing in the array
+ * needs to start at zero (every word the second kernel reads is written by
+ * the first in the same call).  PA_DEBUG=1 validation is not done here (it
+ * would copy to the host and synchronize).
+ */
+pa_status pa_decode_noalloc(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                            const void* q, int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, float scale, void* out,
+                            int32_t partition_tokens, void* stream);
+
+/* Bytes of the fixed scratch array of pa_decode_noalloc. */
+size_t pa_decode_noalloc_max_bytes(void);
 
 /*
  * Multi-token paged attention: extend / chunked prefill over a paged prefix

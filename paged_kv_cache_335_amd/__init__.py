@@ -25,7 +25,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 
-PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_EUNSUPPORTED = range(5)
+PA_OK, PA_EINVAL, PA_ENOMEM, PA_EHIP, PA_EUNSUPPORTED, PA_ESCRATCH = range(6)
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
@@ -66,6 +66,8 @@ def _load():
         "pa_decode": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp, sz, vp]),
         "pa_decode_shared": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, i32, vp,
                                    vp, vp, sz, vp]),
+        "pa_decode_noalloc": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp]),
+        "pa_decode_noalloc_max_bytes": (sz, []),
         "pa_decode_shared_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_block_copy": (i32, [P, vp, vp, vp, i32, vp]),
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
@@ -105,7 +107,8 @@ def _load():
 _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
-    "pa_decode_shared", "pa_decode_shared_workspace_bytes",
+    "pa_decode_shared", "pa_decode_shared_workspace_bytes", "pa_decode_noalloc",
+    "pa_decode_noalloc_max_bytes",
     "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
     "pa_status_str", "pa_probe_sink_bytes", "pa_probe_read",
     "pa_version", "pa_bm_create",
@@ -308,6 +311,26 @@ def pa_decode_shared(q, k_pool, v_pool, block_tables, context_lens, scale, group
         ws_ptr, ws_bytes, _stream(stream))
     _check(st, "pa_decode_shared")
     return out
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
+                      partition_tokens=0, stream=None):
+    """pa_decode on the library's fixed device scratch: allocates nothing
+    (``out`` must be given).  Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("pa_decode_noalloc needs out (it allocates nothing)")
+    desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    st = _lib.pa_decode_noalloc(ctypes.byref(desc), _dev(k_pool, "k_pool"),
+                                _dev(v_pool, "v_pool"), _dev(q, "q"), S, Hq,
+                                _dev(block_tables, "block_tables"), maxB,
+                                _dev(context_lens, "context_lens"), float(scale),
+                                _dev(out, "out"), int(partition_tokens), _stream(stream))
+    _check(st, "pa_decode_noalloc")
+    return out
+
+
+def pa_decode_noalloc_max_bytes():
+    return int(_lib.pa_decode_noalloc_max_bytes())
 
 
 def pa_extend(q, k_pool, v_pool, q_start, block_tables, context_lens, scale, out=None,

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "pa_internal.h"
@@ -211,6 +212,29 @@ pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_poo
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
+// Fixed device scratch of pa_decode_noalloc (for callers that cannot
+// allocate): the decode workspace, one copy per GPU, held until the process
+// ends.  Host code never names it: each device's address comes from
+// hipGetSymbolAddress, taken once per device.
+constexpr size_t kScratchBytes = (size_t)18 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Address of this device's scratch (nullptr if the runtime refuses).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = p;
+    else (void)hipGetLastError();
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -222,6 +246,7 @@ const char* pa_status_str(pa_status s) {
     case PA_ENOMEM: return "block pool exhausted";
     case PA_EHIP: return "HIP runtime error";
     case PA_EUNSUPPORTED: return "unsupported shape";
+    case PA_ESCRATCH: return "sizes exceed the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -339,6 +364,28 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
                      max_blocks_per_seq, context_lens, scale, out, partition_tokens, num_groups,
                      group_start, shared_blocks, workspace, workspace_bytes, debug_checks(),
                      as_stream(stream));
+}
+
+size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+pa_status pa_decode_noalloc(const pa_pool* pool, const void* k_pool, const void* v_pool,
+                            const void* q, int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, float scale, void* out,
+                            int32_t partition_tokens, void* stream) {
+  int32_t P;
+  size_t ws;
+  const pa_status st = decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                    partition_tokens, false, &P, &ws);
+  if (st != PA_OK) return st;
+  if (ws > kScratchBytes) return PA_ESCRATCH;
+  if (num_seqs == 0) return PA_OK;
+  void* ptr = scratch_ptr();
+  if (!ptr) return PA_EHIP;
+  // no host-side validation copy here (it would synchronize the stream)
+  return decode_impl(pool, k_pool, v_pool, q, num_seqs, num_q_heads, block_tables,
+                     max_blocks_per_seq, context_lens, scale, out, partition_tokens, 0, nullptr,
+                     nullptr, ptr, kScratchBytes, false, as_stream(stream));
 }
 
 pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,

@@ -88,6 +88,9 @@ def test_workspace_and_partition_sizing():
     rows = 2 * 256 * 4 * 15
     assert L.pa_decode_workspace_bytes(ctypes.byref(d3), 8, 6, 64, 0) == \
         2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(8 * 16)
+    # the fixed scratch of the no-allocation entry point covers the largest
+    # workspace on 256 CUs: 16 head slots, 128 dims, a full launch of sequences
+    assert L.pa_decode_noalloc_max_bytes() >= big + 4096 * 16
     # prefix groups add two rows per query head of each sequence of one
     # launch (2048 with groups)
     rows = 2 * 256 * 4 * 16
@@ -110,6 +113,28 @@ def test_workspace_and_partition_sizing():
     # invalid: piece not a multiple of the block, heads not divisible
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 100) == 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 30, 8192, 512) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_launch():
+    """A shape whose workspace exceeds the fixed scratch (here 8192 kv heads:
+    a grid of 2048 workgroups) returns PA_ESCRATCH; invalid arguments return
+    PA_EINVAL; neither touches the device."""
+    import paged_kv_cache_335_amd as pk
+    L = pk.lib()
+    dummy = ctypes.c_void_p(0x1000)  # never dereferenced: rejected first
+    null = ctypes.c_void_p(0)
+    huge = _desc(nb=64, nkv=8192)
+    st = L.pa_decode_noalloc(ctypes.byref(huge), dummy, dummy, dummy, 4, 8192, dummy, 4, dummy,
+                             0.1, dummy, 0, null)
+    assert st == pk.PA_ESCRATCH
+    assert "scratch" in pk.status_str(pk.PA_ESCRATCH)
+    d = _desc()
+    st = L.pa_decode_noalloc(ctypes.byref(d), dummy, dummy, dummy, 4, 30, dummy, 4, dummy, 0.1,
+                             dummy, 0, null)
+    assert st == pk.PA_EINVAL
+    st = L.pa_decode_noalloc(None, dummy, dummy, dummy, 4, 32, dummy, 4, dummy, 0.1, dummy, 0,
+                             null)
+    assert st == pk.PA_EINVAL
 
 
 def test_host_checks_reject_before_any_launch():
