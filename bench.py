@@ -12,9 +12,10 @@ bf16 scale per token and kv head; queries and new tokens stay bf16).
 With --config prefix_sharing (or prefix_sharing_cow) 64 prompts are written
 once and forked into 4 samples each, which share the prompt's blocks (the
 copy-on-write variant's partly filled shared tail is copied on the first
-private append).  `value` counts every sequence's context (logical bytes);
-the roofline uses the distinct token slots read (a shared prefix once),
-since repeated reads of shared blocks can hit in the caches.
+private append).  The decode reads each prompt's shared blocks once for its
+samples (prefix groups; --no-share reads them per sample).  `value` counts
+every sequence's context (logical bytes); the roofline uses the distinct
+token slots read (a shared prefix once).
 
 One step = the whole hot path for one batch: the host block manager appends
 one token to every sequence (slots, new blocks, copy-on-write decisions), one
@@ -22,12 +23,17 @@ packed host-to-device metadata copy, the device table update, the slot write
 of the 256 new tokens, and paged decode attention over every context.
 
 Prints one JSON line.  `value` is KV bytes read per step / step time (GB/s);
-`roofline` reports the decode kernel (HIP events on its stream) against the
-8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a bounded sample of
-the same batch.
+`roofline` reports the decode call (decode and reduce kernels) against the
+8 TB/s HBM peak, timed per iteration with HIP events on its stream with the
+caches flushed before each iteration (a 512 MiB write outside the events),
+median of the iterations (minimum reported beside it), and beside it the
+read ceiling a streaming-read probe measures on this GPU.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same batch.  The default
+run adds short legs for the other workloads under `legs`.
 """
 import argparse
 import gc
+import hashlib
 import json
 import math
 import os
@@ -42,46 +48,66 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV bytes read GB/s (% HBM peak) + decode tokens/s"
 HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 512 * 1024 * 1024
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_gqa_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
 DECODE_SOURCES = ("paged_kv_cache_335_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_335_amd/csrc/pa_device.h",
                   "paged_kv_cache_335_amd/csrc/pa_internal.h")
 
 
-def measured_traffic(kv_bytes):
-    """HBM bytes per decode launch from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy's counters), or
-    None when the decode sources changed since the counters were taken or this
-    run's workload is not the one they were taken on."""
-    import hashlib
-    try:
-        text = open(TRAFFIC_PROFILE).read()
-    except OSError:
-        return None
-    fields = dict(ln.split(": ", 1) for ln in text.splitlines()
-                  if ln.startswith(("traffic_bytes_per_launch:", "algorithmic_bytes_per_launch:",
-                                    "decode_source_sha256:")))
+def decode_source_hash():
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("decode_source_sha256") != h.hexdigest():
+    return h.hexdigest()
+
+
+def measured_traffic(workload, algorithmic_bytes):
+    """HBM bytes per decode launch: the traffic / algorithmic-bytes ratio that
+    the committed counter summary records for this workload (FETCH_SIZE and
+    WRITE_SIZE passes, scaled by a plain copy's counters), applied to this
+    run's algorithmic bytes; None when the decode sources changed since the
+    counters were taken or the summary has no entry for the workload."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
         return None
-    if int(fields.get("algorithmic_bytes_per_launch", -1)) != int(kv_bytes):
+    src = None
+    ratios = {}
+    for ln in text.splitlines():
+        if ln.startswith("decode_source_sha256: "):
+            src = ln.split(": ", 1)[1].strip()
+        elif ln.startswith("traffic_ratio "):
+            key, val = ln[len("traffic_ratio "):].split(": ", 1)
+            ratios[key.strip()] = float(val)
+    if src != decode_source_hash() or workload not in ratios:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return {"bytes_per_launch": int(round(ratios[workload] * algorithmic_bytes)),
+            "ratio_to_algorithmic": ratios[workload],
+            "source": os.path.relpath(TRAFFIC_PROFILE, ROOT)}
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama3_8b_gqa",
                     choices=["llama2_7b_mha", "llama3_8b_gqa", "prefix_sharing",
@@ -92,6 +118,8 @@ def parse():
     ap.add_argument("--mode", default="decode", choices=["decode", "extend"],
                     help="decode (default) or extend: chunked prefill over paged prefixes")
     ap.add_argument("--extend-seqs", type=int, default=32)
+    ap.add_argument("--extend-prefix", type=int, default=0,
+                    help="extend: every sequence's cached prefix (0: the workload's lengths)")
     ap.add_argument("--chunk", type=int, default=256, help="new tokens per sequence per step")
     ap.add_argument("--no-share", action="store_true",
                     help="prefix-sharing configs: read shared blocks once per sequence, not "
@@ -101,7 +129,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="decode iterations timed one by one with the caches flushed before each")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the short legs of the other workloads")
+    ap.add_argument("--leg-steps", type=int, default=10)
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--swap-blocks", type=int, default=1024,
                     help="after timing, swap this many resident blocks out to pinned host memory "
                          "and back, timed (0: skip)")
@@ -124,20 +157,54 @@ def main():
     import paged_kv_cache_335_amd as pk
     from paged_kv_cache_335_amd.runtime import DeviceEvent, PagedKVCache
     from workloads import CONFIGS, draw_lengths
-    from workloads.gen import unique_blocks
 
-    if args.mode == "extend":
-        return bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths)
-
-    cfg = CONFIGS[args.config]
-    if args.block_size != cfg.block_size:
-        cfg = cfg.scaled(block_size=args.block_size)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(dev)
     torch.cuda.set_stream(stream)
+
+    if args.mode == "extend":
+        return bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths)
+
+    res = run_decode(args, args.config, args.kv, args.block_size, args.steps, args.warmup,
+                     max(1, args.cold_iters), stream, full=True)
+    result = res.pop("result")
+    if not args.no_read_probe:
+        result["read_ceiling"] = read_probe(pk, stream)
+        result["roofline"]["measured_read_ceiling_GBps"] = \
+            result["read_ceiling"]["random_16KiB_chunks"]["GBps"]
+    if not args.no_legs and args.config == "llama3_8b_gqa" and args.kv == "bf16" \
+            and args.block_size == 16 and args.partition == 0:
+        legs = {}
+        for name, key, kv, B in (("llama2_7b_mha", "llama2_7b_mha", "bf16", 16),
+                                 ("prefix_sharing", "prefix_sharing", "bf16", 16),
+                                 ("prefix_sharing_cow", "prefix_sharing_cow", "bf16", 16),
+                                 ("long_context_128k", "long_context_128k", "bf16", 16),
+                                 ("llama3_8b_gqa_fp8", "llama3_8b_gqa", "fp8", 16),
+                                 ("llama3_8b_gqa_block32", "llama3_8b_gqa", "bf16", 32),
+                                 ("llama3_8b_gqa_block8", "llama3_8b_gqa", "bf16", 8)):
+            legs[name] = run_decode(args, key, kv, B, args.leg_steps, 3,
+                                    max(5, args.cold_iters // 2), stream, full=False)
+        result["legs"] = legs
+    print(json.dumps(result), flush=True)
+
+
+def run_decode(args, key, kv, block_size, K, W, cold_iters, stream, full):
+    """One workload: build and fill the cache through the slot write, time K
+    whole steps after W warm-up steps, then the decode call alone (warm back
+    to back, and cold: caches flushed before each iteration).  full=True
+    adds the cache-op and swap probes and the CPU oracle baseline and
+    returns the whole JSON line under "result"; otherwise a compact dict."""
+    import paged_kv_cache_335_amd as pk
+    from paged_kv_cache_335_amd.runtime import DeviceEvent, PagedKVCache
+    from workloads import CONFIGS, draw_lengths
+    from workloads.gen import unique_blocks
+
+    cfg = CONFIGS[key]
+    if block_size != cfg.block_size:
+        cfg = cfg.scaled(block_size=block_size)
+    dev = torch.device("cuda:0")
     S, Hq, Hkv, d, B = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
-    W, K = args.warmup, args.steps
     steps = W + K
 
     rng = np.random.default_rng(cfg.seed)
@@ -150,11 +217,12 @@ def main():
     num_blocks = int(math.ceil(1.1 * need_blocks)) if cfg.pool[0] == "plus" else max(
         int(cfg.pool[1]), need_blocks)
     width = int((final.max() + B - 1) // B)
-    log(f"{cfg.key}: S={S} Hq={Hq} Hkv={Hkv} d={d} sum L={int(lens0.sum())} "
-        f"pool={num_blocks} blocks width={width}")
-
-    fp8 = args.kv == "fp8"
+    fp8 = kv == "fp8"
     share = bool(shared) and not args.no_share
+    tag = f"{cfg.key}{' fp8' if fp8 else ''}{'' if B == 16 else f' B={B}'}"
+    log(f"{tag}: S={S} Hq={Hq} Hkv={Hkv} d={d} sum L={int(lens0.sum())} "
+        f"pool={num_blocks} blocks width={width}{' (prefix groups)' if share else ''}")
+
     cache = PagedKVCache(num_blocks, Hkv, d, S, width, block_size=B, shuffle_seed=cfg.seed,
                          dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev,
                          share_prefixes=share, max_group=max(1, 16 // (Hq // Hkv)))
@@ -163,7 +231,6 @@ def main():
     if shared:
         # each prompt's shared tokens once, then its forks (so a prompt's
         # samples take adjacent table rows)
-        log(f"prefill {cfg.prompts} prompts x {shared} shared tokens, {cfg.samples} samples each")
         seq_list = []
         for _ in range(cfg.prompts):
             s0 = cache.add_sequence()
@@ -171,7 +238,7 @@ def main():
             vn = torch.randn((shared, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
             cache.append(np.array([s0], np.int32), np.array([shared], np.int32), kn, vn,
                          stream=stream)
-            seq_list += [s0] + [cache.fork(s0) for _ in range(cfg.samples - 1)]
+            seq_list += [s0] + [cache.fork(s0, stream=stream) for _ in range(cfg.samples - 1)]
         seqs = np.array(seq_list, dtype=np.int32)
     else:
         seqs = np.array([cache.add_sequence() for _ in range(S)], dtype=np.int32)
@@ -179,10 +246,8 @@ def main():
     # prefill: every context token but the one each first step appends (past
     # the shared prefix, which is already in place)
     pre = (lens0 - 1 - shared).astype(np.int32)
-    log(f"prefill {int(pre.sum())} tokens through the slot write")
     chunk = 16384
     start = 0
-    order = np.arange(S)
     while start < S:
         # batches of whole sequences, about `chunk` tokens each
         tot, end = 0, start
@@ -191,7 +256,7 @@ def main():
             end += 1
         kn = torch.randn((tot, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
         vn = torch.randn((tot, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
-        cache.append(seqs[order[start:end]], pre[start:end], kn, vn, stream=stream)
+        cache.append(seqs[start:end], pre[start:end], kn, vn, stream=stream)
         start = end
     torch.cuda.synchronize()
 
@@ -225,10 +290,9 @@ def main():
     # milliseconds in this process and, when one fell inside the timed steps,
     # left the GPU idle for a few steps' worth of time.  Collect before the
     # warm-up (whose steps then also warm the host path) and keep it off
-    # until the timed steps and the roofline calls have run.
+    # until the timed steps and the decode timings have run.
     gc.collect()
     gc.disable()
-    log(f"warmup {W} steps (partition {P} tokens)")
     for i in range(W):
         step(i)
         step_bytes.append(int(cache.host_lens[:S].sum()) * kv_per_token)
@@ -237,7 +301,6 @@ def main():
     # the timed steps carry no events: recording one leaves the GPU idle for
     # a few microseconds before the next kernel, which is instrumentation,
     # not part of the path
-    log(f"timing {K} steps")
     t0 = time.perf_counter()
     for i in range(W, steps):
         step(i)
@@ -248,57 +311,88 @@ def main():
     t1 = time.perf_counter()
     host_ms = (t_enq - t0) * 1e3 / K
     ms_step = (t1 - t0) * 1e3 / K
-    timed_bytes = step_bytes[W:]
-    kv_avg = float(np.mean(timed_bytes))
+    kv_avg = float(np.mean(step_bytes[W:]))
     value = kv_avg / (ms_step * 1e-3) / 1e9
+    last_bytes, last_unique = step_bytes[-1], step_unique[-1]
 
-    # decode duration for the roofline: K decode calls back to back on the
-    # same stream, over the last step's batch, between two fence-free HIP
-    # events (each call = the decode kernel and its reduce kernel)
+    def decode_call():
+        cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
+
+    # warm: K decode calls back to back over the last step's batch, between
+    # two fence-free HIP events on the decode stream
     ea, eb = DeviceEvent(timing=True), DeviceEvent(timing=True)
     ea.record(stream)
     for _ in range(K):
-        cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
+        decode_call()
     eb.record(stream)
     eb.synchronize()
-    gc.enable()  # off since before the warm-up
-    dec_ms_avg = ea.elapsed_ms(eb) / K
-    last_bytes = step_bytes[-1]
-    dec_gbps = last_bytes / (dec_ms_avg * 1e-3) / 1e9
-    # with a shared prefix, the bytes that must come from HBM are the
-    # distinct slots; repeated reads of shared blocks can hit in the caches
-    dec_gbps_unique = step_unique[-1] / (dec_ms_avg * 1e-3) / 1e9
-    log(f"step {ms_step:.3f} ms ({value:.0f} GB/s); decode {dec_ms_avg * 1e3:.1f} us "
-        f"({dec_gbps:.0f} GB/s); host enqueue {host_ms:.3f} ms/step")
+    warm_us = ea.elapsed_ms(eb) / K * 1e3
 
-    # cold decode: caches flushed before each call (outside the event window)
-    cold = None
-    if args.cold_iters > 0:
-        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        cold_ms = []
-        for _ in range(args.cold_iters):
-            flush.fill_(1.0)
-            a, b = DeviceEvent(timing=True), DeviceEvent(timing=True)
-            a.record(stream)
-            cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
-            b.record(stream)
-            b.synchronize()
-            cold_ms.append(a.elapsed_ms(b))
-        del flush
-        cold = {"us_mean": float(np.mean(cold_ms)) * 1e3, "us_min": float(np.min(cold_ms)) * 1e3,
-                "GBps": step_bytes[-1] / (np.mean(cold_ms) * 1e-3) / 1e9}
-        log(f"cold decode {cold['us_mean']:.1f} us ({cold['GBps']:.0f} GB/s)")
+    # cold: each iteration timed on its own, the caches (L2 and the last-level
+    # cache) flushed before it by a 512 MiB write outside the events
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    evs = [(DeviceEvent(timing=True), DeviceEvent(timing=True)) for _ in range(cold_iters)]
+    for i in range(5 + cold_iters):
+        flush.fill_(float(i))
+        if i >= 5:
+            evs[i - 5][0].record(stream)
+        decode_call()
+        if i >= 5:
+            evs[i - 5][1].record(stream)
+    torch.cuda.synchronize()
+    gc.enable()  # off since before the warm-up
+    cold_us = np.array([a.elapsed_ms(b) * 1e3 for a, b in evs])
+    del flush
+    med, mn = float(np.median(cold_us)), float(np.min(cold_us))
+    roof_bytes = last_unique  # a shared prefix counts once
+    achieved = roof_bytes / (med * 1e-6) / 1e9
+    log(f"{tag}: step {ms_step:.3f} ms ({value:.0f} GB/s); decode warm {warm_us:.1f} us, "
+        f"cold median {med:.1f} us (min {mn:.1f}) = {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBPS:.3f} of peak); host enqueue {host_ms:.3f} ms/step")
+
+    workload = f"{cfg.key}/{kv}/B{B}" + ("/shared" if share else "") + (
+        f"/P{args.partition}" if args.partition else "")
+    traffic = measured_traffic(workload, roof_bytes)
+    total_blocks = int(((cache.host_lens[:S].astype(np.int64) + B - 1) // B).sum())
+    piece = pk.pa_decode_piece_tokens(cache.k_pool, cache.v_pool, S, Hq, width, total_blocks,
+                                      args.partition)
+    lens_now = cache.host_lens[:S].copy()
+    pieces = int(np.sum(-(-lens_now.astype(np.int64) // piece))) if piece else None
+    decode = {"us_warm": round(warm_us, 2), "us_cold_median": round(med, 2),
+              "us_cold_min": round(mn, 2), "cold_iters": int(cold_iters),
+              "kv_bytes": int(last_bytes), "kv_bytes_unique": int(roof_bytes),
+              "GBps_cold_median": round(achieved, 1),
+              "GBps_cold_best": round(roof_bytes / (mn * 1e-6) / 1e9, 1),
+              "GBps_warm": round(roof_bytes / (warm_us * 1e-6) / 1e9, 1),
+              "GBps_logical_cold_median": round(last_bytes / (med * 1e-6) / 1e9, 1),
+              "tokens_per_s": round(S / (med * 1e-6), 1),
+              "piece_tokens": piece, "pieces_about": pieces,
+              "prefix_groups": int(cache.num_groups) if share else None}
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "timing": f"decode call (decode + reduce kernels), median of {cold_iters} "
+                          "iterations, each between its own HIP events, caches flushed before "
+                          "each; bytes = distinct K/V token slots read"}
+    if traffic:
+        roofline["traffic_ratio"] = traffic["ratio_to_algorithmic"]
+        roofline["traffic_source"] = traffic["source"]
+
+    if not full:
+        res = {"workload": f"{cfg.key}: {cfg.description}" + (
+                   "; 8-bit cache" if fp8 else "") + (f"; {B}-token blocks" if B != 16 else ""),
+               "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5),
+               "step_GBps": round(value, 1), "decode": decode, "roofline": roofline}
+        del cache, qs, kns, vns, out
+        gc.collect()
+        torch.cuda.empty_cache()
+        return res
 
     # the last step's output again, for the sampled parity check below
-    cache.decode(qs[-1], out=out, partition_tokens=args.partition, stream=stream)
+    decode_call()
     torch.cuda.synchronize()
-
     copy_write = copy_write_probe(pk, cache, kns[-1], vns[-1], stream)
-
-    swap = None
-    if args.swap_blocks > 0:
-        swap = swap_probe(pk, cache, args.swap_blocks, stream)
-
+    swap = swap_probe(pk, cache, args.swap_blocks, stream) if args.swap_blocks > 0 else None
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 1024 * 1024 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -309,12 +403,10 @@ def main():
         log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
         del src, dst
 
-    lens_now = cache.host_lens[:S].copy()
     stats = cache.bm.stats()
     tail_waste = 100.0 * (stats["allocated_slots"] - stats["stored_tokens"]) / max(
         1, stats["allocated_slots"])
     contiguous_util = 100.0 * float(lens_now.sum()) / (S * int(final.max()))
-
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -323,7 +415,7 @@ def main():
         "config": {
             "workload": f"{cfg.key}: {cfg.description}" + (
                 "; 8-bit cache (E4M3 + per-token bf16 scales)" if fp8 else ""),
-            "kv_storage": args.kv,
+            "kv_storage": kv,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
             "block_size": B, "pool_blocks": num_blocks, "partition_tokens": P,
             "mean_context_tokens": round(float(lens_now.mean()), 1),
@@ -333,17 +425,8 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "host_enqueue_ms_per_step": round(host_ms, 4),
-        "decode": {"us_mean": round(dec_ms_avg * 1e3, 2), "GBps": round(dec_gbps, 1),
-                   "kv_bytes": int(last_bytes), "calls": K,
-                   "tokens_per_s": round(S / (dec_ms_avg * 1e-3), 1),
-                   "GBps_unique": round(dec_gbps_unique, 1),
-                   "kv_bytes_unique": int(step_unique[-1])},
-        "decode_cold": cold,
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps_unique, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps_unique / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(kv_avg)
-                     if args.partition == 0 and not fp8 else None},
+        "decode": decode,
+        "roofline": roofline,
         "cache_ops": copy_write,
         "block_swap": swap,
         "block_manager": {"tail_waste_pct": round(tail_waste, 3),
@@ -353,12 +436,62 @@ def main():
             "prior_systems_kv_utilisation": "20-40%", "paging_waste": "under 4%",
             "vllm_throughput_vs_prior": "2-4x"},
     }
-
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(
             cache, qs[-1], out, lens_now, S, Hq, d, kv_per_token, args.cpu_seconds)
+    del cache, qs, kns, vns, out
+    gc.collect()
+    torch.cuda.empty_cache()
+    return {"result": result}
 
-    print(json.dumps(result), flush=True)
+
+def read_probe(pk, stream, total_bytes=2 << 30, reps=3):
+    """The read ceiling of this GPU: a 2 GiB buffer read once per pass with
+    16-byte non-temporal loads (pa_probe_read), as a contiguous stream (1 MiB
+    chunks in order) and as gathers of 16 KiB and 4 KiB chunks in random
+    order (the regions a decode workgroup and a wave read per block).  Each
+    pattern is tried at 1, 2, 4 and 8 workgroups per CU with 2 and 8 loads
+    in flight per thread; the best pass (each between its own HIP events)
+    is the ceiling."""
+    from paged_kv_cache_335_amd.runtime import DeviceEvent
+    dev = torch.device("cuda:0")
+    buf = torch.empty(total_bytes, dtype=torch.uint8, device=dev)
+    buf.fill_(7)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(int(pk.lib().pa_probe_sink_bytes(cus * 8)), dtype=torch.uint8, device=dev)
+    rng = np.random.default_rng(0)
+    res = {}
+    for name, chunk, shuffled in (("contiguous", 1 << 20, False),
+                                  ("random_16KiB_chunks", 16 << 10, True),
+                                  ("random_4KiB_chunks", 4 << 10, True)):
+        n = total_bytes // chunk
+        order = rng.permutation(n) if shuffled else np.arange(n)
+        d_order = torch.from_numpy(order.astype(np.int32)).to(dev)
+        best = None
+        for per_cu in (1, 2, 4, 8):
+            for lif in (2, 8):
+                wgs = cus * per_cu
+                pk.pa_probe_read(buf, d_order, chunk, wgs, lif, sink=sink, stream=stream)
+                for _ in range(reps):
+                    a, b = DeviceEvent(timing=True), DeviceEvent(timing=True)
+                    a.record(stream)
+                    pk.pa_probe_read(buf, d_order, chunk, wgs, lif, sink=sink, stream=stream)
+                    b.record(stream)
+                    b.synchronize()
+                    ms = a.elapsed_ms(b)
+                    if best is None or ms < best[0]:
+                        best = (ms, per_cu, lif)
+        gbps = total_bytes / (best[0] * 1e-3) / 1e9
+        res[name] = {"chunk_bytes": chunk, "GBps": round(gbps, 1),
+                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "workgroups_per_cu": best[1], "loads_in_flight": best[2]}
+    log("read ceiling: " + ", ".join(f"{k} {v['GBps']:.0f} GB/s" for k, v in res.items()))
+    del buf, sink
+    torch.cuda.empty_cache()
+    res["method"] = ("pa_probe_read over a 2 GiB buffer, 16-byte non-temporal loads, 256 "
+                     "threads per workgroup; best pass over 1-8 workgroups per CU and 2 or 8 "
+                     "loads in flight per thread")
+    return res
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -379,7 +512,10 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
                         cfg.block_size)
     W, K, C = args.warmup, args.steps, args.chunk
     rng = np.random.default_rng(cfg.seed)
-    lens0 = draw_lengths(cfg, rng)[:S].astype(np.int64)
+    if args.extend_prefix > 0:
+        lens0 = np.full(S, args.extend_prefix, np.int64)
+    else:
+        lens0 = draw_lengths(cfg, rng)[:S].astype(np.int64)
     final = lens0 + (W + K) * C
     need = int(((final + B - 1) // B).sum())
     num_blocks = int(math.ceil(1.1 * need))
@@ -502,7 +638,7 @@ def extend_cpu_baseline(cache, q, out, tables, lens, C, Hq, d, scale, seconds):
     log(f"cpu baseline (extend): {n} sequences x {C} queries on {threads} threads, {dt:.2f} s, "
         f"{fl / dt / 1e12:.4f} TFLOP/s; sampled parity max|err| {err:.3e}")
     base = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n} of {len(lens)} sequences of the last timed step's batch, all {C} "
                       f"queries and {Hq} query heads each ({dt:.1f} s); fp64 C oracle, OpenMP",
             "seconds": round(dt, 3), "query_tokens_per_s": round(n * C / dt, 2)}
@@ -636,7 +772,7 @@ def cpu_baseline(cache, q, out, lens, S, Hq, d, kv_per_token, seconds):
         f"threads, {dt:.3f} s per pass, {sample_bytes / dt / 1e9:.3f} GB/s; sampled parity "
         f"max|err| {err:.3e}")
     base = {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{len(seqs)} of {S} sequences of the last timed step's batch ({tok} "
                       f"tokens), all {Hq} query heads, {reps} passes ({elapsed:.1f} s); fp64 C "
                       f"oracle, OpenMP over (sequence, head)",

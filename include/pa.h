@@ -132,6 +132,18 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
                                    int32_t partition_tokens);
 
 /*
+ * The length (tokens) of the ranges pa_decode cuts a batch of total_blocks
+ * blocks into (all sequences of one launch of at most 4096, with the
+ * launch grid of the current device): at least partition_tokens (or the
+ * library's choice), and long enough that the ranges of one kv head cover
+ * the batch with one range per wave.  A sequence of L tokens is then cut
+ * into about L / this pieces.  For reports; 0 on invalid arguments.
+ */
+int32_t pa_decode_piece_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, int32_t partition_tokens,
+                               int64_t total_blocks);
+
+/*
  * Paged decode attention: for every sequence s and query head h, with
  * g = h / (num_q_heads / num_kv_heads) and L = context_lens[s],
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t,   t in [0, L),

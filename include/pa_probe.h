@@ -28,7 +28,8 @@ size_t pa_probe_sink_bytes(int32_t workgroups);
  * Read n_chunks chunks of chunk_bytes bytes each, chunk order[i] being the
  * bytes [order[i] * chunk_bytes, (order[i] + 1) * chunk_bytes) of buf, with
  * 16-byte non-temporal loads; workgroup w reads chunks i = w, w + workgroups,
- * and so on.  The XOR of the bytes each thread read goes to sink.
+ * and so on, each of its 256 threads keeping loads_in_flight (1, 2, 4 or 8)
+ * loads outstanding.  The XOR of the bytes each thread read goes to sink.
  *   buf:   device buffer holding every chunk order names (caller-checked);
  *   order: int32 [n_chunks] device array of chunk indices (a permutation
  *          for a random gather, the identity for a contiguous stream);
@@ -37,7 +38,8 @@ size_t pa_probe_sink_bytes(int32_t workgroups);
  * for null pointers or non-positive counts).  Asynchronous on `stream`.
  */
 pa_status pa_probe_read(const void* buf, const int32_t* order, int32_t n_chunks,
-                        uint32_t chunk_bytes, int32_t workgroups, void* sink, void* stream);
+                        uint32_t chunk_bytes, int32_t workgroups, int32_t loads_in_flight,
+                        void* sink, void* stream);
 
 #ifdef __cplusplus
 }

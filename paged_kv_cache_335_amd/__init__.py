@@ -63,6 +63,7 @@ def _load():
         "pa_kv_write": (i32, [P, vp, vp, vp, vp, vp, i32, vp]),
         "pa_decode_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_decode_partition_tokens": (i32, [P, i32, i32, i32, i32]),
+        "pa_decode_piece_tokens": (i32, [P, i32, i32, i32, i32, i64]),
         "pa_decode": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp, sz, vp]),
         "pa_decode_shared": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, i32, vp,
                                    vp, vp, sz, vp]),
@@ -75,7 +76,7 @@ def _load():
         "pa_block_swap": (i32, [P, vp, vp, vp, vp, i32, vp, i32, i32, vp]),
         "pa_extend": (i32, [P, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, f32, vp, vp]),
         "pa_probe_sink_bytes": (sz, [i32]),
-        "pa_probe_read": (i32, [vp, vp, i32, ctypes.c_uint32, i32, vp, vp]),
+        "pa_probe_read": (i32, [vp, vp, i32, ctypes.c_uint32, i32, i32, vp, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
         "pa_version": (ctypes.c_char_p, []),
         "pa_bm_create": (vp, [i32, i32, ctypes.c_uint64]),
@@ -106,7 +107,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = (
-    "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode",
+    "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
+    "pa_decode_piece_tokens", "pa_decode",
     "pa_decode_shared", "pa_decode_shared_workspace_bytes", "pa_decode_noalloc",
     "pa_decode_noalloc_max_bytes",
     "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
@@ -237,6 +239,15 @@ def pa_decode_shared_workspace_bytes(k_pool, v_pool, num_seqs, num_q_heads,
     desc = pool_desc(k_pool, v_pool)
     return int(_lib.pa_decode_shared_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
                                                      max_blocks_per_seq, partition_tokens))
+
+
+def pa_decode_piece_tokens(k_pool, v_pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                           total_blocks, partition_tokens=0):
+    """Length of the ranges pa_decode cuts a batch of total_blocks blocks into."""
+    desc = pool_desc(k_pool, v_pool)
+    return int(_lib.pa_decode_piece_tokens(ctypes.byref(desc), num_seqs, num_q_heads,
+                                           max_blocks_per_seq, partition_tokens,
+                                           int(total_blocks)))
 
 
 def pa_decode_partition_tokens(k_pool, v_pool, num_seqs, num_q_heads, max_blocks_per_seq,
@@ -453,7 +464,8 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, seq_i
     _check(st, "pa_kv_append")
 
 
-def pa_probe_read(buf, order, chunk_bytes, workgroups, sink=None, stream=None):
+def pa_probe_read(buf, order, chunk_bytes, workgroups, loads_in_flight=4, sink=None,
+                  stream=None):
     """Read buf's chunks in the given order (pa_probe_read); returns sink."""
     if order.dtype != torch.int32:
         raise TypeError("order must be int32")
@@ -468,7 +480,8 @@ def pa_probe_read(buf, order, chunk_bytes, workgroups, sink=None, stream=None):
     if n and int(order.max()) * int(chunk_bytes) + int(chunk_bytes) > buf.numel() * buf.element_size():
         raise ValueError("a chunk index reaches past the buffer")
     st = _lib.pa_probe_read(_dev(buf, "buf"), _dev(order, "order"), n, int(chunk_bytes),
-                            int(workgroups), _dev(sink, "sink"), _stream(stream))
+                            int(workgroups), int(loads_in_flight), _dev(sink, "sink"),
+                            _stream(stream))
     _check(st, "pa_probe_read")
     return sink
 

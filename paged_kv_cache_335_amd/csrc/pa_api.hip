@@ -332,6 +332,21 @@ size_t pa_decode_shared_workspace_bytes(const pa_pool* pool, int32_t num_seqs,
   return ws;
 }
 
+int32_t pa_decode_piece_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_blocks_per_seq, int32_t partition_tokens,
+                               int64_t total_blocks) {
+  int32_t P;
+  size_t ws;
+  if (total_blocks < 0 || decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                       partition_tokens, false, &P, &ws) != PA_OK)
+    return 0;
+  // as the plan computes it: R ranges per kv head over the launch's waves
+  const int64_t R = std::max<int64_t>(
+      1, (int64_t)pakv::decode_grid(pool->num_kv_heads) * pakv::kWaves / pool->num_kv_heads);
+  const int64_t q = std::max<int64_t>(P / pool->block_size, (total_blocks + R - 1) / R);
+  return q * pool->block_size > INT32_MAX ? 0 : static_cast<int32_t>(q * pool->block_size);
+}
+
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_blocks_per_seq, int32_t partition_tokens) {
   int32_t P;

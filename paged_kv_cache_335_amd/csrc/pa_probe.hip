@@ -56,12 +56,20 @@ size_t pa_probe_sink_bytes(int32_t workgroups) {
 }
 
 pa_status pa_probe_read(const void* buf, const int32_t* order, int32_t n_chunks,
-                        uint32_t chunk_bytes, int32_t workgroups, void* sink, void* stream) {
+                        uint32_t chunk_bytes, int32_t workgroups, int32_t loads_in_flight,
+                        void* sink, void* stream) {
   if (!buf || !order || !sink || n_chunks <= 0 || workgroups <= 0) return PA_EINVAL;
   if (chunk_bytes == 0 || chunk_bytes % 16 != 0) return PA_EINVAL;
-  gather_read_kernel<4><<<workgroups, kThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(buf), order, n_chunks, chunk_bytes,
-      static_cast<uint32_t*>(sink));
+  const auto* b = static_cast<const uint8_t*>(buf);
+  auto* k = static_cast<uint32_t*>(sink);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (loads_in_flight) {
+    case 1: gather_read_kernel<1><<<workgroups, kThreads, 0, st>>>(b, order, n_chunks, chunk_bytes, k); break;
+    case 2: gather_read_kernel<2><<<workgroups, kThreads, 0, st>>>(b, order, n_chunks, chunk_bytes, k); break;
+    case 4: gather_read_kernel<4><<<workgroups, kThreads, 0, st>>>(b, order, n_chunks, chunk_bytes, k); break;
+    case 8: gather_read_kernel<8><<<workgroups, kThreads, 0, st>>>(b, order, n_chunks, chunk_bytes, k); break;
+    default: return PA_EINVAL;
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_EHIP;
 }
 
