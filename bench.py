@@ -18,9 +18,13 @@ every sequence's context (logical bytes); the roofline uses the distinct
 token slots read (a shared prefix once).
 
 One step = the whole hot path for one batch: the host block manager appends
-one token to every sequence (slots, new blocks, copy-on-write decisions), one
-packed host-to-device metadata copy, the device table update, the slot write
-of the 256 new tokens, and paged decode attention over every context.
+one token to every sequence (slots, new blocks, copy-on-write decisions),
+then one launch (pa_decode_step) stores the 256 new tokens, grows the block
+tables and lengths on the device, and runs paged decode attention over
+every context; the host's only input to it is each token's block id, read
+by the kernel from pinned memory.  (--two-call: a packed host-to-device
+metadata copy, pa_kv_append, then pa_decode; the 8-bit cache always takes
+this path.)
 
 Prints one JSON line.  `value` is KV bytes read per step / step time (GB/s);
 `roofline` reports the decode call (decode and reduce kernels) against the
@@ -124,6 +128,9 @@ def parse():
     ap.add_argument("--no-share", action="store_true",
                     help="prefix-sharing configs: read shared blocks once per sequence, not "
                          "once per prefix group")
+    ap.add_argument("--two-call", action="store_true",
+                    help="run each step as pa_kv_append then pa_decode instead of the fused "
+                         "pa_decode_step")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="cache storage: bf16, or 8-bit E4M3 codes + per-token scales")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -282,9 +289,15 @@ def run_decode(args, key, kv, block_size, K, W, cold_iters, stream, full):
         lens = lens.astype(np.int64)
         return int(cfg.prompts * base + (lens - base).sum()) if shared else int(lens.sum())
 
+    fused = not args.two_call and not fp8
+
     def step(i):
-        cache.append(seqs, ones, kns[i], vns[i], stream=stream)
-        cache.decode(qs[i], out=out, partition_tokens=args.partition, stream=stream)
+        if fused:   # one launch: slot write, table growth and decode (pa_decode_step)
+            cache.step(qs[i], kns[i], vns[i], out=out, partition_tokens=args.partition,
+                       stream=stream)
+        else:       # pa_kv_append, then pa_decode
+            cache.append(seqs, ones, kns[i], vns[i], stream=stream)
+            cache.decode(qs[i], out=out, partition_tokens=args.partition, stream=stream)
 
     # Python's cyclic garbage collector: a full collection takes tens of
     # milliseconds in this process and, when one fell inside the timed steps,
@@ -381,6 +394,7 @@ def run_decode(args, key, kv, block_size, K, W, cold_iters, stream, full):
     if not full:
         res = {"workload": f"{cfg.key}: {cfg.description}" + (
                    "; 8-bit cache" if fp8 else "") + (f"; {B}-token blocks" if B != 16 else ""),
+               "step": "pa_decode_step (one launch)" if fused else "pa_kv_append + pa_decode",
                "steps": K, "warmup": W, "ms_per_step": round(ms_step, 5),
                "step_GBps": round(value, 1), "decode": decode, "roofline": roofline}
         del cache, qs, kns, vns, out
@@ -418,6 +432,7 @@ def run_decode(args, key, kv, block_size, K, W, cold_iters, stream, full):
             "kv_storage": kv,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
             "block_size": B, "pool_blocks": num_blocks, "partition_tokens": P,
+            "step": "pa_decode_step (one launch)" if fused else "pa_kv_append + pa_decode",
             "mean_context_tokens": round(float(lens_now.mean()), 1),
             "kv_bytes_per_step": int(kv_avg),
             "kv_bytes_unique_per_step": int(np.mean(step_unique[W:])),

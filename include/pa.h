@@ -222,6 +222,48 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step in one launch: each sequence's new token is stored in its
+ * slot, its block table grows, and decode attention runs over every context
+ * including the new token (glossary entry, "Dynamic Growth": the cache grows
+ * a token at a time; vLLM post, "PagedAttention: paging, borrowed from the
+ * operating system": a sequence that fills its last block takes a new one
+ * and appends it to its table).  The same result as pa_kv_append of the
+ * new tokens (with their table entries) followed by pa_decode_shared (or
+ * pa_decode) over the grown contexts, up to the order of fp32 sums.
+ *   q, out:       [num_seqs][num_q_heads][head_dim] bf16.
+ *   k_new, v_new: [num_seqs][num_kv_heads][head_dim] bf16, device: the new
+ *                 token of sequence s, at position lens_in[s].
+ *   lens_in:      int32 [num_seqs], device: context lengths before the
+ *                 step, 0 <= lens_in[s] < max_blocks_per_seq * block_size.
+ *   lens_out:     int32 [num_seqs], device, not lens_in: receives
+ *                 lens_in[s] + 1.
+ *   new_blocks:   int32 [num_seqs], HOST memory, read during the call (it
+ *                 travels with the kernel arguments, so the step needs no
+ *                 copy of its own): the block holding the new token when
+ *                 the block manager gave one -- a new block (lens_in[s] a
+ *                 multiple of block_size) or a private copy of a shared
+ *                 tail (after pa_block_copy) -- else -1 (the token goes to
+ *                 the block block_tables[s][lens_in[s] / block_size]).
+ *                 Batches of more than 512 sequences run as several
+ *                 launches of at most 512.
+ *   block_tables: as for pa_decode; the entry of every given block is
+ *                 written (block_tables[s][lens_in[s] / block_size] =
+ *                 new_blocks[s]).
+ *   groups, workspace: as for pa_decode_shared (num_groups = 0: none; the
+ *                 groups describe the contexts after the step).
+ * bf16 pools only (PA_EUNSUPPORTED otherwise: use pa_kv_append and
+ * pa_decode).  With PA_DEBUG=1 the lengths, blocks and tables are validated
+ * first, as for pa_decode after the step.
+ */
+pa_status pa_decode_step(const pa_pool* pool, void* k_pool, void* v_pool, const void* q,
+                         const void* k_new, const void* v_new, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* lens_in, int32_t* lens_out, const int32_t* new_blocks,
+                         float scale, void* out, int32_t partition_tokens, int32_t num_groups,
+                         const int32_t* group_start, const int32_t* shared_blocks,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace pa_decode_shared needs: pa_decode's, plus two
  * partial rows (fp32 max, sum and head_dim outputs) per query head of each
  * sequence of one launch (up to 2048 sequences), since a grouped sequence's

@@ -20,6 +20,7 @@ the V codes dim-major.  Their q, out, k_new and v_new are bfloat16.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,8 @@ def _load():
         "pa_decode_shared": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, i32, vp,
                                    vp, vp, sz, vp]),
         "pa_decode_noalloc": (i32, [P, vp, vp, vp, i32, i32, vp, i32, vp, f32, vp, i32, vp]),
+        "pa_decode_step": (i32, [P, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, f32, vp,
+                                 i32, i32, vp, vp, vp, sz, vp]),
         "pa_decode_noalloc_max_bytes": (sz, []),
         "pa_decode_shared_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_block_copy": (i32, [P, vp, vp, vp, i32, vp]),
@@ -109,7 +112,8 @@ _lib = _load()
 EXPORTED = (
     "pa_kv_write", "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
     "pa_decode_piece_tokens", "pa_decode",
-    "pa_decode_shared", "pa_decode_shared_workspace_bytes", "pa_decode_noalloc",
+    "pa_decode_shared", "pa_decode_shared_workspace_bytes", "pa_decode_step",
+    "pa_decode_noalloc",
     "pa_decode_noalloc_max_bytes",
     "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
     "pa_status_str", "pa_probe_sink_bytes", "pa_probe_read",
@@ -321,6 +325,41 @@ def pa_decode_shared(q, k_pool, v_pool, block_tables, context_lens, scale, group
         _dev(shared_blocks, "shared_blocks") if n else ctypes.c_void_p(0),
         ws_ptr, ws_bytes, _stream(stream))
     _check(st, "pa_decode_shared")
+    return out
+
+
+def pa_decode_step(q, k_pool, v_pool, k_new, v_new, block_tables, lens_in, lens_out,
+                   new_blocks, scale, out=None, group_start=None, shared_blocks=None,
+                   partition_tokens=0, workspace=None, stream=None):
+    """One decode step: store each sequence's new token (k_new/v_new
+    [S][Hkv][d] at position lens_in[s], in block new_blocks[s] or the
+    table's tail block when -1), grow the tables, write lens_out = lens_in
+    + 1 and decode over the grown contexts.  new_blocks: int32 [S] on the
+    host (a numpy array or CPU tensor), read during the call."""
+    desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, lens_in, out)
+    shape = (S, desc.num_kv_heads, desc.head_dim)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new and v_new must be {shape}")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("k_new/v_new must be bf16")
+    if lens_out.dtype != torch.int32 or lens_out.numel() != S or not lens_out.is_contiguous():
+        raise ValueError("lens_out must be int32 [S], contiguous")
+    nb_host = np.ascontiguousarray(np.asarray(new_blocks, dtype=np.int32).reshape(-1))
+    if nb_host.size != S:
+        raise ValueError("new_blocks must have one entry per sequence")
+    nb_ptr = nb_host.ctypes.data_as(ctypes.c_void_p)
+    n = 0 if shared_blocks is None else shared_blocks.numel()
+    ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device,
+                                  shared=n > 0)
+    st = _lib.pa_decode_step(
+        ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(q, "q"),
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), S, Hq, _dev(block_tables, "block_tables"),
+        maxB, _dev(lens_in, "lens_in"), _dev(lens_out, "lens_out"), nb_ptr, float(scale),
+        _dev(out, "out"), int(partition_tokens), n,
+        _dev(group_start, "group_start") if n else ctypes.c_void_p(0),
+        _dev(shared_blocks, "shared_blocks") if n else ctypes.c_void_p(0),
+        ws_ptr, ws_bytes, _stream(stream))
+    _check(st, "pa_decode_step")
     return out
 
 

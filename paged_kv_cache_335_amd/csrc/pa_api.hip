@@ -73,13 +73,14 @@ int32_t part_slots(int32_t group, bool grouped) {
 }
 
 // Workspace layout: part_m, part_l [rows], part_o [rows][d] (fp32), then
-// seg_info int32 [min(S, plan size)][4].  rows = 2 * waves of the grid *
+// seg_info int32 [min(S, plan size)][4] and the reduce's list of sequences
+// int32 [1 + min(S, plan size)][8] (a header, then one record each).  rows = 2 * waves of the grid *
 // head slots (each (range, kv head) wave leaves at most two cut pieces);
 // with prefix groups 2 * Hq more per sequence of one launch (segments that
 // are not cut but still combine: a member's own blocks and its share of
 // the group's blocks).
 struct WsLayout {
-  size_t rows, range_rows, off_l, off_o, off_info, bytes;
+  size_t rows, range_rows, off_l, off_o, off_info, off_list, bytes;
 };
 
 WsLayout ws_layout(const pa_pool* pool, int32_t S, int32_t Hq, bool grouped) {
@@ -92,7 +93,9 @@ WsLayout ws_layout(const pa_pool* pool, int32_t S, int32_t Hq, bool grouped) {
   w.off_l = align_up(w.rows * sizeof(float));
   w.off_o = w.off_l + align_up(w.rows * sizeof(float));
   w.off_info = w.off_o + align_up(w.rows * pool->head_dim * sizeof(float));
-  w.bytes = w.off_info + align_up((size_t)std::min(S, pakv::kMaxPlanSeqs) * 4 * sizeof(int32_t));
+  const size_t sx = (size_t)std::min(S, pakv::kMaxPlanSeqs);
+  w.off_list = w.off_info + align_up(sx * 4 * sizeof(int32_t));
+  w.bytes = w.off_list + align_up((sx + 1) * 8 * sizeof(int32_t));
   return w;
 }
 
@@ -136,13 +139,22 @@ pa_status check_groups(const pa_pool* pool, int32_t S, int32_t maxB, const int32
 
 // The decode entry points share this: validation, then the launch over a
 // workspace of ws_bytes at ws.
+// A decode step's extra inputs (pa_decode_step); all null for plain decode.
+struct StepArgs {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* new_blocks = nullptr;  // host memory, read during the call
+  int32_t* tables_w = nullptr;
+  int32_t* lens_out = nullptr;
+};
+
 pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_pool,
                       const void* q, int32_t num_seqs, int32_t num_q_heads,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, float scale, void* out,
                       int32_t partition_tokens, int32_t num_groups, const int32_t* group_start,
                       const int32_t* shared_blocks, void* workspace, size_t workspace_bytes,
-                      bool debug, hipStream_t hs) {
+                      bool debug, hipStream_t hs, const StepArgs& step = StepArgs{}) {
   int32_t P;
   size_t ws;
   if (num_groups < 0) return PA_EINVAL;
@@ -160,10 +172,21 @@ pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_poo
     return PA_EUNSUPPORTED;
   if (!workspace || workspace_bytes < ws) return PA_EINVAL;
   if (debug) {
-    std::vector<int32_t> lens, tab;
+    std::vector<int32_t> lens, tab, nbk;
     if (!fetch(lens, context_lens, (size_t)num_seqs, hs)) return PA_EHIP;
     if (!fetch(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, hs)) return PA_EHIP;
     const int64_t max_len = (int64_t)max_blocks_per_seq * pool->block_size;
+    if (step.k_new) {
+      // lengths after the step, and the given blocks in the tables
+      nbk.assign(step.new_blocks, step.new_blocks + num_seqs);
+      for (int32_t s = 0; s < num_seqs; ++s) {
+        if (lens[s] < 0 || lens[s] >= max_len) return PA_EINVAL;
+        if (nbk[s] >= pool->num_blocks) return PA_EINVAL;
+        if (nbk[s] < 0 && lens[s] % pool->block_size == 0) return PA_EINVAL;  // needs a block
+        if (nbk[s] >= 0) tab[(size_t)s * max_blocks_per_seq + lens[s] / pool->block_size] = nbk[s];
+        lens[s] += 1;
+      }
+    }
     for (int32_t s = 0; s < num_seqs; ++s) {
       if (lens[s] < 1 || lens[s] > max_len) return PA_EINVAL;
       const int32_t nb = (lens[s] + pool->block_size - 1) / pool->block_size;
@@ -199,6 +222,7 @@ pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_poo
   a.part_l = reinterpret_cast<float*>(w + L.off_l);
   a.part_o = reinterpret_cast<float*>(w + L.off_o);
   a.seg_info = reinterpret_cast<int32_t*>(w + L.off_info);
+  a.cut_list = reinterpret_cast<int32_t*>(w + L.off_list);
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -208,7 +232,12 @@ pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_poo
   a.own_row0 = static_cast<int32_t>(L.range_rows);
   a.sh_row0 = static_cast<int32_t>(L.range_rows + (L.rows - L.range_rows) / 2);
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, pool->block_size, hs);
+  a.k_new = step.k_new;
+  a.v_new = step.v_new;
+  a.tables_w = step.tables_w;
+  a.lens_out = step.lens_out;
+  hipError_t e = pakv::launch_decode(a, pool->dtype, pool->head_dim, group, pool->block_size, hs,
+                                     step.new_blocks);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -379,6 +408,31 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
                      max_blocks_per_seq, context_lens, scale, out, partition_tokens, num_groups,
                      group_start, shared_blocks, workspace, workspace_bytes, debug_checks(),
                      as_stream(stream));
+}
+
+pa_status pa_decode_step(const pa_pool* pool, void* k_pool, void* v_pool, const void* q,
+                         const void* k_new, const void* v_new, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* lens_in, int32_t* lens_out, const int32_t* new_blocks,
+                         float scale, void* out, int32_t partition_tokens, int32_t num_groups,
+                         const int32_t* group_start, const int32_t* shared_blocks,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pool_ok(pool)) return PA_EINVAL;
+  if (num_seqs > 0 && (!k_new || !v_new || !lens_in || !lens_out || !new_blocks))
+    return PA_EINVAL;
+  if (lens_out == lens_in && num_seqs > 0) return PA_EINVAL;
+  // bf16 pools only: the step stores the new token as it reads it
+  if (pool->dtype != PA_BF16) return PA_EUNSUPPORTED;
+  StepArgs step;
+  step.k_new = k_new;
+  step.v_new = v_new;
+  step.new_blocks = new_blocks;
+  step.tables_w = block_tables;
+  step.lens_out = lens_out;
+  return decode_impl(pool, k_pool, v_pool, q, num_seqs, num_q_heads, block_tables,
+                     max_blocks_per_seq, lens_in, scale, out, partition_tokens, num_groups,
+                     group_start, shared_blocks, workspace, workspace_bytes, debug_checks(),
+                     as_stream(stream), step);
 }
 
 size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -68,12 +68,14 @@ namespace {
 struct Unit {
   int s, nmem, g, t0, t1, prow, mstride;
   bool in_place;
+  bool last;  // the piece ends the sequence (its own segment's last token)
 };
 
 // The plan every workgroup builds in LDS from the context lengths (and the
 // prefix groups): segments in order, and their block prefix sums.  Built
 // from scans only, so every workgroup gets the same plan.
 struct Plan {
+  int* wsum;         // [8] scan scratch in LDS
   const int* pre;    // [K + 1] blocks before segment k; pre[K] = T
   const int* lens;   // [S] context lengths (clamped to the table capacity)
   const int* sdesc;  // [K] first member | member count << 16 (nullptr: segment k is sequence k)
@@ -120,7 +122,8 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   // lengths outside [0, table capacity] violate the contract; clamping them
   // keeps every LDS and table index in range whatever the device data says
   const int cap = a.max_blocks * B;
-  for (int s = t; s < S; s += T_) lens[s] = min(max(a.context_lens[s], 0), cap);
+  const int add = a.k_new != nullptr ? 1 : 0;  // a decode step appends one token
+  for (int s = t; s < S; s += T_) lens[s] = min(max(a.context_lens[s] + add, 0), cap);
   __syncthreads();
   int K = 0, T = 0;
   bool use_groups = grouped;
@@ -180,6 +183,7 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   if (t == 0) pre[K] = T;
   __syncthreads();
   Plan pl;
+  pl.wsum = wsum;
   pl.pre = pre;
   pl.lens = lens;
   pl.sdesc = use_groups ? sdesc : nullptr;
@@ -188,7 +192,7 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   pl.K = K;
   pl.T = T;
   // every wave of the grid streams one (kv head, range) pair: R ranges per head
-  pl.R = max(1, (int)(gridDim.x * kWaves) / a.num_kv_heads);
+  pl.R = max(1, a.decode_wgs * kWaves / a.num_kv_heads);
   pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
   return pl;
 }
@@ -254,6 +258,26 @@ __device__ void write_seg_info(const DecodeArgs& a, const Plan& pl) {
       }
     }
   }
+  // the sequences the reduce must combine (cut, or sharing a group's
+  // blocks), in order, as records {s, seg_info[s]} of 8 ints after a
+  // header record whose first int is their count
+  __syncthreads();
+  const int C = (pl.S + blockDim.x - 1) / blockDim.x;
+  const int s0 = min(pl.S, (int)threadIdx.x * C), s1 = min(pl.S, s0 + C);
+  auto info_of = [&](int s) { return *reinterpret_cast<const int4*>(a.seg_info + (size_t)s * 4); };
+  auto needs = [&](const int4& i) { return i.y > 1 || (i.w & 0xffff) > 0; };
+  int n = 0;
+  for (int s = s0; s < s1; ++s) n += needs(info_of(s));
+  int total;
+  int at = block_excl_scan(n, pl.wsum, &total);
+  for (int s = s0; s < s1; ++s) {
+    const int4 i = info_of(s);
+    if (!needs(i)) continue;
+    int4* rec = reinterpret_cast<int4*>(a.cut_list + 8 * (1 + at++));
+    rec[0] = int4{s, i.x, i.y, i.z};
+    rec[1] = int4{i.w, 0, 0, 0};
+  }
+  if (threadIdx.x == 0) a.cut_list[0] = total;
 }
 
 // Walk range r for kv head g, calling f(unit) per piece (the part of one
@@ -286,6 +310,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, 
     u.t0 = (j0 + b0 - sb) * B;
     const int seg_end = nmem > 1 ? (j0 + se - sb) * B : pl.lens[s];
     u.t1 = min(seg_end, (j0 + e - sb) * B);
+    u.last = nmem == 1 && u.t1 == seg_end;
     const bool cut = (se - 1) / pl.q != sb / pl.q;
     u.in_place = nmem == 1 && j0 == 0 && !cut;
     if (cut) {
@@ -387,36 +412,118 @@ struct TileGeom {
 // ---------------------------------------------------------------------------
 // MFMA kernel: bf16 pools, 1..16 query heads per kv head.
 // ---------------------------------------------------------------------------
-template <int D, int B, int NBUF>
-__device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
+template <int D, int B, int NBUF, bool STEP>
+__device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit& unit, int lane,
+                                          const int32_t* step_blk) {
   using TG = TileGeom<B>;
   constexpr int KJ = D / 32;  // q.K MFMAs per tile (32 dims each)
   constexpr int NT = D / 16;  // P.V MFMAs per tile (16 output dims each)
   constexpr uint32_t ROW = D * 2;  // bytes per K row
 
-  const int s = u.s, g = u.g;
-  const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
+  const int s = unit.s, g = unit.g;
   const int col = lane & 15, grp = lane >> 4;
 
   // B operand of q.K: lane holds q[head slot col][kj*32 + grp*8 .. +8]
   bf16x8 qop[KJ];
-  load_q_operand<KJ>(a, G, u, col, ROW, [&](int kj) { return grp * 16 + kj * 64; }, qop);
+  load_q_operand<KJ>(a, G, unit, col, ROW, [&](int kj) { return grp * 16 + kj * 64; }, qop);
 
   // wave-uniform base of this kv head's slice of block 0, plus 32-bit lane
   // offsets: each load is a scalar block base + vector lane offset
   const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+
+  // A decode step's new token (the sequence's last position p) belongs to
+  // the piece that ends the sequence: its K and V come from k_new / v_new
+  // and join the attention as one extra tile; the pool tiles stop before
+  // p, so they need neither the token's slot nor a given block: a new
+  // block holds only p, and a copy-on-write copy holds the same tokens
+  // before p as the shared block the table still names.  Other workgroups
+  // of the launch store the token and grow the table (step_store).
+  Unit u = unit;
+  const bool new_tok = STEP && u.last;
+  int p_new = 0;
+  uint32_t kpre = 0, vpre = 0;  // lane l: dword l of the new token's K row and V row
+  if (new_tok) {
+    p_new = u.t1 - 1;
+    u.t1 = p_new;
+    // issued now, so their latency hides behind the piece's pool tiles
+    const size_t row_off = ((size_t)s * a.num_kv_heads + g) * ROW;
+    if (lane < D / 2) {
+      kpre = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.k_new) + row_off)[lane];
+      vpre = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.v_new) + row_off)[lane];
+    }
+  }
+  const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
+
   // lane offsets inside a tile's block: K row (token) col, V dim col, tokens
   // 4*grp..+4 (with B = 8, rows and tokens are taken modulo the block)
   const uint32_t koff = (B >= 16 ? col : col % 8) * ROW + grp * 16;
   const uint32_t voff = col * (B * 2) + (B >= 16 ? grp : grp % 2) * 8;
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
 
   float m_ref = kNegInf, l_run = 0.f;
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One 16-token tile: scores of the tile's tokens (K operand kb), the
+  // first `valid` of them live, folded into the running softmax and P.V
+  // (V operand vb, 4 tokens of one dim per lane).
+  auto tile = [&](const u32x4* kb, u32x2* vb, int valid) {
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
+                                                   qop[kj], sc, 0, 0, 0);
+    // sc[r] = score of token 4*grp + r for head col
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = sc[r] * a.scale_log2;
+    // tokens past the valid ones (past the context, or a second block that
+    // belongs to another unit) get score -inf and zero V, so stale bits in
+    // an unused slot never reach the output
+    if (valid < 16) {
+      const int t = 4 * grp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (t + r >= valid) x[r] = kNegInf;
+      const uint32_t m0 = (t + 0 < valid ? 0x0000ffffu : 0u) | (t + 1 < valid ? 0xffff0000u : 0u);
+      const uint32_t m1 = (t + 2 < valid ? 0x0000ffffu : 0u) | (t + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        vb[nt].x &= m0;
+        vb[nt].y &= m1;
+      }
+    }
+    // A head's max passes m_ref + kSlack exactly when some lane's own max
+    // does, so only the (rare) rescale exchanges values between lanes.
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__ballot(bm > m_ref + kSlack)) {  // rare: move the reference, rescale
+      bm = max_xor32(max_xor16(bm));
+      const float m_new = fmaxf(m_ref, bm);
+      const float alpha = fexp2(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+    }
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fexp2(x[r] - m_ref);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    // P.V: A = P (16 head slots x this lane's 4 tokens, which are exactly
+    // its 4 scores), B = V (the lane's 8-byte V^T load: 4 tokens of one dim)
+    const bf16x8 pp = p_split(pr);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[nt], 0, 0, 0);
+  };
 
   u32x4 kring[NBUF][KJ];
   u32x2 vring[NBUF][NT];
@@ -425,7 +532,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
   for (int c0 = 0; c0 < nblk; c0 += 64) {
     const int cnt = min(64, nblk - c0);
     // physical block ids of up to 64 blocks, one per lane (every lane loads a
-    // valid entry)
+    // valid entry); the new token's block as the step decided it
     const int tab = trow[jb + c0 + min(lane, cnt - 1)];
     const int ntile = TG::tiles(u, c0, cnt);
 
@@ -458,64 +565,38 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
       }
     };
     auto compute = [&](int i, auto slot) {
-      u32x4* kb = kring[slot];
-      u32x2* vb = vring[slot];
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
-                                                     qop[kj], sc, 0, 0, 0);
-      // sc[r] = score of token 4*grp + r for head col
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = sc[r] * a.scale_log2;
-      // tokens of this tile inside the unit; the rest (past the context, or
-      // a second block that belongs to another unit) get score -inf and zero
-      // V, so stale bits in an unused slot never reach the output
-      const int valid = u.t1 - (u.t0 + c0 * B + i * 16);
-      if (valid < 16) {
-        const int t = 4 * grp;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t + r >= valid) x[r] = kNegInf;
-        const uint32_t m0 = (t + 0 < valid ? 0x0000ffffu : 0u) | (t + 1 < valid ? 0xffff0000u : 0u);
-        const uint32_t m1 = (t + 2 < valid ? 0x0000ffffu : 0u) | (t + 3 < valid ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          vb[nt].x &= m0;
-          vb[nt].y &= m1;
-        }
-      }
-      // A head's max passes m_ref + kSlack exactly when some lane's own max
-      // does, so only the (rare) rescale exchanges values between lanes.
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__ballot(bm > m_ref + kSlack)) {  // rare: move the reference, rescale
-        bm = max_xor32(max_xor16(bm));
-        const float m_new = fmaxf(m_ref, bm);
-        const float alpha = fexp2(m_ref - m_new);
-        l_run *= alpha;
-        m_ref = m_new;
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      // P.V: A = P (16 head slots x this lane's 4 tokens, which are exactly
-      // its 4 scores), B = V (the lane's 8-byte V^T load: 4 tokens of one dim)
-      const bf16x8 pp = p_split(p);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[nt], 0, 0, 0);
+      tile(kring[slot], vring[slot], u.t1 - (u.t0 + c0 * B + i * 16));
     };
 
     block_ring<NBUF>(ntile, load, compute);
+  }
+
+  if (new_tok) {
+    // The new token as tile token 0.  K operand: lane (col 0, grp) holds
+    // dims kj*32 + grp*8 .. +8, i.e. dwords grp*4 + kj*16 + w of the row;
+    // V operand: lane (col, grp 0) holds dim nt*16 + col as its token 0,
+    // the low or high half of dword dim / 2.  Both come from the
+    // prefetched dwords through ds_bpermute.
+    u32x4 kb[KJ];
+    u32x2 vb[NT];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = __builtin_amdgcn_ds_bpermute((grp * 4 + kj * 16 + w) * 4, kpre);
+        w4[w] = col == 0 ? x : 0u;
+      }
+      kb[kj] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int dim = nt * 16 + col;
+      const uint32_t x = __builtin_amdgcn_ds_bpermute((dim >> 1) * 4, vpre);
+      const uint32_t h = (dim & 1) ? x >> 16 : x & 0xffffu;
+      vb[nt] = u32x2{grp == 0 ? h : 0u, 0u};
+    }
+    tile(kb, vb, 1);
   }
 
   // l over the four lane groups holding the same head; m_ref is uniform
@@ -740,8 +821,47 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
 }
 
-template <int D, int B, int NBUF>
-__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
+// A decode step's stores, by the reduce kernel that follows the decode
+// kernel (the decode took the new tokens from k_new / v_new and never
+// reads their slots; the next step reads them): each new token's K and V
+// rows go to its slot, every kv head, non-temporal like the slot write; a
+// given block becomes the table entry of the token's position; the
+// lengths after the step go to lens_out.  Workgroup w of nw takes
+// sequences w, w + nw, ...
+template <int D, int B>
+__device__ void step_store(const DecodeArgs& a, const int32_t* step_blk, int w, int nw) {
+  constexpr int ROW = D * 2;
+  const int H = a.num_kv_heads;
+  const size_t blk_bytes = (size_t)H * B * ROW;
+  for (int s = w; s < a.num_seqs; s += nw) {
+    const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);  // position of the new token
+    const int j = L / B, r = L % B;
+    const int given = step_blk[s];
+    int32_t* entry = a.tables_w + (size_t)s * a.max_blocks + j;
+    const int blk = given >= 0 ? given : *entry;
+    if (threadIdx.x == 0) {
+      if (given >= 0) *entry = given;
+      a.lens_out[s] = L + 1;
+    }
+    const uint8_t* kn = static_cast<const uint8_t*>(a.k_new) + (size_t)s * H * ROW;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.v_new) +
+                                                           (size_t)s * H * ROW);
+    uint8_t* kb = static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) + (size_t)blk * blk_bytes;
+    uint16_t* vb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) +
+                                               (size_t)blk * blk_bytes);
+    for (int c = threadIdx.x; c < H * ROW / 16; c += blockDim.x) {  // K: [g][r][:] per head
+      const int g = c / (ROW / 16), off = (c % (ROW / 16)) * 16;
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(kn + (size_t)c * 16),
+                                  reinterpret_cast<u32x4*>(kb + ((size_t)g * B + r) * ROW + off));
+    }
+    for (int c = threadIdx.x; c < H * D; c += blockDim.x)  // V: [g][d][r] per element
+      __builtin_nontemporal_store(vn[c], vb + (size_t)c * B + r);
+  }
+}
+
+template <int D, int B, int NBUF, bool STEP>
+__device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int G,
+                                                 const int32_t* step_blk) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B>(a, G, plan_lds);
   if (blockIdx.x == 0) write_seg_info(a, pl);
@@ -750,7 +870,21 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kerne
   const int lane = threadIdx.x & 63;
   int g, r;
   if (!wave_work(a, pl, wave, &g, &r)) return;
-  walk_range<B>(a, pl, G, r, g, [&](const Unit& u) { mfma_unit<D, B, NBUF>(a, G, u, lane); });
+  walk_range<B>(a, pl, G, r, g, [&](const Unit& u) {
+    mfma_unit<D, B, NBUF, STEP>(a, G, u, lane, step_blk);
+  });
+}
+
+template <int D, int B, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
+  decode_mfma_body<D, B, NBUF, false>(a, G, nullptr);
+}
+
+// A decode step: the new tokens' blocks arrive with the kernel arguments.
+template <int D, int B, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_step_kernel(DecodeArgs a, int G,
+                                                                                  StepBlocks nb) {
+  decode_mfma_body<D, B, NBUF, true>(a, G, nb.blk);
 }
 
 template <int D, int B, int NBUF>
@@ -977,46 +1111,48 @@ struct PieceMap {
   }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(DecodeArgs a) {
-  constexpr int EPL = D / 64, UNR = 16;
-  const int s = blockIdx.y;
-  const int4 info = *reinterpret_cast<const int4*>(a.seg_info + (size_t)s * 4);
+// One (sequence, query head) of the reduce, over the pieces 16 at a time
+// with a running reference: M = max of the pieces' references so far, and
+// out = sum 2^(m_p - M) o_p / sum 2^(m_p - M) l_p (the sums rescaled when M
+// moves).  A sequence has at most a few pieces, so one round of loads.
+template <typename T, int D, int EPL, int UNR>
+__device__ __forceinline__ void reduce_one(const DecodeArgs& a, int s, const int4 info, int hq,
+                                           int G, int lane) {
   const int np_sh = info.w & 0xffff;
   const int np = info.y + np_sh;
-  if (np_sh == 0 && info.y <= 1) return;  // finished in place (or no context)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int hq = blockIdx.x * kReduceHeads + wave;
-  if (hq >= a.num_q_heads) return;
-  const int G = a.num_q_heads / a.num_kv_heads;
   const int g = hq / G, h = hq - g * G;
   const int srow = s * a.num_q_heads + hq;
   const PieceMap pm{info.x, info.y, info.z, np_sh, (info.w >> 16) * G + h, h, a.num_kv_heads,
                     a.slots, g, a.own_row0 + srow, a.sh_row0 + srow};
-
-  float M = kNegInf;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, a.part_m[pm.row(p)]);
-  M = wave_max(M);
-
-  float den = 0.f, num[EPL];
+  float M = kNegInf, den = 0.f, num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
   for (int p0 = 0; p0 < np; p0 += UNR) {
-    float f[UNR], o[UNR][EPL];
+    float m[UNR], l[UNR], o[UNR][EPL];
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int row = pm.row(min(p0 + k, np - 1));  // clamped: past-the-end terms get f = 0
-      f[k] = p0 + k < np ? fexp2(a.part_m[row] - M) : 0.f;
-      den = fmaf(f[k], a.part_l[row], den);
+      m[k] = p0 + k < np ? a.part_m[row] : kNegInf;
+      l[k] = a.part_l[row];
       const float* po = a.part_o + (size_t)row * D;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[k][e] = po[e * 64 + lane];
     }
+    float Mn = M;
 #pragma unroll
-    for (int k = 0; k < UNR; ++k)
+    for (int k = 0; k < UNR; ++k) Mn = fmaxf(Mn, m[k]);
+    const float alpha = M == kNegInf ? 0.f : fexp2(M - Mn);
+    den *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) num[e] = fmaf(f[k], o[k][e], num[e]);
+    for (int e = 0; e < EPL; ++e) num[e] *= alpha;
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const float f = m[k] == kNegInf ? 0.f : fexp2(m[k] - Mn);
+      den = fmaf(f, l[k], den);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) num[e] = fmaf(f, o[k][e], num[e]);
+    }
+    M = Mn;
   }
   const float inv = 1.f / den;
 #pragma unroll
@@ -1025,9 +1161,61 @@ __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(Decode
 }
 
 template <typename T, int D>
+__device__ __forceinline__ void decode_reduce_body(const DecodeArgs& a) {
+  constexpr int EPL = D / 64, UNR = 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int Hq = a.num_q_heads;
+  const int G = Hq / a.num_kv_heads;
+  // the records sit past the header; a record past the count holds stale
+  // data that is loaded (in bounds) but not used
+  const int cap = a.num_seqs * Hq;
+  for (int i = blockIdx.x * kReduceHeads + wave; i < cap; i += gridDim.x * kReduceHeads) {
+    const int4* rec = reinterpret_cast<const int4*>(a.cut_list + 8 * (1 + i / Hq));
+    const int4 r0 = rec[0], r1 = rec[1];
+    if (i >= a.cut_list[0] * Hq) break;
+    reduce_one<T, D, EPL, UNR>(a, r0.x, int4{r0.y, r0.z, r0.w, r1.x}, i % Hq, G, lane);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(DecodeArgs a) {
+  decode_reduce_body<T, D>(a);
+}
+
+// A decode step's reduce: first the step's stores (independent of the
+// reduce), then the reduce.
+template <int D, int B>
+__global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_step_kernel(DecodeArgs a,
+                                                                               StepBlocks nb) {
+  step_store<D, B>(a, nb.blk, blockIdx.x, gridDim.x);
+  decode_reduce_body<__bf16, D>(a);
+}
+
+int cu_count();
+
+// A grid over the (cut sequence, query head) pairs the decode kernel
+// listed.
+// One wave per possible (sequence, query head) pair, so that no wave walks
+// pairs one after another: the reduce is a few dependent loads long, and
+// waves past the listed pairs leave after their first load.
+template <typename T, int D>
+int reduce_grid(const DecodeArgs& a) {
+  return std::max(1, (a.num_seqs * a.num_q_heads + kReduceHeads - 1) / kReduceHeads);
+}
+
+template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((a.num_q_heads + kReduceHeads - 1) / kReduceHeads, a.num_seqs);
-  decode_reduce_kernel<T, D><<<grid, kReduceHeads * 64, 0, st>>>(a);
+  decode_reduce_kernel<T, D><<<dim3(reduce_grid<T, D>(a)), kReduceHeads * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// The step's reduce also stores the new tokens: at least one workgroup
+// per sequence.
+template <int D, int B>
+hipError_t launch_reduce_step(const DecodeArgs& a, const StepBlocks& nb, hipStream_t st) {
+  const int grid = std::max(reduce_grid<__bf16, D>(a), a.num_seqs);
+  decode_reduce_step_kernel<D, B><<<dim3(grid), kReduceHeads * 64, 0, st>>>(a, nb);
   return hipGetLastError();
 }
 
@@ -1097,18 +1285,29 @@ namespace {
 // The head group (1..16) fills the 16 head slots of the MFMA tiles at run
 // time, so one instantiation per head_dim serves every group size.
 template <int D, int B>
-hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_mfma_kernel<D, B, kNBuf>);
-  decode_mfma_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(a, G);
+hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st, const StepBlocks* nb) {
+  if (nb) {
+    const Launch l = decode_launch(a, decode_step_kernel<D, B, kNBuf>);
+    DecodeArgs b = a;
+    b.decode_wgs = (int)l.grid.x;
+    decode_step_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(b, G, *nb);
+  } else {
+    const Launch l = decode_launch(a, decode_mfma_kernel<D, B, kNBuf>);
+    DecodeArgs b = a;
+    b.decode_wgs = (int)l.grid.x;
+    decode_mfma_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(b, G);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce<__bf16, D>(a, st);
+  return nb ? launch_reduce_step<D, B>(a, *nb, st) : launch_reduce<__bf16, D>(a, st);
 }
 
 template <int D, int B>
 hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
   const Launch l = decode_launch(a, decode_mfma8_kernel<D, B, kNBuf8>);
-  decode_mfma8_kernel<D, B, kNBuf8><<<l.grid, l.block, l.lds, st>>>(a, G);
+  DecodeArgs b = a;
+  b.decode_wgs = (int)l.grid.x;
+  decode_mfma8_kernel<D, B, kNBuf8><<<l.grid, l.block, l.lds, st>>>(b, G);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
@@ -1117,7 +1316,9 @@ hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
 template <int D, int G>
 hipError_t launch_valu_g(const DecodeArgs& a, hipStream_t st) {
   const Launch l = decode_launch(a, decode_valu_kernel<D, G, kNBuf>);
-  decode_valu_kernel<D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(a);
+  DecodeArgs b = a;
+  b.decode_wgs = (int)l.grid.x;
+  decode_valu_kernel<D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(b);
   return hipGetLastError();
 }
 
@@ -1154,33 +1355,40 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size) 
 namespace {
 // One instantiation per (head_dim, block size) of each MFMA kernel.
 template <template <int, int> class K, int D>
-hipError_t by_block(int block_size, const DecodeArgs& a, int group, hipStream_t st) {
+hipError_t by_block(int block_size, const DecodeArgs& a, int group, hipStream_t st,
+                    const StepBlocks* nb) {
   switch (block_size) {
-    case 8: return K<D, 8>::run(a, group, st);
-    case 16: return K<D, 16>::run(a, group, st);
-    case 32: return K<D, 32>::run(a, group, st);
+    case 8: return K<D, 8>::run(a, group, st, nb);
+    case 16: return K<D, 16>::run(a, group, st, nb);
+    case 32: return K<D, 32>::run(a, group, st, nb);
     default: return hipErrorInvalidValue;
   }
 }
 template <int D, int B>
 struct MfmaLaunch {
-  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st) { return launch_mfma<D, B>(a, G, st); }
+  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st, const StepBlocks* nb) {
+    return launch_mfma<D, B>(a, G, st, nb);
+  }
 };
 template <int D, int B>
 struct Mfma8Launch {
-  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st) { return launch_mfma8<D, B>(a, G, st); }
+  static hipError_t run(const DecodeArgs& a, int G, hipStream_t st, const StepBlocks* nb) {
+    return nb ? hipErrorInvalidValue : launch_mfma8<D, B>(a, G, st);
+  }
 };
 
+// nb: a decode step's new blocks (bf16 pools only), nullptr otherwise.
 hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
-                               int block_size, hipStream_t st) {
+                               int block_size, hipStream_t st, const StepBlocks* nb) {
   switch (decode_path(dtype, head_dim, group, block_size)) {
     case DecodePath::kMfma:
-      return head_dim == 128 ? by_block<MfmaLaunch, 128>(block_size, a, group, st)
-                             : by_block<MfmaLaunch, 64>(block_size, a, group, st);
+      return head_dim == 128 ? by_block<MfmaLaunch, 128>(block_size, a, group, st, nb)
+                             : by_block<MfmaLaunch, 64>(block_size, a, group, st, nb);
     case DecodePath::kMfma8:
-      return head_dim == 128 ? by_block<Mfma8Launch, 128>(block_size, a, group, st)
-                             : by_block<Mfma8Launch, 64>(block_size, a, group, st);
+      return head_dim == 128 ? by_block<Mfma8Launch, 128>(block_size, a, group, st, nb)
+                             : by_block<Mfma8Launch, 64>(block_size, a, group, st, nb);
     case DecodePath::kValu:
+      if (nb) return hipErrorInvalidValue;
       return head_dim == 128 ? launch_valu<128>(a, group, st) : launch_valu<64>(a, group, st);
     default:
       return hipErrorInvalidValue;
@@ -1189,13 +1397,15 @@ hipError_t launch_decode_slice(const DecodeArgs& a, pa_dtype dtype, int head_dim
 }  // namespace
 
 // Batches larger than one plan are launched in slices (the per-workgroup
-// plan lives in LDS); every per-sequence array is offset to the slice, the
-// prefix groups are clipped to it, and the slices reuse the partial buffers
-// and seg_info one after another on the stream.
+// plan lives in LDS; a decode step's new blocks ride in the kernel
+// arguments, kStepSeqs at a time); every per-sequence array is offset to
+// the slice, the prefix groups are clipped to it, and the slices reuse the
+// partial buffers and seg_info one after another on the stream.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
-                         int block_size, hipStream_t st) {
+                         int block_size, hipStream_t st, const int32_t* host_new_blocks) {
   const size_t es = dtype == PA_F32 ? 4 : 2;  // q / out element (bf16 for 8-bit pools)
-  const int step = a.group_start ? kMaxPlanSeqsGrouped : kMaxPlanSeqs;
+  int step = a.group_start ? kMaxPlanSeqsGrouped : kMaxPlanSeqs;
+  if (a.k_new) step = std::min(step, kStepSeqs);
   for (int32_t s0 = 0; s0 < a.num_seqs; s0 += step) {
     DecodeArgs b = a;
     b.num_seqs = std::min(step, a.num_seqs - s0);
@@ -1205,7 +1415,18 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int 
     b.out = static_cast<uint8_t*>(a.out) + (size_t)s0 * qrow;
     b.block_tables = a.block_tables + (size_t)s0 * a.max_blocks;
     b.context_lens = a.context_lens + s0;
-    const hipError_t e = launch_decode_slice(b, dtype, head_dim, group, block_size, st);
+    StepBlocks nb;
+    if (a.k_new) {
+      const size_t krow = (size_t)a.num_kv_heads * head_dim * es;
+      b.k_new = static_cast<const uint8_t*>(a.k_new) + (size_t)s0 * krow;
+      b.v_new = static_cast<const uint8_t*>(a.v_new) + (size_t)s0 * krow;
+      b.tables_w = a.tables_w + (size_t)s0 * a.max_blocks;
+      b.lens_out = a.lens_out + s0;
+      for (int i = 0; i < kStepSeqs; ++i)
+        nb.blk[i] = i < b.num_seqs ? host_new_blocks[s0 + i] : -1;
+    }
+    const hipError_t e =
+        launch_decode_slice(b, dtype, head_dim, group, block_size, st, a.k_new ? &nb : nullptr);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

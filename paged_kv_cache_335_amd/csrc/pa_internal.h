@@ -68,15 +68,37 @@ struct DecodeArgs {
   float* part_l;       // [rows]    sum of exp2(score - m)
   float* part_o;       // [rows][D] unnormalised output
   int32_t* seg_info;   // [S][4] where each sequence's pieces went (reduce input)
+  int32_t* cut_list;   // [1 + S][8] count, then {s, seg_info[s]} of the sequences the reduce combines
+  // A decode step (pa_decode_step; k_new == nullptr: plain decode): each
+  // sequence's new token sits at position context_lens[s] (the lengths
+  // before the step), its K/V rows are k_new/v_new [S][Hkv][D] (bf16) and
+  // its block comes with the launch (StepBlocks).  The step stores the
+  // token, writes the table entry of a given block, and writes the lengths
+  // after the step to lens_out.
+  const void* k_new;
+  const void* v_new;
+  int32_t* tables_w;
+  int32_t* lens_out;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
   int32_t min_seg_blocks;  // smallest range a wave streams (blocks)
+  int32_t decode_wgs;      // workgroups of the decode grid (a step adds store workgroups)
   int32_t slots;           // head slots per (wave slot, end): G, or members * G with groups
   int32_t own_row0;        // first per-sequence row of own segments (groups only)
   int32_t sh_row0;         // first per-sequence row of shared segments (groups only)
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
+};
+
+// The block of each sequence's new token in a decode step (-1: the table's
+// tail entry), passed by value with the launch: the host's array reaches
+// the kernel with its arguments, with no copy of its own and no read of
+// host memory from the kernel.  A step launch covers at most kStepSeqs
+// sequences.
+constexpr int kStepSeqs = 512;
+struct StepBlocks {
+  int32_t blk[kStepSeqs];
 };
 
 // Workgroups of a decode launch for this many kv heads (a persistent grid:
@@ -108,9 +130,11 @@ hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream
 enum class DecodePath { kUnsupported, kValu, kMfma, kMfma8 };
 DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size);
 
+// host_new_blocks: a decode step's new blocks (host memory, [num_seqs]),
+// read during the call; nullptr for plain decode.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int group,
-                         int block_size,
-                         hipStream_t stream);
+                         int block_size, hipStream_t stream,
+                         const int32_t* host_new_blocks = nullptr);
 
 // block_tables == nullptr: no table update (plain slot write).  For
 // PA_FP8_E4M3 pools k_new / v_new are bf16 and are quantised.

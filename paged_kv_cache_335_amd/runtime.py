@@ -36,8 +36,8 @@ import torch
 
 from . import (PA_OK, PA_SWAP_IN, PA_SWAP_OUT, PagedKVError, alloc_host_pools, alloc_pools,
                pa_block_copy, pa_block_swap, pa_decode, pa_decode_partition_tokens,
-               pa_decode_shared, pa_decode_shared_workspace_bytes, pa_decode_workspace_bytes,
-               pa_extend, pa_kv_append)
+               pa_decode_shared, pa_decode_shared_workspace_bytes, pa_decode_step,
+               pa_decode_workspace_bytes, pa_extend, pa_kv_append)
 from .block_manager import BlockManager
 
 # Staging for the per-step metadata: a ring of pinned host buffers, each
@@ -145,6 +145,11 @@ class PagedKVCache:
         self._ring_events = [None] * (_RING // _GROUP)
         self._ring_pos = 0
         self._ws = None
+        # decode steps: device lengths alternate between two buffers (a step
+        # reads one and writes the other)
+        self._lens_bufs = [torch.zeros(max_seqs, dtype=torch.int32, device=self.device)
+                           for _ in range(2)]
+        self._step_groups = None   # (host gs, host sb, device gs, device sb)
 
     # --- sequences ------------------------------------------------------
     def _stream(self, stream):
@@ -256,6 +261,63 @@ class PagedKVCache:
             pa_kv_append(self.k_pool, self.v_pool, k_new, v_new, d_slots, self.tables, d_rows,
                          d_pos, stream=stream)
         return len(pairs)
+
+    # --- one decode step in one launch ------------------------------------------
+    def step(self, q, k_new, v_new, out=None, scale=None, partition_tokens=0, stream=None):
+        """One decode step of every live sequence (rows in table order): the
+        block manager gives each sequence one new slot, then one launch
+        (pa_decode_step) stores the new tokens k_new/v_new [S][Hkv][d], grows
+        the tables and lengths, and decodes q [S][Hq][d] over the grown
+        contexts.  The host sends only each token's block id, with the
+        launch's arguments; copy-on-write copies (after a fork) run first.
+        bf16 pools; other pools take append + decode."""
+        if self.swapped:
+            raise ValueError("sequences are swapped out")
+        stream = self._stream(stream)
+        S = len(self.rows)
+        if self.k_pool.dtype != torch.bfloat16:
+            self.append(np.asarray(self.row_seqs, np.int32), np.ones(S, np.int32), k_new, v_new,
+                        stream=stream)
+            return self.decode(q, out=out, scale=scale, partition_tokens=partition_tokens,
+                               stream=stream)
+        seqs = np.asarray(self.row_seqs, np.int32)
+        st, slots, _, pos, pairs = self.bm.append_batch(seqs, np.ones(S, np.int32))
+        if st != PA_OK:
+            raise PagedKVError(st, "pa_bm_append_batch")
+        # every token's block is given (the kernel writes its table entry)
+        nb = (slots // self.B).astype(np.int32)
+        lens_in = self.lens[:S]
+        lens_out = self._lens_bufs[0]
+        if lens_out.data_ptr() == lens_in.data_ptr():
+            lens_out = self._lens_bufs[1]
+        self.host_lens[:S] += 1
+        gs = sb = None
+        if self.share_prefixes:
+            st, hgs, hsb = self.bm.prefix_groups(seqs, self.max_group)
+            if st != PA_OK:
+                raise PagedKVError(st, "pa_bm_prefix_groups")
+            cached = self._step_groups
+            if cached is None or not (np.array_equal(cached[0], hgs) and
+                                      np.array_equal(cached[1], hsb)):
+                with torch.cuda.stream(stream):
+                    cached = (hgs, hsb, torch.from_numpy(hgs).to(self.device, non_blocking=False),
+                              torch.from_numpy(hsb).to(self.device, non_blocking=False))
+                self._step_groups = cached
+            gs, sb = cached[2], cached[3]
+        scale = self.head_dim ** -0.5 if scale is None else scale
+        with torch.cuda.stream(stream):
+            if len(pairs):
+                d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device,
+                                                                           non_blocking=False)
+                pa_block_copy(self.k_pool, self.v_pool, d_pairs, stream=stream)
+            ws = self.workspace(q.shape[1], partition_tokens)
+            out = pa_decode_step(q, self.k_pool, self.v_pool, k_new, v_new, self.tables[:S],
+                                 lens_in, lens_out[:S], nb, scale, out=out,
+                                 group_start=gs, shared_blocks=sb,
+                                 partition_tokens=partition_tokens, workspace=ws, stream=stream)
+        self.lens = lens_out
+        self.groups = None if gs is None else (gs, sb)
+        return out
 
     # --- preemption by swapping ------------------------------------------------
     def _swap(self, seq, out, stream):

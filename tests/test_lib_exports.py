@@ -70,27 +70,29 @@ def test_workspace_and_partition_sizing():
     P = L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 512)
     assert P == 512
     rows = 2 * 256 * 4 * 16
-    expect = 2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(4 * 16)
+    expect = 2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(4 * 16) + _align(5 * 32)
     for width, piece in ((8192, 512), (8192, 0), (516, 0), (1, 16)):
         assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, width, piece) == expect
     # 4 ints per sequence, up to the 4096 of one launch (larger batches run
     # in slices that reuse the workspace)
     big = 2 * _align(rows * 4) + _align(rows * 128 * 4)
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1000, 32, 64, 0) == big + _align(1000 * 16)
-    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 9000, 32, 64, 0) == big + 4096 * 16
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 1000, 32, 64, 0) == \
+        big + _align(1000 * 16) + _align(1001 * 32)
+    assert L.pa_decode_workspace_bytes(ctypes.byref(d), 9000, 32, 64, 0) == \
+        big + 4096 * 16 + _align(4097 * 32)
     # multi-head attention (1 query head per kv head): 16 members' heads per tile
     mha = _desc(nb=4096, nkv=32)
     rows = 2 * 256 * 4 * 16
     assert L.pa_decode_workspace_bytes(ctypes.byref(mha), 64, 32, 128, 0) == \
-        2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(64 * 16)
+        2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(64 * 16) + _align(65 * 32)
     # 3 query heads per kv head: 5 members fill 15 slots
     d3 = _desc(nkv=2)
     rows = 2 * 256 * 4 * 15
     assert L.pa_decode_workspace_bytes(ctypes.byref(d3), 8, 6, 64, 0) == \
-        2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(8 * 16)
+        2 * _align(rows * 4) + _align(rows * 128 * 4) + _align(8 * 16) + _align(9 * 32)
     # the fixed scratch of the no-allocation entry point covers the largest
     # workspace on 256 CUs: 16 head slots, 128 dims, a full launch of sequences
-    assert L.pa_decode_noalloc_max_bytes() >= big + 4096 * 16
+    assert L.pa_decode_noalloc_max_bytes() >= big + 4096 * 16 + _align(4097 * 32)
     # prefix groups add two rows per query head of each sequence of one
     # launch (2048 with groups)
     rows = 2 * 256 * 4 * 16
@@ -98,7 +100,7 @@ def test_workspace_and_partition_sizing():
         extra = 2 * min(S, 2048) * 32
         assert L.pa_decode_shared_workspace_bytes(ctypes.byref(d), S, 32, 64, 0) == \
             2 * _align((rows + extra) * 4) + _align((rows + extra) * 128 * 4) + \
-            _align(min(S, 4096) * 16)
+            _align(min(S, 4096) * 16) + _align((min(S, 4096) + 1) * 32)
     # library choice: 256-token minimum pieces, or for a table shorter than
     # 8192 tokens its capacity in 32 pieces rounded up to whole blocks
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 0) == 256
