@@ -558,6 +558,10 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
     ev = [(DeviceEvent(timing=True), DeviceEvent(timing=True)) for _ in range(steps)]
     scale = d ** -0.5
     q_start = torch.from_numpy(np.arange(S + 1, dtype=np.int32) * C).to(dev)
+    # the split (and its workspace) depends only on the batch shape and table width
+    ws_bytes = pk.pa_extend_workspace_bytes(cache.k_pool, cache.v_pool, T, S, Hq, width)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    log(f"extend workspace {ws_bytes} bytes")
 
     def step(i):
         cache.append(seqs, ns, kns[i], vns[i], stream=stream)
@@ -566,7 +570,7 @@ def bench_extend(args, pk, DeviceEvent, PagedKVCache, CONFIGS, draw_lengths):
         d_lens = torch.from_numpy(lens).to(dev, non_blocking=False)
         ev[i][0].record(stream)
         pk.pa_extend(qs[i], cache.k_pool, cache.v_pool, q_start, d_tables, d_lens, scale,
-                     out=out, stream=stream)
+                     out=out, workspace=workspace, stream=stream)
         ev[i][1].record(stream)
         L = lens.astype(np.int64)
         # sum over queries of (position + 1): query j of a sequence sees L - C + j + 1 tokens

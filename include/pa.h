@@ -315,15 +315,34 @@ size_t pa_decode_noalloc_max_bytes(void);
  *   q_start:     int32 [num_seqs + 1], q_start[0] = 0, non-decreasing;
  *                sequences with no queries are allowed.
  *   block_tables, context_lens: as for pa_decode.
+ *   workspace:   device buffer of pa_extend_workspace_bytes(...) bytes for a
+ *                batch too small to fill the chip: each sequence's context is
+ *                then cut into chunks streamed in parallel, whose partial
+ *                (max, sum-exp, unnormalised output) rows a second kernel
+ *                combines.  NULL, or fewer bytes: no split (the same result,
+ *                on fewer workgroups).  Contents on entry are irrelevant.
  * Requires bf16 pools, block_size 16, head_dim 64 or 128 and at most 16
- * query heads per kv head (PA_EUNSUPPORTED otherwise).  No workspace.
+ * query heads per kv head (PA_EUNSUPPORTED otherwise).
  * With PA_DEBUG=1, q_start, lengths and table entries are validated first.
  */
 pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const void* q, int32_t total_q, const int32_t* q_start, int32_t num_seqs,
                     int32_t num_q_heads, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
-                    void* out, void* stream);
+                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace pa_extend uses to split the contexts of a batch of
+ * total_q query rows over num_seqs sequences (0: the batch fills the chip
+ * without a split, or invalid arguments).  The split is chosen from these
+ * sizes and the device: when the batch's workgroup units (4 waves of
+ * 16-row tiles of one sequence and kv head) number fewer than four per
+ * workgroup slot of the grid, each context is cut into up to 32 chunks of
+ * at least 1024 tokens; the partials take total_q * num_q_heads * chunks *
+ * (head_dim + 2) fp32 values.
+ */
+size_t pa_extend_workspace_bytes(const pa_pool* pool, int32_t total_q, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq);
 
 /*
  * Copy-on-write block copy ("The bonus contiguous storage can't give you:

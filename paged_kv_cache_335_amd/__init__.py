@@ -77,7 +77,8 @@ def _load():
         "pa_table_update": (i32, [vp, i32, i32, vp, vp, vp, i32, vp]),
         "pa_kv_append": (i32, [P, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp]),
         "pa_block_swap": (i32, [P, vp, vp, vp, vp, i32, vp, i32, i32, vp]),
-        "pa_extend": (i32, [P, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, f32, vp, vp]),
+        "pa_extend": (i32, [P, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp, f32, vp, vp, sz, vp]),
+        "pa_extend_workspace_bytes": (sz, [P, i32, i32, i32, i32]),
         "pa_probe_sink_bytes": (sz, [i32]),
         "pa_probe_read": (i32, [vp, vp, i32, ctypes.c_uint32, i32, i32, vp, vp]),
         "pa_status_str": (ctypes.c_char_p, [i32]),
@@ -116,6 +117,7 @@ EXPORTED = (
     "pa_decode_noalloc",
     "pa_decode_noalloc_max_bytes",
     "pa_block_copy", "pa_table_update", "pa_kv_append", "pa_block_swap", "pa_extend",
+    "pa_extend_workspace_bytes",
     "pa_status_str", "pa_probe_sink_bytes", "pa_probe_read",
     "pa_version", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_fork", "pa_bm_append", "pa_bm_append_batch",
@@ -383,8 +385,14 @@ def pa_decode_noalloc_max_bytes():
     return int(_lib.pa_decode_noalloc_max_bytes())
 
 
+def pa_extend_workspace_bytes(k_pool, v_pool, total_q, num_seqs, num_q_heads, max_blocks_per_seq):
+    desc = pool_desc(k_pool, v_pool)
+    return int(_lib.pa_extend_workspace_bytes(ctypes.byref(desc), total_q, num_seqs, num_q_heads,
+                                              max_blocks_per_seq))
+
+
 def pa_extend(q, k_pool, v_pool, q_start, block_tables, context_lens, scale, out=None,
-              stream=None):
+              workspace=None, stream=None):
     """Multi-token causal attention (extend / chunked prefill); returns out
     [total_q][num_q_heads][head_dim].  Query j of sequence s (rows
     q_start[s] .. q_start[s+1]) sits at position context_lens[s] - n_s + j
@@ -404,11 +412,18 @@ def pa_extend(q, k_pool, v_pool, q_start, block_tables, context_lens, scale, out
         out = torch.empty_like(q)
     elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
         raise ValueError("out must match q")
+    if workspace is None:
+        need = int(_lib.pa_extend_workspace_bytes(ctypes.byref(desc), T, S, Hq,
+                                                  block_tables.shape[1])) if T and S else 0
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.pa_extend(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                         _dev(q, "q"), T, _dev(q_start, "q_start"), S, Hq,
                         _dev(block_tables, "block_tables"), block_tables.shape[1],
                         _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
-                        _stream(stream))
+                        ws_ptr, ws_bytes, _stream(stream))
     _check(st, "pa_extend")
     return out
 

@@ -26,11 +26,13 @@ HIPCC_FLAGS = [
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Extra hipcc flags per source.  pa_extend.hip: MFMAs in the VGPR form.  Its
-# accumulators need more registers than the 256 VGPRs leave; in the AGPR
-# form the compiler copied every accumulator out to VGPRs and back around
-# each K/V block (for the softmax rescale), which doubled the VALU work.
-SOURCE_FLAGS = {"pa_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Extra hipcc flags per source.  pa_extend.hip: MFMAs in the VGPR form (in
+# the AGPR form the compiler moved accumulators between the two register
+# files around the softmax rescale), and no NaN operands assumed, so that a
+# max of MFMA results is one v_max3 per three values instead of a
+# canonicalising v_max per value first.  The kernel keeps every NaN it can
+# meet (stale cache slots) out of its arithmetic by selects, not by max.
+SOURCE_FLAGS = {"pa_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
 
 

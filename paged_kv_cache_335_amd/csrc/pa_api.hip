@@ -457,11 +457,21 @@ pa_status pa_decode_noalloc(const pa_pool* pool, const void* k_pool, const void*
                      nullptr, ptr, kScratchBytes, false, as_stream(stream));
 }
 
+size_t pa_extend_workspace_bytes(const pa_pool* pool, int32_t total_q, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_blocks_per_seq) {
+  if (!pool_ok(pool) || total_q <= 0 || num_seqs <= 0 || num_q_heads <= 0 ||
+      max_blocks_per_seq <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return 0;
+  const int splits = pakv::extend_splits(total_q, num_q_heads, pool->num_kv_heads,
+                                         max_blocks_per_seq, pool->head_dim);
+  return pakv::extend_workspace_bytes(total_q, num_q_heads, splits, pool->head_dim);
+}
+
 pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
                     const void* q, int32_t total_q, const int32_t* q_start, int32_t num_seqs,
                     int32_t num_q_heads, const int32_t* block_tables,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, float scale,
-                    void* out, void* stream) {
+                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!pool_ok(pool) || num_seqs < 0 || total_q < 0 || num_q_heads <= 0 ||
       max_blocks_per_seq <= 0)
     return PA_EINVAL;
@@ -507,6 +517,19 @@ pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
   a.num_kv_heads = pool->num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.total_q = total_q;
+  // the library's split, or none when the workspace cannot hold it
+  a.splits = pakv::extend_splits(total_q, num_q_heads, pool->num_kv_heads, max_blocks_per_seq,
+                                 pool->head_dim);
+  const size_t need = pakv::extend_workspace_bytes(total_q, num_q_heads, a.splits, pool->head_dim);
+  if (a.splits > 1 && (!workspace || workspace_bytes < need)) a.splits = 1;
+  if (a.splits > 1) {
+    const size_t n = (size_t)total_q * num_q_heads * a.splits;
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.part_m = reinterpret_cast<float*>(w);
+    a.part_l = reinterpret_cast<float*>(w + align_up(n * sizeof(float)));
+    a.part_o = reinterpret_cast<float*>(w + 2 * align_up(n * sizeof(float)));
+  }
   hipError_t e = pakv::launch_extend(a, pool->head_dim, group, hs);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }

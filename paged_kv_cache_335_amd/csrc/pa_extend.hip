@@ -13,14 +13,27 @@
 //   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t,
 // K_t, V_t read from block_tables[s][t / 16], slot t % 16, kv head h / G.
 //
-// Decomposition: the 16 "head slots" of the decode kernel's MFMA tiles hold
-// (query, head) pairs here: a row tile is QPT = 16 / G consecutive queries
-// of one sequence times the G query heads of one kv head.  A workgroup's
-// four waves take 4R consecutive row tiles of one (sequence, kv head) and
-// stream blocks 0 .. p_max of the sequence: each 16-token K/V tile is
-// loaded once per workgroup into LDS and read by all four waves, and each
-// wave masks its rows at their own positions.  No context split: every row
-// tile finishes in place.
+// Decomposition.  A row tile is 16 MFMA "head slots" holding (query, head)
+// pairs: 16 / G consecutive queries of one sequence times the G query heads
+// of one kv head.  A workgroup's four waves take R row tiles each (4R tiles
+// of one (sequence, kv head)) and stream the sequence's context in stages
+// of 64 tokens: each wave loads one 16-token block of the stage straight
+// from the pool into LDS (global_load_lds_dwordx4, no registers, no LDS
+// writes), and all four waves read the whole stage.  Several stages are in
+// flight; one barrier per stage.  A batch too small to fill the chip cuts
+// each context into chunks whose (m, l, o) partials a second kernel
+// combines.
+//
+// Tiles.  q.K runs as v_mfma_f32_16x16x32_bf16 with A = 16 tokens x 32 dims
+// of K and B = 32 dims x 16 head slots of q, so a lane ends with 4 tokens'
+// scores of one head slot.  A 32-token pair of blocks is scored as two such
+// tiles whose token rows are chosen so that lane group grp holds tokens
+// 8 grp .. 8 grp + 7 of the pair; P.V is then one v_mfma_f32_16x16x32_bf16
+// per 16 dims with A = P (bf16, k = those 8 tokens) and B = a 16-byte LDS
+// read of V holding the same 8 tokens of one dim.  K rows sit in LDS with
+// their 16-byte chunks XOR-swizzled by row, so a tile's reads are free of
+// bank conflicts with no padding; the swizzle is applied by choosing each
+// lane's source address of the direct-to-LDS load.
 #include <algorithm>
 #include <type_traits>
 
@@ -31,92 +44,163 @@ namespace pakv {
 namespace {
 
 constexpr int kExtBlock = 16;
-// Tuning (measured on 32 sequences x 256-token chunks, GQA 32/8, d 128):
-// two row tiles per wave and two workgroups per CU (two waves per SIMD, so
-// one wave's MFMAs hide the other's softmax) ran at 530-537 TFLOP/s before
-// the mask-free interior blocks and the fused scale (590 with both); three
-// row tiles at 409, four at one workgroup per CU at about 330 (the last two
-// with P carried to 16 bits: 332-337 and 458-479 for two row tiles), and
-// one row tile at four workgroups per CU at 438.  One block in flight beyond
-// the staged one is what fits two workgroups per CU (a deeper ring spills).
-#ifndef PA_EXT_ROWS
-#define PA_EXT_ROWS 2
-#endif
-constexpr int kExtRows = PA_EXT_ROWS;  // row tiles per wave
-#ifndef PA_EXT_MIN_WG
-#define PA_EXT_MIN_WG 2
-#endif
-constexpr int kExtWgPerCu = PA_EXT_MIN_WG;  // workgroups per CU (register budget 512 / this)
-#ifndef PA_EXT_PREFETCH
-#define PA_EXT_PREFETCH 1
-#endif
-constexpr int kExtPrefetch = PA_EXT_PREFETCH;  // blocks in flight beyond the staged one
-constexpr int kExtTabWindow = 1024;             // table entries staged in LDS at a time
+constexpr int kStageTok = kWaves * kExtBlock;  // 64 tokens a stage: one block per wave
+static_assert(kWaves == 4, "a stage holds one block per wave");
 
-// Plan in LDS: units before each sequence (prefix sums of ceil(n_s / qpt),
-// with qpt the queries of one unit).
-__device__ int build_extend_plan(const ExtendArgs& a, int qpt, int* pre, int* wsum) {
+// Per head size: row tiles per wave (R), LDS stage buffers (stages in
+// flight + 1) and workgroups per CU.  R row tiles share every K and V read
+// from LDS, so R sets the LDS bytes per MFMA.  Two workgroups per CU (two
+// waves per SIMD, one computing while the other waits at its barrier or on
+// its MFMA results) measured faster than one workgroup with a deeper stage
+// ring, even where R = 2 at head size 128 spills a few registers outside
+// the streaming loop.
+#ifndef PA_EXT128_ROWS
+#define PA_EXT128_ROWS 2
+#endif
+#ifndef PA_EXT128_STAGES
+#define PA_EXT128_STAGES 2
+#endif
+#ifndef PA_EXT128_WG
+#define PA_EXT128_WG 2
+#endif
+#ifndef PA_EXT64_ROWS
+#define PA_EXT64_ROWS 2
+#endif
+#ifndef PA_EXT64_STAGES
+#define PA_EXT64_STAGES 2
+#endif
+#ifndef PA_EXT64_WG
+#define PA_EXT64_WG 2
+#endif
+template <int D>
+struct ExtCfg;
+template <>
+struct ExtCfg<128> {
+  static constexpr int R = PA_EXT128_ROWS, NST = PA_EXT128_STAGES, WG = PA_EXT128_WG;
+};
+template <>
+struct ExtCfg<64> {
+  static constexpr int R = PA_EXT64_ROWS, NST = PA_EXT64_STAGES, WG = PA_EXT64_WG;
+};
+constexpr int kExtTabWindow = 1024;          // table entries staged in LDS at a time
+static_assert(kExtTabWindow % kWaves == 0, "whole stages per table window");
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// s_waitcnt immediate for gfx9: vector-memory count at most n, LDS/scalar
+// count 0, export count untouched.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+template <int D>
+struct StageGeom {
+  static constexpr int ROW = D * 2;           // bytes of one K row
+  static constexpr int KCH = ROW / 16;        // 16-byte chunks per K row
+  static constexpr int kK = kStageTok * ROW;  // K bytes of a stage
+  static constexpr int kVPair = 4 * D * 16;   // V bytes of a 32-token pair
+  static constexpr int kV = 2 * kVPair;       // V bytes of a stage
+  static constexpr int kLoads = kExtBlock * ROW / 1024;  // 1 KiB loads per wave, K and V each
+  static_assert(kV == kK && kLoads * 1024 == kExtBlock * ROW, "a block is whole 1 KiB loads");
+};
+
+// LDS of one workgroup: the stage buffers (separate arrays, so that the
+// compiler sees which buffer a direct-to-LDS load writes and which one a
+// read touches) and the block-table window.
+template <int D>
+struct ExtLds {
+  static constexpr int kBuf = StageGeom<D>::kK + StageGeom<D>::kV;
+};
+
+// Plan in LDS: units before each sequence (prefix sums of
+// ceil(n_s / qpu) * splits, qpu = queries of one unit).
+__device__ int build_extend_plan(const ExtendArgs& a, int qpu, int* pre, int* wsum) {
   const int S = a.num_seqs, T_ = blockDim.x, t = threadIdx.x;
   const int C = (S + T_ - 1) / T_;
   const int s0 = min(S, t * C), s1 = min(S, s0 + C);
   int nt = 0;
   for (int s = s0; s < s1; ++s) {
     const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
-    nt += (n + qpt - 1) / qpt;
+    nt += (n + qpu - 1) / qpu * a.splits;
   }
   int total;
   int run = block_excl_scan(nt, wsum, &total);
   for (int s = s0; s < s1; ++s) {
     pre[s] = run;
     const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
-    run += (n + qpt - 1) / qpt;
+    run += (n + qpu - 1) / qpu * a.splits;
   }
   if (t == 0) pre[S] = total;
   __syncthreads();
   return total;
 }
 
-// Workgroup-shared K/V: the four waves of a workgroup take 4R row tiles of
-// the same (sequence, kv head), and each 16-token K/V tile is loaded once
-// per workgroup into LDS (every thread fetches one chunk of K and one of V)
-// and read by all four waves, so one load feeds 4R row tiles.  Global loads
-// run NPF blocks ahead of the staged one in a small per-thread register
-// ring; LDS holds two tiles, so one barrier per block separates the store
-// of tile i + 1 from its readers and the readers of tile i - 1 from its
-// overwrite.
-template <int D>
-struct WgTile {
-  // K rows padded by 32 bytes: the LDS bank-conflict counter read a third of
-  // what it read with 16 or 64 bytes of padding (8 times less than unpadded)
-  static constexpr int kStrideK = D * 2 + 32;
-  static constexpr int kBytesK = 16 * kStrideK;
-  static constexpr int kBytesV = D * 32;        // V as [dim tile][token quad][dim][4 tokens]
-  static constexpr int kBytes = kBytesK + kBytesV;
-  // each thread fetches one chunk of K and one of V: 32 D / 256 bytes each
-  static constexpr int kChunk = D * 32 / (kWaves * 64);
-  static_assert(kChunk == 8 || kChunk == 16, "8- or 16-byte chunks");
+// K swizzle key of token t (0..31) of a pair.  The 16 lanes of one lane
+// group read, for one K tile, tokens 8 a + 4 tau + b (a, b = 0..3) at the
+// same chunk index; the key sends them to distinct 16-byte bank groups
+// whether the LDS serves a 16-byte read 8 lanes at a time over 32 banks or
+// 16 lanes at a time over 64.  Head size 128 (16 chunks a row, a row spans
+// every bank): key b + 4 a.  Head size 64 (8 chunks, a row is 128 bytes, so
+// two rows of different parity b mod 2 share a 64-bank line): key
+// ((b / 2) + 2 a) ^ (4 (b mod 2)), distinct over a = 0, 1 for all b and,
+// for a fixed b mod 2, over all a and b / 2.
+template <int KCH>
+__device__ __forceinline__ int kswz(int t) {
+  static_assert(KCH == 16 || KCH == 8, "head size 128 or 64");
+  const int a = (t >> 3) & 3, b = t & 3;
+  return KCH == 16 ? b + 4 * a : (((b >> 1) + 2 * a) ^ (4 * (b & 1)));
+}
+
+// The reference a row's softmax starts from: finite, so that a row that sees
+// no token of its chunk (its position lies before the chunk) keeps p = 0,
+// l = 0, o = 0 instead of exp2(-inf + inf).
+constexpr float kRefFloor = -1e30f;
+
+// The stage buffers, picked by a compile-time index.
+struct StageBufs {
+  uint8_t* b0;
+  uint8_t* b1;
+  uint8_t* b2;
+  uint8_t* b3;
+  template <int I>
+  __device__ __forceinline__ uint8_t* get(std::integral_constant<int, I>) const {
+    static_assert(I < 4, "four stage buffers at most");
+    return I == 0 ? b0 : I == 1 ? b1 : I == 2 ? b2 : b3;
+  }
 };
 
-template <int D, int R, int NPF, bool kPos>
-__device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int qpt, int s, int unit,
-                                               int g, int wave, int lane, uint8_t* lds, int* tab) {
-  using T = WgTile<D>;
+template <int D, int R, int NST, bool kPos>
+__device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt, int s, int unit,
+                                            int chunk, int g, int wave, int lane,
+                                            const StageBufs& sbuf, int* tab) {
+  using SG = StageGeom<D>;
   constexpr int B = kExtBlock;
-  constexpr int KJ = D / 32;
-  constexpr int NT = D / 16;
-  constexpr uint32_t ROW = D * 2;
+  constexpr int KJ = D / 32;   // q.K MFMAs per 16-token tile (32 dims each)
+  constexpr int NT = D / 16;   // P.V MFMAs per pair (16 dims each)
+  constexpr int ROW = SG::ROW;
+  constexpr int KCH = SG::KCH;
   const int col = lane & 15, grp = lane >> 4;
-  const int tid = threadIdx.x;
 
   const int q0 = a.q_start[s];
   const int n = a.q_start[s + 1] - q0;
   const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
-  const int ufirst = unit * kWaves * R * qpt;      // first query of the workgroup's row tiles
-  const int ulast = min(n - 1, ufirst + kWaves * R * qpt - 1);
-  const int p_max = L - n + ulast;                 // furthest position any row attends
-  const int first = ufirst + wave * R * qpt;       // this wave's first query
+  const int qpu = kWaves * R * qpt;               // queries of the unit
+  const int ufirst = unit * qpu;                  // first query of the workgroup's row tiles
+  const int ulast = min(n - 1, ufirst + qpu - 1);
+  const int p_max = max(0, L - n + ulast);        // furthest position any row attends
+  const int first = ufirst + wave * R * qpt;      // this wave's first query
   const int last = min(ulast, first + R * qpt - 1);
   const int p_lo = first <= last ? L - n + first : p_max;  // nearest position of the wave's rows
+
+  // this chunk's tokens: [kv0, kv1), whole stages, within 0 .. p_max
+  int kv0 = 0, kv1 = p_max + 1;
+  if (a.splits > 1) {
+    const int per = (L + a.splits * kStageTok - 1) / (a.splits * kStageTok) * kStageTok;
+    kv0 = chunk * per;
+    kv1 = min(kv1, kv0 + per);
+  }
+  // (an empty context, which valid input never pairs with queries, reads
+  // no table entry)
+  const int nst = kv1 > kv0 && L > 0 ? (kv1 - kv0 + kStageTok - 1) / kStageTok : 0;
 
   int p_row[R];
   bool live[R];
@@ -127,7 +211,7 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     live[rr] = f <= last;
     const int qi = f + col / G;
     const bool row_ok = col < qpt * G && qi <= last;
-    p_row[rr] = row_ok ? L - n + qi : p_max;       // padding slots: harmless finite rows
+    p_row[rr] = row_ok ? L - n + qi : p_max;      // padding slots: harmless finite rows
     u32x4 w[KJ];
 #pragma unroll
     for (int kj = 0; kj < KJ; ++kj) w[kj] = u32x4{0u, 0u, 0u, 0u};
@@ -141,192 +225,233 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
   }
 
-  const size_t blk_bytes = (size_t)a.num_kv_heads * B * D * 2;
+  // Direct-to-LDS loads: wave w loads block w of each stage, its K rows into
+  // rows 16 w .. 16 w + 15 of the stage's K tile (chunk c of the row that is
+  // token t of its 32-token pair at chunk position c ^ kswz<KCH>(t)) and its
+  // V into the stage's V chunks whose tokens it holds.  Load j of a wave
+  // fills 1 KiB: lane l's 16 bytes land at 16 l, from the source offsets
+  // below (the same for every stage).
+  const size_t blk_bytes = (size_t)a.num_kv_heads * B * ROW;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
-  // this thread's chunks: byte offset inside the K (and V) tile of a block,
-  // and LDS offsets.  A 16-byte V chunk is 8 tokens of one dim: two 4-token
-  // quads, stored 128 bytes apart; an 8-byte chunk is one quad.
-  constexpr int CB = T::kChunk;
-  const uint32_t goff = tid * CB;
-  const uint32_t lk = (goff / ROW) * T::kStrideK + goff % ROW;
-  const int vdim = goff / 32, vquad = (goff % 32) / 8;
-  const uint32_t lv = T::kBytesK + (vdim >> 4) * 512 + vquad * 128 + (vdim & 15) * 8;
-  const int vtok = vquad * 4;                      // first token of the chunk in its block
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
-  // blocks holding tokens 0 .. p_max (at least one, so that lengths shorter
-  // than the query count, which the caller must not pass, still read in bounds)
-  const int nblk = max(1, p_max / B + 1);
+  // K: load j, lane l -> row r16 = j * (1024 / ROW) + l / KCH of the block
+  // (token 16 (w mod 2) + r16 of the pair), position l mod KCH; V: chunk
+  // ci = (wave * kLoads + j) * 64 + l of the stage -> dim ci mod D, token
+  // half (ci / D) mod 2.
+  auto ksrc = [&](int j) {
+    const int r16 = j * (1024 / ROW) + lane / KCH;
+    const int key = kswz<KCH>(16 * (wave & 1) + r16);
+    return (uint32_t)(r16 * ROW + (((lane % KCH) ^ key) * 16));
+  };
+  auto vsrc = [&](int j) {
+    const int ci = (wave * SG::kLoads + j) * 64 + lane;
+    return (uint32_t)((ci % D) * (B * 2) + ((ci / D) % 2) * 16);
+  };
+  const uint32_t kdst = wave * B * ROW;                   // the wave's K rows
+  const uint32_t vdst = SG::kK + wave * SG::kLoads * 1024;  // the wave's V chunks
 
-  // Block ids come from a window of the table row staged in LDS: a table
-  // read from global memory would be counted with the K/V loads, and
-  // waiting for it would drain every K/V load in flight.
-  using Chunk = std::conditional_t<CB == 16, u32x4, u32x2>;
-  Chunk kring[NPF], vring[NPF];
-  int cn = 1;                                      // blocks in the current window
-  auto gload = [&](int i, auto slot) {
-    // the block id is the same in every lane: its offset is scalar work
-    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tab[min(i, cn - 1)]) * blk_bytes;
-    kring[slot] = *reinterpret_cast<const Chunk*>(kpool + off + goff);
-    vring[slot] = *reinterpret_cast<const Chunk*>(vpool + off + goff);
+  // LDS read offsets of this lane (stage-relative).  K tile tau of a pair:
+  // MFMA row m reads token 8 (m / 4) + 4 tau + m % 4 of the pair, chunk
+  // kj * 4 + grp (swizzled).  V: chunk (grp, dim) of the pair.
+  auto kread = [&](int tau, int kj) {
+    const int t = 8 * (col / 4) + 4 * tau + col % 4;
+    return (uint32_t)(t * ROW + (((kj * 4 + grp) ^ kswz<KCH>(t)) * 16));
   };
-  // Stages block `blk` (index in the sequence) from ring slot `slot`.  V of
-  // tokens past p_max (past every row, or past the context) is zeroed, so
-  // stale bits never meet a zero probability.
-  auto lstore = [&](auto slot, int buf, int blk) {
-    uint8_t* t = lds + buf * T::kBytes;
-    *reinterpret_cast<Chunk*>(t + lk) = kring[slot];
-    uint32_t v[CB / 4];
-    if constexpr (CB == 16) {
-      v[0] = vring[slot].x; v[1] = vring[slot].y; v[2] = vring[slot].z; v[3] = vring[slot].w;
-    } else {
-      v[0] = vring[slot].x; v[1] = vring[slot].y;
-    }
-    if (blk * B + B - 1 > p_max) {                 // uniform: the block reaches past p_max
-      const int tok = blk * B + vtok;
-#pragma unroll
-      for (int e = 0; e < CB / 2; ++e)
-        if (tok + e > p_max) v[e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-    }
-    *reinterpret_cast<u32x2*>(t + lv) = u32x2{v[0], v[1]};
-    if constexpr (CB == 16) *reinterpret_cast<u32x2*>(t + lv + 128) = u32x2{v[2], v[3]};
-  };
+  const uint32_t vread = SG::kK + (grp * D + col) * 16;
 
   float m_ref[R], thr[R], l_run[R];               // thr = m_ref + kSlack
   f32x4 acc[R][NT];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
-    m_ref[rr] = kNegInf;
-    thr[rr] = kNegInf;
+    m_ref[rr] = kRefFloor;
+    thr[rr] = kRefFloor + kSlack;
     l_run[rr] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[rr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int i, int buf) {
-    const uint8_t* t = lds + buf * T::kBytes;
-    u32x4 kb[KJ];
-    u32x2 vq[NT];
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
+  const int tid = threadIdx.x;
+
+  // one stage's loads into buffer `buf`: block w of stage i of the window
+  // (clamped to the window's last block, so loads past it re-read it)
+  auto dma = [&](int i, int cn, auto buf) {
+    const int bi = min(i * kWaves + wave, cn - 1);
+    const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tab[bi]) * blk_bytes;
+    const gptr kb = uniform_ptr(kpool + off);
+    const gptr vb = uniform_ptr(vpool + off);
+    uint8_t* d = sbuf.get(buf);
 #pragma unroll
-    for (int kj = 0; kj < KJ; ++kj)
-      kb[kj] = *reinterpret_cast<const u32x4*>(t + col * T::kStrideK + kj * 64 + grp * 16);
+    for (int j = 0; j < SG::kLoads; ++j)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(kb + ksrc(j)),
+                                       (lds_void*)(d + kdst + j * 1024), 16, 0, 0);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      vq[nt] = *reinterpret_cast<const u32x2*>(t + T::kBytesK + nt * 512 + grp * 128 + col * 8);
-    const int t0 = i * B + 4 * grp;                // this lane's first token of the tile
-    f32x4 sc[R];
+    for (int j = 0; j < SG::kLoads; ++j)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<gbl_void*>(vb + vsrc(j)),
+                                       (lds_void*)(d + vdst + j * 1024), 16, 0, 0);
+  };
+
+  // one stage from buffer `buf`: logical tokens t0 .. t0 + 63, a 32-token
+  // pair at a time (scores, softmax, P.V).  Scores of tokens past a row's
+  // position become -inf; that takes instructions only in stages that reach
+  // past the nearest row of the wave (the causal edge and the context's
+  // end).  V needs no mask here: stale slots are zeroed in LDS first.
+  auto compute = [&](int t0, auto buf) {
+    const uint8_t* d = sbuf.get(buf);
+    const bool cmask = t0 + kStageTok - 1 > p_lo;
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      sc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pp = 0; pp < 2; ++pp) {
+      // scores: sc[rr][tau], lane's tokens 8 grp + 4 tau + r of the pair
+      f32x4 sc[R][2];
 #pragma unroll
-      for (int kj = 0; kj < KJ; ++kj)
-        sc[rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[kj]),
-                                                         qop[rr][kj], sc[rr], 0, 0, 0);
-    }
-    // Softmax of the R row tiles, stage by stage so that one wave-wide
-    // branch covers the (rare) moves of any tile's reference and the rest
-    // of the step is one basic block in which the compiler can interleave
-    // the tiles' VALU work with their MFMAs.
-    // With a positive scale (kPos) the scores stay unscaled until the
-    // exponent: x = masked raw score, the lane's max is scaled once, and
-    // p = exp2(fma(x, scale, -m)).  Otherwise x is the scaled score.
-    float x[R][4], bm[R];
-    // A block whose tokens every row of the wave sees (all but the blocks
-    // near the diagonal and steps past the last block) skips the mask.
-    const bool seen = i * B + B - 1 <= p_lo;
+      for (int tau = 0; tau < 2; ++tau) {
+        u32x4 kb[KJ];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
+        for (int kj = 0; kj < KJ; ++kj)
+          kb[kj] = *reinterpret_cast<const u32x4*>(d + pp * 32 * ROW + kread(tau, kj));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[rr][r] = kPos ? sc[rr][r] : sc[rr][r] * a.scale_log2;
-    if (!seen) {
+        for (int rr = 0; rr < R; ++rr) {
+          sc[rr][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kj = 0; kj < KJ; ++kj)
+            sc[rr][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kb[kj]), qop[rr][kj], sc[rr][tau], 0, 0, 0);
+        }
+      }
+      // With a positive scale (kPos) the scores stay unscaled until the
+      // exponent: x = masked raw score, the lane's max is scaled once, and
+      // p = exp2(fma(x, scale, -m)).  Otherwise x is the scaled score.
+      float x[R][8];
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = sc[rr][e / 4][e % 4];
+          x[rr][e] = kPos ? v : v * a.scale_log2;
+        }
+      if (cmask) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const int lim = p_row[rr] - (t0 + pp * 32 + 8 * grp);  // lane token e at offset e
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e > lim) x[rr][e] = kNegInf;
+        }
+      }
+      float bm[R];
+      bool grow = false;
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        const int lim = p_row[rr] - t0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[rr][r] = r <= lim ? x[rr][r] : kNegInf;
+        float mx = fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(x[rr][4], x[rr][5]), fmaxf(x[rr][6], x[rr][7])));
+        bm[rr] = kPos ? mx * a.scale_log2 : mx;
+        grow = grow || bm[rr] > thr[rr];
       }
-    }
-    // bm: this lane's max of each row's scores.  A row's max passes its
-    // threshold exactly when some lane's does, so the common path needs no
-    // exchange between lanes; the (rare) branch that moves references takes
-    // the max over the row's four lanes first.
+      if (__ballot(grow)) {   // rare: move references that grew, rescale
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      bm[rr] = fmaxf(fmaxf(x[rr][0], x[rr][1]), fmaxf(x[rr][2], x[rr][3]));
-      if constexpr (kPos) bm[rr] *= a.scale_log2;
-    }
-    bool grow = false;
+        for (int rr = 0; rr < R; ++rr) {
+          bm[rr] = max_xor32(max_xor16(bm[rr]));
+          const float m_new = bm[rr] > thr[rr] ? bm[rr] : m_ref[rr];
+          const float alpha = fexp2(m_ref[rr] - m_new);
+          l_run[rr] *= alpha;
+          m_ref[rr] = m_new;
+          thr[rr] = m_new + kSlack;
+          float ar[4];
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) grow = grow || bm[rr] > thr[rr];
-    if (__ballot(grow)) {                          // rare: move references that grew, rescale
+          for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
+        }
+      }
+      // P in bf16 (nearest even): the A operand of P.V, k = the lane's 8
+      // tokens of the pair in order
+      bf16x8 pk[R];
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
-        bm[rr] = max_xor32(max_xor16(bm[rr]));
-        const float m_new = bm[rr] > thr[rr] ? bm[rr] : m_ref[rr];
-        const float alpha = fexp2(m_ref[rr] - m_new);
-        l_run[rr] *= alpha;
-        m_ref[rr] = m_new;
-        thr[rr] = m_new + kSlack;
-        float ar[4];
+        float pr[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+        for (int e = 0; e < 8; ++e)
+          pr[e] = kPos ? fexp2(fmaf(x[rr][e], a.scale_log2, -m_ref[rr])) : fexp2(x[rr][e] - m_ref[rr]);
+        l_run[rr] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        bf16x8 v;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(pr[e]);
+        pk[rr] = v;
       }
-    }
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-      float p[4];
+      for (int nt = 0; nt < NT; ++nt) {
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(d + pp * SG::kVPair + vread + nt * 256);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        p[r] = kPos ? fexp2(fmaf(x[rr][r], a.scale_log2, -m_ref[rr])) : fexp2(x[rr][r] - m_ref[rr]);
-      l_run[rr] += (p[0] + p[1]) + (p[2] + p[3]);
-      // P rounded to bf16 (nearest even) is the A operand of a 16x16x16
-      // MFMA whose B operand is the lane's V quad as read.  The softmax VALU
-      // work, not the MFMAs, bounds this kernel: carrying P to 16 bits as the
-      // decode does (a high and a low part, with V duplicated into a
-      // 16x16x32 operand) cost 15%.  Its error stays within the bf16 bar: a
-      // weight is off by at most 2^-9 of itself.
-      const bf16x2 p01 = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1])};
-      const bf16x2 p23 = {static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
-      const i16x4 pq = __builtin_bit_cast(
-          i16x4, u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)});
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pq, __builtin_bit_cast(i16x4, vq[nt]),
-                                                                acc[rr][nt], 0, 0, 0);
+        for (int rr = 0; rr < R; ++rr)
+          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pk[rr], __builtin_bit_cast(bf16x8, vb),
+                                                               acc[rr][nt], 0, 0, 0);
+      }
     }
   };
 
-  for (int w0 = 0; w0 < nblk; w0 += kExtTabWindow) {
-    cn = min(kExtTabWindow, nblk - w0);
-    for (int e = tid; e < cn; e += kWaves * 64) tab[e] = trow[w0 + e];
+  // V of the stage's tokens at or past the context's end (stale slots of
+  // the last block, and the re-read copies of it that pad the last stage)
+  // is zeroed in LDS before any wave reads the stage: their probabilities
+  // are 0, and stale bits (NaN included) must not meet them.  V chunk
+  // (c8, dim) of a stage holds tokens t0 + 8 c8 .. t0 + 8 c8 + 7.
+  auto zero_tail = [&](int t0, auto buf) {
+    uint8_t* d = sbuf.get(buf);
+    for (int idx = tid; idx < 8 * D; idx += kWaves * 64) {
+      const int c8 = idx / D, dim = idx % D;
+      const int lim = L - (t0 + 8 * c8);   // leading tokens of the chunk that are valid
+      if (lim >= 8) continue;
+      u32x4* v = reinterpret_cast<u32x4*>(d + SG::kK + (c8 * D + dim) * 16);
+      u32x4 x = *v;
+      x.x &= (0 < lim ? 0x0000ffffu : 0u) | (1 < lim ? 0xffff0000u : 0u);
+      x.y &= (2 < lim ? 0x0000ffffu : 0u) | (3 < lim ? 0xffff0000u : 0u);
+      x.z &= (4 < lim ? 0x0000ffffu : 0u) | (5 < lim ? 0xffff0000u : 0u);
+      x.w &= (6 < lim ? 0x0000ffffu : 0u) | (7 < lim ? 0xffff0000u : 0u);
+      *v = x;
+    }
+  };
+
+  // the chunk's blocks, a table window at a time
+  const int b_first = kv0 / B;
+  const int b_end = nst > 0 ? b_first + nst * kWaves : b_first;
+  for (int w0 = b_first; w0 < b_end; w0 += kExtTabWindow) {
+    const int cn = min(kExtTabWindow, b_end - w0);
+    // every wave is past the previous window (its loads landed, its reads
+    // done) before the window is overwritten; entries past the context
+    // re-read the last one
+    const int last_blk = max(0, (L - 1) / B);
     __syncthreads();
-    // prologue: the window's blocks 0 .. NPF - 1 in flight, block 0 staged
-    static_for<NPF>([&](auto j) { gload(j, j); });
-    lstore(std::integral_constant<int, 0>{}, 0, w0);
-    gload(NPF, std::integral_constant<int, 0>{});
+    for (int e = tid; e < cn; e += kWaves * 64) tab[e] = trow[min(w0 + e, last_blk)];
     __syncthreads();
-    // block i of the window is in LDS buffer i & 1 and block i + 1 in ring
-    // slot (i + 1) % NPF.  Steps run in whole groups of NPF without a
-    // branch (so the compiler counts the loads in flight exactly): loads
-    // past the window's last block re-read it, and a step past it computes
-    // on that block with every token beyond p_max, so its scores are masked
-    // and its V is zeroed.  The barrier closing each step also guards the
-    // reuse of both buffers and of the table window.
-    for (int i0 = 0; i0 < cn; i0 += NPF) {
-      static_for<NPF>([&](auto j) {
+    const int ns = cn / kWaves;                     // stages of the window
+    // prologue: stages 0 .. NST-2 in flight
+    static_for<NST - 1>([&](auto j) { dma((int)j, cn, j); });
+    for (int i0 = 0; i0 < ns; i0 += NST) {
+      static_for<NST>([&](auto j) {
         const int i = i0 + j;
-        constexpr int nxt = (j + 1) % NPF;
-        compute(w0 + i, i & 1);
-        lstore(std::integral_constant<int, nxt>{}, (i + 1) & 1, w0 + i + 1);
-        gload(i + 1 + NPF, std::integral_constant<int, nxt>{});
-        __syncthreads();
+        // this wave's loads of stage i landed (NST - 2 later stages may be
+        // in flight), then every wave's have, and every wave is done with
+        // the buffer the next loads overwrite
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NST - 2) * 2 * SG::kLoads));
+        __builtin_amdgcn_s_barrier();
+        dma(i + NST - 1, cn, std::integral_constant<int, (j + NST - 1) % NST>{});
+        if (i < ns) {
+          const int t0 = (w0 + i * kWaves) * B;
+          if (t0 + kStageTok > L) {   // the context ends in this stage (uniform)
+            zero_tail(t0, j);
+            // the zeros are in LDS before any wave reads the stage; the
+            // loads just issued may stay in flight
+            __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+            __builtin_amdgcn_s_barrier();
+          }
+          compute(t0, j);
+        }
       });
     }
   }
+  // no load may still be writing this workgroup's LDS when it moves on or ends
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
   // acc[rr][nt][r] holds slot 4*grp + r of row tile rr (query first + rr*qpt
   // + slot / G, head slot % G), dim nt*16 + col
@@ -335,31 +460,50 @@ __device__ __forceinline__ void extend_wg_unit(const ExtendArgs& a, int G, int q
     if (!live[rr]) continue;
     float l_tot = sum_xor16(l_run[rr]);
     l_tot = sum_xor32(l_tot);
-    float den[4];
+    float den[4], mr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) den[r] = lane_bcast(l_tot, 4 * grp + r);
+    for (int r = 0; r < 4; ++r) {
+      den[r] = lane_bcast(l_tot, 4 * grp + r);
+      mr[r] = lane_bcast(m_ref[rr], 4 * grp + r);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int slot = 4 * grp + r;
-      const int q = first + rr * qpt + slot / G;
-      if (slot >= qpt * G || q > last) continue;
-      const size_t ob = ((size_t)(q0 + q) * a.num_q_heads + g * G + slot % G) * D + col;
+      const int qq = first + rr * qpt + slot / G;
+      if (slot >= qpt * G || qq > last) continue;
+      const size_t row = (size_t)(q0 + qq) * a.num_q_heads + g * G + slot % G;
+      if (a.splits == 1) {
+        const size_t ob = row * D + col;
+        const float inv = 1.f / den[r];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] / den[r]);
+        for (int nt = 0; nt < NT; ++nt)
+          static_cast<__bf16*>(a.out)[ob + nt * 16] = static_cast<__bf16>(acc[rr][nt][r] * inv);
+      } else {
+        const size_t pr = row * a.splits + chunk;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) a.part_o[pr * D + nt * 16 + col] = acc[rr][nt][r];
+        if (col == 0) {
+          a.part_m[pr] = mr[r];
+          a.part_l[pr] = den[r];
+        }
+      }
     }
   }
 }
 
-template <int D, int R, int NPF, bool kPos>
-__global__ __launch_bounds__(kWaves * 64, kExtWgPerCu) void extend_wg_kernel(ExtendArgs a, int G,
-                                                                             int qpt) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * WgTile<D>::kBytes];
+template <int D, int R, int NST, int WG, bool kPos>
+__global__ __launch_bounds__(kWaves * 64, WG) void extend_kernel(ExtendArgs a, int G, int qpt) {
+  static_assert(NST >= 2 && NST <= 4, "two to four stage buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[ExtLds<D>::kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[ExtLds<D>::kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? ExtLds<D>::kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? ExtLds<D>::kBuf : 16];
   __shared__ int tab_lds[kExtTabWindow];
   extern __shared__ int ext_lds[];
+  const StageBufs sbuf{st0, st1, st2, st3};
   int* pre = ext_lds;                 // [S + 1]
   int* wsum = ext_lds + a.num_seqs + 1;
-  // a unit is the workgroup's 4R row tiles of qpt queries each
+  // a unit is the workgroup's 4R row tiles of qpt queries each, over one chunk
   const int tiles = build_extend_plan(a, kWaves * R * qpt, pre, wsum);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -374,8 +518,42 @@ __global__ __launch_bounds__(kWaves * 64, kExtWgPerCu) void extend_wg_kernel(Ext
     int s = lo;
     while (pre[s + 1] <= k) ++s;  // skip sequences without queries
     s = __builtin_amdgcn_readfirstlane(s);
-    extend_wg_unit<D, R, NPF, kPos>(a, G, qpt, s, k - pre[s], g, wave, lane, kv_lds, tab_lds);
+    const int local = k - pre[s];
+    extend_unit<D, R, NST, kPos>(a, G, qpt, s, local / a.splits, local % a.splits, g, wave, lane,
+                                 sbuf, tab_lds);
   }
+}
+
+// Combine of a split context: one wave per (query row, head), over the
+// chunks' partials: M = max m_c, out = sum 2^(m_c - M) o_c / sum 2^(m_c - M) l_c.
+constexpr int kCombineHeads = 4;
+
+template <int D>
+__global__ __launch_bounds__(kCombineHeads * 64) void extend_combine_kernel(ExtendArgs a) {
+  constexpr int EPL = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * kCombineHeads + wave;
+  if (row >= (size_t)a.total_q * a.num_q_heads) return;
+  const int C = a.splits;
+  const float* pm = a.part_m + row * C;
+  const float* pl = a.part_l + row * C;
+  float M = kNegInf;
+  for (int c = lane; c < C; c += 64) M = fmaxf(M, pm[c]);
+  M = wave_max(M);
+  float den = 0.f, num[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+  for (int c = 0; c < C; ++c) {
+    const float f = fexp2(pm[c] - M);
+    den = fmaf(f, pl[c], den);
+    const float* po = a.part_o + (row * C + c) * D;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(f, po[e * 64 + lane], num[e]);
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    static_cast<__bf16*>(a.out)[row * D + e * 64 + lane] = static_cast<__bf16>(num[e] * inv);
 }
 
 int cu_count_ext() {
@@ -393,16 +571,25 @@ int cu_count_ext() {
 
 template <int D>
 hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
+  using C = ExtCfg<D>;
   const int qpt = std::max(1, 16 / G);
-  // persistent grid: kExtWgPerCu workgroups per CU take the units in turn
+  // persistent grid: C::WG workgroups per CU take the units in turn
   const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
-  const int grid = std::max(1, std::min(cu_count_ext() * kExtWgPerCu, 1 << 16));
+  const int grid = std::max(1, std::min(cu_count_ext() * C::WG, 1 << 16));
   // a positive scale folds into the exponent's fma; any other takes the
   // plain form
   if (a.scale_log2 > 0.f)
-    extend_wg_kernel<D, kExtRows, kExtPrefetch, true><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+    extend_kernel<D, C::R, C::NST, C::WG, true><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
   else
-    extend_wg_kernel<D, kExtRows, kExtPrefetch, false><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+    extend_kernel<D, C::R, C::NST, C::WG, false><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_combine_d(const ExtendArgs& a, hipStream_t st) {
+  const size_t rows = (size_t)a.total_q * a.num_q_heads;
+  extend_combine_kernel<D><<<dim3((unsigned)((rows + kCombineHeads - 1) / kCombineHeads)),
+                             dim3(kCombineHeads * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -413,9 +600,34 @@ bool extend_supported(pa_dtype dtype, int head_dim, int group, int block_size) {
          group >= 1 && group <= 16;
 }
 
+// Split each context when the batch's units (each workgroup's row tiles of
+// one sequence and kv head) would not give every workgroup slot of the
+// grid about four: into as many chunks as make up for it, each at least
+// 1024 tokens, at most 32.
+int extend_splits(int total_q, int num_q_heads, int num_kv_heads, int max_blocks, int head_dim) {
+  const int G = num_q_heads / num_kv_heads;
+  const int rows = head_dim == 128 ? ExtCfg<128>::R : ExtCfg<64>::R;
+  const int wg = head_dim == 128 ? ExtCfg<128>::WG : ExtCfg<64>::WG;
+  const int qpu = kWaves * rows * std::max(1, 16 / G);
+  const int64_t units = ((int64_t)total_q + qpu - 1) / qpu * num_kv_heads;
+  const int64_t want = 4LL * cu_count_ext() * wg;
+  if (units <= 0 || units >= want) return 1;
+  const int64_t by_len = std::max<int64_t>(1, (int64_t)max_blocks * kExtBlock / 1024);
+  const int64_t k = std::min<int64_t>({(want + units - 1) / units, by_len, 32});
+  return static_cast<int>(std::max<int64_t>(1, k));
+}
+
+size_t extend_workspace_bytes(int total_q, int num_q_heads, int splits, int head_dim) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)total_q * num_q_heads * splits;
+  const auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return 2 * al(n * sizeof(float)) + al(n * head_dim * sizeof(float));
+}
+
 // Batches larger than kMaxPlanSeqs sequences run in slices (the plan lives
 // in LDS); q_start holds absolute row indices, so only the per-sequence
-// arrays move.
+// arrays move, and a split batch's partials (indexed by row) are combined
+// once, after every slice.
 hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream_t st) {
   for (int32_t s0 = 0; s0 < a.num_seqs; s0 += kMaxPlanSeqs) {
     ExtendArgs b = a;
@@ -427,7 +639,8 @@ hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream
         head_dim == 128 ? launch_extend_d<128>(b, group, st) : launch_extend_d<64>(b, group, st);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  if (a.splits <= 1) return hipSuccess;
+  return head_dim == 128 ? launch_combine_d<128>(a, st) : launch_combine_d<64>(a, st);
 }
 
 }  // namespace pakv

@@ -115,6 +115,14 @@ struct ExtendArgs {
   const int32_t* q_start;      // [S + 1] first query row of each sequence
   const int32_t* block_tables;
   const int32_t* context_lens;
+  // Context split: each sequence's context is cut into `splits` chunks
+  // (whole 64-token stages); with more than one, every (query, head) row
+  // leaves one (m, l, o) partial per chunk and a second kernel combines them.
+  float* part_m;               // [total_q][Hq][splits] reference max, log2 units
+  float* part_l;               // [total_q][Hq][splits]
+  float* part_o;               // [total_q][Hq][splits][D] unnormalised output
+  int32_t splits;
+  int32_t total_q;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -124,6 +132,10 @@ struct ExtendArgs {
 
 // Supported: bf16 pools, 16-token blocks, head_dim 64 / 128, group <= 16.
 bool extend_supported(pa_dtype dtype, int head_dim, int group, int block_size);
+// How many chunks the library cuts each context into for this batch (1: no
+// split), and the workspace that needs.
+int extend_splits(int total_q, int num_q_heads, int num_kv_heads, int max_blocks, int head_dim);
+size_t extend_workspace_bytes(int total_q, int num_q_heads, int splits, int head_dim);
 hipError_t launch_extend(const ExtendArgs& a, int head_dim, int group, hipStream_t stream);
 
 // Which decode kernel family handles a shape.

@@ -45,9 +45,9 @@ def _dev(a, bf16=False):
     return t.cuda()
 
 
-def _run(pk, k, v, q, qs, tables, lens, scale):
+def _run(pk, k, v, q, qs, tables, lens, scale, workspace=None):
     out = pk.pa_extend(_dev(q, True), _dev(k, True), _dev(v, True), _dev(qs), _dev(tables),
-                       _dev(lens), scale)
+                       _dev(lens), scale, workspace=workspace)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -95,6 +95,43 @@ def test_extend_contexts_longer_than_one_table_window(pk, d):
     err = np.abs(got - ref)
     _log(f"long contexts d={d}: max|err| {err.max():.3e}")
     assert np.isfinite(got).all() and err.max() <= 2e-2
+
+
+@pytest.mark.parametrize("G,d", [(4, 128), (8, 64), (1, 128)])
+def test_extend_context_split_long_prefixes(pk, G, d):
+    """Few sequences with long cached prefixes: too few units to fill the
+    chip, so the library cuts each context into chunks (partials + combine).
+    The split result and the unsplit one (a workspace too small to hold the
+    partials) both match the oracle; unused slots of the last blocks hold
+    NaN, which no chunk may let through."""
+    rng = np.random.default_rng(340 + G + d)
+    Hkv = 2
+    lens, ns = [30000, 9001, 1500], [40, 7, 1]
+    width = -(-max(lens) // 16)
+    k, v, q, qs, tables, lens = _case(rng, lens, ns, G * Hkv, Hkv, d, nb=2 * width + 200)
+    # tables of different sequences may share blocks: NaN only where no
+    # sequence reads
+    used = np.zeros((k.shape[0], 16), bool)
+    for s, L in enumerate(lens):
+        for t0 in range(0, L, 16):
+            used[tables[s, t0 // 16], :min(16, L - t0)] = True
+    nan = f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    for s, L in enumerate(lens):
+        b = tables[s, (L - 1) // 16]
+        for r in np.flatnonzero(~used[b]):
+            k[b, :, r, :] = nan
+            v[b, :, :, r] = nan
+    ws = pk.pa_extend_workspace_bytes(_dev(k, True), _dev(v, True), int(qs[-1]), len(lens),
+                                      G * Hkv, tables.shape[1])
+    assert ws > 0, "this batch should take the split path"
+    ref = oracle.extend(k, v, q, qs, tables, lens, d ** -0.5)
+    split = _run(pk, k, v, q, qs, tables, lens, d ** -0.5)
+    whole = _run(pk, k, v, q, qs, tables, lens, d ** -0.5,
+                 workspace=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    for name, got in (("split", split), ("whole", whole)):
+        err = np.abs(got - ref)
+        _log(f"G={G} d={d} {name}: max|err| {err.max():.3e}")
+        assert np.isfinite(got).all() and err.max() <= 2e-2
 
 
 def test_extend_many_sequences_and_determinism(pk):
