@@ -44,34 +44,46 @@ namespace pakv {
 namespace {
 
 constexpr int kExtBlock = 16;
-constexpr int kStageTok = kWaves * kExtBlock;  // 64 tokens a stage: one block per wave
-static_assert(kWaves == 4, "a stage holds one block per wave");
+constexpr int kStageBlocks = 4;                       // blocks of one stage
+constexpr int kStageTok = kStageBlocks * kExtBlock;   // 64 tokens a stage
 
-// Per head size: row tiles per wave (R), LDS stage buffers (stages in
-// flight + 1) and workgroups per CU.  R row tiles share every K and V read
-// from LDS, so R sets the LDS bytes per MFMA.  Two workgroups per CU (two
-// waves per SIMD, one computing while the other waits at its barrier or on
-// its MFMA results) measured faster than one workgroup with a deeper stage
-// ring, even where R = 2 at head size 128 spills a few registers outside
-// the streaming loop.
+// Per head size: waves per workgroup (W), row tiles per wave (R), LDS stage
+// buffers (stages in flight + 1) and workgroups per CU.  R row tiles share
+// every K and V read from LDS, so R sets the LDS bytes per MFMA.  Eight
+// waves (two per SIMD: one computes its softmax while the other keeps the
+// matrix core busy) share each stage, which halves the K/V bytes staged per
+// query against four, and leave LDS for four stages, three in flight: a
+// stage load has three stages of compute to arrive.
+#ifndef PA_EXT_WAVES
+#define PA_EXT_WAVES 8
+#endif
 #ifndef PA_EXT128_ROWS
 #define PA_EXT128_ROWS 2
 #endif
 #ifndef PA_EXT128_STAGES
-#define PA_EXT128_STAGES 2
+#define PA_EXT128_STAGES 3
 #endif
 #ifndef PA_EXT128_WG
-#define PA_EXT128_WG 2
+#define PA_EXT128_WG 1
 #endif
 #ifndef PA_EXT64_ROWS
 #define PA_EXT64_ROWS 2
 #endif
 #ifndef PA_EXT64_STAGES
-#define PA_EXT64_STAGES 2
+#define PA_EXT64_STAGES 4
 #endif
 #ifndef PA_EXT64_WG
-#define PA_EXT64_WG 2
+#define PA_EXT64_WG 1
 #endif
+#ifdef PA_EXT_SETPRIO
+#define PA_EXT_PRIO_MFMA() __builtin_amdgcn_s_setprio(1)
+#define PA_EXT_PRIO_VALU() __builtin_amdgcn_s_setprio(0)
+#else
+#define PA_EXT_PRIO_MFMA() ((void)0)
+#define PA_EXT_PRIO_VALU() ((void)0)
+#endif
+constexpr int kExtWaves = PA_EXT_WAVES;
+static_assert(kExtWaves == 4 || kExtWaves == 8, "four or eight waves share a stage");
 template <int D>
 struct ExtCfg;
 template <>
@@ -83,7 +95,7 @@ struct ExtCfg<64> {
   static constexpr int R = PA_EXT64_ROWS, NST = PA_EXT64_STAGES, WG = PA_EXT64_WG;
 };
 constexpr int kExtTabWindow = 1024;          // table entries staged in LDS at a time
-static_assert(kExtTabWindow % kWaves == 0, "whole stages per table window");
+static_assert(kExtTabWindow % kStageBlocks == 0, "whole stages per table window");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
@@ -99,8 +111,9 @@ struct StageGeom {
   static constexpr int kK = kStageTok * ROW;  // K bytes of a stage
   static constexpr int kVPair = 4 * D * 16;   // V bytes of a 32-token pair
   static constexpr int kV = 2 * kVPair;       // V bytes of a stage
-  static constexpr int kLoads = kExtBlock * ROW / 1024;  // 1 KiB loads per wave, K and V each
-  static_assert(kV == kK && kLoads * 1024 == kExtBlock * ROW, "a block is whole 1 KiB loads");
+  static constexpr int kLoads = kK / kExtWaves / 1024;  // 1 KiB loads per wave, K and V each
+  static_assert(kV == kK && kLoads >= 1 && kLoads * 1024 * kExtWaves == kK,
+                "a stage is whole 1 KiB loads per wave");
 };
 
 // LDS of one workgroup: the stage buffers (separate arrays, so that the
@@ -183,7 +196,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   const int q0 = a.q_start[s];
   const int n = a.q_start[s + 1] - q0;
   const int L = min(max(a.context_lens[s], 0), a.max_blocks * B);
-  const int qpu = kWaves * R * qpt;               // queries of the unit
+  const int qpu = kExtWaves * R * qpt;            // queries of the unit
   const int ufirst = unit * qpu;                  // first query of the workgroup's row tiles
   const int ulast = min(n - 1, ufirst + qpu - 1);
   const int p_max = max(0, L - n + ulast);        // furthest position any row attends
@@ -225,29 +238,31 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
     for (int kj = 0; kj < KJ; ++kj) qop[rr][kj] = __builtin_bit_cast(bf16x8, w[kj]);
   }
 
-  // Direct-to-LDS loads: wave w loads block w of each stage, its K rows into
-  // rows 16 w .. 16 w + 15 of the stage's K tile (chunk c of the row that is
-  // token t of its 32-token pair at chunk position c ^ kswz<KCH>(t)) and its
-  // V into the stage's V chunks whose tokens it holds.  Load j of a wave
-  // fills 1 KiB: lane l's 16 bytes land at 16 l, from the source offsets
-  // below (the same for every stage).
+  // Direct-to-LDS loads: the W waves split each stage evenly.  Wave w
+  // loads stage K rows w * RPW .. w * RPW + RPW - 1 (RPW = 64 / W; chunk c
+  // of the row that is token t of its 32-token pair at chunk position
+  // c ^ kswz<KCH>(t)) and the V chunks w * kLoads * 64 .. of the stage, all
+  // from block w * 4 / W of the stage.  Load j of a wave fills 1 KiB: lane
+  // l's 16 bytes land at 16 l, from the source offsets below (the same for
+  // every stage).
+  constexpr int RPW = kStageTok / kExtWaves;
+  const int wblk = wave * kStageBlocks / kExtWaves;   // the wave's block of each stage
   const size_t blk_bytes = (size_t)a.num_kv_heads * B * ROW;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * D * B * 2;
-  // K: load j, lane l -> row r16 = j * (1024 / ROW) + l / KCH of the block
-  // (token 16 (w mod 2) + r16 of the pair), position l mod KCH; V: chunk
-  // ci = (wave * kLoads + j) * 64 + l of the stage -> dim ci mod D, token
-  // half (ci / D) mod 2.
+  // K: load j, lane l -> stage row r = w * RPW + j * (1024 / ROW) + l / KCH
+  // (row r mod 16 of the block, token r mod 32 of its pair), position
+  // l mod KCH; V: chunk ci = (w * kLoads + j) * 64 + l of the stage ->
+  // dim ci mod D, token half (ci / D) mod 2 of the block.
   auto ksrc = [&](int j) {
-    const int r16 = j * (1024 / ROW) + lane / KCH;
-    const int key = kswz<KCH>(16 * (wave & 1) + r16);
-    return (uint32_t)(r16 * ROW + (((lane % KCH) ^ key) * 16));
+    const int r = wave * RPW + j * (1024 / ROW) + lane / KCH;
+    return (uint32_t)((r % B) * ROW + (((lane % KCH) ^ kswz<KCH>(r % 32)) * 16));
   };
   auto vsrc = [&](int j) {
     const int ci = (wave * SG::kLoads + j) * 64 + lane;
     return (uint32_t)((ci % D) * (B * 2) + ((ci / D) % 2) * 16);
   };
-  const uint32_t kdst = wave * B * ROW;                   // the wave's K rows
+  const uint32_t kdst = wave * RPW * ROW;                  // the wave's K rows
   const uint32_t vdst = SG::kK + wave * SG::kLoads * 1024;  // the wave's V chunks
 
   // LDS read offsets of this lane (stage-relative).  K tile tau of a pair:
@@ -273,10 +288,10 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
   const int tid = threadIdx.x;
 
-  // one stage's loads into buffer `buf`: block w of stage i of the window
-  // (clamped to the window's last block, so loads past it re-read it)
+  // one stage's loads into buffer `buf`: the wave's block of stage i of the
+  // window (clamped to the window's last block, so loads past it re-read it)
   auto dma = [&](int i, int cn, auto buf) {
-    const int bi = min(i * kWaves + wave, cn - 1);
+    const int bi = min(i * kStageBlocks + wblk, cn - 1);
     const size_t off = (size_t)__builtin_amdgcn_readfirstlane(tab[bi]) * blk_bytes;
     const gptr kb = uniform_ptr(kpool + off);
     const gptr vb = uniform_ptr(vpool + off);
@@ -303,6 +318,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
     for (int pp = 0; pp < 2; ++pp) {
       // scores: sc[rr][tau], lane's tokens 8 grp + 4 tau + r of the pair
       f32x4 sc[R][2];
+      PA_EXT_PRIO_MFMA();
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         u32x4 kb[KJ];
@@ -318,6 +334,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
                 __builtin_bit_cast(bf16x8, kb[kj]), qop[rr][kj], sc[rr][tau], 0, 0, 0);
         }
       }
+      PA_EXT_PRIO_VALU();
       // With a positive scale (kPos) the scores stay unscaled until the
       // exponent: x = masked raw score, the lane's max is scaled once, and
       // p = exp2(fma(x, scale, -m)).  Otherwise x is the scaled score.
@@ -380,6 +397,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
         for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(pr[e]);
         pk[rr] = v;
       }
+      PA_EXT_PRIO_MFMA();
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const u32x4 vb = *reinterpret_cast<const u32x4*>(d + pp * SG::kVPair + vread + nt * 256);
@@ -388,6 +406,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
           acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pk[rr], __builtin_bit_cast(bf16x8, vb),
                                                                acc[rr][nt], 0, 0, 0);
       }
+      PA_EXT_PRIO_VALU();
     }
   };
 
@@ -398,7 +417,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   // (c8, dim) of a stage holds tokens t0 + 8 c8 .. t0 + 8 c8 + 7.
   auto zero_tail = [&](int t0, auto buf) {
     uint8_t* d = sbuf.get(buf);
-    for (int idx = tid; idx < 8 * D; idx += kWaves * 64) {
+    for (int idx = tid; idx < 8 * D; idx += kExtWaves * 64) {
       const int c8 = idx / D, dim = idx % D;
       const int lim = L - (t0 + 8 * c8);   // leading tokens of the chunk that are valid
       if (lim >= 8) continue;
@@ -414,7 +433,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
 
   // the chunk's blocks, a table window at a time
   const int b_first = kv0 / B;
-  const int b_end = nst > 0 ? b_first + nst * kWaves : b_first;
+  const int b_end = nst > 0 ? b_first + nst * kStageBlocks : b_first;
   for (int w0 = b_first; w0 < b_end; w0 += kExtTabWindow) {
     const int cn = min(kExtTabWindow, b_end - w0);
     // every wave is past the previous window (its loads landed, its reads
@@ -422,9 +441,9 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
     // re-read the last one
     const int last_blk = max(0, (L - 1) / B);
     __syncthreads();
-    for (int e = tid; e < cn; e += kWaves * 64) tab[e] = trow[min(w0 + e, last_blk)];
+    for (int e = tid; e < cn; e += kExtWaves * 64) tab[e] = trow[min(w0 + e, last_blk)];
     __syncthreads();
-    const int ns = cn / kWaves;                     // stages of the window
+    const int ns = cn / kStageBlocks;               // stages of the window
     // prologue: stages 0 .. NST-2 in flight
     static_for<NST - 1>([&](auto j) { dma((int)j, cn, j); });
     for (int i0 = 0; i0 < ns; i0 += NST) {
@@ -437,7 +456,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
         __builtin_amdgcn_s_barrier();
         dma(i + NST - 1, cn, std::integral_constant<int, (j + NST - 1) % NST>{});
         if (i < ns) {
-          const int t0 = (w0 + i * kWaves) * B;
+          const int t0 = (w0 + i * kStageBlocks) * B;
           if (t0 + kStageTok > L) {   // the context ends in this stage (uniform)
             zero_tail(t0, j);
             // the zeros are in LDS before any wave reads the stage; the
@@ -492,7 +511,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
 }
 
 template <int D, int R, int NST, int WG, bool kPos>
-__global__ __launch_bounds__(kWaves * 64, WG) void extend_kernel(ExtendArgs a, int G, int qpt) {
+__global__ __launch_bounds__(kExtWaves * 64, WG) void extend_kernel(ExtendArgs a, int G, int qpt) {
   static_assert(NST >= 2 && NST <= 4, "two to four stage buffers");
   __shared__ __attribute__((aligned(1024))) uint8_t st0[ExtLds<D>::kBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[ExtLds<D>::kBuf];
@@ -504,7 +523,7 @@ __global__ __launch_bounds__(kWaves * 64, WG) void extend_kernel(ExtendArgs a, i
   int* pre = ext_lds;                 // [S + 1]
   int* wsum = ext_lds + a.num_seqs + 1;
   // a unit is the workgroup's 4R row tiles of qpt queries each, over one chunk
-  const int tiles = build_extend_plan(a, kWaves * R * qpt, pre, wsum);
+  const int tiles = build_extend_plan(a, kExtWaves * R * qpt, pre, wsum);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int units = tiles * a.num_kv_heads;
@@ -579,9 +598,9 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   // a positive scale folds into the exponent's fma; any other takes the
   // plain form
   if (a.scale_log2 > 0.f)
-    extend_kernel<D, C::R, C::NST, C::WG, true><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+    extend_kernel<D, C::R, C::NST, C::WG, true><<<dim3(grid), dim3(kExtWaves * 64), lds, st>>>(a, G, qpt);
   else
-    extend_kernel<D, C::R, C::NST, C::WG, false><<<dim3(grid), dim3(kWaves * 64), lds, st>>>(a, G, qpt);
+    extend_kernel<D, C::R, C::NST, C::WG, false><<<dim3(grid), dim3(kExtWaves * 64), lds, st>>>(a, G, qpt);
   return hipGetLastError();
 }
 
@@ -608,7 +627,7 @@ int extend_splits(int total_q, int num_q_heads, int num_kv_heads, int max_blocks
   const int G = num_q_heads / num_kv_heads;
   const int rows = head_dim == 128 ? ExtCfg<128>::R : ExtCfg<64>::R;
   const int wg = head_dim == 128 ? ExtCfg<128>::WG : ExtCfg<64>::WG;
-  const int qpu = kWaves * rows * std::max(1, 16 / G);
+  const int qpu = kExtWaves * rows * std::max(1, 16 / G);
   const int64_t units = ((int64_t)total_q + qpu - 1) / qpu * num_kv_heads;
   const int64_t want = 4LL * cu_count_ext() * wg;
   if (units <= 0 || units >= want) return 1;
