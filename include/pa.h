@@ -335,11 +335,11 @@ pa_status pa_extend(const pa_pool* pool, const void* k_pool, const void* v_pool,
  * Bytes of workspace pa_extend uses to split the contexts of a batch of
  * total_q query rows over num_seqs sequences (0: the batch fills the chip
  * without a split, or invalid arguments).  The split is chosen from these
- * sizes and the device: when the batch's workgroup units (4 waves of
- * 16-row tiles of one sequence and kv head) number fewer than four per
- * workgroup slot of the grid, each context is cut into up to 32 chunks of
- * at least 1024 tokens; the partials take total_q * num_q_heads * chunks *
- * (head_dim + 2) fp32 values.
+ * sizes and the device: when the batch's workgroup units (8 waves of two
+ * 16-row tiles of one sequence and kv head) number fewer than the grid's
+ * workgroups (one per CU), each context is cut into up to 32 chunks of
+ * equal token count (at least 1024 tokens); the partials take total_q *
+ * num_q_heads * chunks * (head_dim + 2) fp32 values.
  */
 size_t pa_extend_workspace_bytes(const pa_pool* pool, int32_t total_q, int32_t num_seqs,
                                  int32_t num_q_heads, int32_t max_blocks_per_seq);

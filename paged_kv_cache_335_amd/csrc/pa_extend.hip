@@ -82,6 +82,9 @@ constexpr int kStageTok = kStageBlocks * kExtBlock;   // 64 tokens a stage
 #define PA_EXT_PRIO_MFMA() ((void)0)
 #define PA_EXT_PRIO_VALU() ((void)0)
 #endif
+#ifndef PA_EXT_SPLIT_UNITS
+#define PA_EXT_SPLIT_UNITS 1
+#endif
 constexpr int kExtWaves = PA_EXT_WAVES;
 static_assert(kExtWaves == 4 || kExtWaves == 8, "four or eight waves share a stage");
 template <int D>
@@ -204,10 +207,15 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   const int last = min(ulast, first + R * qpt - 1);
   const int p_lo = first <= last ? L - n + first : p_max;  // nearest position of the wave's rows
 
-  // this chunk's tokens: [kv0, kv1), whole stages, within 0 .. p_max
+  // this chunk's tokens: [kv0, kv1), whole stages, within 0 .. p_max.
+  // Chunks hold the same number of tokens in every sequence (the table's
+  // capacity cut in `splits`), so units of long contexts cost the same
+  // whatever the batch's other lengths; a short context's later chunks are
+  // empty.
   int kv0 = 0, kv1 = p_max + 1;
   if (a.splits > 1) {
-    const int per = (L + a.splits * kStageTok - 1) / (a.splits * kStageTok) * kStageTok;
+    const int cap = a.max_blocks * B;
+    const int per = (cap + a.splits * kStageTok - 1) / (a.splits * kStageTok) * kStageTok;
     kv0 = chunk * per;
     kv1 = min(kv1, kv0 + per);
   }
@@ -620,16 +628,18 @@ bool extend_supported(pa_dtype dtype, int head_dim, int group, int block_size) {
 }
 
 // Split each context when the batch's units (each workgroup's row tiles of
-// one sequence and kv head) would not give every workgroup slot of the
-// grid about four: into as many chunks as make up for it, each at least
-// 1024 tokens, at most 32.
+// one sequence and kv head) would not give every workgroup slot of the grid
+// one: into as many chunks as make up for it, each at least 1024 tokens, at
+// most 32.  One unit per workgroup measured fastest for long prefixes: each
+// chunk adds a partial row (m, l and a fp32 o) per query head that the
+// combine reads back, traffic that finer splits multiply.
 int extend_splits(int total_q, int num_q_heads, int num_kv_heads, int max_blocks, int head_dim) {
   const int G = num_q_heads / num_kv_heads;
   const int rows = head_dim == 128 ? ExtCfg<128>::R : ExtCfg<64>::R;
   const int wg = head_dim == 128 ? ExtCfg<128>::WG : ExtCfg<64>::WG;
   const int qpu = kExtWaves * rows * std::max(1, 16 / G);
   const int64_t units = ((int64_t)total_q + qpu - 1) / qpu * num_kv_heads;
-  const int64_t want = 4LL * cu_count_ext() * wg;
+  const int64_t want = (int64_t)PA_EXT_SPLIT_UNITS * cu_count_ext() * wg;
   if (units <= 0 || units >= want) return 1;
   const int64_t by_len = std::max<int64_t>(1, (int64_t)max_blocks * kExtBlock / 1024);
   const int64_t k = std::min<int64_t>({(want + units - 1) / units, by_len, 32});

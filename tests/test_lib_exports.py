@@ -126,15 +126,15 @@ def test_extend_workspace_sizing():
     """pa_extend splits contexts only for a batch whose units (8 waves x 2 row
     tiles of one sequence and kv head; 64 queries at 4 query heads per kv
     head) give the grid (one workgroup per CU, 256 CUs when no GPU is
-    visible) fewer than four each: then into enough chunks of at least 1024
+    visible) fewer than one each: then into enough chunks of at least 1024
     tokens, at most 32, each holding (m, l, o[128]) fp32 per row."""
     import paged_kv_cache_335_amd as pk
     L = pk.lib()
     d = _desc(nb=8192)
     # 32 sequences x 256 queries: 128 x 8 = 1024 units, no split
     assert L.pa_extend_workspace_bytes(ctypes.byref(d), 8192, 32, 32, 4096) == 0
-    # 2 sequences x 256 queries over 64k-token tables: 64 units -> 16 chunks
-    n = 512 * 32 * 16
+    # 2 sequences x 256 queries over 64k-token tables: 64 units -> 4 chunks
+    n = 512 * 32 * 4
     assert L.pa_extend_workspace_bytes(ctypes.byref(d), 512, 2, 32, 4096) == \
         2 * _align(n * 4) + _align(n * 128 * 4)
     # one query over a 4096-token table: 8 units, but chunks of >= 1024 tokens -> 4
