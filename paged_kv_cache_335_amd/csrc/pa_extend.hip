@@ -127,23 +127,73 @@ struct ExtLds {
   static constexpr int kBuf = StageGeom<D>::kK + StageGeom<D>::kV;
 };
 
-// Plan in LDS: units before each sequence (prefix sums of
-// ceil(n_s / qpu) * splits, qpu = queries of one unit).
-__device__ int build_extend_plan(const ExtendArgs& a, int qpu, int* pre, int* wsum) {
+// Work order.  A unit's cost is about its sequence's context length (every
+// row tile of a sequence streams the same context), and lengths in a batch
+// can differ by orders of magnitude.  Units are therefore handed out
+// longest sequence first, in a snake over the grid (round r gives rank
+// r * grid + b to workgroup b for even r and r * grid + grid - 1 - b for
+// odd r), which pairs each workgroup's long units with shorter ones.  Every
+// workgroup computes the same order: a bitonic sort of (length, sequence)
+// keys in LDS, for batches of up to kExtSortMax sequences; larger batches
+// keep sequence order (their many units even out without it).
+constexpr int kExtSortMax = 1024;
+
+__device__ void sort_desc(unsigned long long* key, int n) {  // n a power of two
+  for (int k = 2; k <= n; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = key[i], y = key[ixj];
+          if ((i & k) == 0 ? x < y : x > y) {
+            key[i] = y;
+            key[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// Plan in LDS: ord[i] = the sequence at position i of the work order, and
+// pre[i] = units before position i (units of a sequence: ceil(n_s / qpu)
+// row-tile groups times `splits` chunks).  Returns the total.
+__device__ int build_extend_plan(const ExtendArgs& a, int qpu, int* pre, int* wsum,
+                                 unsigned long long* key, int* ord) {
   const int S = a.num_seqs, T_ = blockDim.x, t = threadIdx.x;
-  const int C = (S + T_ - 1) / T_;
-  const int s0 = min(S, t * C), s1 = min(S, s0 + C);
-  int nt = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
-    nt += (n + qpu - 1) / qpu * a.splits;
+  const int cap = a.max_blocks * kExtBlock;
+  if (S > 1 && S <= kExtSortMax) {
+    int n = 2;
+    while (n < S) n <<= 1;
+    for (int i = t; i < n; i += T_) {
+      unsigned long long k = 0;
+      if (i < S) {
+        const int L = min(max(a.context_lens[i], 0), cap);
+        k = ((unsigned long long)L << 32) | (0xffffffffu - (unsigned)i);
+      }
+      key[i] = k;
+    }
+    __syncthreads();
+    sort_desc(key, n);
+    for (int i = t; i < S; i += T_) ord[i] = (int)(0xffffffffu - (unsigned)(key[i] & 0xffffffffu));
+  } else {
+    for (int i = t; i < S; i += T_) ord[i] = i;
   }
+  __syncthreads();
+  const int C = (S + T_ - 1) / T_;
+  const int i0 = min(S, t * C), i1 = min(S, i0 + C);
+  auto units_of = [&](int i) {
+    const int s = ord[i];
+    const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
+    return (n + qpu - 1) / qpu * a.splits;
+  };
+  int nt = 0;
+  for (int i = i0; i < i1; ++i) nt += units_of(i);
   int total;
   int run = block_excl_scan(nt, wsum, &total);
-  for (int s = s0; s < s1; ++s) {
-    pre[s] = run;
-    const int n = max(0, a.q_start[s + 1] - a.q_start[s]);
-    run += (n + qpu - 1) / qpu * a.splits;
+  for (int i = i0; i < i1; ++i) {
+    pre[i] = run;
+    run += units_of(i);
   }
   if (t == 0) pre[S] = total;
   __syncthreads();
@@ -526,26 +576,32 @@ __global__ __launch_bounds__(kExtWaves * 64, WG) void extend_kernel(ExtendArgs a
   __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? ExtLds<D>::kBuf : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? ExtLds<D>::kBuf : 16];
   __shared__ int tab_lds[kExtTabWindow];
+  __shared__ unsigned long long sort_key[kExtSortMax];
   extern __shared__ int ext_lds[];
   const StageBufs sbuf{st0, st1, st2, st3};
   int* pre = ext_lds;                 // [S + 1]
-  int* wsum = ext_lds + a.num_seqs + 1;
-  // a unit is the workgroup's 4R row tiles of qpt queries each, over one chunk
-  const int tiles = build_extend_plan(a, kExtWaves * R * qpt, pre, wsum);
+  int* ord = ext_lds + a.num_seqs + 1;  // [S]
+  int* wsum = ord + a.num_seqs;         // [8]
+  // a unit is the workgroup's W R row tiles of qpt queries each, over one chunk
+  const int tiles = build_extend_plan(a, kExtWaves * R * qpt, pre, wsum, sort_key, ord);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int units = tiles * a.num_kv_heads;
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+  const int grid = gridDim.x;
+  for (int r = 0;; ++r) {
+    const int u = r * grid + ((r & 1) ? grid - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (u >= units) break;  // ranks grow with r: no later round has work either
     const int g = u % a.num_kv_heads, k = u / a.num_kv_heads;
     int lo = 0, hi = a.num_seqs - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= k) lo = mid; else hi = mid - 1;
     }
-    int s = lo;
-    while (pre[s + 1] <= k) ++s;  // skip sequences without queries
-    s = __builtin_amdgcn_readfirstlane(s);
-    const int local = k - pre[s];
+    int i = lo;
+    while (pre[i + 1] <= k) ++i;  // skip sequences without queries
+    i = __builtin_amdgcn_readfirstlane(i);
+    const int s = __builtin_amdgcn_readfirstlane(ord[i]);
+    const int local = k - pre[i];
     extend_unit<D, R, NST, kPos>(a, G, qpt, s, local / a.splits, local % a.splits, g, wave, lane,
                                  sbuf, tab_lds);
   }
@@ -601,7 +657,7 @@ hipError_t launch_extend_d(const ExtendArgs& a, int G, hipStream_t st) {
   using C = ExtCfg<D>;
   const int qpt = std::max(1, 16 / G);
   // persistent grid: C::WG workgroups per CU take the units in turn
-  const size_t lds = ((size_t)a.num_seqs + 1 + 8) * sizeof(int);
+  const size_t lds = (2 * (size_t)a.num_seqs + 1 + 8) * sizeof(int);
   const int grid = std::max(1, std::min(cu_count_ext() * C::WG, 1 << 16));
   // a positive scale folds into the exponent's fma; any other takes the
   // plain form

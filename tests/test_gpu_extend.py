@@ -147,6 +147,27 @@ def test_extend_many_sequences_and_determinism(pk):
     assert np.abs(a - ref).max() <= 2e-2
 
 
+def test_extend_work_order_mixed_lengths(pk):
+    """Units go out longest sequence first (a sort of up to 1024 sequences
+    in LDS) in a snake over the grid: every unit exactly once whatever the
+    order.  A batch of widely mixed lengths with some query-less sequences,
+    then one past the sort's limit (sequence order), both against the
+    oracle."""
+    rng = np.random.default_rng(350)
+    for S, Lmax in ((300, 3000), (1100, 80)):
+        lens = np.maximum(1, (rng.lognormal(0, 1.2, S) * Lmax / 8).astype(int))
+        lens = np.minimum(lens, Lmax)
+        ns = np.minimum(lens, rng.integers(0, 24, S))
+        ns[rng.random(S) < 0.2] = 0
+        k, v, q, qs, tables, lens = _case(rng, lens.tolist(), ns.tolist(), 8, 2, 128,
+                                          nb=max(4000, int(lens.sum()) // 16 + 64))
+        ref = oracle.extend(k, v, q, qs, tables, lens, 128 ** -0.5)
+        got = _run(pk, k, v, q, qs, tables, lens, 128 ** -0.5)
+        err = np.abs(got - ref)
+        _log(f"S={S}: max|err| {err.max():.3e}")
+        assert np.isfinite(got).all() and err.max() <= 2e-2
+
+
 def test_extend_nan_in_unused_slots_never_reaches_output(pk):
     """Slots past each context (the tail of the last block, unused blocks)
     hold NaN: masked tokens contribute nothing."""
