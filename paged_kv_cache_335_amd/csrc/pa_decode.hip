@@ -525,10 +525,113 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(vb[nt]), acc[nt], 0, 0, 0);
   };
 
+  // One whole 32-token block (B = 32): two q.K tiles whose MFMA rows take
+  // tokens 8 (m / 4) + 4 tau + m % 4, so that a lane's eight scores are
+  // tokens 8 grp .. 8 grp + 7, the k entries of its P.V operand; V comes as
+  // one 16-byte load per dim (those eight tokens of a dim-major row), and
+  // P.V runs twice per 16 dims, on P's high and low bf16 parts (the same
+  // precision as p_split).  Every lane reads whole 64-byte V rows and whole
+  // K rows, so no line is fetched twice.
+  auto tile32 = [&](const u32x4 (*kb)[KJ], u32x4* vb, int valid) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      sc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
+        sc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[tau][kj]),
+                                                          qop[kj], sc[tau], 0, 0, 0);
+    }
+    float x[8];  // token 8 grp + e
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sc[e / 4][e % 4] * a.scale_log2;
+    if (valid < 32) {
+      const int t = 8 * grp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t + e >= valid) x[e] = kNegInf;
+      uint32_t m[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        m[w] = (t + 2 * w < valid ? 0x0000ffffu : 0u) | (t + 2 * w + 1 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vb[nt] = u32x4{vb[nt].x & m[0], vb[nt].y & m[1],
+                                                      vb[nt].z & m[2], vb[nt].w & m[3]};
+    }
+    float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    if (__ballot(bm > m_ref + kSlack)) {  // rare: move the reference, rescale
+      bm = max_xor32(max_xor16(bm));
+      const float m_new = fmaxf(m_ref, bm);
+      const float alpha = fexp2(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+    }
+    float pr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = fexp2(x[e] - m_ref);
+    l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    // high part: truncation to bf16; low part: the residual, rounded
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = __float_as_uint(pr[2 * w]), a1 = __float_as_uint(pr[2 * w + 1]);
+      hi[w] = (a0 >> 16) | (a1 & 0xffff0000u);
+      const bf16x2 l2 = {static_cast<__bf16>(pr[2 * w] - bf16_hi(a0)),
+                         static_cast<__bf16>(pr[2 * w + 1] - bf16_hi(a1))};
+      lo[w] = __builtin_bit_cast(uint32_t, l2);
+    }
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, vb[nt]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, v, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, v, acc[nt], 0, 0, 0);
+    }
+  };
+
+  const int nblk = je - jb;
+  if constexpr (B == 32) {
+    u32x4 kring[NBUF][2][KJ];
+    u32x4 vring[NBUF][NT];
+    // lane offsets in a block: K row of MFMA row col in tile tau, dims
+    // kj*32 + grp*8 ..; V row of dim col (+ nt*16), tokens 8 grp .. + 7
+    const uint32_t krow0 = (8 * (col / 4) + col % 4) * ROW + grp * 16;
+    const uint32_t voff32 = col * (B * 2) + grp * 16;
+    for (int c0 = 0; c0 < nblk; c0 += 64) {
+      const int cnt = min(64, nblk - c0);
+      const int tab = trow[jb + c0 + min(lane, cnt - 1)];
+      auto load = [&](int i, auto slot) {
+        const size_t off = (size_t)__builtin_amdgcn_readlane(tab, i) * blk_bytes;
+        const gptr kblk = uniform_ptr(kpool + off);
+        const gptr vblk = uniform_ptr(vpool + off);
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int kj = 0; kj < KJ; ++kj)
+            kring[slot][tau][kj] = ldg_stream<u32x4>(kblk + krow0 + tau * 4 * ROW + kj * 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          vring[slot][nt] = ldg_stream<u32x4>(vblk + voff32 + nt * 16 * (B * 2));
+      };
+      // units start on block boundaries (pieces are ranges of whole blocks)
+      auto compute = [&](int i, auto slot) {
+        tile32(kring[slot], vring[slot], u.t1 - (u.t0 + (c0 + i) * B));
+      };
+      block_ring<NBUF>(cnt, load, compute);
+    }
+  } else {
   u32x4 kring[NBUF][KJ];
   u32x2 vring[NBUF][NT];
 
-  const int nblk = je - jb;
   for (int c0 = 0; c0 < nblk; c0 += 64) {
     const int cnt = min(64, nblk - c0);
     // physical block ids of up to 64 blocks, one per lane (every lane loads a
@@ -569,6 +672,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
     };
 
     block_ring<NBUF>(ntile, load, compute);
+  }
   }
 
   if (new_tok) {
@@ -876,14 +980,15 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int G,
 }
 
 template <int D, int B, int NBUF>
-__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma_kernel(DecodeArgs a, int G) {
+__global__ __launch_bounds__(kWaves * 64, B == 32 ? 1 : PA_MFMA_MIN_WG) void decode_mfma_kernel(
+    DecodeArgs a, int G) {
   decode_mfma_body<D, B, NBUF, false>(a, G, nullptr);
 }
 
 // A decode step: the new tokens' blocks arrive with the kernel arguments.
 template <int D, int B, int NBUF>
-__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_step_kernel(DecodeArgs a, int G,
-                                                                                  StepBlocks nb) {
+__global__ __launch_bounds__(kWaves * 64, B == 32 ? 1 : PA_MFMA_MIN_WG) void decode_step_kernel(
+    DecodeArgs a, int G, StepBlocks nb) {
   decode_mfma_body<D, B, NBUF, true>(a, G, nb.blk);
 }
 
