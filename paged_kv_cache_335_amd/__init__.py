@@ -164,14 +164,36 @@ def fp8_region_bytes(block_size: int, head_dim: int):
     return block_size * head_dim + 4 * block_size, block_size * head_dim
 
 
+def side_by_side(buf: torch.Tensor, rk: int):
+    """(k_pool, v_pool) views of one uint8 buffer [num_blocks][num_kv_heads]
+    [R_k + R_v] whose (block, kv head) regions hold K (codes and scales) and
+    then V: the 8-bit layout the library reads with one contiguous run per
+    (block, kv head)."""
+    return buf[:, :, :rk], buf[:, :, rk:]
+
+
+def fp8_pools_side_by_side(k_pool, v_pool, device="cuda"):
+    """Copy two-buffer 8-bit pools (arrays or tensors [nb][H][R_k], [nb][H]
+    [R_v]) into one side-by-side buffer on `device`; returns its views."""
+    k = torch.as_tensor(k_pool)
+    v = torch.as_tensor(v_pool)
+    buf = torch.empty((k.shape[0], k.shape[1], k.shape[2] + v.shape[2]), dtype=torch.uint8,
+                      device=device)
+    kv, vv = side_by_side(buf, k.shape[2])
+    kv.copy_(k)
+    vv.copy_(v)
+    return kv, vv
+
+
 def alloc_pools(num_blocks, num_kv_heads, head_dim, block_size=16, dtype=torch.bfloat16,
                 device="cuda"):
     """Uninitialised (k_pool, v_pool) in the library's layout; dtype
-    torch.uint8 gives 8-bit (E4M3 + scale) pools."""
+    torch.uint8 gives 8-bit (E4M3 + scale) pools, as views of one buffer
+    with each (block, kv head)'s K and V regions side by side."""
     if dtype == torch.uint8:
         rk, rv = fp8_region_bytes(block_size, head_dim)
-        return (torch.empty((num_blocks, num_kv_heads, rk), dtype=dtype, device=device),
-                torch.empty((num_blocks, num_kv_heads, rv), dtype=dtype, device=device))
+        buf = torch.empty((num_blocks, num_kv_heads, rk + rv), dtype=dtype, device=device)
+        return side_by_side(buf, rk)
     return (torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype,
                         device=device),
             torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype,
@@ -184,6 +206,27 @@ def _dev(t: torch.Tensor, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _is_side_by_side(k_pool: torch.Tensor, v_pool: torch.Tensor) -> bool:
+    """k_pool / v_pool are the K and V views of one side-by-side 8-bit
+    buffer (see side_by_side)."""
+    if k_pool.dtype != torch.uint8 or k_pool.dim() != 3 or v_pool.dim() != 3:
+        return False
+    nb, h, rk = k_pool.shape
+    r = rk + v_pool.shape[2]
+    want = (h * r, r, 1)
+    return (k_pool.stride() == want and v_pool.stride() == want and
+            v_pool.data_ptr() == k_pool.data_ptr() + rk and
+            tuple(v_pool.shape[:2]) == (nb, h))
+
+
+def _pools(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    """Device pointers of a pool pair: two contiguous buffers, or the views
+    of one side-by-side 8-bit buffer."""
+    if _is_side_by_side(k_pool, v_pool) and k_pool.is_cuda:
+        return ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr())
+    return _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool")
 
 
 def _stream(stream):
@@ -227,7 +270,7 @@ def pa_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None):
         raise TypeError("k_new/v_new must have the pool's element type (bf16 for 8-bit)")
     if T == 0:
         return
-    st = _lib.pa_kv_write(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_kv_write(ctypes.byref(desc), *_pools(k_pool, v_pool),
                           _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                           _dev(slot_mapping, "slot_mapping"), T, _stream(stream))
     _check(st, "pa_kv_write")
@@ -298,7 +341,7 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
     never allocates)."""
     desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
     ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device)
-    st = _lib.pa_decode(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_decode(ctypes.byref(desc), *_pools(k_pool, v_pool),
                         _dev(q, "q"), S, Hq, _dev(block_tables, "block_tables"), maxB,
                         _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
                         int(partition_tokens), ws_ptr, ws_bytes, _stream(stream))
@@ -320,7 +363,7 @@ def pa_decode_shared(q, k_pool, v_pool, block_tables, context_lens, scale, group
     ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device,
                                   shared=n > 0)
     st = _lib.pa_decode_shared(
-        ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(q, "q"), S, Hq,
+        ctypes.byref(desc), *_pools(k_pool, v_pool), _dev(q, "q"), S, Hq,
         _dev(block_tables, "block_tables"), maxB, _dev(context_lens, "context_lens"),
         float(scale), _dev(out, "out"), int(partition_tokens), n,
         _dev(group_start, "group_start") if n else ctypes.c_void_p(0),
@@ -354,7 +397,7 @@ def pa_decode_step(q, k_pool, v_pool, k_new, v_new, block_tables, lens_in, lens_
     ws_ptr, ws_bytes = _workspace(desc, S, Hq, maxB, partition_tokens, workspace, q.device,
                                   shared=n > 0)
     st = _lib.pa_decode_step(
-        ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(q, "q"),
+        ctypes.byref(desc), *_pools(k_pool, v_pool), _dev(q, "q"),
         _dev(k_new, "k_new"), _dev(v_new, "v_new"), S, Hq, _dev(block_tables, "block_tables"),
         maxB, _dev(lens_in, "lens_in"), _dev(lens_out, "lens_out"), nb_ptr, float(scale),
         _dev(out, "out"), int(partition_tokens), n,
@@ -372,8 +415,7 @@ def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
     if out is None:
         raise ValueError("pa_decode_noalloc needs out (it allocates nothing)")
     desc, S, Hq, maxB, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
-    st = _lib.pa_decode_noalloc(ctypes.byref(desc), _dev(k_pool, "k_pool"),
-                                _dev(v_pool, "v_pool"), _dev(q, "q"), S, Hq,
+    st = _lib.pa_decode_noalloc(ctypes.byref(desc), *_pools(k_pool, v_pool), _dev(q, "q"), S, Hq,
                                 _dev(block_tables, "block_tables"), maxB,
                                 _dev(context_lens, "context_lens"), float(scale),
                                 _dev(out, "out"), int(partition_tokens), _stream(stream))
@@ -419,7 +461,7 @@ def pa_extend(q, k_pool, v_pool, q_start, block_tables, context_lens, scale, out
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.pa_extend(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_extend(ctypes.byref(desc), *_pools(k_pool, v_pool),
                         _dev(q, "q"), T, _dev(q_start, "q_start"), S, Hq,
                         _dev(block_tables, "block_tables"), block_tables.shape[1],
                         _dev(context_lens, "context_lens"), float(scale), _dev(out, "out"),
@@ -436,14 +478,19 @@ def pa_block_copy(k_pool, v_pool, pairs, stream=None):
     n = pairs.numel() // 2
     if n == 0:
         return
-    st = _lib.pa_block_copy(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_block_copy(ctypes.byref(desc), *_pools(k_pool, v_pool),
                             _dev(pairs, "pairs"), n, _stream(stream))
     _check(st, "pa_block_copy")
 
 
 def alloc_host_pools(num_host_blocks, k_pool, v_pool):
     """Pinned host pools of num_host_blocks blocks with k_pool / v_pool's
-    per-block layout (swap space for pa_block_swap)."""
+    per-block layout (swap space for pa_block_swap); side-by-side 8-bit
+    pools get a side-by-side host buffer."""
+    if _is_side_by_side(k_pool, v_pool):
+        buf = torch.empty((num_host_blocks, k_pool.shape[1], k_pool.shape[2] + v_pool.shape[2]),
+                          dtype=torch.uint8, pin_memory=True)
+        return side_by_side(buf, k_pool.shape[2])
     return (torch.empty((num_host_blocks,) + tuple(k_pool.shape[1:]), dtype=k_pool.dtype,
                         pin_memory=True),
             torch.empty((num_host_blocks,) + tuple(v_pool.shape[1:]), dtype=v_pool.dtype,
@@ -455,10 +502,14 @@ def pa_block_swap(k_pool, v_pool, host_k, host_v, pairs, direction, stream=None)
     PA_SWAP_OUT copies device block src to host block dst, PA_SWAP_IN host
     block src to device block dst, for each (src, dst) row of ``pairs``."""
     desc = pool_desc(k_pool, v_pool)
+    sbs = _is_side_by_side(k_pool, v_pool)
+    if sbs != _is_side_by_side(host_k, host_v):
+        raise ValueError("host_k / host_v must share the pools' layout (side-by-side 8-bit "
+                         "regions or two buffers)")
     for t, pool, name in ((host_k, k_pool, "host_k"), (host_v, v_pool, "host_v")):
         if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
             raise TypeError(f"{name} must be a pinned host tensor")
-        if not t.is_contiguous() or t.dtype != pool.dtype or \
+        if not (sbs or t.is_contiguous()) or t.dtype != pool.dtype or \
                 tuple(t.shape[1:]) != tuple(pool.shape[1:]):
             raise ValueError(f"{name} must be contiguous with the pool's block layout")
     if host_k.shape[0] != host_v.shape[0]:
@@ -468,7 +519,7 @@ def pa_block_swap(k_pool, v_pool, host_k, host_v, pairs, direction, stream=None)
     n = pairs.numel() // 2
     if n == 0:
         return
-    st = _lib.pa_block_swap(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_block_swap(ctypes.byref(desc), *_pools(k_pool, v_pool),
                             ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
                             int(host_k.shape[0]), _dev(pairs, "pairs"), n, int(direction),
                             _stream(stream))
@@ -509,7 +560,7 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, block_tables, seq_i
         raise ValueError("seq_ids, positions and slot_mapping must have one entry per token")
     if T == 0:
         return
-    st = _lib.pa_kv_append(ctypes.byref(desc), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+    st = _lib.pa_kv_append(ctypes.byref(desc), *_pools(k_pool, v_pool),
                            _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                            _dev(slot_mapping, "slot_mapping"), T,
                            _dev(block_tables, "block_tables"), block_tables.shape[1],

@@ -28,13 +28,36 @@ bool pool_ok(const pa_pool* p) {
   return p->dtype == PA_F32 || p->dtype == PA_BF16;
 }
 
-// Bytes of one block (every kv head) in the K buffer and in the V buffer; an
-// 8-bit K region also carries the block's scales.
-size_t block_bytes(const pa_pool* p, bool v_side) {
+// Bytes of one (block, kv head) region in the K buffer and in the V buffer;
+// an 8-bit K region also carries the block's scales.
+size_t region_bytes(const pa_pool* p, bool v_side) {
   const size_t B = (size_t)p->block_size, d = (size_t)p->head_dim;
-  size_t per_head = B * d * (p->dtype == PA_F32 ? 4 : p->dtype == PA_BF16 ? 2 : 1);
-  if (p->dtype == PA_FP8_E4M3 && !v_side) per_head += 4 * B;
-  return (size_t)p->num_kv_heads * per_head;
+  size_t r = B * d * (p->dtype == PA_F32 ? 4 : p->dtype == PA_BF16 ? 2 : 1);
+  if (p->dtype == PA_FP8_E4M3 && !v_side) r += 4 * B;
+  return r;
+}
+
+// An 8-bit pool in one buffer: the K and V regions of each (block, kv head)
+// side by side, v_pool = k_pool + R_k.
+bool side_by_side(const pa_pool* p, const void* k_pool, const void* v_pool) {
+  return p->dtype == PA_FP8_E4M3 && k_pool &&
+         static_cast<const uint8_t*>(v_pool) ==
+             static_cast<const uint8_t*>(k_pool) + region_bytes(p, false);
+}
+
+// Bytes from one (block, kv head) region to the next in each buffer.
+size_t region_stride(const pa_pool* p, const void* k_pool, const void* v_pool, bool v_side) {
+  if (side_by_side(p, k_pool, v_pool)) return region_bytes(p, false) + region_bytes(p, true);
+  return region_bytes(p, v_side);
+}
+
+// Bytes of one block (every kv head) in the K buffer and in the V buffer, as
+// block copies and swaps move them: with side-by-side 8-bit regions the K
+// buffer's block holds both, and nothing is left to move on the V side.
+size_t block_bytes(const pa_pool* p, const void* k_pool, const void* v_pool, bool v_side) {
+  if (side_by_side(p, k_pool, v_pool))
+    return v_side ? 0 : (size_t)p->num_kv_heads * region_stride(p, k_pool, v_pool, false);
+  return (size_t)p->num_kv_heads * region_bytes(p, v_side);
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -210,6 +233,8 @@ pa_status decode_impl(const pa_pool* pool, const void* k_pool, const void* v_poo
   DecodeArgs a{};
   a.k_pool = k_pool;
   a.v_pool = v_pool;
+  a.k_rstride = (int32_t)region_stride(pool, k_pool, v_pool, false);
+  a.v_rstride = (int32_t)region_stride(pool, k_pool, v_pool, true);
   a.q = q;
   a.out = out;
   a.block_tables = block_tables;
@@ -302,7 +327,9 @@ pa_status pa_kv_write(const pa_pool* pool, void* k_pool, void* v_pool, const voi
   }
   hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
                                        pool->num_kv_heads, pool->block_size, pool->head_dim,
-                                       pool->dtype, nullptr, 0, nullptr, nullptr, st);
+                                       pool->dtype, nullptr, 0, nullptr, nullptr,
+                                       region_stride(pool, k_pool, v_pool, false),
+                                       region_stride(pool, k_pool, v_pool, true), st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -336,7 +363,9 @@ pa_status pa_kv_append(const pa_pool* pool, void* k_pool, void* v_pool, const vo
   hipError_t e = pakv::launch_kv_write(k_pool, v_pool, k_new, v_new, slot_mapping, T,
                                        pool->num_kv_heads, pool->block_size, pool->head_dim,
                                        pool->dtype, block_tables,
-                                       max_blocks_per_seq, seq_ids, positions, st);
+                                       max_blocks_per_seq, seq_ids, positions,
+                                       region_stride(pool, k_pool, v_pool, false),
+                                       region_stride(pool, k_pool, v_pool, true), st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -556,7 +585,8 @@ pa_status pa_block_copy(const pa_pool* pool, void* k_pool, void* v_pool, const i
       if (is_src[(size_t)b] && is_dst[(size_t)b]) return PA_EINVAL;
   }
   hipError_t e = pakv::launch_block_copy(k_pool, v_pool, pairs, num_pairs,
-                                         block_bytes(pool, false), block_bytes(pool, true), st);
+                                         block_bytes(pool, k_pool, v_pool, false),
+                                         block_bytes(pool, k_pool, v_pool, true), st);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -590,7 +620,11 @@ pa_status pa_block_swap(const pa_pool* pool, void* k_pool, void* v_pool, void* h
       seen[(size_t)d] = 1;
     }
   }
-  const size_t kb = block_bytes(pool, false), vb = block_bytes(pool, true);
+  // host buffers take the device pools' layout: side-by-side 8-bit regions
+  // in one host buffer too
+  if (side_by_side(pool, k_pool, v_pool) != side_by_side(pool, host_k, host_v)) return PA_EINVAL;
+  const size_t kb = block_bytes(pool, k_pool, v_pool, false);
+  const size_t vb = block_bytes(pool, k_pool, v_pool, true);
   hipError_t e = dir == PA_SWAP_OUT
                      ? pakv::launch_block_move(k_pool, v_pool, dk, dv, pairs, num_pairs, kb, vb, st)
                      : pakv::launch_block_move(dk, dv, k_pool, v_pool, pairs, num_pairs, kb, vb, st);

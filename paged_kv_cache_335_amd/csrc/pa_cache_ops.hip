@@ -116,12 +116,15 @@ __device__ __forceinline__ uint8_t to_e4m3(float x) {
 // 8-bit slot write: one workgroup per new token, one wave per (kv head,
 // K or V) row at a time.  K region of (block b, kv head g): [B*d codes,
 // token-major r*d + e][scale groups: per 4 slots, 4 K then 4 V bf16 scales];
-// V region: [B*d codes, dim-major e*B + r].
+// V region: [B*d codes, dim-major e*B + r].  Region (b, g) starts at
+// (b * H + g) * k_rstride in k_pool and at (b * H + g) * v_rstride in
+// v_pool (the two strides are equal when K and V regions alternate in one
+// buffer, with v_pool = k_pool + R_k).
 __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int64_t* __restrict__ slots, int32_t num_kv_heads, int32_t block_size,
-    int32_t head_dim, TableArgs ta) {
+    int32_t head_dim, size_t k_rstride, size_t v_rstride, TableArgs ta) {
   const int i = blockIdx.x;
   const int64_t slot = slots[i];
   if (slot < 0) return;
@@ -129,14 +132,13 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
   update_table(ta, i, blk, block_size);
   const int r = static_cast<int>(slot % block_size);
   const int B = block_size, d = head_dim;
-  const size_t k_region = (size_t)B * d + 4u * (size_t)B, v_region = (size_t)B * d;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int row = wave; row < 2 * num_kv_heads; row += kThreads / 64) {
     const bool is_v = row >= num_kv_heads;
     const int g = is_v ? row - num_kv_heads : row;
     const uint16_t* src = (is_v ? v_new : k_new) + ((size_t)i * num_kv_heads + g) * d;
-    uint8_t* kreg = k_pool + ((size_t)blk * num_kv_heads + g) * k_region;
-    uint8_t* vreg = v_pool + ((size_t)blk * num_kv_heads + g) * v_region;
+    uint8_t* kreg = k_pool + ((size_t)blk * num_kv_heads + g) * k_rstride;
+    uint8_t* vreg = v_pool + ((size_t)blk * num_kv_heads + g) * v_rstride;
     float amax = 0.f;  // NaN inputs are skipped by fmaxf
     for (int e = lane; e < d; e += 64)
       amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)src[e] << 16)));
@@ -235,7 +237,8 @@ hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const 
                            const int64_t* slots, int32_t T, int32_t num_kv_heads,
                            int32_t block_size, int32_t head_dim, pa_dtype dtype,
                            int32_t* block_tables, int32_t max_blocks, const int32_t* seq_ids,
-                           const int32_t* positions, hipStream_t st) {
+                           const int32_t* positions, size_t k_rstride, size_t v_rstride,
+                           hipStream_t st) {
   if (T <= 0) return hipSuccess;
   auto kp = static_cast<uint8_t*>(k_pool);
   auto vp = static_cast<uint8_t*>(v_pool);
@@ -245,7 +248,8 @@ hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new, const 
   if (dtype == PA_FP8_E4M3)
     kv_write_fp8_kernel<<<T, kThreads, 0, st>>>(kp, vp, static_cast<const uint16_t*>(k_new),
                                                 static_cast<const uint16_t*>(v_new), slots,
-                                                num_kv_heads, block_size, head_dim, ta);
+                                                num_kv_heads, block_size, head_dim, k_rstride,
+                                                v_rstride, ta);
   else if (dtype == PA_BF16)
     kv_write_kernel<uint16_t><<<T, kThreads, 0, st>>>(kp, vp, kn, vn, slots, num_kv_heads,
                                                       block_size, head_dim, ta);

@@ -759,8 +759,6 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   constexpr int NT = D / 16;              // P.V MFMAs per block
   constexpr uint32_t QROW = D * 2;         // bytes per bf16 q row
   constexpr uint32_t SOFF = B * D;         // offset of the scales in a K region
-  constexpr uint32_t RBK = B * D + 4 * B;  // K region bytes per (block, kv head)
-  constexpr uint32_t RBV = B * D;          // V region bytes per (block, kv head)
 
   const int s = u.s, g = u.g;
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
@@ -774,10 +772,13 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   load_q_operand<KJ>(a, G, u, col, QROW,
                      [&](int kj) { return grp * 32 + (kj >> 1) * 128 + (kj & 1) * 16; }, qop);
 
-  const size_t kblk_bytes = (size_t)a.num_kv_heads * RBK;
-  const size_t vblk_bytes = (size_t)a.num_kv_heads * RBV;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * RBK;
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * RBV;
+  // regions (block b, kv head g) at (b * H + g) * stride: R_k / R_v for two
+  // buffers, R_k + R_v when K and V regions alternate in one buffer (one
+  // contiguous read of a block's K and V per kv head)
+  const size_t kblk_bytes = (size_t)a.num_kv_heads * a.k_rstride;
+  const size_t vblk_bytes = (size_t)a.num_kv_heads * a.v_rstride;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * a.k_rstride;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * a.v_rstride;
   // K row (token) col; scales of tokens 4*grp..+4 (with B = 8, rows and
   // scale groups are taken modulo the block); V: load h gives lane l the 16
   // tokens of dim h*64 + l (two 8-token halves with B = 8)

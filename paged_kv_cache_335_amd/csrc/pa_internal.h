@@ -89,6 +89,11 @@ struct DecodeArgs {
   int32_t own_row0;        // first per-sequence row of own segments (groups only)
   int32_t sh_row0;         // first per-sequence row of shared segments (groups only)
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
+  // 8-bit pools: bytes from one (block, kv head) region to the next in
+  // k_pool and in v_pool -- R_k and R_v for two buffers, R_k + R_v for both
+  // when the regions sit side by side in one buffer
+  int32_t k_rstride;
+  int32_t v_rstride;
 };
 
 // The block of each sequence's new token in a decode step (-1: the table's
@@ -150,12 +155,13 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int head_dim, int 
 
 // block_tables == nullptr: no table update (plain slot write).  For
 // PA_FP8_E4M3 pools k_new / v_new are bf16 and are quantised.
+// k_rstride / v_rstride: 8-bit pools' region strides (as in DecodeArgs).
 hipError_t launch_kv_write(void* k_pool, void* v_pool, const void* k_new,
                            const void* v_new, const int64_t* slots, int32_t T,
                            int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                            pa_dtype dtype, int32_t* block_tables, int32_t max_blocks,
                            const int32_t* seq_ids, const int32_t* positions,
-                           hipStream_t stream);
+                           size_t k_rstride, size_t v_rstride, hipStream_t stream);
 
 hipError_t launch_block_copy(void* k_pool, void* v_pool, const int32_t* pairs,
                              int32_t num_pairs, size_t k_block_bytes, size_t v_block_bytes,

@@ -34,11 +34,20 @@ def pk():
     return pk
 
 
-def _decode(pk, c, P=0):
-    out = pk.pa_decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
-                       partition_tokens=P)
+def _decode(pk, c, P=0, pools=None):
+    k, v = pools or (c.k_pool, c.v_pool)
+    out = pk.pa_decode(c.q, k, v, c.block_tables, c.context_lens, c.scale, partition_tokens=P)
     torch.cuda.synchronize()
     return out
+
+
+def _layout(pk, k, v, layout):
+    """The pools as two device buffers, or as the K and V views of one
+    buffer with each (block, kv head)'s regions side by side."""
+    k, v = torch.as_tensor(k), torch.as_tensor(v)
+    if layout == "side":
+        return pk.fp8_pools_side_by_side(k, v, "cuda")
+    return k.cuda(), v.cuda()
 
 
 def _to64(t):
@@ -64,13 +73,17 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("layout", ["two", "side"])
 @pytest.mark.parametrize("key", list(SMALL))
-def test_fp8_decode_small_configs_all_elements(pk, key):
+def test_fp8_decode_small_configs_all_elements(pk, key, layout):
     cfg = SMALL[key]
     c = decode_case(cfg, payload="numpy", device="cuda")
     ref = oracle.decode(*c.oracle_inputs(), c.scale)
+    pools = _layout(pk, c.k_pool, c.v_pool, layout)
+    if layout == "side":
+        assert pools[1].data_ptr() == pools[0].data_ptr() + pools[0].shape[2]
     for P in (0, cfg.partition_tokens or 64, 16):
-        _check(_to64(_decode(pk, c, P)), ref, f"fp8 {key} P={P}")
+        _check(_to64(_decode(pk, c, P, pools)), ref, f"fp8 {key} {layout} P={P}")
 
 
 def _custom_fp8_case(lens, Hq, Hkv, d, nb, width, seed):
@@ -161,9 +174,10 @@ def _tie_row(d):
     return bits
 
 
+@pytest.mark.parametrize("layout", ["two", "side"])
 @pytest.mark.parametrize("T,skip,d", [(256, 0.0, 128), (1000, 0.2, 128), (1, 0.0, 128),
                                       (77, 0.1, 64)])
-def test_fp8_kv_write_bit_exact(pk, T, skip, d):
+def test_fp8_kv_write_bit_exact(pk, T, skip, d, layout):
     """Codes and scales of the quantising slot write equal the oracle's bit
     for bit, including every nearest-even tie, subnormal codes and an all-zero
     row."""
@@ -174,8 +188,7 @@ def test_fp8_kv_write_bit_exact(pk, T, skip, d):
         w.k_new[1, 2] = 0
         w.v_new[1, 3] = 0
     kref, vref = oracle.kv_write(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping)
-    k = torch.from_numpy(w.k_pool).cuda()
-    v = torch.from_numpy(w.v_pool).cuda()
+    k, v = _layout(pk, w.k_pool, w.v_pool, layout)
     pk.pa_kv_write(k, v, from_numpy_storage(w.k_new, "bf16", "cuda"),
                    from_numpy_storage(w.v_new, "bf16", "cuda"),
                    torch.from_numpy(w.slot_mapping).cuda())
@@ -216,16 +229,16 @@ def test_fp8_kv_append_bit_exact(pk):
     assert np.array_equal(t.cpu().numpy(), expect)
 
 
+@pytest.mark.parametrize("layout", ["two", "side"])
 @pytest.mark.parametrize("P", [1, 150])
-def test_fp8_block_copy_bit_exact(pk, P):
+def test_fp8_block_copy_bit_exact(pk, P, layout):
     rng = np.random.default_rng(P)
     nb, Hkv, d, B = 400, 8, 128, 16
     k_pool, v_pool = fp8_pools_np(rng, nb, Hkv, B, d)
     perm = rng.permutation(nb).astype(np.int32)
     pairs = np.stack([perm[P:][rng.integers(0, nb - P, P)], perm[:P]], axis=1).astype(np.int32)
     kref, vref = oracle.block_copy(k_pool, v_pool, pairs)
-    k = torch.from_numpy(k_pool).cuda()
-    v = torch.from_numpy(v_pool).cuda()
+    k, v = _layout(pk, k_pool, v_pool, layout)
     pk.pa_block_copy(k, v, torch.from_numpy(pairs).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(k.cpu().numpy(), kref)
@@ -235,13 +248,16 @@ def test_fp8_block_copy_bit_exact(pk, P):
 @pytest.mark.slow
 def test_fp8_decode_full_size_all_outputs(pk):
     """The 256-sequence GQA workload with an 8-bit cache at full size, in the
-    benchmark's launch configuration: every output against the oracle, and a
-    second call bit-identical."""
+    benchmark's launch configuration (the pools' regions side by side in one
+    buffer, as the runtime allocates them): every output against the
+    oracle, and a second call bit-identical."""
     cfg = CONFIGS["llama3_8b_gqa"].scaled(dtype="fp8")
     _log("fp8 llama3_8b_gqa: generating on the GPU")
     c = decode_case(cfg, payload="torch", device="cuda")
-    got = _decode(pk, c).clone()
-    assert torch.equal(got, _decode(pk, c))
+    pools = pk.fp8_pools_side_by_side(c.k_pool, c.v_pool, "cuda")
+    got = _decode(pk, c, 0, pools).clone()
+    assert torch.equal(got, _decode(pk, c, 0, pools))
+    del pools
     S, Hq = cfg.num_seqs, cfg.num_q_heads
     pairs = np.array([[s, h] for s in range(S) for h in range(Hq)], np.int32)
     _log(f"fp8 llama3_8b_gqa: copying pools to the host for all {len(pairs)} outputs")

@@ -44,17 +44,28 @@ def _host_np(t, dtype):
     return to_numpy_storage(t)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp8_side"])
 def test_block_swap_bit_exact(pk, dtype):
+    """fp8_side: 8-bit pools whose (block, kv head) K and V regions sit side
+    by side in one buffer, and host pools of the same layout."""
+    side = dtype == "fp8_side"
+    dtype = "fp8" if side else dtype
     nb, H, P = 300, 120, 90
     c = block_copy_case(nb, 8, 128, 16, 0, dtype=dtype, seed=5)
     h = block_copy_case(H, 8, 128, 16, 0, dtype=dtype, seed=6)
     rng = np.random.default_rng(7)
     out_pairs = np.stack([rng.permutation(nb)[:P], rng.permutation(H)[:P]], 1).astype(np.int32)
-    k = _to_torch(c.k_pool, dtype, "cuda")
-    v = _to_torch(c.v_pool, dtype, "cuda")
-    hk = _to_torch(h.k_pool, dtype, pinned=True)
-    hv = _to_torch(h.v_pool, dtype, pinned=True)
+    if side:
+        k, v = pk.fp8_pools_side_by_side(c.k_pool, c.v_pool, "cuda")
+        hk, hv = pk.alloc_host_pools(H, k, v)
+        hk.copy_(torch.from_numpy(h.k_pool))
+        hv.copy_(torch.from_numpy(h.v_pool))
+        assert hv.data_ptr() == hk.data_ptr() + hk.shape[2]
+    else:
+        k = _to_torch(c.k_pool, dtype, "cuda")
+        v = _to_torch(c.v_pool, dtype, "cuda")
+        hk = _to_torch(h.k_pool, dtype, pinned=True)
+        hv = _to_torch(h.v_pool, dtype, pinned=True)
     pk.pa_block_swap(k, v, hk, hv, torch.from_numpy(out_pairs).cuda(), pk.PA_SWAP_OUT)
     torch.cuda.synchronize()
     _, _, rk, rv = oracle.block_swap(c.k_pool, c.v_pool, h.k_pool, h.v_pool, out_pairs,
