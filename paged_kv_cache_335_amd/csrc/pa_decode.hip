@@ -1280,7 +1280,16 @@ __device__ __forceinline__ void decode_reduce_body(const DecodeArgs& a) {
     const int4* rec = reinterpret_cast<const int4*>(a.cut_list + 8 * (1 + i / Hq));
     const int4 r0 = rec[0], r1 = rec[1];
     if (i >= a.cut_list[0] * Hq) break;
-    reduce_one<T, D, EPL, UNR>(a, r0.x, int4{r0.y, r0.z, r0.w, r1.x}, i % Hq, G, lane);
+    // most sequences have one or two pieces (a grouped member: its own
+    // blocks' and its group's shared blocks'): load just those
+    const int np = r0.z + (r1.x & 0xffff);
+    const int4 info{r0.y, r0.z, r0.w, r1.x};
+    if (np <= 2)
+      reduce_one<T, D, EPL, 2>(a, r0.x, info, i % Hq, G, lane);
+    else if (np <= 4)
+      reduce_one<T, D, EPL, 4>(a, r0.x, info, i % Hq, G, lane);
+    else
+      reduce_one<T, D, EPL, UNR>(a, r0.x, info, i % Hq, G, lane);
   }
 }
 
