@@ -225,7 +225,7 @@ __device__ __forceinline__ bool wave_work(const DecodeArgs& a, const Plan& pl, i
   return *r < pl.R;
 }
 
-// Collective over workgroup 0: where each sequence's cut pieces went, for
+// Collective over one workgroup: where each sequence's cut pieces went, for
 // the reduce kernel.  seg_info[s] = {range of its first piece * 2 + end of
 // that piece, pieces} of the sequence's own segment, then the same for the
 // shared segment of its group (pieces | member index << 16; 0 pieces when
@@ -969,7 +969,12 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int G,
                                                  const int32_t* step_blk) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B>(a, G, plan_lds);
-  if (blockIdx.x == 0) write_seg_info(a, pl);
+  // one workgroup past the decode grid lists the pieces for the reduce; the
+  // grid's workgroups only stream their ranges (none of them is delayed)
+  if ((int)blockIdx.x == a.decode_wgs) {
+    write_seg_info(a, pl);
+    return;
+  }
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -997,7 +1002,12 @@ template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B>(a, G, plan_lds);
-  if (blockIdx.x == 0) write_seg_info(a, pl);
+  // one workgroup past the decode grid lists the pieces for the reduce; the
+  // grid's workgroups only stream their ranges (none of them is delayed)
+  if ((int)blockIdx.x == a.decode_wgs) {
+    write_seg_info(a, pl);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int g, r;
@@ -1178,7 +1188,12 @@ template <int D, int G, int NBUF>
 __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeArgs a) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<kBlock>(a, G, plan_lds);
-  if (blockIdx.x == 0) write_seg_info(a, pl);
+  // one workgroup past the decode grid lists the pieces for the reduce; the
+  // grid's workgroups only stream their ranges (none of them is delayed)
+  if ((int)blockIdx.x == a.decode_wgs) {
+    write_seg_info(a, pl);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int g, r;
@@ -1405,12 +1420,12 @@ hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st, const StepBlo
     const Launch l = decode_launch(a, decode_step_kernel<D, B, kNBuf>);
     DecodeArgs b = a;
     b.decode_wgs = (int)l.grid.x;
-    decode_step_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(b, G, *nb);
+    decode_step_kernel<D, B, kNBuf><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G, *nb);
   } else {
     const Launch l = decode_launch(a, decode_mfma_kernel<D, B, kNBuf>);
     DecodeArgs b = a;
     b.decode_wgs = (int)l.grid.x;
-    decode_mfma_kernel<D, B, kNBuf><<<l.grid, l.block, l.lds, st>>>(b, G);
+    decode_mfma_kernel<D, B, kNBuf><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1422,7 +1437,7 @@ hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
   const Launch l = decode_launch(a, decode_mfma8_kernel<D, B, kNBuf8>);
   DecodeArgs b = a;
   b.decode_wgs = (int)l.grid.x;
-  decode_mfma8_kernel<D, B, kNBuf8><<<l.grid, l.block, l.lds, st>>>(b, G);
+  decode_mfma8_kernel<D, B, kNBuf8><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_reduce<__bf16, D>(a, st);
@@ -1433,7 +1448,7 @@ hipError_t launch_valu_g(const DecodeArgs& a, hipStream_t st) {
   const Launch l = decode_launch(a, decode_valu_kernel<D, G, kNBuf>);
   DecodeArgs b = a;
   b.decode_wgs = (int)l.grid.x;
-  decode_valu_kernel<D, G, kNBuf><<<l.grid, l.block, l.lds, st>>>(b);
+  decode_valu_kernel<D, G, kNBuf><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b);
   return hipGetLastError();
 }
 
