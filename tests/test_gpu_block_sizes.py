@@ -103,3 +103,33 @@ def test_kv_write_and_block_copy_block_sizes_bit_exact(pk, dtype, B):
     torch.cuda.synchronize()
     assert np.array_equal(to_numpy_storage(k), kref)
     assert np.array_equal(to_numpy_storage(v), vref)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("B", [8, 32])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_block_sizes_full_size_all_outputs(pk, dtype, B):
+    """The 256-sequence GQA workload at full size with 8- and 32-token
+    blocks, bf16 and 8-bit (regions side by side, as the runtime allocates
+    them), in the benchmark's launch configuration: every output against
+    the oracle, and a second call bit-identical."""
+    cfg = CONFIGS["llama3_8b_gqa"].scaled(block_size=B, dtype=dtype, table_width=512 * 16 // B)
+    _log(f"llama3_8b_gqa {dtype} B={B}: generating on the GPU")
+    c = decode_case(cfg, payload="torch", device="cuda")
+    k, v = c.k_pool, c.v_pool
+    if dtype == "fp8":
+        k, v = pk.fp8_pools_side_by_side(k, v, "cuda")
+    got = pk.pa_decode(c.q, k, v, c.block_tables, c.context_lens, c.scale).clone()
+    again = pk.pa_decode(c.q, k, v, c.block_tables, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(got, again)
+    del k, v, again
+    S, Hq = cfg.num_seqs, cfg.num_q_heads
+    pairs = np.array([[s, h] for s in range(S) for h in range(Hq)], np.int32)
+    _log(f"llama3_8b_gqa {dtype} B={B}: oracle over all {len(pairs)} outputs")
+    ref = oracle.decode_pairs(*c.oracle_inputs(), c.scale, pairs)
+    err = np.abs(got.float().cpu().numpy().astype(np.float64)[pairs[:, 0], pairs[:, 1]] - ref)
+    _log(f"llama3_8b_gqa {dtype} B={B} full size: max|err| {err.max():.3e}")
+    assert np.isfinite(err).all() and err.max() <= 2e-2
+    del c
+    torch.cuda.empty_cache()
