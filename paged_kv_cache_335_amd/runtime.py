@@ -145,6 +145,9 @@ class PagedKVCache:
         self._ring_events = [None] * (_RING // _GROUP)
         self._ring_pos = 0
         self._ws = None
+        self._ws_key = None     # sizes the workspace was last sized for
+        self._ws_view = None
+        self._rows_cache = None  # (row sequence ids, ones) as int32 arrays
         # decode steps: device lengths alternate between two buffers (a step
         # reads one and writes the other)
         self._lens_bufs = [torch.zeros(max_seqs, dtype=torch.int32, device=self.device)
@@ -280,8 +283,8 @@ class PagedKVCache:
                         stream=stream)
             return self.decode(q, out=out, scale=scale, partition_tokens=partition_tokens,
                                stream=stream)
-        seqs = np.asarray(self.row_seqs, np.int32)
-        st, slots, _, pos, pairs = self.bm.append_batch(seqs, np.ones(S, np.int32))
+        seqs, ones = self._row_arrays()
+        st, slots, _, pos, pairs = self.bm.append_batch(seqs, ones)
         if st != PA_OK:
             raise PagedKVError(st, "pa_bm_append_batch")
         # every token's block is given (the kernel writes its table entry)
@@ -305,16 +308,22 @@ class PagedKVCache:
                 self._step_groups = cached
             gs, sb = cached[2], cached[3]
         scale = self.head_dim ** -0.5 if scale is None else scale
-        with torch.cuda.stream(stream):
-            if len(pairs):
+        if len(pairs):
+            with torch.cuda.stream(stream):
                 d_pairs = torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device,
                                                                            non_blocking=False)
-                pa_block_copy(self.k_pool, self.v_pool, d_pairs, stream=stream)
-            ws = self.workspace(q.shape[1], partition_tokens)
-            out = pa_decode_step(q, self.k_pool, self.v_pool, k_new, v_new, self.tables[:S],
-                                 lens_in, lens_out[:S], nb, scale, out=out,
-                                 group_start=gs, shared_blocks=sb,
-                                 partition_tokens=partition_tokens, workspace=ws, stream=stream)
+            pa_block_copy(self.k_pool, self.v_pool, d_pairs, stream=stream)
+        # the launch takes the stream explicitly and the output is allocated
+        # on it, so no stream context is needed around the launch (one costs
+        # ~10 us of host time a step)
+        if out is None:
+            with torch.cuda.stream(stream):
+                out = torch.empty_like(q)
+        ws = self.workspace(q.shape[1], partition_tokens, stream)
+        out = pa_decode_step(q, self.k_pool, self.v_pool, k_new, v_new, self.tables[:S],
+                             lens_in, lens_out[:S], nb, scale, out=out,
+                             group_start=gs, shared_blocks=sb,
+                             partition_tokens=partition_tokens, workspace=ws, stream=stream)
         self.lens = lens_out
         self.groups = None if gs is None else (gs, sb)
         return out
@@ -352,16 +361,29 @@ class PagedKVCache:
         return pairs
 
     # --- decode -------------------------------------------------------------
-    def workspace(self, num_q_heads, partition_tokens=0):
+    def workspace(self, num_q_heads, partition_tokens=0, stream=None):
         S = len(self.rows)
+        key = (S, num_q_heads, partition_tokens, self.share_prefixes)
+        if self._ws_key == key:
+            return self._ws_view
         query = pa_decode_shared_workspace_bytes if self.share_prefixes else \
             pa_decode_workspace_bytes
         need = query(self.k_pool, self.v_pool, S, num_q_heads, self.width, partition_tokens)
         if need and (self._ws is None or self._ws.numel() < need):
             if self._ws is not None:
                 torch.cuda.synchronize(self.device)  # the old workspace may still be in use
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
-        return self._ws if need else None
+            with torch.cuda.stream(self._stream(stream)):
+                self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        self._ws_key, self._ws_view = key, (self._ws if need else None)
+        return self._ws_view
+
+    def _row_arrays(self):
+        """The table rows' sequence ids and a ones vector, as int32 arrays
+        (rebuilt only when rows change)."""
+        if self._rows_cache is None or len(self._rows_cache[0]) != len(self.row_seqs):
+            self._rows_cache = (np.asarray(self.row_seqs, np.int32),
+                                np.ones(len(self.row_seqs), np.int32))
+        return self._rows_cache
 
     def partition_tokens(self, num_q_heads, partition_tokens=0):
         return pa_decode_partition_tokens(self.k_pool, self.v_pool, len(self.rows), num_q_heads,
