@@ -422,6 +422,37 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
         bm[rr] = kPos ? mx * a.scale_log2 : mx;
         grow = grow || bm[rr] > thr[rr];
       }
+      // P.V of the pair; called on each side of the rescale branch so that
+      // the accumulators stay in place on the common side (one copy after
+      // the branch would have to merge rescaled and unscaled values, and
+      // the compiler does that by copying every accumulator register)
+      auto pv = [&]() {
+        // P in bf16 (nearest even): the A operand of P.V, k = the lane's 8
+        // tokens of the pair in order
+        bf16x8 pk[R];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          float pr[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pr[e] = kPos ? fexp2(fmaf(x[rr][e], a.scale_log2, -m_ref[rr]))
+                         : fexp2(x[rr][e] - m_ref[rr]);
+          l_run[rr] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(pr[e]);
+          pk[rr] = v;
+        }
+        PA_EXT_PRIO_MFMA();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4 vb = *reinterpret_cast<const u32x4*>(d + pp * SG::kVPair + vread + nt * 256);
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr)
+            acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                pk[rr], __builtin_bit_cast(bf16x8, vb), acc[rr][nt], 0, 0, 0);
+        }
+      };
       if (__ballot(grow)) {   // rare: move references that grew, rescale
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
@@ -439,30 +470,10 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[rr][nt][r] *= ar[r];
         }
-      }
-      // P in bf16 (nearest even): the A operand of P.V, k = the lane's 8
-      // tokens of the pair in order
-      bf16x8 pk[R];
-#pragma unroll
-      for (int rr = 0; rr < R; ++rr) {
-        float pr[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pr[e] = kPos ? fexp2(fmaf(x[rr][e], a.scale_log2, -m_ref[rr])) : fexp2(x[rr][e] - m_ref[rr]);
-        l_run[rr] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(pr[e]);
-        pk[rr] = v;
-      }
-      PA_EXT_PRIO_MFMA();
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(d + pp * SG::kVPair + vread + nt * 256);
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-          acc[rr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pk[rr], __builtin_bit_cast(bf16x8, vb),
-                                                               acc[rr][nt], 0, 0, 0);
+        pv();
+        asm volatile("");  // the two sides differ: no merging them back
+      } else {
+        pv();
       }
       PA_EXT_PRIO_VALU();
     }
