@@ -44,8 +44,13 @@ namespace pakv {
 namespace {
 
 constexpr int kExtBlock = 16;
-constexpr int kStageBlocks = 4;                       // blocks of one stage
-constexpr int kStageTok = kStageBlocks * kExtBlock;   // 64 tokens a stage
+#ifndef PA_EXT_STAGE_BLOCKS
+#define PA_EXT_STAGE_BLOCKS 4
+#endif
+constexpr int kStageBlocks = PA_EXT_STAGE_BLOCKS;     // blocks of one stage
+constexpr int kStageTok = kStageBlocks * kExtBlock;   // tokens of a stage (64)
+constexpr int kStagePairs = kStageTok / 32;           // 32-token pairs of a stage
+static_assert(kStageBlocks % 2 == 0, "whole pairs per stage");
 
 // Per head size: waves per workgroup (W), row tiles per wave (R), LDS stage
 // buffers (stages in flight + 1) and workgroups per CU.  R row tiles share
@@ -75,7 +80,13 @@ constexpr int kStageTok = kStageBlocks * kExtBlock;   // 64 tokens a stage
 #ifndef PA_EXT64_WG
 #define PA_EXT64_WG 1
 #endif
-#ifdef PA_EXT_SETPRIO
+// A wave issuing its MFMAs (q.K, P.V) runs at raised priority, so that the
+// other wave of the SIMD fills the gaps with its softmax rather than
+// competing for the same issue slots.
+#ifndef PA_EXT_SETPRIO
+#define PA_EXT_SETPRIO 1
+#endif
+#if PA_EXT_SETPRIO
 #define PA_EXT_PRIO_MFMA() __builtin_amdgcn_s_setprio(1)
 #define PA_EXT_PRIO_VALU() __builtin_amdgcn_s_setprio(0)
 #else
@@ -113,7 +124,7 @@ struct StageGeom {
   static constexpr int KCH = ROW / 16;        // 16-byte chunks per K row
   static constexpr int kK = kStageTok * ROW;  // K bytes of a stage
   static constexpr int kVPair = 4 * D * 16;   // V bytes of a 32-token pair
-  static constexpr int kV = 2 * kVPair;       // V bytes of a stage
+  static constexpr int kV = kStagePairs * kVPair;  // V bytes of a stage
   static constexpr int kLoads = kK / kExtWaves / 1024;  // 1 KiB loads per wave, K and V each
   static_assert(kV == kK && kLoads >= 1 && kLoads * 1024 * kExtWaves == kK,
                 "a stage is whole 1 KiB loads per wave");
@@ -364,16 +375,16 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
                                        (lds_void*)(d + vdst + j * 1024), 16, 0, 0);
   };
 
-  // one stage from buffer `buf`: logical tokens t0 .. t0 + 63, a 32-token
-  // pair at a time (scores, softmax, P.V).  Scores of tokens past a row's
-  // position become -inf; that takes instructions only in stages that reach
-  // past the nearest row of the wave (the causal edge and the context's
-  // end).  V needs no mask here: stale slots are zeroed in LDS first.
+  // one stage from buffer `buf`: logical tokens t0 .. t0 + kStageTok - 1,
+  // a 32-token pair at a time (scores, softmax, P.V).  Scores of tokens past
+  // a row's position become -inf; that takes instructions only in pairs that
+  // reach past the nearest row of the wave (the causal edge and the
+  // context's end).  V needs no mask here: stale slots are zeroed in LDS first.
   auto compute = [&](int t0, auto buf) {
     const uint8_t* d = sbuf.get(buf);
-    const bool cmask = t0 + kStageTok - 1 > p_lo;
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
+    for (int pp = 0; pp < kStagePairs; ++pp) {
+      const bool cmask = t0 + pp * 32 + 31 > p_lo;
       // scores: sc[rr][tau], lane's tokens 8 grp + 4 tau + r of the pair
       f32x4 sc[R][2];
       PA_EXT_PRIO_MFMA();
@@ -486,7 +497,7 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   // (c8, dim) of a stage holds tokens t0 + 8 c8 .. t0 + 8 c8 + 7.
   auto zero_tail = [&](int t0, auto buf) {
     uint8_t* d = sbuf.get(buf);
-    for (int idx = tid; idx < 8 * D; idx += kExtWaves * 64) {
+    for (int idx = tid; idx < (kStageTok / 8) * D; idx += kExtWaves * 64) {
       const int c8 = idx / D, dim = idx % D;
       const int lim = L - (t0 + 8 * c8);   // leading tokens of the chunk that are valid
       if (lim >= 8) continue;
