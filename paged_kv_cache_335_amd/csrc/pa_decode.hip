@@ -598,6 +598,41 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
     }
   };
 
+  // The new token is scored while the first pool tiles' loads are in
+  // flight (block_ring's `pre`), off the end of the piece's serial chain.
+  bool new_done = !new_tok;
+  auto new_tile = [&]() {
+    // The new token as tile token 0.  K operand: lane (col 0, grp) holds
+    // dims kj*32 + grp*8 .. +8, i.e. dwords grp*4 + kj*16 + w of the row;
+    // V operand: lane (col, grp 0) holds dim nt*16 + col as its token 0,
+    // the low or high half of dword dim / 2.  Both come from the
+    // prefetched dwords through ds_bpermute.
+    u32x4 kb[KJ];
+    u32x2 vb[NT];
+#pragma unroll
+    for (int kj = 0; kj < KJ; ++kj) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = __builtin_amdgcn_ds_bpermute((grp * 4 + kj * 16 + w) * 4, kpre);
+        w4[w] = col == 0 ? x : 0u;
+      }
+      kb[kj] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int dim = nt * 16 + col;
+      const uint32_t x = __builtin_amdgcn_ds_bpermute((dim >> 1) * 4, vpre);
+      const uint32_t h = (dim & 1) ? x >> 16 : x & 0xffffu;
+      vb[nt] = u32x2{grp == 0 ? h : 0u, 0u};
+    }
+    tile(kb, vb, 1);
+    new_done = true;
+  };
+  auto pre = [&]() {
+    if (!new_done) new_tile();
+  };
+
   const int nblk = je - jb;
   if constexpr (B == 32) {
     u32x4 kring[NBUF][2][KJ];
@@ -626,7 +661,7 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
       auto compute = [&](int i, auto slot) {
         tile32(kring[slot], vring[slot], u.t1 - (u.t0 + (c0 + i) * B));
       };
-      block_ring<NBUF>(cnt, load, compute);
+      block_ring<NBUF>(cnt, load, compute, pre);
     }
   } else {
   u32x4 kring[NBUF][KJ];
@@ -671,37 +706,11 @@ __device__ __forceinline__ void mfma_unit(const DecodeArgs& a, int G, const Unit
       tile(kring[slot], vring[slot], u.t1 - (u.t0 + c0 * B + i * 16));
     };
 
-    block_ring<NBUF>(ntile, load, compute);
+    block_ring<NBUF>(ntile, load, compute, pre);
   }
   }
 
-  if (new_tok) {
-    // The new token as tile token 0.  K operand: lane (col 0, grp) holds
-    // dims kj*32 + grp*8 .. +8, i.e. dwords grp*4 + kj*16 + w of the row;
-    // V operand: lane (col, grp 0) holds dim nt*16 + col as its token 0,
-    // the low or high half of dword dim / 2.  Both come from the
-    // prefetched dwords through ds_bpermute.
-    u32x4 kb[KJ];
-    u32x2 vb[NT];
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj) {
-      uint32_t w4[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = __builtin_amdgcn_ds_bpermute((grp * 4 + kj * 16 + w) * 4, kpre);
-        w4[w] = col == 0 ? x : 0u;
-      }
-      kb[kj] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int dim = nt * 16 + col;
-      const uint32_t x = __builtin_amdgcn_ds_bpermute((dim >> 1) * 4, vpre);
-      const uint32_t h = (dim & 1) ? x >> 16 : x & 0xffffu;
-      vb[nt] = u32x2{grp == 0 ? h : 0u, 0u};
-    }
-    tile(kb, vb, 1);
-  }
+  if (!new_done) new_tile();  // a piece with no pool tiles
 
   // l over the four lane groups holding the same head; m_ref is uniform
   float l_tot = sum_xor16(l_run);

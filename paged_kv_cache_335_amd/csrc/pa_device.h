@@ -207,10 +207,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 // compute only covers the oldest buffer; the drain (at most 2*NBUF - 2
 // blocks) is separate code, so its shorter waits do not leak into the loop.
 // The prologue clamps its block indices so that it is unconditional (a unit
-// shorter than the ring re-reads its last block into unused slots).
-template <int NBUF, typename LoadF, typename ComputeF>
-__device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& compute) {
+// shorter than the ring re-reads its last block into unused slots).  `pre`
+// runs while the prologue's loads are in flight.
+template <int NBUF, typename LoadF, typename ComputeF, typename PreF>
+__device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& compute, PreF&& pre) {
   static_for<NBUF - 1>([&](auto b) { load(min((int)b, cnt - 1), b); });
+  pre();
   int i = 0;
   for (; i + 2 * NBUF - 2 < cnt; i += NBUF) {
     static_for<NBUF>([&](auto b) {
@@ -225,6 +227,10 @@ __device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& com
       compute(i + b, std::integral_constant<int, b % NBUF>{});
     }
   });
+}
+template <int NBUF, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void block_ring(int cnt, LoadF&& load, ComputeF&& compute) {
+  block_ring<NBUF>(cnt, load, compute, [] {});
 }
 
 }  // namespace
