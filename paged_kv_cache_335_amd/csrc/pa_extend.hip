@@ -15,14 +15,14 @@
 //
 // Decomposition.  A row tile is 16 MFMA "head slots" holding (query, head)
 // pairs: 16 / G consecutive queries of one sequence times the G query heads
-// of one kv head.  A workgroup's four waves take R row tiles each (4R tiles
-// of one (sequence, kv head)) and stream the sequence's context in stages
-// of 64 tokens: each wave loads one 16-token block of the stage straight
-// from the pool into LDS (global_load_lds_dwordx4, no registers, no LDS
-// writes), and all four waves read the whole stage.  Several stages are in
-// flight; one barrier per stage.  A batch too small to fill the chip cuts
-// each context into chunks whose (m, l, o) partials a second kernel
-// combines.
+// of one kv head.  A workgroup's W waves (eight: two per SIMD) take R row
+// tiles each (W R tiles of one (sequence, kv head)) and stream the
+// sequence's context in stages of 64 tokens: the waves split each stage's
+// loads evenly (eight waves: half a 16-token block each), straight from the
+// pool into LDS (global_load_lds_dwordx4, no registers, no LDS writes), and
+// every wave reads the whole stage.  Several stages are in flight; one
+// barrier per stage.  A batch too small to fill the chip cuts each context
+// into chunks whose (m, l, o) partials a second kernel combines.
 //
 // Tiles.  q.K runs as v_mfma_f32_16x16x32_bf16 with A = 16 tokens x 32 dims
 // of K and B = 32 dims x 16 head slots of q, so a lane ends with 4 tokens'
@@ -57,8 +57,9 @@ static_assert(kStageBlocks % 2 == 0, "whole pairs per stage");
 // every K and V read from LDS, so R sets the LDS bytes per MFMA.  Eight
 // waves (two per SIMD: one computes its softmax while the other keeps the
 // matrix core busy) share each stage, which halves the K/V bytes staged per
-// query against four, and leave LDS for four stages, three in flight: a
-// stage load has three stages of compute to arrive.
+// query against four.  Head size 128 keeps three stage buffers (a stage's
+// loads have two stages of compute to arrive; four measured slower), head
+// size 64 four.
 #ifndef PA_EXT_WAVES
 #define PA_EXT_WAVES 8
 #endif
