@@ -136,8 +136,10 @@ int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs,
  * blocks into (all sequences of one launch of at most 4096, with the
  * launch grid of the current device): at least partition_tokens (or the
  * library's choice), and long enough that the ranges of one kv head cover
- * the batch with one range per wave.  A sequence of L tokens is then cut
- * into about L / this pieces.  For reports; 0 on invalid arguments.
+ * the batch with one range per wave, each sequence counted a few blocks
+ * longer than it is (the plan's start cost of a piece).  A sequence of L
+ * tokens is then cut into about L / this pieces.  For reports; 0 on
+ * invalid arguments.
  */
 int32_t pa_decode_piece_tokens(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                int32_t max_blocks_per_seq, int32_t partition_tokens,

@@ -398,10 +398,13 @@ int32_t pa_decode_piece_tokens(const pa_pool* pool, int32_t num_seqs, int32_t nu
   if (total_blocks < 0 || decode_sizes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
                                        partition_tokens, false, &P, &ws) != PA_OK)
     return 0;
-  // as the plan computes it: R ranges per kv head over the launch's waves
+  // as the plan computes it: R ranges per kv head over the launch's waves,
+  // every sequence taken as one segment with its start cost
   const int64_t R = std::max<int64_t>(
       1, (int64_t)pakv::decode_grid(pool->num_kv_heads) * pakv::kWaves / pool->num_kv_heads);
-  const int64_t q = std::max<int64_t>(P / pool->block_size, (total_blocks + R - 1) / R);
+  const int64_t cs = (pool->dtype == PA_FP8_E4M3 ? 2 : 1) * pakv::kSegStartBlocks;
+  const int64_t places = total_blocks + cs * num_seqs;
+  const int64_t q = std::max<int64_t>(P / pool->block_size, (places + R - 1) / R);
   return q * pool->block_size > INT32_MAX ? 0 : static_cast<int32_t>(q * pool->block_size);
 }
 

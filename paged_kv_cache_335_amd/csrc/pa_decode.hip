@@ -80,7 +80,10 @@ struct Plan {
   const int* lens;   // [S] context lengths (clamped to the table capacity)
   const int* sdesc;  // [K] first member | member count << 16 (nullptr: segment k is sequence k)
   const int* sj0;    // [K] first logical block of the segment
-  int S, K, T, q, R;  // R: ranges per kv head, q: blocks per range
+  int S, K, T, q, R;  // R: ranges per kv head, q: places per range
+  int cs;             // start cost of a segment (empty places before its blocks)
+  // places [sb, se) of segment k: its blocks sit at [first(k), se)
+  __device__ int first(int k) const { return pre[k + 1] > pre[k] ? pre[k] + cs : pre[k]; }
 };
 
 // Dynamic LDS bytes for a plan over S sequences (with prefix groups a
@@ -107,8 +110,19 @@ __device__ __forceinline__ void group_view(const DecodeArgs& a, const int* lens,
   *P = p;
 }
 
+// The plan's position space: each non-empty segment of n blocks takes
+// n + cs places (cs: the plan's start cost), the first cs of them empty.  A
+// piece costs a wave more than its blocks' loads (its q rows and table
+// entries, then its first loads' latency with nothing else in flight), so
+// ranges cut in this space give a wave that holds many short pieces fewer
+// blocks.  The cost is counted in blocks of the kernel's pool: an 8-bit
+// block is half the bytes of a bf16 one, so it counts twice as many.
+constexpr int kSegStart16 = kSegStartBlocks;      // bf16 and fp32 pools
+constexpr int kSegStart8 = 2 * kSegStartBlocks;   // 8-bit pools
+__device__ __forceinline__ int seg_cost(int blocks, int cs) { return blocks > 0 ? blocks + cs : 0; }
+
 // Collective over the workgroup; ends with a barrier.  B = tokens per block.
-template <int B>
+template <int B, int CS = kSegStart16>
 __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   const int S = a.num_seqs;
   const bool grouped = a.group_start != nullptr;
@@ -138,8 +152,8 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
       int m0, m1, P;
       group_view<B>(a, lens, G, i, &m0, &m1, &P);
       nseg += (P > 0) + (m1 - m0);
-      nb += P;
-      for (int m = m0; m < m1; ++m) nb += (lens[m] + B - 1) / B - P;
+      nb += seg_cost(P, CS);
+      for (int m = m0; m < m1; ++m) nb += seg_cost((lens[m] + B - 1) / B - P, CS);
     }
     int k = block_excl_scan(nseg, wsum, &K);
     int run = block_excl_scan(nb, wsum, &T);
@@ -155,14 +169,14 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
           pre[k] = run;
           sdesc[k] = m0 | (m1 - m0) << 16;
           sj0[k] = 0;
-          run += P;
+          run += seg_cost(P, CS);
           ++k;
         }
         for (int m = m0; m < m1; ++m) {
           pre[k] = run;
           sdesc[k] = m | 1 << 16;
           sj0[k] = P;
-          run += (lens[m] + B - 1) / B - P;
+          run += seg_cost((lens[m] + B - 1) / B - P, CS);
           ++k;
         }
       }
@@ -172,11 +186,11 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
     const int C = (S + T_ - 1) / T_;  // contiguous chunk of sequences per thread
     const int s0 = min(S, t * C), s1 = min(S, s0 + C);
     int nb = 0;
-    for (int s = s0; s < s1; ++s) nb += (lens[s] + B - 1) / B;
+    for (int s = s0; s < s1; ++s) nb += seg_cost((lens[s] + B - 1) / B, CS);
     int run = block_excl_scan(nb, wsum, &T);
     for (int s = s0; s < s1; ++s) {
       pre[s] = run;
-      run += (lens[s] + B - 1) / B;
+      run += seg_cost((lens[s] + B - 1) / B, CS);
     }
     K = S;
   }
@@ -194,6 +208,7 @@ __device__ Plan build_plan(const DecodeArgs& a, int G, int* lds) {
   // every wave of the grid streams one (kv head, range) pair: R ranges per head
   pl.R = max(1, a.decode_wgs * kWaves / a.num_kv_heads);
   pl.q = max(a.min_seg_blocks, (T + pl.R - 1) / pl.R);
+  pl.cs = CS;
   return pl;
 }
 
@@ -240,7 +255,7 @@ __device__ void write_seg_info(const DecodeArgs& a, const Plan& pl) {
   for (int k = threadIdx.x; k < pl.K; k += blockDim.x) {
     int s, nmem, j0;
     seg_desc(pl, k, &s, &nmem, &j0);
-    const int sb = pl.pre[k], se = pl.pre[k + 1];
+    const int sb = pl.first(k), se = pl.pre[k + 1];
     int first = 0, np = 0;
     if (se > sb) {
       const int r0 = sb / pl.q;
@@ -296,33 +311,36 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const Plan& pl, 
     if (pl.pre[mid] <= b0) lo = mid; else hi = mid - 1;
   }
   int k = lo;
-  int end = 0;  // 0 for the piece that starts at the range's first block
+  const int rb0 = b0;  // the range's first place
   while (b0 < b1) {
     while (pl.pre[k + 1] <= b0) ++k;  // skip empty segments
-    const int sb = pl.pre[k], se = pl.pre[k + 1];
+    const int sb = pl.first(k), se = pl.pre[k + 1];
     const int e = min(b1, se);
+    const int bs = max(b0, sb);  // the piece's first block
+    b0 = e;
+    if (bs >= e) continue;  // only the segment's empty places fall in the range
     int s, nmem, j0;
     seg_desc(pl, k, &s, &nmem, &j0);
     Unit u;
     u.s = s;
     u.nmem = nmem;
     u.g = g;
-    u.t0 = (j0 + b0 - sb) * B;
+    u.t0 = (j0 + bs - sb) * B;
     const int seg_end = nmem > 1 ? (j0 + se - sb) * B : pl.lens[s];
     u.t1 = min(seg_end, (j0 + e - sb) * B);
     u.last = nmem == 1 && u.t1 == seg_end;
     const bool cut = (se - 1) / pl.q != sb / pl.q;
     u.in_place = nmem == 1 && j0 == 0 && !cut;
     if (cut) {
-      u.prow = ((r * a.num_kv_heads + g) * 2 + end) * a.slots;
+      // partial rows: end 0 for the piece that starts at the range's first
+      // place, 1 for the one that starts inside it (at most one of each)
+      u.prow = ((r * a.num_kv_heads + g) * 2 + (bs != rb0)) * a.slots;
       u.mstride = G;
     } else {  // one piece: its rows are the sequences' own
       u.prow = (nmem == 1 ? a.own_row0 : a.sh_row0) + s * a.num_q_heads + g * G;
       u.mstride = a.num_q_heads;
     }
     f(u);
-    b0 = e;
-    end = 1;
   }
 }
 
@@ -1010,7 +1028,7 @@ __global__ __launch_bounds__(kWaves * 64, B == 32 ? 1 : PA_MFMA_MIN_WG) void dec
 template <int D, int B, int NBUF>
 __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
   extern __shared__ int plan_lds[];
-  const Plan pl = build_plan<B>(a, G, plan_lds);
+  const Plan pl = build_plan<B, kSegStart8>(a, G, plan_lds);
   // one workgroup past the decode grid lists the pieces for the reduce; the
   // grid's workgroups only stream their ranges (none of them is delayed)
   if ((int)blockIdx.x == a.decode_wgs) {

@@ -34,6 +34,13 @@ constexpr int kNBuf = PA_NBUF;
 constexpr int kNBuf8 = PA_NBUF8;
 constexpr int kMaxMfmaGroup = 16;   // head slots of one MFMA tile
 constexpr int kMaxPlanSeqs = 4096;  // sequences per decode launch (LDS work plan; 2048 with groups)
+// The decode plan's start cost of a segment, in blocks of a bf16 or fp32
+// pool (twice as many for an 8-bit pool): a range cut of the batch counts
+// each non-empty segment this much longer than its blocks.
+#ifndef PA_SEG_START_BLOCKS
+#define PA_SEG_START_BLOCKS 2
+#endif
+constexpr int kSegStartBlocks = PA_SEG_START_BLOCKS;
 
 // Work is cut into "segments": the part of one sequence it streams alone, or
 // the full blocks at the head of a prefix group's tables, which every member

@@ -112,10 +112,11 @@ def test_workspace_and_partition_sizing():
         assert P0 % 16 == 0 and P0 >= 16
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8, 256) > 0
     assert L.pa_decode_workspace_bytes(ctypes.byref(d), 0, 32, 8, 256) == 0
-    # ranges: 1024 waves over 8 kv heads = 128 ranges per head, at least the floor
-    assert L.pa_decode_piece_tokens(ctypes.byref(d), 4, 32, 8192, 512, 32768) == 4096
+    # ranges: 1024 waves over 8 kv heads = 128 ranges per head, at least the
+    # floor; every sequence counts 2 blocks more (a piece's start cost)
+    assert L.pa_decode_piece_tokens(ctypes.byref(d), 4, 32, 8192, 512, 32768) == 257 * 16
     assert L.pa_decode_piece_tokens(ctypes.byref(d), 4, 32, 8192, 512, 1000) == 512
-    assert L.pa_decode_piece_tokens(ctypes.byref(d), 256, 32, 516, 0, 26000) == 204 * 16
+    assert L.pa_decode_piece_tokens(ctypes.byref(d), 256, 32, 516, 0, 26000) == 208 * 16
     assert L.pa_decode_piece_tokens(ctypes.byref(d), 4, 32, 8192, 100, 1000) == 0
     # invalid: piece not a multiple of the block, heads not divisible
     assert L.pa_decode_partition_tokens(ctypes.byref(d), 4, 32, 8192, 100) == 0
