@@ -173,10 +173,11 @@ int32_t pa_decode_piece_tokens(const pa_pool* pool, int32_t num_seqs, int32_t nu
  *                  go to `workspace` and are combined by a second kernel.
  *   workspace:     device buffer of at least pa_decode_workspace_bytes(...)
  *                  bytes; contents on entry are irrelevant.
- * Requires num_q_heads % num_kv_heads == 0 and head_dim 64 or 128; bf16 and
- * 8-bit pools: block_size 8, 16 or 32 and at most 16 query heads per kv
- * head; fp32 pools: block_size 16 and at most 4 query heads per kv head
- * (PA_EUNSUPPORTED otherwise).  The result does not depend on where blocks
+ * Requires num_q_heads % num_kv_heads == 0, head_dim 64 or 128 and at most
+ * 16 query heads per kv head; bf16 and 8-bit pools: block_size 8, 16 or 32;
+ * fp32 pools: block_size 16 (PA_EUNSUPPORTED otherwise).  fp32 pools with
+ * more than 4 query heads per kv head stream each kv head's blocks once per
+ * group of up to 4 of its query heads.  The result does not depend on where blocks
  * sit in the pool, and two calls with the same inputs give identical bits.
  */
 pa_status pa_decode(const pa_pool* pool, const void* k_pool, const void* v_pool,

@@ -1075,9 +1075,11 @@ __device__ __forceinline__ void valu_unit(const DecodeArgs& a, const Unit& u, in
     }
   }
 
-  const size_t blk_bytes = (size_t)a.num_kv_heads * B * ROW;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)g * B * ROW;
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)g * B * ROW;
+  // g counts head groups; kv_div of them share one kv head of the pool
+  const int div = a.kv_div > 1 ? a.kv_div : 1;
+  const size_t blk_bytes = (size_t)(a.num_kv_heads / div) * B * ROW;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool) + (size_t)(g / div) * B * ROW;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool) + (size_t)(g / div) * B * ROW;
   const uint32_t koff = tok * ROW + qc * 16;
   const uint32_t voff = lane * (EPL * B * ES);
   const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks;
@@ -1479,18 +1481,31 @@ hipError_t launch_valu_g(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// A kv head with more than four query heads is taken as kv_div head groups
+// of Gs = 4, 3, 2 or 1 heads (the largest that divides G): each group is a
+// head of the plan and streams the kv head's blocks itself.  The groups'
+// query heads are consecutive, so the partial rows and the reduce see a
+// pool of G / Gs times the kv heads with Gs query heads each.
 template <int D>
 hipError_t launch_valu(const DecodeArgs& a, int G, hipStream_t st) {
+  int Gs = G;
+  DecodeArgs b = a;
+  if (G > 4) {
+    Gs = G % 4 == 0 ? 4 : G % 3 == 0 ? 3 : G % 2 == 0 ? 2 : 1;
+    b.kv_div = G / Gs;
+    b.num_kv_heads = a.num_kv_heads * b.kv_div;
+    b.slots = Gs;
+  }
   hipError_t e;
-  switch (G) {
-    case 1: e = launch_valu_g<D, 1>(a, st); break;
-    case 2: e = launch_valu_g<D, 2>(a, st); break;
-    case 3: e = launch_valu_g<D, 3>(a, st); break;
-    case 4: e = launch_valu_g<D, 4>(a, st); break;
+  switch (Gs) {
+    case 1: e = launch_valu_g<D, 1>(b, st); break;
+    case 2: e = launch_valu_g<D, 2>(b, st); break;
+    case 3: e = launch_valu_g<D, 3>(b, st); break;
+    case 4: e = launch_valu_g<D, 4>(b, st); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  return launch_reduce<float, D>(a, st);
+  return launch_reduce<float, D>(b, st);
 }
 
 }  // namespace
@@ -1505,7 +1520,7 @@ DecodePath decode_path(pa_dtype dtype, int head_dim, int group, int block_size) 
     return DecodePath::kUnsupported;
   }
   if (dtype == PA_FP8_E4M3 && group <= kMaxMfmaGroup) return DecodePath::kMfma8;
-  if (dtype == PA_F32 && group <= 4) return DecodePath::kValu;
+  if (dtype == PA_F32 && group <= kMaxMfmaGroup) return DecodePath::kValu;
   return DecodePath::kUnsupported;
 }
 

@@ -93,6 +93,8 @@ struct DecodeArgs {
   int32_t min_seg_blocks;  // smallest range a wave streams (blocks)
   int32_t decode_wgs;      // workgroups of the decode grid (a step adds store workgroups)
   int32_t slots;           // head slots per (wave slot, end): G, or members * G with groups
+  int32_t kv_div;          // fp32 path: head groups per pool kv head (0 or 1: one); with
+                           // more, num_kv_heads counts the groups of at most 4 query heads
   int32_t own_row0;        // first per-sequence row of own segments (groups only)
   int32_t sh_row0;         // first per-sequence row of shared segments (groups only)
   float scale_log2;  // scale * log2(e): scores are kept in log2 units

@@ -143,7 +143,10 @@ def test_decode_kv_head_counts(pk, Hkv):
 
 
 def test_decode_fp32_group_sizes(pk):
-    for G in (1, 2, 4):
+    """fp32 pools, 1 to 16 query heads per kv head: above four the kernel
+    takes the query heads in groups of 4, 3, 2 or 1 (the largest that
+    divides G), each group a head of the plan over the same kv head."""
+    for G in (1, 2, 4, 5, 6, 8, 9, 16):
         cfg = CONFIGS["tiny_f32"].scaled(num_seqs=5, num_q_heads=G, num_kv_heads=1, head_dim=128,
                                      lengths=("uniform", 1, 200), pool=("fixed", 80),
                                      table_width=16, seed=30 + G, key="f32g")
