@@ -154,6 +154,14 @@ def test_decode_fp32_group_sizes(pk):
         ref = oracle.decode(*c.oracle_inputs(), c.scale)
         for P in (0, 32):
             _check(_to64(_gpu_decode(pk, c, P)), ref, "f32", f"fp32 G={G} P={P}")
+    # several kv heads, each taken as head groups (6 = 2 groups of 3; 8 = 2 of
+    # 4): the groups' pool offsets and query heads interleave per kv head
+    for G, Hkv in ((6, 3), (8, 5)):
+        c = _custom_case((1, 16, 17, 100, 511), Hq=G * Hkv, Hkv=Hkv, d=64, nb=200, width=40,
+                         seed=540 + G, dtype="f32")
+        ref = oracle.decode(*c.oracle_inputs(), c.scale)
+        for P in (0, 64):
+            _check(_to64(_gpu_decode(pk, c, P)), ref, "f32", f"fp32 Hkv={Hkv} G={G} P={P}")
 
 
 def test_nan_in_unused_tail_slots_never_reaches_output(pk):
