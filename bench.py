@@ -323,7 +323,7 @@ def run_decode(args, key, kv, block_size, K, W, cold_iters, stream, full):
         lens = lens.astype(np.int64)
         return int(cfg.prompts * base + (lens - base).sum()) if shared else int(lens.sum())
 
-    fused = not args.two_call and not fp8
+    fused = not args.two_call
 
     def step(i):
         if fused:   # one launch: slot write, table growth and decode (pa_decode_step)

@@ -235,7 +235,9 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
  * pa_decode) over the grown contexts, up to the order of fp32 sums.
  *   q, out:       [num_seqs][num_q_heads][head_dim] bf16.
  *   k_new, v_new: [num_seqs][num_kv_heads][head_dim] bf16, device: the new
- *                 token of sequence s, at position lens_in[s].
+ *                 token of sequence s, at position lens_in[s].  An 8-bit
+ *                 pool receives its codes and scales exactly as from
+ *                 pa_kv_write, and the decode uses those quantised values.
  *   lens_in:      int32 [num_seqs], device: context lengths before the
  *                 step, 0 <= lens_in[s] < max_blocks_per_seq * block_size.
  *   lens_out:     int32 [num_seqs], device, not lens_in: receives
@@ -254,7 +256,7 @@ pa_status pa_decode_shared(const pa_pool* pool, const void* k_pool, const void* 
  *                 new_blocks[s]).
  *   groups, workspace: as for pa_decode_shared (num_groups = 0: none; the
  *                 groups describe the contexts after the step).
- * bf16 pools only (PA_EUNSUPPORTED otherwise: use pa_kv_append and
+ * bf16 and 8-bit pools (fp32 pools: PA_EUNSUPPORTED, use pa_kv_append and
  * pa_decode).  With PA_DEBUG=1 the lengths, blocks and tables are validated
  * first, as for pa_decode after the step.
  */

@@ -453,8 +453,9 @@ pa_status pa_decode_step(const pa_pool* pool, void* k_pool, void* v_pool, const 
   if (num_seqs > 0 && (!k_new || !v_new || !lens_in || !lens_out || !new_blocks))
     return PA_EINVAL;
   if (lens_out == lens_in && num_seqs > 0) return PA_EINVAL;
-  // bf16 pools only: the step stores the new token as it reads it
-  if (pool->dtype != PA_BF16) return PA_EUNSUPPORTED;
+  // bf16 and 8-bit pools (an 8-bit step quantises the new token as the
+  // slot write does); fp32 pools take pa_kv_append and pa_decode
+  if (pool->dtype != PA_BF16 && pool->dtype != PA_FP8_E4M3) return PA_EUNSUPPORTED;
   StepArgs step;
   step.k_new = k_new;
   step.v_new = v_new;

@@ -777,8 +777,9 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-template <int D, int B, int NBUF>
-__device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Unit& u, int lane) {
+template <int D, int B, int NBUF, bool STEP>
+__device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Unit& unit, int lane,
+                                           uint8_t* nts) {
   using TG = TileGeom<B>;
   constexpr int KC = D / 64;              // 16-byte K code loads per lane per block
   constexpr int VC = D / 64;              // 16-byte V code loads per lane per block
@@ -787,6 +788,22 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   constexpr uint32_t QROW = D * 2;         // bytes per bf16 q row
   constexpr uint32_t SOFF = B * D;         // offset of the scales in a K region
 
+  // A decode step's new token (the sequence's last position) joins the
+  // piece that ends the sequence as one extra tile, quantised here exactly
+  // as the slot write quantises it (the reduce kernel that follows stores
+  // those codes and scales); the pool tiles stop before it.
+  Unit u = unit;
+  const bool new_tok = STEP && u.last;
+  uint32_t kpre = 0, vpre = 0;  // lane l: dword l (dims 2l, 2l + 1) of the token's K and V rows
+  if (new_tok) {
+    u.t1 -= 1;
+    // issued now, so their latency hides behind the piece's pool tiles
+    const size_t row_off = ((size_t)u.s * a.num_kv_heads + u.g) * QROW;
+    if (lane < D / 2) {
+      kpre = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.k_new) + row_off)[lane];
+      vpre = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.v_new) + row_off)[lane];
+    }
+  }
   const int s = u.s, g = u.g;
   const int jb = u.t0 / B, je = (u.t1 + B - 1) / B;
   const int col = lane & 15, grp = lane >> 4;
@@ -822,6 +839,129 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
   u32x4 kring[NBUF][KC];
   u32x4 sring[NBUF];
   u32x4 vring[NBUF][VC];
+
+  // one 16-token tile: scores, softmax, P.V; `valid` = its leading tokens
+  // inside the unit (the rest masked)
+  auto tile8 = [&](const u32x4* kr, const u32x4& sw_in, const u32x4* vr, int valid) {
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 w = kr[c];
+      const u32x2 k0 = e4m3x4_to_bf16(w.x), k1 = e4m3x4_to_bf16(w.y);
+      const u32x2 k2 = e4m3x4_to_bf16(w.z), k3 = e4m3x4_to_bf16(w.w);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, u32x4{k0.x, k0.y, k1.x, k1.y}), qop[2 * c], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, u32x4{k2.x, k2.y, k3.x, k3.y}), qop[2 * c + 1], sc, 0, 0,
+          0);
+    }
+    // scales of tokens 4*grp + r: bf16 pairs, K in words x, y and V in z, w
+    const u32x4 sw = sw_in;
+    const f32x4 ks = {__uint_as_float(sw.x << 16), bf16_hi(sw.x), __uint_as_float(sw.y << 16),
+                      bf16_hi(sw.y)};
+    f32x4 vs = {__uint_as_float(sw.z << 16), bf16_hi(sw.z), __uint_as_float(sw.w << 16),
+                bf16_hi(sw.w)};
+    // load h, row r held dim h*64 + r*16 + col (tile 4h + r), token group j
+    // in word j; after the transpose word t of row g is tile 4h + t, tokens
+    // 4g .. 4g + 3 of dim col: the B operand layout of P.V
+    uint32_t vb[NT];
+#pragma unroll
+    for (int h = 0; h < VC; ++h) {
+      uint32_t w0 = vr[h].x, w1 = vr[h].y, w2 = vr[h].z, w3 = vr[h].w;
+      transpose_rows4(w0, w1, w2, w3);
+      vb[4 * h + 0] = w0;
+      vb[4 * h + 1] = w1;
+      vb[4 * h + 2] = w2;
+      vb[4 * h + 3] = w3;
+    }
+    // sc[r] = code-level score of token 4*grp + r for head col
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks[r] * a.scale_log2;
+    if (valid < 16) {
+      // slots past the context: score -inf, V codes and scale zeroed
+      const int t = 4 * grp;
+      uint32_t m = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (t + r >= valid) {
+          x[r] = kNegInf;
+          vs[r] = 0.f;
+        } else {
+          m |= 0xffu << (8 * r);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vb[nt] &= m;
+    }
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__ballot(bm > m_ref + kSlack)) {  // rare: as in mfma_unit
+      bm = max_xor32(max_xor16(bm));
+      const float m_new = fmaxf(m_ref, bm);
+      const float alpha = fexp2(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    // the V scale rides on the probability: o += (p * s_v) * code
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] *= vs[r];
+    const bf16x8 pp = p_split(p);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(e4m3x4_to_bf16(vb[nt])),
+                                                        acc[nt], 0, 0, 0);
+  };
+
+  // The new token as tile token 0: quantised (scale = bf16(max|x| / 448),
+  // codes = E4M3(x / scale), nearest even), the codes passed through this
+  // wave's LDS scratch into the tile's operand layout: K codes of token 0
+  // for lanes (col 0, grp), V code of dim h*64 + lane for every lane, the
+  // two scales in the lanes of token group 0.
+  bool new_done = !new_tok;
+  auto new_tile = [&]() {
+    auto quant = [&](uint32_t w, uint16_t* sbits) {
+      const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+      // from 0, as the slot write: NaN inputs are skipped by fmaxf
+      const float am = wave_max(fmaxf(0.f, fmaxf(fabsf(x0), fabsf(x1))));
+      const __bf16 sb = static_cast<__bf16>(am / 448.f);
+      const float sc = static_cast<float>(sb);
+      *sbits = __builtin_bit_cast(uint16_t, sb);
+      const uint32_t c0 = sc > 0.f ? (__builtin_amdgcn_cvt_pk_fp8_f32(x0 / sc, 0.f, 0, false) & 0xffu) : 0u;
+      const uint32_t c1 = sc > 0.f ? (__builtin_amdgcn_cvt_pk_fp8_f32(x1 / sc, 0.f, 0, false) & 0xffu) : 0u;
+      return static_cast<uint16_t>(c0 | (c1 << 8));
+    };
+    uint16_t ksb, vsb;
+    const uint16_t kc = quant(kpre, &ksb), vc = quant(vpre, &vsb);
+    if (lane < D / 2) {
+      reinterpret_cast<uint16_t*>(nts)[lane] = kc;
+      reinterpret_cast<uint16_t*>(nts + D)[lane] = vc;
+    }
+    u32x4 kr[KC], vr[VC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(nts + c * 64 + grp * 16);
+      kr[c] = col == 0 ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int h = 0; h < VC; ++h) vr[h] = u32x4{(uint32_t)nts[D + h * 64 + lane], 0u, 0u, 0u};
+    const u32x4 sw = grp == 0 ? u32x4{(uint32_t)ksb, 0u, (uint32_t)vsb, 0u} : u32x4{0u, 0u, 0u, 0u};
+    tile8(kr, sw, vr, 1);
+    new_done = true;
+  };
+  auto pre = [&]() {
+    if (!new_done) new_tile();
+  };
 
   const int nblk = je - jb;
   for (int c0 = 0; c0 < nblk; c0 += 64) {
@@ -863,91 +1003,13 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
     };
 
     auto compute = [&](int i, auto slot) {
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4 w = kring[slot][c];
-        const u32x2 k0 = e4m3x4_to_bf16(w.x), k1 = e4m3x4_to_bf16(w.y);
-        const u32x2 k2 = e4m3x4_to_bf16(w.z), k3 = e4m3x4_to_bf16(w.w);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, u32x4{k0.x, k0.y, k1.x, k1.y}), qop[2 * c], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, u32x4{k2.x, k2.y, k3.x, k3.y}), qop[2 * c + 1], sc, 0, 0,
-            0);
-      }
-      // scales of tokens 4*grp + r: bf16 pairs, K in words x, y and V in z, w
-      const u32x4 sw = sring[slot];
-      const f32x4 ks = {__uint_as_float(sw.x << 16), bf16_hi(sw.x), __uint_as_float(sw.y << 16),
-                        bf16_hi(sw.y)};
-      f32x4 vs = {__uint_as_float(sw.z << 16), bf16_hi(sw.z), __uint_as_float(sw.w << 16),
-                  bf16_hi(sw.w)};
-      // load h, row r held dim h*64 + r*16 + col (tile 4h + r), token group j
-      // in word j; after the transpose word t of row g is tile 4h + t, tokens
-      // 4g .. 4g + 3 of dim col: the B operand layout of P.V
-      uint32_t vb[NT];
-#pragma unroll
-      for (int h = 0; h < VC; ++h) {
-        uint32_t w0 = vring[slot][h].x, w1 = vring[slot][h].y, w2 = vring[slot][h].z,
-                 w3 = vring[slot][h].w;
-        transpose_rows4(w0, w1, w2, w3);
-        vb[4 * h + 0] = w0;
-        vb[4 * h + 1] = w1;
-        vb[4 * h + 2] = w2;
-        vb[4 * h + 3] = w3;
-      }
-      // sc[r] = code-level score of token 4*grp + r for head col
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = sc[r] * ks[r] * a.scale_log2;
-      const int valid = u.t1 - (u.t0 + c0 * B + i * 16);  // tokens of the tile in the unit
-      if (valid < 16) {
-        // slots past the context: score -inf, V codes and scale zeroed
-        const int t = 4 * grp;
-        uint32_t m = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (t + r >= valid) {
-            x[r] = kNegInf;
-            vs[r] = 0.f;
-          } else {
-            m |= 0xffu << (8 * r);
-          }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) vb[nt] &= m;
-      }
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__ballot(bm > m_ref + kSlack)) {  // rare: as in mfma_unit
-        bm = max_xor32(max_xor16(bm));
-        const float m_new = fmaxf(m_ref, bm);
-        const float alpha = fexp2(m_ref - m_new);
-        l_run *= alpha;
-        m_ref = m_new;
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = lane_bcast(alpha, 4 * grp + r);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[nt][r] *= ar[r];
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fexp2(x[r] - m_ref);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      // the V scale rides on the probability: o += (p * s_v) * code
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] *= vs[r];
-      const bf16x8 pp = p_split(p);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, v_twice(e4m3x4_to_bf16(vb[nt])),
-                                                          acc[nt], 0, 0, 0);
+      tile8(kring[slot], sring[slot], vring[slot], u.t1 - (u.t0 + c0 * B + i * 16));
     };
 
-    block_ring<NBUF>(ntile, load, compute);
+    block_ring<NBUF>(ntile, load, compute, pre);
   }
 
+  if (!new_done) new_tile();  // a piece with no pool tiles
   float l_tot = sum_xor16(l_run);
   l_tot = sum_xor32(l_tot);
   finish_mfma_unit<D>(a, G, u, acc, m_ref, l_tot, lane);
@@ -991,6 +1053,53 @@ __device__ void step_store(const DecodeArgs& a, const int32_t* step_blk, int w, 
   }
 }
 
+// The 8-bit pool's version: the new token's codes and scales, quantised
+// as the slot write quantises (one wave per (kv head, K or V) row), into
+// its slot of the K and V regions; table entry and length as above.
+template <int D, int B>
+__device__ void step_store8(const DecodeArgs& a, const int32_t* step_blk, int w, int nw) {
+  const int H = a.num_kv_heads;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwv = blockDim.x >> 6;
+  for (int s = w; s < a.num_seqs; s += nw) {
+    const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);  // position of the new token
+    const int j = L / B, r = L % B;
+    const int given = step_blk[s];
+    int32_t* entry = a.tables_w + (size_t)s * a.max_blocks + j;
+    const int blk = given >= 0 ? given : *entry;
+    if (threadIdx.x == 0) {
+      if (given >= 0) *entry = given;
+      a.lens_out[s] = L + 1;
+    }
+    for (int row = wave; row < 2 * H; row += nwv) {
+      const bool is_v = row >= H;
+      const int g = is_v ? row - H : row;
+      const uint16_t* src =
+          static_cast<const uint16_t*>(is_v ? a.v_new : a.k_new) + ((size_t)s * H + g) * D;
+      uint8_t* kreg =
+          static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) + ((size_t)blk * H + g) * a.k_rstride;
+      uint8_t* vreg =
+          static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) + ((size_t)blk * H + g) * a.v_rstride;
+      float amax = 0.f;  // NaN inputs are skipped by fmaxf
+      for (int e = lane; e < D; e += 64)
+        amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)src[e] << 16)));
+      amax = wave_max(amax);
+      const __bf16 sb = static_cast<__bf16>(amax / 448.f);
+      const float scale = static_cast<float>(sb);
+      for (int e = lane; e < D; e += 64) {
+        const float x = __uint_as_float((uint32_t)src[e] << 16);
+        const uint8_t c = scale > 0.f
+                              ? static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x / scale, 0.f, 0, false) & 0xffu)
+                              : uint8_t{0};
+        __builtin_nontemporal_store(c, is_v ? vreg + (size_t)e * B + r : kreg + (size_t)r * D + e);
+      }
+      if (lane == 0)
+        __builtin_nontemporal_store(
+            __builtin_bit_cast(uint16_t, sb),
+            reinterpret_cast<uint16_t*>(kreg + (size_t)B * D + 16u * (r / 4) + 8u * is_v) + (r % 4));
+    }
+  }
+}
+
 template <int D, int B, int NBUF, bool STEP>
 __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a, int G,
                                                  const int32_t* step_blk) {
@@ -1025,8 +1134,8 @@ __global__ __launch_bounds__(kWaves * 64, B == 32 ? 1 : PA_MFMA_MIN_WG) void dec
   decode_mfma_body<D, B, NBUF, true>(a, G, nb.blk);
 }
 
-template <int D, int B, int NBUF>
-__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
+template <int D, int B, int NBUF, bool STEP>
+__device__ __forceinline__ void decode_mfma8_body(const DecodeArgs& a, int G, uint8_t* nts) {
   extern __shared__ int plan_lds[];
   const Plan pl = build_plan<B, kSegStart8>(a, G, plan_lds);
   // one workgroup past the decode grid lists the pieces for the reduce; the
@@ -1039,7 +1148,22 @@ __global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kern
   const int lane = threadIdx.x & 63;
   int g, r;
   if (!wave_work(a, pl, wave, &g, &r)) return;
-  walk_range<B>(a, pl, G, r, g, [&](const Unit& u) { mfma8_unit<D, B, NBUF>(a, G, u, lane); });
+  uint8_t* wnts = STEP ? nts + wave * 2 * D : nullptr;
+  walk_range<B>(a, pl, G, r, g,
+                [&](const Unit& u) { mfma8_unit<D, B, NBUF, STEP>(a, G, u, lane, wnts); });
+}
+
+template <int D, int B, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_mfma8_kernel(DecodeArgs a, int G) {
+  decode_mfma8_body<D, B, NBUF, false>(a, G, nullptr);
+}
+
+// A decode step over an 8-bit pool: each wave's LDS scratch takes the new
+// token's codes (K, then V) on their way into the tile's operand layout.
+template <int D, int B, int NBUF>
+__global__ __launch_bounds__(kWaves * 64, PA_MFMA_MIN_WG) void decode_step8_kernel(DecodeArgs a, int G) {
+  __shared__ __attribute__((aligned(16))) uint8_t nts[kWaves * 2 * D];
+  decode_mfma8_body<D, B, NBUF, true>(a, G, nts);
 }
 
 // ---------------------------------------------------------------------------
@@ -1351,6 +1475,13 @@ __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_step_kernel(D
   decode_reduce_body<__bf16, D>(a);
 }
 
+template <int D, int B>
+__global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_step8_kernel(DecodeArgs a,
+                                                                                StepBlocks nb) {
+  step_store8<D, B>(a, nb.blk, blockIdx.x, gridDim.x);
+  decode_reduce_body<__bf16, D>(a);
+}
+
 int cu_count();
 
 // A grid over the (cut sequence, query head) pairs the decode kernel
@@ -1375,6 +1506,13 @@ template <int D, int B>
 hipError_t launch_reduce_step(const DecodeArgs& a, const StepBlocks& nb, hipStream_t st) {
   const int grid = std::max(reduce_grid<__bf16, D>(a), a.num_seqs);
   decode_reduce_step_kernel<D, B><<<dim3(grid), kReduceHeads * 64, 0, st>>>(a, nb);
+  return hipGetLastError();
+}
+
+template <int D, int B>
+hipError_t launch_reduce_step8(const DecodeArgs& a, const StepBlocks& nb, hipStream_t st) {
+  const int grid = std::max(reduce_grid<__bf16, D>(a), a.num_seqs);
+  decode_reduce_step8_kernel<D, B><<<dim3(grid), kReduceHeads * 64, 0, st>>>(a, nb);
   return hipGetLastError();
 }
 
@@ -1462,14 +1600,21 @@ hipError_t launch_mfma(const DecodeArgs& a, int G, hipStream_t st, const StepBlo
 }
 
 template <int D, int B>
-hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st) {
-  const Launch l = decode_launch(a, decode_mfma8_kernel<D, B, kNBuf8>);
-  DecodeArgs b = a;
-  b.decode_wgs = (int)l.grid.x;
-  decode_mfma8_kernel<D, B, kNBuf8><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G);
+hipError_t launch_mfma8(const DecodeArgs& a, int G, hipStream_t st, const StepBlocks* nb) {
+  if (nb) {
+    const Launch l = decode_launch(a, decode_step8_kernel<D, B, kNBuf8>);
+    DecodeArgs b = a;
+    b.decode_wgs = (int)l.grid.x;
+    decode_step8_kernel<D, B, kNBuf8><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G);
+  } else {
+    const Launch l = decode_launch(a, decode_mfma8_kernel<D, B, kNBuf8>);
+    DecodeArgs b = a;
+    b.decode_wgs = (int)l.grid.x;
+    decode_mfma8_kernel<D, B, kNBuf8><<<dim3(l.grid.x + 1), l.block, l.lds, st>>>(b, G);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce<__bf16, D>(a, st);
+  return nb ? launch_reduce_step8<D, B>(a, *nb, st) : launch_reduce<__bf16, D>(a, st);
 }
 
 template <int D, int G>
@@ -1545,7 +1690,7 @@ struct MfmaLaunch {
 template <int D, int B>
 struct Mfma8Launch {
   static hipError_t run(const DecodeArgs& a, int G, hipStream_t st, const StepBlocks* nb) {
-    return nb ? hipErrorInvalidValue : launch_mfma8<D, B>(a, G, st);
+    return launch_mfma8<D, B>(a, G, st, nb);
   }
 };
 

@@ -273,12 +273,12 @@ class PagedKVCache:
         the tables and lengths, and decodes q [S][Hq][d] over the grown
         contexts.  The host sends only each token's block id, with the
         launch's arguments; copy-on-write copies (after a fork) run first.
-        bf16 pools; other pools take append + decode."""
+        bf16 and 8-bit pools; fp32 pools take append + decode."""
         if self.swapped:
             raise ValueError("sequences are swapped out")
         stream = self._stream(stream)
         S = len(self.rows)
-        if self.k_pool.dtype != torch.bfloat16:
+        if self.k_pool.dtype == torch.float32:
             self.append(np.asarray(self.row_seqs, np.int32), np.ones(S, np.int32), k_new, v_new,
                         stream=stream)
             return self.decode(q, out=out, scale=scale, partition_tokens=partition_tokens,

@@ -143,7 +143,7 @@ def test_decode_step_matches_append_then_decode(pk, S, maxlen):
 
 
 def test_decode_step_rejects_what_it_does_not_serve(pk, monkeypatch):
-    """8-bit pools are refused (PA_EUNSUPPORTED); with PA_DEBUG=1 a token
+    """fp32 pools are refused (PA_EUNSUPPORTED); with PA_DEBUG=1 a token
     that starts a block without a given block, and lengths at the table's
     capacity, are refused before any launch."""
     import ctypes
@@ -164,12 +164,65 @@ def test_decode_step_rejects_what_it_does_not_serve(pk, monkeypatch):
     out = pk.pa_decode_step(*args, new_blocks, d ** -0.5)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    desc = pk.PoolDesc(16, B, Hkv, d, pk.PA_FP8_E4M3)
+    desc = pk.PoolDesc(16, B, Hkv, d, pk.PA_F32)
     dummy = ctypes.c_void_p(0x1000)
     st = pk.lib().pa_decode_step(ctypes.byref(desc), dummy, dummy, dummy, dummy, dummy, 3, Hq,
                                  dummy, 4, dummy, ctypes.c_void_p(0x2000), dummy, 0.1, dummy,
                                  0, 0, None, None, dummy, 1 << 30, None)
     assert st == pk.PA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("layout,B,G,d,share", [("side", 16, 4, 128, 0), ("two", 16, 8, 64, 0),
+                                                ("side", 8, 4, 128, 0), ("side", 32, 1, 128, 0),
+                                                ("side", 16, 4, 128, 3)])
+def test_fp8_step_state_and_output(pk, layout, B, G, d, share):
+    """8-bit pools: the step quantises each new token as the slot write does
+    and decodes with those values.  Pools (codes and scales), tables and
+    lengths after the step bit-exact against the oracle's slot write of the
+    same tokens; every output against the oracle's decode of the grown
+    contexts (2e-2, as for the 8-bit decode)."""
+    from workloads.gen import fp8_pools_np
+    Hkv = 2
+    Hq = G * Hkv
+    lens_in = [0, 1, 15, 16, 17, 31, 32, 47, 100, 255, 256, 511, 700]
+    if share:
+        lens_in = [share * B + x for x in (3, 9, 0, 17)] + lens_in
+    rng, tables, new_blocks, k, v, q, kn, vn, lens_in = _step_case(
+        lens_in, Hq, Hkv, d, B, seed=700 + G * 10 + B + share, share_first=share)
+    S, nb = len(lens_in), k.shape[0]
+    k8, v8 = fp8_pools_np(rng, nb, Hkv, B, d)
+    slots = np.array([(new_blocks[s] if new_blocks[s] >= 0 else tables[s, lens_in[s] // B]) * B
+                      + lens_in[s] % B for s in range(S)], np.int64)
+    k_ref, v_ref = oracle.kv_write(k8, v8, to_numpy_storage(kn), to_numpy_storage(vn), slots)
+    t_ref = tables.copy()
+    for s in range(S):
+        t_ref[s, lens_in[s] // B] = slots[s] // B
+    lens_out_ref = lens_in + 1
+    ref = oracle.decode(k_ref, v_ref, to_numpy_storage(q), t_ref, lens_out_ref, d ** -0.5)
+    if layout == "side":
+        dk, dv = pk.fp8_pools_side_by_side(torch.from_numpy(k8), torch.from_numpy(v8), "cuda")
+    else:
+        dk, dv = torch.from_numpy(k8).cuda(), torch.from_numpy(v8).cuda()
+    d_tab = torch.from_numpy(tables).cuda()
+    d_out = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    gs = sb = None
+    if share:
+        gs = torch.tensor([0, 4] + list(range(5, S + 1)), dtype=torch.int32, device="cuda")
+        sb = torch.tensor([share] + [0] * (S - 4), dtype=torch.int32, device="cuda")
+    out = pk.pa_decode_step(q.cuda(), dk, dv, kn.cuda(), vn.cuda(), d_tab,
+                            torch.from_numpy(lens_in).cuda(), d_out, new_blocks, d ** -0.5,
+                            group_start=gs, shared_blocks=sb)
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), k_ref), "K regions differ from the oracle's write"
+    assert np.array_equal(dv.cpu().numpy(), v_ref), "V regions differ from the oracle's write"
+    assert np.array_equal(d_out.cpu().numpy(), lens_out_ref)
+    got_t = d_tab.cpu().numpy()
+    for s in range(S):
+        n = (lens_out_ref[s] + B - 1) // B
+        assert np.array_equal(got_t[s, :n], t_ref[s, :n]), f"table row {s}"
+    err = np.abs(out.float().cpu().numpy().astype(np.float64) - ref)
+    _log(f"fp8 step {layout} G={G} d={d} B={B} share={share}: max|err| {err.max():.3e}")
+    assert np.isfinite(err).all() and err.max() <= TOL
 
 
 @pytest.mark.parametrize("share,B", [(False, 16), (True, 16), (True, 8), (False, 32)])
