@@ -1020,83 +1020,103 @@ __device__ __forceinline__ void mfma8_unit(const DecodeArgs& a, int G, const Uni
 // reads their slots; the next step reads them): each new token's K and V
 // rows go to its slot, every kv head, non-temporal like the slot write; a
 // given block becomes the table entry of the token's position; the
-// lengths after the step go to lens_out.  Workgroup w of nw takes
-// sequences w, w + nw, ...
+// lengths after the step go to lens_out.  The stores are spread over every
+// thread of the grid, at most one 16-byte K piece and one V element each,
+// so no thread's reduce work waits behind a run of its own stores.
 template <int D, int B>
-__device__ void step_store(const DecodeArgs& a, const int32_t* step_blk, int w, int nw) {
+__device__ void step_store(const DecodeArgs& a, const int32_t* step_blk) {
   constexpr int ROW = D * 2;
+  constexpr int KP = ROW / 16;  // 16-byte pieces of a K row
   const int H = a.num_kv_heads;
   const size_t blk_bytes = (size_t)H * B * ROW;
-  for (int s = w; s < a.num_seqs; s += nw) {
-    const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);  // position of the new token
-    const int j = L / B, r = L % B;
+  const size_t nt = (size_t)gridDim.x * blockDim.x;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto slot_of = [&](int s, int* r) {  // the new token's block and row of sequence s
+    const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);
+    *r = L % B;
     const int given = step_blk[s];
-    int32_t* entry = a.tables_w + (size_t)s * a.max_blocks + j;
-    const int blk = given >= 0 ? given : *entry;
-    if (threadIdx.x == 0) {
-      if (given >= 0) *entry = given;
-      a.lens_out[s] = L + 1;
-    }
-    const uint8_t* kn = static_cast<const uint8_t*>(a.k_new) + (size_t)s * H * ROW;
-    const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.v_new) +
-                                                           (size_t)s * H * ROW);
-    uint8_t* kb = static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) + (size_t)blk * blk_bytes;
-    uint16_t* vb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) +
-                                               (size_t)blk * blk_bytes);
-    for (int c = threadIdx.x; c < H * ROW / 16; c += blockDim.x) {  // K: [g][r][:] per head
-      const int g = c / (ROW / 16), off = (c % (ROW / 16)) * 16;
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(kn + (size_t)c * 16),
-                                  reinterpret_cast<u32x4*>(kb + ((size_t)g * B + r) * ROW + off));
-    }
-    for (int c = threadIdx.x; c < H * D; c += blockDim.x)  // V: [g][d][r] per element
-      __builtin_nontemporal_store(vn[c], vb + (size_t)c * B + r);
+    return given >= 0 ? given : a.tables_w[(size_t)s * a.max_blocks + L / B];
+  };
+  for (size_t i = t; i < (size_t)a.num_seqs * H * KP; i += nt) {  // K: [g][r][:] per head
+    const int s = (int)(i / (H * KP)), c = (int)(i % (H * KP));
+    const int g = c / KP, off = (c % KP) * 16;
+    int r;
+    const int blk = slot_of(s, &r);
+    __builtin_nontemporal_store(
+        *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(a.k_new) + (size_t)s * H * ROW +
+                                        (size_t)c * 16),
+        reinterpret_cast<u32x4*>(static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) +
+                                 (size_t)blk * blk_bytes + ((size_t)g * B + r) * ROW + off));
+  }
+  for (size_t i = t; i < (size_t)a.num_seqs * H * D; i += nt) {  // V: [g][d][r] per element
+    const int s = (int)(i / (H * D)), c = (int)(i % (H * D));
+    int r;
+    const int blk = slot_of(s, &r);
+    __builtin_nontemporal_store(
+        reinterpret_cast<const uint16_t*>(a.v_new)[(size_t)s * H * D + c],
+        reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) +
+                                    (size_t)blk * blk_bytes) + (size_t)c * B + r);
+  }
+  // table entries and lengths last: the loops above read the entries that
+  // no given block replaces, and these writes touch only the given ones
+  for (size_t s = t; s < (size_t)a.num_seqs; s += nt) {
+    const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);
+    if (step_blk[s] >= 0) a.tables_w[s * a.max_blocks + L / B] = step_blk[s];
+    a.lens_out[s] = L + 1;
   }
 }
 
 // The 8-bit pool's version: the new token's codes and scales, quantised
-// as the slot write quantises (one wave per (kv head, K or V) row), into
-// its slot of the K and V regions; table entry and length as above.
+// as the slot write quantises, into its slot of the K and V regions; table
+// entry and length as above.  One wave per (sequence, kv head, K or V) row,
+// over every wave of the grid, so no wave takes rows one after another
+// (each is a load, a wave max and a few stores); lane l takes dims 2l and
+// 2l + 1.
 template <int D, int B>
-__device__ void step_store8(const DecodeArgs& a, const int32_t* step_blk, int w, int nw) {
+__device__ void step_store8(const DecodeArgs& a, const int32_t* step_blk) {
   const int H = a.num_kv_heads;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwv = blockDim.x >> 6;
-  for (int s = w; s < a.num_seqs; s += nw) {
+  const int nwv = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * nwv + (threadIdx.x >> 6), ngw = gridDim.x * nwv;
+  for (int row = gw; row < a.num_seqs * 2 * H; row += ngw) {
+    const int s = row / (2 * H), k = row % (2 * H);
+    const bool is_v = k >= H;
+    const int g = is_v ? k - H : k;
     const int L = min(max(a.context_lens[s], 0), a.max_blocks * B - 1);  // position of the new token
     const int j = L / B, r = L % B;
     const int given = step_blk[s];
     int32_t* entry = a.tables_w + (size_t)s * a.max_blocks + j;
-    const int blk = given >= 0 ? given : *entry;
-    if (threadIdx.x == 0) {
+    const int blk = given >= 0 ? given : *entry;  // read only when nothing writes it
+    if (k == 0 && lane == 0) {
       if (given >= 0) *entry = given;
       a.lens_out[s] = L + 1;
     }
-    for (int row = wave; row < 2 * H; row += nwv) {
-      const bool is_v = row >= H;
-      const int g = is_v ? row - H : row;
-      const uint16_t* src =
-          static_cast<const uint16_t*>(is_v ? a.v_new : a.k_new) + ((size_t)s * H + g) * D;
-      uint8_t* kreg =
-          static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) + ((size_t)blk * H + g) * a.k_rstride;
-      uint8_t* vreg =
-          static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) + ((size_t)blk * H + g) * a.v_rstride;
-      float amax = 0.f;  // NaN inputs are skipped by fmaxf
-      for (int e = lane; e < D; e += 64)
-        amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)src[e] << 16)));
-      amax = wave_max(amax);
-      const __bf16 sb = static_cast<__bf16>(amax / 448.f);
-      const float scale = static_cast<float>(sb);
-      for (int e = lane; e < D; e += 64) {
-        const float x = __uint_as_float((uint32_t)src[e] << 16);
-        const uint8_t c = scale > 0.f
-                              ? static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x / scale, 0.f, 0, false) & 0xffu)
-                              : uint8_t{0};
-        __builtin_nontemporal_store(c, is_v ? vreg + (size_t)e * B + r : kreg + (size_t)r * D + e);
+    const uint8_t* src = static_cast<const uint8_t*>(is_v ? a.v_new : a.k_new) +
+                         ((size_t)s * H + g) * D * 2;
+    const uint32_t w = lane < D / 2 ? reinterpret_cast<const uint32_t*>(src)[lane] : 0u;
+    const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xffff0000u);
+    // from 0, as the slot write: NaN inputs are skipped by fmaxf
+    const float amax = wave_max(fmaxf(0.f, fmaxf(fabsf(x0), fabsf(x1))));
+    const __bf16 sb = static_cast<__bf16>(amax / 448.f);
+    const float scale = static_cast<float>(sb);
+    const uint32_t c0 = scale > 0.f ? (__builtin_amdgcn_cvt_pk_fp8_f32(x0 / scale, 0.f, 0, false) & 0xffu) : 0u;
+    const uint32_t c1 = scale > 0.f ? (__builtin_amdgcn_cvt_pk_fp8_f32(x1 / scale, 0.f, 0, false) & 0xffu) : 0u;
+    uint8_t* kreg =
+        static_cast<uint8_t*>(const_cast<void*>(a.k_pool)) + ((size_t)blk * H + g) * a.k_rstride;
+    uint8_t* vreg =
+        static_cast<uint8_t*>(const_cast<void*>(a.v_pool)) + ((size_t)blk * H + g) * a.v_rstride;
+    if (lane < D / 2) {
+      if (is_v) {
+        __builtin_nontemporal_store(static_cast<uint8_t>(c0), vreg + (size_t)(2 * lane) * B + r);
+        __builtin_nontemporal_store(static_cast<uint8_t>(c1), vreg + (size_t)(2 * lane + 1) * B + r);
+      } else {
+        __builtin_nontemporal_store(static_cast<uint16_t>(c0 | (c1 << 8)),
+                                    reinterpret_cast<uint16_t*>(kreg + (size_t)r * D) + lane);
       }
-      if (lane == 0)
-        __builtin_nontemporal_store(
-            __builtin_bit_cast(uint16_t, sb),
-            reinterpret_cast<uint16_t*>(kreg + (size_t)B * D + 16u * (r / 4) + 8u * is_v) + (r % 4));
     }
+    if (lane == 0)
+      __builtin_nontemporal_store(
+          __builtin_bit_cast(uint16_t, sb),
+          reinterpret_cast<uint16_t*>(kreg + (size_t)B * D + 16u * (r / 4) + 8u * is_v) + (r % 4));
   }
 }
 
@@ -1471,14 +1491,14 @@ __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_kernel(Decode
 template <int D, int B>
 __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_step_kernel(DecodeArgs a,
                                                                                StepBlocks nb) {
-  step_store<D, B>(a, nb.blk, blockIdx.x, gridDim.x);
+  step_store<D, B>(a, nb.blk);
   decode_reduce_body<__bf16, D>(a);
 }
 
 template <int D, int B>
 __global__ __launch_bounds__(kReduceHeads * 64) void decode_reduce_step8_kernel(DecodeArgs a,
                                                                                 StepBlocks nb) {
-  step_store8<D, B>(a, nb.blk, blockIdx.x, gridDim.x);
+  step_store8<D, B>(a, nb.blk);
   decode_reduce_body<__bf16, D>(a);
 }
 
