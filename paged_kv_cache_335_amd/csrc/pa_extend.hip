@@ -554,7 +554,13 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
   // acc[rr][nt][r] holds slot 4*grp + r of row tile rr (query first + rr*qpt
-  // + slot / G, head slot % G), dim nt*16 + col
+  // + slot / G, head slot % G), dim nt*16 + col.  The lane index goes
+  // through an opaque copy, so that the output addresses are computed here
+  // rather than before the stage loop (where the compiler would keep them
+  // in scratch and reload each behind a wait for every store issued)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int ecol = ln & 15, egrp = ln >> 4;
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     if (!live[rr]) continue;
@@ -563,17 +569,17 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
     float den[4], mr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      den[r] = lane_bcast(l_tot, 4 * grp + r);
-      mr[r] = lane_bcast(m_ref[rr], 4 * grp + r);
+      den[r] = lane_bcast(l_tot, 4 * egrp + r);
+      mr[r] = lane_bcast(m_ref[rr], 4 * egrp + r);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int slot = 4 * grp + r;
+      const int slot = 4 * egrp + r;
       const int qq = first + rr * qpt + slot / G;
       if (slot >= qpt * G || qq > last) continue;
       const size_t row = (size_t)(q0 + qq) * a.num_q_heads + g * G + slot % G;
       if (a.splits == 1) {
-        const size_t ob = row * D + col;
+        const size_t ob = row * D + ecol;
         const float inv = 1.f / den[r];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -581,8 +587,8 @@ __device__ __forceinline__ void extend_unit(const ExtendArgs& a, int G, int qpt,
       } else {
         const size_t pr = row * a.splits + chunk;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) a.part_o[pr * D + nt * 16 + col] = acc[rr][nt][r];
-        if (col == 0) {
+        for (int nt = 0; nt < NT; ++nt) a.part_o[pr * D + nt * 16 + ecol] = acc[rr][nt][r];
+        if (ecol == 0) {
           a.part_m[pr] = mr[r];
           a.part_l[pr] = den[r];
         }
