@@ -225,6 +225,39 @@ def test_fp8_step_state_and_output(pk, layout, B, G, d, share):
     assert np.isfinite(err).all() and err.max() <= TOL
 
 
+def test_fp8_step_matches_append_then_decode(pk):
+    """8-bit pools at the benchmark's batch size (256 sequences, 32/8 heads,
+    d 128, lengths up to 3000): the one-launch step against pa_kv_append then
+    pa_decode on the same inputs, side-by-side regions: identical codes,
+    scales and tables, outputs within the bar."""
+    from workloads.gen import fp8_pools_np
+    Hq, Hkv, d, B, S = 32, 8, 128, 16, 256
+    lens_in = list(np.random.default_rng(44).integers(0, 3000, S))
+    rng, tables, new_blocks, k, v, q, kn, vn, lens_in = _step_case(lens_in, Hq, Hkv, d, B, 45)
+    k8, v8 = fp8_pools_np(rng, k.shape[0], Hkv, B, d)
+    slots = np.array([(new_blocks[s] if new_blocks[s] >= 0 else tables[s, lens_in[s] // B]) * B
+                      + lens_in[s] % B for s in range(S)], np.int64)
+    k1, v1 = pk.fp8_pools_side_by_side(torch.from_numpy(k8), torch.from_numpy(v8), "cuda")
+    t1 = torch.from_numpy(tables).cuda()
+    pk.pa_kv_append(k1, v1, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda(), t1,
+                    torch.arange(S, dtype=torch.int32).cuda(), torch.from_numpy(lens_in).cuda())
+    o1 = pk.pa_decode(q.cuda(), k1, v1, t1, torch.from_numpy(lens_in + 1).cuda(), d ** -0.5)
+    k2, v2 = pk.fp8_pools_side_by_side(torch.from_numpy(k8), torch.from_numpy(v8), "cuda")
+    t2 = torch.from_numpy(tables).cuda()
+    lo = torch.empty(S, dtype=torch.int32, device="cuda")
+    o2 = pk.pa_decode_step(q.cuda(), k2, v2, kn.cuda(), vn.cuda(), t2,
+                           torch.from_numpy(lens_in).cuda(), lo, new_blocks, d ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert np.array_equal(lo.cpu().numpy(), lens_in + 1)
+    nblk = (lens_in + 1 + B - 1) // B
+    for s in range(S):
+        assert torch.equal(t1[s, :nblk[s]], t2[s, :nblk[s]])
+    err = (o1.float() - o2.float()).abs().max().item()
+    _log(f"fp8 fused vs two-call: max|diff| {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("share,B", [(False, 16), (True, 16), (True, 8), (False, 32)])
 def test_runtime_steps_with_forks(pk, share, B):
     """Prompts forked into samples (copy-on-write of partly filled tails on
